@@ -1,0 +1,269 @@
+"""CPU oracle for the INT8 KV cache: quantize-append and single-token decode attention.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The library
+(``int8_quantized_kv_quant_amd``) never imports, links or calls it, and this
+module shares no code, table or helper with the HIP path.
+
+Everything is plain numpy in float64 unless a page fixes the precision (the
+scales are float16 because the pages store them that way). It is slow and
+written to be checked by eye against the pages:
+
+* genie-ai-runtime release v0.1.0-alpha.12 ("Path I: INT8 KV cache"), the
+  "Path I series" table: one scale per (layer, position, kv head), captured by
+  a per-head conversion (#64); attention dequantizes with the scale of its
+  position and kv head (#65).
+* genie-ai-runtime release v0.1.0-alpha.11, "--int8-kv triage": a missing
+  scale must not silently become 1.0, and the scale rows are one per kv head.
+* genie-ai-runtime releases, v1.3.0 "split-K decode attention": the KV range
+  is split into blocks that each form an online-softmax partial, and a reduce
+  combines them; results equal the single-pass kernel. "Details": sliding
+  window mask, Gemma slot width (v1.2.1 "Bugs fixed").
+* Strata pull request 2698, "What it does": int8 codes with one FP16 scale per
+  64 values, the scale being the group absmax / 127; k8v32 / k32v8 quantize
+  one store only; the fp32 store is plain attention.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+  * the fp16 scale is the round-to-nearest-even fp16 value of absmax / 127;
+  * codes are computed against that stored fp16 scale, rounded half to even,
+    and clamped to [-127, 127];
+  * a group whose scale is 0 has all-zero codes;
+  * the softmax scale is a parameter (1/sqrt(head_dim) in the workloads);
+  * query head h uses kv head h // (n_q_heads / n_kv_heads);
+  * with window W > 0 the query at position L-1 sees keys p with
+    L - W <= p < L (exactly W keys once L >= W);
+  * an empty context (L = 0) yields an all-zero output row.
+The GQA mapping, the softmax scale and the window inequality are not fixed by
+the pages (parity unpinned against the pages; pinned only against this
+module's stated definition by brute force).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+CODE_MAX = 127          # symmetric int8 range used by the codes
+SCALE_DIVISOR = 127.0   # scale = group absmax / 127 (Strata PR 2698, "What it does")
+
+
+# --------------------------------------------------------------------------
+# Quantization (a1 of the hot path)
+# --------------------------------------------------------------------------
+
+def scale_from_absmax(absmax) -> np.ndarray:
+    """FP16 scale of a group from its absolute maximum: the fp16 value nearest
+    to absmax / 127 (ties to even).
+
+    Strata pull request 2698, "What it does": one FP16 scale per 64 values,
+    equal to the group absmax / 127. The float64 quotient is rounded once to
+    float16 by numpy (round-to-nearest-even)."""
+    a = np.asarray(absmax, dtype=np.float64)
+    return (a / SCALE_DIVISOR).astype(np.float16)
+
+
+def quantize_rows(x, group: int):
+    """Quantize rows of fp16 values in groups of ``group`` consecutive elements.
+
+    x: float16 [..., d] with d % group == 0.
+    Returns (codes int8 [..., d], scales float16 [..., d // group]).
+
+    Per group: a = max |x_i|; s = scale_from_absmax(a); c_i = the integer
+    nearest to x_i / s (ties to even) clamped to [-127, 127]; c = 0 where s = 0.
+    genie v0.1.0-alpha.12 "Path I series" (#64, per-head conversion and scale
+    capture) with group == head_dim; Strata PR 2698 "What it does" with
+    group == 64."""
+    x = np.asarray(x, dtype=np.float16)
+    d = x.shape[-1]
+    if d % group:
+        raise ValueError("head_dim must be a multiple of the scale group")
+    xg = x.astype(np.float64).reshape(x.shape[:-1] + (d // group, group))
+    a = np.abs(xg).max(axis=-1)
+    s16 = scale_from_absmax(a)
+    s = s16.astype(np.float64)[..., None]
+    safe = np.where(s > 0.0, s, 1.0)
+    q = np.where(s > 0.0, xg / safe, 0.0)
+    c = np.clip(np.rint(q), -CODE_MAX, CODE_MAX).astype(np.int8)
+    return c.reshape(x.shape), s16
+
+
+def dequantize_rows(codes, scales, group: int) -> np.ndarray:
+    """x_hat = code * scale in float64 (exact: an 8-bit integer times an fp16).
+
+    genie v0.1.0-alpha.12 "Path I series" (#65): attention dequantizes each
+    position with the scale stored for that position and kv head."""
+    c = np.asarray(codes).astype(np.float64)
+    d = c.shape[-1]
+    cg = c.reshape(c.shape[:-1] + (d // group, group))
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)[..., None]
+    return (cg * s).reshape(c.shape)
+
+
+class Cache:
+    """Logical KV cache of one layer: per store either int8 codes + fp16 scales
+    or fp32 values, indexed [seq][position][kv head][element] (positions
+    major, as the genie pool indexes its scales by position * n_kv_heads +
+    kv head, "Path I series" #65).
+
+    Strata PR 2698 "What it does": k8v8 quantizes both stores, k8v32 only K,
+    k32v8 only V; an fp32 store keeps the values themselves."""
+
+    def __init__(self, batch, max_ctx, n_kv_heads, head_dim, group,
+                 k_dtype="int8", v_dtype="int8"):
+        self.batch, self.max_ctx = batch, max_ctx
+        self.n_kv_heads, self.head_dim, self.group = n_kv_heads, head_dim, group
+        self.dtypes = {"k": k_dtype, "v": v_dtype}
+        self.data, self.scales = {}, {}
+        for s in ("k", "v"):
+            shape = (batch, max_ctx, n_kv_heads, head_dim)
+            if self.dtypes[s] == "int8":
+                self.data[s] = np.zeros(shape, dtype=np.int8)
+                self.scales[s] = np.zeros(shape[:-1] + (head_dim // group,), dtype=np.float16)
+            elif self.dtypes[s] == "fp32":
+                self.data[s] = np.zeros(shape, dtype=np.float32)
+                self.scales[s] = None
+            else:
+                raise ValueError(self.dtypes[s])
+
+    def append(self, k_new, v_new, start_pos):
+        """Quantize-append: rows k_new/v_new float16 [batch][n_tok][n_kv][d]
+        land at positions start_pos[b] .. start_pos[b] + n_tok - 1.
+
+        int8 stores get codes + scales from quantize_rows; fp32 stores get the
+        fp16 values widened exactly (Strata PR 2698: k8v32 / k32v8 quantize
+        one store only)."""
+        n_tok = k_new.shape[1]
+        for s, new in (("k", k_new), ("v", v_new)):
+            new = np.asarray(new, dtype=np.float16)
+            for b in range(self.batch):
+                p0 = int(start_pos[b])
+                if self.dtypes[s] == "int8":
+                    c, sc = quantize_rows(new[b], self.group)
+                    self.data[s][b, p0:p0 + n_tok] = c
+                    self.scales[s][b, p0:p0 + n_tok] = sc
+                else:
+                    self.data[s][b, p0:p0 + n_tok] = new[b].astype(np.float32)
+
+    def values(self, s, b, lo, hi, h):
+        """float64 [hi-lo][d]: dequantized (or widened) rows of store s."""
+        if self.dtypes[s] == "int8":
+            return dequantize_rows(self.data[s][b, lo:hi, h], self.scales[s][b, lo:hi, h], self.group)
+        return self.data[s][b, lo:hi, h].astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Decode attention (a3 + a4 of the hot path)
+# --------------------------------------------------------------------------
+
+def attended_range(L: int, window: int):
+    """Positions [lo, L) that the query at position L-1 attends to.
+    genie releases v1.3.0 "Details" (sliding-window mask) and v1.1.0 (512-token
+    sliding window); the inequality L - W <= p is this oracle's reading."""
+    lo = max(0, L - window) if window > 0 else 0
+    return lo, L
+
+
+def attend_one(q, K, V, sm_scale: float) -> np.ndarray:
+    """Softmax attention of query rows q [G][d] over keys K [n][d] and values
+    V [n][d], all float64: out = softmax(sm_scale * q K^T) V, two-pass
+    (max, then exp and sum)."""
+    z = sm_scale * (np.asarray(q, np.float64) @ K.T)
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return (e @ V) / e.sum(axis=1, keepdims=True)
+
+
+def attend(q, cache: Cache, seq_lens, window: int, sm_scale: float, heads=None) -> np.ndarray:
+    """Decode attention of q float16 [batch][n_q][d] over the cache.
+
+    Query head h reads kv head h // G with G = n_q / n_kv (GQA, this oracle's
+    reading). Returns float64 [batch][n_q][d]; rows with an empty range are 0.
+    ``heads`` optionally restricts the work to a list of (b, h_q) pairs (the
+    other rows are left at 0)."""
+    q = np.asarray(q, dtype=np.float16)
+    B, Hq, d = q.shape
+    Hkv = cache.n_kv_heads
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    want = None if heads is None else set((int(b), int(h)) for b, h in heads)
+    for b in range(B):
+        lo, hi = attended_range(int(seq_lens[b]), window)
+        if hi <= lo:
+            continue
+        for hk in range(Hkv):
+            hq = [h for h in range(hk * G, (hk + 1) * G) if want is None or (b, h) in want]
+            if not hq:
+                continue
+            K = cache.values("k", b, lo, hi, hk)
+            V = cache.values("v", b, lo, hi, hk)
+            out[b, hq] = attend_one(q[b, hq].astype(np.float64), K, V, sm_scale)
+    return out
+
+
+def split_partials(q, K, V, sm_scale: float, bounds):
+    """Online-softmax partials of one (query group, kv head) over the position
+    ranges [bounds[i], bounds[i+1]) -- genie releases v1.3.0: each split block
+    forms an online-softmax partial.
+
+    Returns m [S][G] (max score), l [S][G] (sum of exp(z - m)), O [S][G][d]
+    (sum of exp(z - m) * v); an empty split has m = -inf, l = 0, O = 0."""
+    q = np.asarray(q, np.float64)
+    G, d = q.shape
+    S = len(bounds) - 1
+    m = np.full((S, G), -np.inf)
+    l = np.zeros((S, G))
+    O = np.zeros((S, G, d))
+    for s in range(S):
+        a, b = bounds[s], bounds[s + 1]
+        if b <= a:
+            continue
+        z = sm_scale * (q @ K[a:b].T)
+        m[s] = z.max(axis=1)
+        e = np.exp(z - m[s][:, None])
+        l[s] = e.sum(axis=1)
+        O[s] = e @ V[a:b]
+    return m, l, O
+
+
+def combine_partials(m, l, O) -> np.ndarray:
+    """Reduce of the split partials (genie releases v1.3.0: a reduce kernel
+    combines them per head): M = max_s m_s, w_s = exp(m_s - M),
+    out = sum_s w_s O_s / sum_s w_s l_s. Empty splits weigh 0; all-empty -> 0."""
+    M = m.max(axis=0)
+    out = np.zeros(O.shape[1:])
+    ok = np.isfinite(M)
+    if not ok.any():
+        return out
+    w = np.where(np.isfinite(m), np.exp(m - np.where(ok, M, 0.0)[None, :]), 0.0)
+    num = np.einsum("sg,sgd->gd", w, O)
+    den = (w * l).sum(axis=0)
+    out[ok] = num[ok] / den[ok][:, None]
+    return out
+
+
+# --------------------------------------------------------------------------
+# Cache sizes (the pages' worked byte counts)
+# --------------------------------------------------------------------------
+
+_DTYPE_BYTES = {"int8": 1, "fp16": 2, "fp32": 4}
+
+
+def cell_bytes(n_kv_heads: int, head_dim: int, group: int, dtype: str,
+               scale_bytes: int = 2) -> int:
+    """Bytes one store spends on one position of one layer (all kv heads):
+    values plus, for int8, one scale per group. Strata PR 2698 "What it does"
+    counts 528 B per cell for int8 + FP16 group-64 scales against 2048 B for
+    FP32 at head_dim 256."""
+    b = n_kv_heads * head_dim * _DTYPE_BYTES[dtype]
+    if dtype == "int8":
+        b += n_kv_heads * (head_dim // group) * scale_bytes
+    return b
+
+
+def pool_bytes(n_layers: int, ctx: int, n_kv_heads: int, head_dim: int, dtype: str,
+               scale_bytes: int = 2):
+    """(body, scales) bytes of a K+V pool with one scale per (layer, position,
+    kv head) when dtype is int8 -- genie v0.1.0-alpha.12 "Headline result"
+    (KV pool memory) and "Path I series" #63 (separate scales region)."""
+    body = 2 * n_layers * ctx * n_kv_heads * head_dim * _DTYPE_BYTES[dtype]
+    scales = 2 * n_layers * ctx * n_kv_heads * scale_bytes if dtype == "int8" else 0
+    return body, scales
