@@ -1,0 +1,187 @@
+/*
+ * kvq.h -- C ABI of the INT8 KV-cache decode path for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements one decode step of attention over a KV cache whose
+ * K and V stores hold int8 codes with FP16 scales (or, per store, fp32 values):
+ *
+ *   kv_quant_append        quantize new K/V rows and write them into the cache
+ *   kv_decode_attn_splitk  split-K partial attention of one query token per
+ *                          sequence (online-softmax partials per split)
+ *   kv_decode_reduce       combine the split partials into the fp16 output
+ *   kvq_plan               host-only choice of the split count and workspace
+ *
+ * Sources of the method (web pages; cited by title and section):
+ *   [G12]  genie-ai-runtime release v0.1.0-alpha.12, "Path I: INT8 KV cache",
+ *          table "Path I series": a separate scales region in the KV pool (#63),
+ *          per-head conversion with scale capture (#64), attention dequantizes
+ *          each position with its (position, kv head) scale (#65).
+ *   [G11]  genie-ai-runtime release v0.1.0-alpha.11, "--int8-kv triage": a null
+ *          scale pointer silently became scale 1.0; the conversion ran with one
+ *          row instead of one per kv head.
+ *   [G130] genie-ai-runtime releases, v1.3.0 "split-K decode attention" and its
+ *          "Details": the KV range of each head is split over blocks, each block
+ *          forms an online-softmax partial, a reduce kernel combines them; the
+ *          split count is fixed on the host while positions come from the
+ *          device; sliding-window mask and slot width are honoured.
+ *   [G121] genie-ai-runtime releases, v1.2.1 "Bugs fixed": head_dim 256 stored
+ *          in a 512-wide cache slot; strides must come from the slot width.
+ *   [S2698] Strata pull request 2698 (int8 K/V cache), "What it does": int8
+ *          codes with one FP16 scale per 64 values equal to the group absmax /
+ *          127; head_dim must be a multiple of 64 or the host refuses; k8v32 and
+ *          k32v8 quantize one store only; the fp32 store is plain attention.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are caller-owned device memory unless stated; the library
+ *     allocates nothing, keeps no state between calls and never synchronizes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it and the call returns at once.
+ *   - Arguments are validated first; on any error a negative kvq_status is
+ *     returned and nothing is enqueued. A launch failure returns KVQ_ERR_HIP.
+ *   - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *   - Device-side preconditions that cannot be checked without a sync are
+ *     listed per call; violating them never makes a kernel read or write
+ *     outside the buffers described by the layout.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = -1,        /* a required pointer is NULL (scales of an int8 store included, [G11]) */
+  KVQ_ERR_SHAPE = -2,       /* inconsistent sizes or strides */
+  KVQ_ERR_UNSUPPORTED = -3, /* a valid request this build does not implement (e.g. head_dim 96) */
+  KVQ_ERR_ALIGN = -4,       /* a pointer or stride breaks the alignment the loads need */
+  KVQ_ERR_WORKSPACE = -5,   /* workspace missing or smaller than kvq_plan_t.ws_bytes */
+  KVQ_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+} kvq_status;
+
+/* Store element types ([S2698]: fp32 = the unquantized store). */
+enum { KVQ_STORE_INT8 = 1, KVQ_STORE_FP32 = 2 };
+
+/* Layout of one layer's KV cache.
+ *
+ * Each store (K and V) is an array of rows; the row of (sequence b, position p,
+ * kv head h) starts at element  b*s_seq + p*s_pos + h*s_head  and holds
+ * head_dim contiguous elements (int8 codes or fp32 values). A row may sit in a
+ * wider slot (slot_dim >= head_dim, [G121]); elements [head_dim, slot_dim) are
+ * never read or written. K and V use the same element strides.
+ *
+ * Each int8 store has an fp16 scale array: the scales of row (b, p, h) start at
+ * element  b*ss_seq + p*ss_pos + h*ss_head  and are head_dim/scale_group
+ * consecutive values, scale j covering elements [j*g, (j+1)*g) of the row.
+ * scale_group == head_dim gives one scale per (position, kv head) [G12 #64];
+ * scale_group == 64 gives one scale per 64 values [S2698]. Both scale arrays use
+ * the same strides. An fp32 store has no scales.
+ *
+ * Supported: head_dim in {64, 128, 256}; scale_group in {64, head_dim}; every
+ * combination of k_dtype/v_dtype in {KVQ_STORE_INT8, KVQ_STORE_FP32}
+ * (k8v8, k8v32, k32v8, k32v32). Row offsets in bytes must be multiples of 16;
+ * scale-row offsets in bytes multiples of 2*(head_dim/scale_group); the byte
+ * extent of one sequence (max_ctx positions) must stay below 2^31.
+ */
+typedef struct {
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t slot_dim;
+  int32_t k_dtype;
+  int32_t v_dtype;
+  int32_t scale_group;
+  int64_t max_ctx;              /* positions allocated per sequence */
+  int64_t s_seq, s_pos, s_head; /* element strides of the stores */
+  int64_t ss_seq, ss_pos, ss_head; /* element strides of the fp16 scale arrays */
+} kvq_layout;
+
+/* Split plan of one decode step ([G130]: split count fixed on the host).
+ * Split s of a sequence with context L covers positions
+ *   [lo + s*chunk, lo + (s+1)*chunk)  clipped to L, where lo = max(0, L - window)
+ * if window > 0 else 0; the last split (s = n_splits-1) runs to L, so a context
+ * longer than the planned one is still covered. ws_bytes is the workspace that
+ * kv_decode_attn_splitk writes and kv_decode_reduce reads. */
+typedef struct {
+  int32_t n_splits;
+  int32_t chunk;       /* positions per split, a multiple of 32 */
+  int64_t ws_bytes;
+} kvq_plan_t;
+
+/* kvq_plan -- host only, no device call.
+ * Chooses n_splits/chunk for `batch` sequences of at most `max_seq_len`
+ * positions (window > 0 limits the attended range to `window` keys) on a device
+ * with `n_cu` compute units, so that the partial kernel's grid covers the chip
+ * while the partial workspace stays a small fraction of the KV bytes read.
+ * Fewer than 64 attended positions always get a single split ([G130] keeps a
+ * single-block kernel below 64 tokens). Writes *out; returns KVQ_OK or an error
+ * for invalid layout/sizes. */
+int kvq_plan(const kvq_layout* layout, int32_t batch, int32_t n_q_heads,
+             int32_t max_seq_len, int32_t window, int32_t n_cu, kvq_plan_t* out);
+
+/* kv_quant_append -- quantize n_tok new K and V rows per sequence into the cache.
+ * [G12 #64], [S2698 "What it does"].
+ *   k_new, v_new  fp16 [batch][n_tok][n_kv_heads][head_dim], contiguous, 16-byte aligned.
+ *   d_start_pos   device int32 [batch]: row t of sequence b lands at position
+ *                 d_start_pos[b] + t.
+ *   k_store/v_store, k_scales/v_scales  as described by `layout`; scales must be
+ *                 non-NULL for an int8 store and are ignored for an fp32 store.
+ * Per group of scale_group values x of a row: a = max|x|; the fp16 scale is the
+ * round-to-nearest-even fp16 value of a/127 (fp32 division, correctly rounded);
+ * code = clamp(round-half-even(x / scale), -127, 127), 0 when the scale is 0.
+ * An fp32 store receives the fp16 values widened exactly.
+ * Device precondition: 0 <= d_start_pos[b] and d_start_pos[b] + n_tok <= max_ctx;
+ * rows that would land outside [0, max_ctx) are not written. */
+int kv_quant_append(const kvq_layout* layout, void* k_store, void* v_store,
+                    uint16_t* k_scales, uint16_t* v_scales,
+                    const uint16_t* k_new, const uint16_t* v_new,
+                    const int32_t* d_start_pos, int32_t batch, int32_t n_tok,
+                    void* stream);
+
+/* kv_decode_attn_splitk -- split-K partials of single-token decode attention.
+ * [G130 "split-K decode attention"], [G12 #65], [S2698].
+ *   q           fp16 [batch][n_q_heads][head_dim], contiguous, 16-byte aligned.
+ *               Query head hq reads kv head hq / (n_q_heads / n_kv_heads).
+ *   d_seq_lens  device int32 [batch]: context length L_b (positions 0..L_b-1 are
+ *               in the cache, the query token's own K/V included).
+ *   window      0 = attend to all L_b positions; > 0 = only the last `window`.
+ *   sm_scale    softmax scale applied to q.k (e.g. 1/sqrt(head_dim)).
+ *   plan        from kvq_plan for at least this batch, n_q_heads and window.
+ *   ws          device workspace of at least plan->ws_bytes bytes, 16-byte aligned;
+ *               written here, read by kv_decode_reduce on the same stream.
+ * Device precondition: 0 <= d_seq_lens[b] <= max_ctx (larger values are clamped
+ * to max_ctx). Keys are dequantized as code * scale; the fp32 store is read as
+ * the fp16 values kv_quant_append widened into it. */
+int kv_decode_attn_splitk(const kvq_layout* layout,
+                          const void* k_store, const void* v_store,
+                          const uint16_t* k_scales, const uint16_t* v_scales,
+                          const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                          const int32_t* d_seq_lens, int32_t window, float sm_scale,
+                          const kvq_plan_t* plan, void* ws, int64_t ws_bytes,
+                          void* stream);
+
+/* kv_decode_reduce -- combine the partials of kv_decode_attn_splitk.
+ * [G130: "a reduce kernel combines them"]. For each (b, hq): with split maxima
+ * m_s, sums l_s and unnormalized outputs O_s, M = max m_s, w_s = exp(m_s - M),
+ * out = sum_s w_s O_s / sum_s w_s l_s, rounded to fp16 (nearest even).
+ * A sequence with no attended position (L_b = 0) gets an all-zero row.
+ *   out  fp16 [batch][n_q_heads][head_dim], contiguous, 16-byte aligned.
+ * The other arguments must equal those of the preceding kv_decode_attn_splitk. */
+int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,
+                     const int32_t* d_seq_lens, int32_t batch, int32_t n_q_heads,
+                     int32_t window, const kvq_plan_t* plan, uint16_t* out,
+                     void* stream);
+
+/* Text for a kvq_status value (static storage). */
+const char* kvq_status_string(int status);
+
+/* Library version as (major << 16) | (minor << 8) | patch. */
+int kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

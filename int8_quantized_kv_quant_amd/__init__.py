@@ -1,0 +1,249 @@
+"""Python binding of libkvq (include/kvq.h): INT8 KV-cache decode attention on MI355X.
+
+Argument marshalling only. Every step of the decode path -- quantize-append,
+split-K partials, reduce -- runs in the HIP kernels of ``libkvq.so``; PyTorch is
+used for device memory and the current stream. If the library has not been
+built, importing works but every call raises ``KvqLibraryMissing``: there is
+no CPU fallback.
+
+Build with ``python -m int8_quantized_kv_quant_amd.build_lib``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+__all__ = [
+    "KVQ_STORE_INT8", "KVQ_STORE_FP32", "KvqError", "KvqLibraryMissing", "Layout", "Plan",
+    "lib_path", "load", "kvq_version", "kvq_status_string", "kvq_plan", "kv_quant_append",
+    "kv_decode_attn_splitk", "kv_decode_reduce", "make_layout", "alloc_cache", "decode",
+    "EXPORTED_SYMBOLS",
+]
+
+KVQ_STORE_INT8 = 1
+KVQ_STORE_FP32 = 2
+_DT = {"int8": KVQ_STORE_INT8, "fp32": KVQ_STORE_FP32}
+
+EXPORTED_SYMBOLS = ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_decode_reduce",
+                    "kvq_status_string", "kvq_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libkvq.so")
+
+
+class KvqLibraryMissing(RuntimeError):
+    pass
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {kvq_status_string(status)} (status {status})")
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("slot_dim", ctypes.c_int32), ("k_dtype", ctypes.c_int32),
+                ("v_dtype", ctypes.c_int32), ("scale_group", ctypes.c_int32),
+                ("max_ctx", ctypes.c_int64),
+                ("s_seq", ctypes.c_int64), ("s_pos", ctypes.c_int64), ("s_head", ctypes.c_int64),
+                ("ss_seq", ctypes.c_int64), ("ss_pos", ctypes.c_int64), ("ss_head", ctypes.c_int64)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("n_splits", ctypes.c_int32), ("chunk", ctypes.c_int32), ("ws_bytes", ctypes.c_int64)]
+
+
+@dataclass(frozen=True)
+class Layout:
+    """Mirror of kvq_layout. Strides are in elements (see include/kvq.h)."""
+    n_kv_heads: int
+    head_dim: int
+    slot_dim: int
+    k_dtype: int
+    v_dtype: int
+    scale_group: int
+    max_ctx: int
+    s_seq: int
+    s_pos: int
+    s_head: int
+    ss_seq: int
+    ss_pos: int
+    ss_head: int
+
+    def c(self) -> _Layout:
+        return _Layout(*[getattr(self, f[0]) for f in _Layout._fields_])
+
+    @property
+    def n_groups(self) -> int:
+        return self.head_dim // self.scale_group
+
+
+@dataclass(frozen=True)
+class Plan:
+    n_splits: int
+    chunk: int
+    ws_bytes: int
+
+    def c(self) -> _Plan:
+        return _Plan(self.n_splits, self.chunk, self.ws_bytes)
+
+
+_lib = None
+
+
+def load():
+    """Load libkvq.so (once). Raises KvqLibraryMissing if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = lib_path()
+    if not os.path.exists(p):
+        raise KvqLibraryMissing(f"{p} not built; run `python -m int8_quantized_kv_quant_amd.build_lib`")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    LP, PP = ctypes.POINTER(_Layout), ctypes.POINTER(_Plan)
+    lib.kvq_plan.argtypes = [LP, i32, i32, i32, i32, i32, PP]
+    lib.kv_quant_append.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
+    lib.kv_decode_attn_splitk.argtypes = [LP, vp, vp, vp, vp, vp, i32, i32, vp, i32, f32, PP, vp, i64, vp]
+    lib.kv_decode_reduce.argtypes = [LP, vp, i64, vp, i32, i32, i32, PP, vp, vp]
+    lib.kvq_status_string.argtypes = [ctypes.c_int]
+    lib.kvq_status_string.restype = ctypes.c_char_p
+    lib.kvq_version.argtypes = []
+    for fn in ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_decode_reduce", "kvq_version"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def kvq_status_string(status: int) -> str:
+    return load().kvq_status_string(int(status)).decode()
+
+
+def kvq_version() -> int:
+    return load().kvq_version()
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise KvqError(fn, st)
+
+
+def _ptr(x) -> int | None:
+    """Device/host address of a tensor (or an int address, or None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        if not torch.cuda.is_available():
+            return None
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def kvq_plan(layout: Layout, batch: int, n_q_heads: int, max_seq_len: int, window: int,
+             n_cu: int) -> Plan:
+    out = _Plan()
+    _check("kvq_plan", load().kvq_plan(ctypes.byref(layout.c()), batch, n_q_heads, max_seq_len,
+                                       window, n_cu, ctypes.byref(out)))
+    return Plan(out.n_splits, out.chunk, out.ws_bytes)
+
+
+def kv_quant_append(layout: Layout, k_store, v_store, k_scales, v_scales, k_new, v_new, start_pos,
+                    batch: int, n_tok: int, stream=None) -> None:
+    _check("kv_quant_append", load().kv_quant_append(
+        ctypes.byref(layout.c()), _ptr(k_store), _ptr(v_store), _ptr(k_scales), _ptr(v_scales),
+        _ptr(k_new), _ptr(v_new), _ptr(start_pos), batch, n_tok, _stream(stream)))
+
+
+def kv_decode_attn_splitk(layout: Layout, k_store, v_store, k_scales, v_scales, q, batch: int,
+                          n_q_heads: int, seq_lens, window: int, sm_scale: float, plan: Plan,
+                          ws, ws_bytes: int, stream=None) -> None:
+    _check("kv_decode_attn_splitk", load().kv_decode_attn_splitk(
+        ctypes.byref(layout.c()), _ptr(k_store), _ptr(v_store), _ptr(k_scales), _ptr(v_scales),
+        _ptr(q), batch, n_q_heads, _ptr(seq_lens), window, sm_scale, ctypes.byref(plan.c()),
+        _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def kv_decode_reduce(layout: Layout, ws, ws_bytes: int, seq_lens, batch: int, n_q_heads: int,
+                     window: int, plan: Plan, out, stream=None) -> None:
+    _check("kv_decode_reduce", load().kv_decode_reduce(
+        ctypes.byref(layout.c()), _ptr(ws), ws_bytes, _ptr(seq_lens), batch, n_q_heads, window,
+        ctypes.byref(plan.c()), _ptr(out), _stream(stream)))
+
+
+# --------------------------------------------------------------------------
+# Allocation helpers (memory plumbing; no arithmetic of the method)
+# --------------------------------------------------------------------------
+
+def make_layout(n_kv_heads: int, head_dim: int, max_ctx: int, batch: int = 1, slot_dim: int | None = None,
+                k_dtype: str = "int8", v_dtype: str = "int8", scale_group: int | None = None,
+                order: str = "pos") -> Layout:
+    """Dense cache layout. order="pos": [seq][pos][head][slot] (positions major,
+    as the genie pool indexes its scales); order="head": [seq][head][pos][slot]."""
+    slot = slot_dim or head_dim
+    g = scale_group or head_dim
+    ng = head_dim // g
+    if order == "pos":
+        s_head, s_pos, s_seq = slot, n_kv_heads * slot, max_ctx * n_kv_heads * slot
+        ss_head, ss_pos, ss_seq = ng, n_kv_heads * ng, max_ctx * n_kv_heads * ng
+    elif order == "head":
+        s_pos, s_head, s_seq = slot, max_ctx * slot, n_kv_heads * max_ctx * slot
+        ss_pos, ss_head, ss_seq = ng, max_ctx * ng, n_kv_heads * max_ctx * ng
+    else:
+        raise ValueError(order)
+    return Layout(n_kv_heads, head_dim, slot, _DT[k_dtype], _DT[v_dtype], g, max_ctx,
+                  s_seq, s_pos, s_head, ss_seq, ss_pos, ss_head)
+
+
+def alloc_cache(layout: Layout, batch: int, device="cuda", fill=0):
+    """Torch tensors for a dense cache of `batch` sequences: dict with k, v
+    (int8 or float32, flat) and k_scales, v_scales (float16 flat or None)."""
+    import torch
+    n = batch * layout.s_seq
+    ns = batch * layout.ss_seq
+    out = {}
+    for s, dt in (("k", layout.k_dtype), ("v", layout.v_dtype)):
+        if dt == KVQ_STORE_INT8:
+            out[s] = torch.full((n,), fill, dtype=torch.int8, device=device)
+            out[s + "_scales"] = torch.zeros((ns,), dtype=torch.float16, device=device)
+        else:
+            out[s] = torch.full((n,), fill, dtype=torch.float32, device=device)
+            out[s + "_scales"] = None
+    return out
+
+
+def decode(layout: Layout, cache: dict, q, seq_lens, window: int, sm_scale: float | None = None,
+           plan: Plan | None = None, ws=None, out=None, n_cu: int | None = None, stream=None):
+    """One decode step over an already-filled cache: kv_decode_attn_splitk then
+    kv_decode_reduce on the current stream. q: fp16 [batch][n_q][head_dim] on the
+    device; seq_lens: int32 [batch] on the device. Returns the fp16 output."""
+    import torch
+    batch, n_q, d = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if plan is None:
+        if n_cu is None:
+            n_cu = torch.cuda.get_device_properties(q.device).multi_processor_count
+        plan = kvq_plan(layout, batch, n_q, layout.max_ctx, window, n_cu)
+    if ws is None:
+        ws = torch.empty(max(plan.ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((batch, n_q, d), dtype=torch.float16, device=q.device)
+    kv_decode_attn_splitk(layout, cache["k"], cache["v"], cache["k_scales"], cache["v_scales"], q,
+                          batch, n_q, seq_lens, window, sm_scale, plan, ws, ws.numel(), stream)
+    kv_decode_reduce(layout, ws, ws.numel(), seq_lens, batch, n_q, window, plan, out, stream)
+    return out

@@ -1,0 +1,125 @@
+// kv_quant_append: quantize new K/V rows into the cache.
+//
+// genie-ai-runtime v0.1.0-alpha.12, "Path I series" #64: per-head conversion
+// with scale capture (one scale per position and kv head). Strata PR 2698,
+// "What it does": one FP16 scale per 64 values equal to the group absmax / 127;
+// k8v32 / k32v8 quantize only one of the stores.
+//
+// Work mapping: each lane owns 4 consecutive elements of a row, so a row of
+// head_dim values spans head_dim/4 lanes (16, 32 or 64) and a wavefront carries
+// 4, 2 or 1 rows. A 64-value scale group is 16 lanes; a per-row group is the
+// whole row. The group absmax is a butterfly max over those lanes.
+//
+// Arithmetic (bit-exact with the CPU definition): absmax is exact on the fp16
+// bit patterns; scale = fp16_rne(a / 127.0f) with a correctly rounded fp32
+// division; code = clamp(rint(x / scale), -127, 127) with a correctly rounded
+// fp32 division (x and scale are fp16, so the fp32 quotient rounds to the same
+// integer as the exact quotient, ties to even); code 0 where scale == 0.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+struct AppendStore {
+  void* store;
+  uint16_t* scales;
+  const uint16_t* src;
+  int32_t is_int8;
+  int32_t pad_;
+};
+
+struct AppendArgs {
+  AppendStore st[2];  // [0] = K, [1] = V
+  const int32_t* start_pos;
+  int64_t s_seq, s_pos, s_head;
+  int64_t ss_seq, ss_pos, ss_head;
+  int64_t max_ctx;
+  int32_t n_kv, n_tok, rows;  // rows = batch * n_tok * n_kv
+  int32_t group_lanes;        // lanes sharing one scale (power of two)
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void kvq_append_kernel(AppendArgs a) {
+  constexpr int TPR = D / 4;      // lanes per row
+  constexpr int RPB = 256 / TPR;  // rows per block
+  const AppendStore S = a.st[blockIdx.y];
+  const int lr = threadIdx.x % TPR;
+  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
+  // Rows, and so scale groups, never straddle this exit: whole groups leave together.
+  if (row >= a.rows) return;
+  const int h = row % a.n_kv;
+  const int t = (row / a.n_kv) % a.n_tok;
+  const int b = row / (a.n_kv * a.n_tok);
+  const int64_t pos = (int64_t)a.start_pos[b] + t;
+  if (pos < 0 || pos >= a.max_ctx) return;
+
+  const u32x2 raw = *reinterpret_cast<const u32x2*>(S.src + (int64_t)row * D + 4 * lr);
+  const uint32_t hb[4] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16};
+  const int64_t row_off = b * a.s_seq + pos * a.s_pos + h * a.s_head;
+
+  if (!S.is_int8) {
+    // fp32 store: the fp16 values widened exactly.
+    float4 v = {h_bits_to_f32(hb[0]), h_bits_to_f32(hb[1]), h_bits_to_f32(hb[2]), h_bits_to_f32(hb[3])};
+    *reinterpret_cast<float4*>(static_cast<float*>(S.store) + row_off + 4 * lr) = v;
+    return;
+  }
+
+  // |x| ordering of finite fp16 values equals the integer ordering of the
+  // bit patterns with the sign cleared.
+  uint32_t amax = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) amax = max(amax, hb[e] & 0x7fffu);
+  for (int o = 1; o < a.group_lanes; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
+
+  const float absmax = h_bits_to_f32(amax);
+  const f16 scale_h = (f16)(absmax / 127.0f);  // fp32 IEEE division, then fp16 RNE
+  const float scale = (float)scale_h;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float c = 0.0f;
+    if (scale > 0.0f) {
+      c = __builtin_rintf(h_bits_to_f32(hb[e]) / scale);
+      c = fminf(fmaxf(c, -127.0f), 127.0f);
+    }
+    packed |= ((uint32_t)(int32_t)c & 0xffu) << (8 * e);
+  }
+  *reinterpret_cast<uint32_t*>(static_cast<int8_t*>(S.store) + row_off + 4 * lr) = packed;
+  if (lr % a.group_lanes == 0) {
+    const int64_t soff = b * a.ss_seq + pos * a.ss_pos + h * a.ss_head + lr / a.group_lanes;
+    S.scales[soff] = __builtin_bit_cast(uint16_t, scale_h);
+  }
+}
+
+int launch_append(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k_scales,
+                  uint16_t* v_scales, const uint16_t* k_new, const uint16_t* v_new,
+                  const int32_t* d_start_pos, int32_t batch, int32_t n_tok, void* stream) {
+  AppendArgs a{};
+  a.st[0] = {k_store, k_scales, k_new, L.k_dtype == KVQ_STORE_INT8, 0};
+  a.st[1] = {v_store, v_scales, v_new, L.v_dtype == KVQ_STORE_INT8, 0};
+  a.start_pos = d_start_pos;
+  a.s_seq = L.s_seq;
+  a.s_pos = L.s_pos;
+  a.s_head = L.s_head;
+  a.ss_seq = L.ss_seq;
+  a.ss_pos = L.ss_pos;
+  a.ss_head = L.ss_head;
+  a.max_ctx = L.max_ctx;
+  a.n_kv = L.n_kv_heads;
+  a.n_tok = n_tok;
+  a.rows = batch * n_tok * L.n_kv_heads;
+  const int tpr = L.head_dim / 4;
+  a.group_lanes = (L.scale_group == 64) ? 16 : tpr;
+  const int rpb = 256 / tpr;
+  dim3 grid((a.rows + rpb - 1) / rpb, 2);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (L.head_dim) {
+    case 64: hipLaunchKernelGGL(kvq_append_kernel<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(kvq_append_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(kvq_append_kernel<256>, grid, dim3(256), 0, s, a); break;
+    default: return KVQ_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace kvq

@@ -1,0 +1,91 @@
+// Device helpers for the gfx950 kernels of libkvq: vector types, bounds-checked
+// buffer loads and the int8 -> fp16 operand construction used by the MFMA path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Resource word 3 of a raw (stride 0) buffer on gfx9-class GPUs: 32-bit data
+// format, bounds checked against num_records.
+constexpr uint32_t kBufWord3 = 0x00020000u;
+// A byte offset that is outside every buffer this library builds (their
+// num_records never exceed INT_MAX): loads from it return zeros.
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufWord3);
+}
+
+__device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x2 ld64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ float h_bits_to_f32(uint32_t bits) {
+  return (float)__builtin_bit_cast(f16, (uint16_t)bits);
+}
+
+// int8 codes -> fp16 without arithmetic. A code c (two's complement byte) XOR
+// 0x80 is the unsigned byte c + 128; placing 0x64 above it gives the fp16 bit
+// pattern of 1024 + (c + 128) = 1152 + c, exact for every byte value.
+constexpr uint32_t kCodeFlip = 0x80808080u;
+constexpr float kCodeBias = 1152.0f;
+// Bytes 0 and 1 of a flipped dword as two biased fp16 values.
+__device__ __forceinline__ uint32_t biased_h2_lo(uint32_t flipped) {
+  return __builtin_amdgcn_perm(0x64646464u, flipped, 0x04010400u);
+}
+// Bytes 2 and 3 of a flipped dword as two biased fp16 values.
+__device__ __forceinline__ uint32_t biased_h2_hi(uint32_t flipped) {
+  return __builtin_amdgcn_perm(0x64646464u, flipped, 0x04030402u);
+}
+// Interleave bytes 0,1 (sel01) or 2,3 (sel23) of two dwords: [b.x, a.x, b.y, a.y].
+__device__ __forceinline__ uint32_t zip_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(a, b, 0x05010400u);
+}
+__device__ __forceinline__ uint32_t zip_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(a, b, 0x07030602u);
+}
+
+// Eight biased fp16 values (1152 + code) from two dwords of codes.
+__device__ __forceinline__ f16x8 codes8_biased(uint32_t d0, uint32_t d1) {
+  d0 ^= kCodeFlip;
+  d1 ^= kCodeFlip;
+  u32x4 r = {biased_h2_lo(d0), biased_h2_hi(d0), biased_h2_lo(d1), biased_h2_hi(d1)};
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// Eight fp16 values from eight fp32 values that are exactly representable in
+// fp16 (the fp32 store holds widened fp16 data), so truncation is exact.
+__device__ __forceinline__ f16x8 f32x8_to_f16x8(u32x4 a, u32x4 b) {
+  auto cv = [](uint32_t x, uint32_t y) {
+    return as_u32(__builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, x),
+                                                                      __builtin_bit_cast(float, y))));
+  };
+  u32x4 r = {cv(a.x, a.y), cv(a.z, a.w), cv(b.x, b.y), cv(b.z, b.w)};
+  return __builtin_bit_cast(f16x8, r);
+}
+
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace kvq

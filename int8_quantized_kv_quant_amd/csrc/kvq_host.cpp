@@ -1,0 +1,204 @@
+// Host side of libkvq: argument validation, the split planner and the C-ABI
+// entry points. Validation always runs before any HIP call, so every error path
+// can be exercised without a device.
+#include <limits.h>
+#include <stddef.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+static bool aligned(const void* p, uint64_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_layout(const kvq_layout* L) {
+  if (!L) return KVQ_ERR_NULL;
+  if (L->n_kv_heads < 1 || L->head_dim < 1 || L->max_ctx < 1) return KVQ_ERR_SHAPE;
+  // Strata PR 2698 "What it does": head_dim must be a multiple of 64 or the
+  // host refuses; this build also bounds it to the instantiated tile shapes.
+  if (L->head_dim % 64 != 0) return KVQ_ERR_UNSUPPORTED;
+  if (L->head_dim != 64 && L->head_dim != 128 && L->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if (L->slot_dim < L->head_dim) return KVQ_ERR_SHAPE;  // genie v1.2.1: slot >= head_dim
+  for (int dt : {L->k_dtype, L->v_dtype})
+    if (dt != KVQ_STORE_INT8 && dt != KVQ_STORE_FP32) return KVQ_ERR_UNSUPPORTED;
+  const bool any_i8 = L->k_dtype == KVQ_STORE_INT8 || L->v_dtype == KVQ_STORE_INT8;
+  if (any_i8 && L->scale_group != 64 && L->scale_group != L->head_dim) return KVQ_ERR_UNSUPPORTED;
+  if (L->s_seq < 0 || L->s_pos < 0 || L->s_head < 0) return KVQ_ERR_SHAPE;
+  if (L->ss_seq < 0 || L->ss_pos < 0 || L->ss_head < 0) return KVQ_ERR_SHAPE;
+  // A row never overlaps the next position's row of the same head: the kernels
+  // rely on it to make positions past the context read as zero.
+  if (L->s_pos < L->head_dim) return KVQ_ERR_SHAPE;
+  for (int dt : {L->k_dtype, L->v_dtype}) {
+    const int64_t eb = store_elem_bytes(dt);
+    if ((L->s_seq * eb) % 16 || (L->s_pos * eb) % 16 || (L->s_head * eb) % 16) return KVQ_ERR_ALIGN;
+    // One (sequence, head) slice is addressed with 32-bit offsets.
+    const int64_t extent = ((L->max_ctx - 1) * L->s_pos + L->head_dim) * eb;
+    if (extent > (int64_t)INT_MAX) return KVQ_ERR_UNSUPPORTED;
+  }
+  if (any_i8) {
+    const int64_t ng = L->head_dim / L->scale_group;
+    if (L->ss_pos < ng) return KVQ_ERR_SHAPE;
+    const int64_t a = 2 * ng;
+    if ((L->ss_seq * 2) % a || (L->ss_pos * 2) % a || (L->ss_head * 2) % a) return KVQ_ERR_ALIGN;
+    const int64_t extent = ((L->max_ctx - 1) * L->ss_pos + ng) * 2;
+    if (extent > (int64_t)INT_MAX) return KVQ_ERR_UNSUPPORTED;
+  }
+  return KVQ_OK;
+}
+
+int check_store_ptrs(const kvq_layout& L, int dtype, const void* store, const void* scales) {
+  if (!store) return KVQ_ERR_NULL;
+  if (!aligned(store, 16)) return KVQ_ERR_ALIGN;
+  if (dtype == KVQ_STORE_INT8) {
+    // genie v0.1.0-alpha.11 "--int8-kv triage": a missing scale pointer must be
+    // refused, never read as scale 1.0.
+    if (!scales) return KVQ_ERR_NULL;
+    if (!aligned(scales, 2 * (L.head_dim / L.scale_group))) return KVQ_ERR_ALIGN;
+  }
+  return KVQ_OK;
+}
+
+static int check_plan(const kvq_layout& L, int32_t batch, int32_t n_q, const kvq_plan_t* plan) {
+  if (!plan) return KVQ_ERR_NULL;
+  if (plan->n_splits < 1 || plan->n_splits > kMaxSplits) return KVQ_ERR_SHAPE;
+  if (plan->chunk < kTile || plan->chunk % kTile) return KVQ_ERR_SHAPE;
+  if (plan->ws_bytes < workspace_bytes(batch, n_q, plan->n_splits, L.head_dim)) return KVQ_ERR_WORKSPACE;
+  return KVQ_OK;
+}
+
+static int check_heads(const kvq_layout& L, int32_t batch, int32_t n_q) {
+  if (batch < 0 || n_q < 1) return KVQ_ERR_SHAPE;
+  if (batch > 65535 || (int64_t)batch * n_q > INT_MAX / 8) return KVQ_ERR_UNSUPPORTED;  // grid limits
+  if (n_q % L.n_kv_heads) return KVQ_ERR_SHAPE;
+  return KVQ_OK;
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+int kvq_version(void) { return (0 << 16) | (1 << 8) | 0; }
+
+const char* kvq_status_string(int s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "null pointer (a required buffer or an int8 store's scales)";
+    case KVQ_ERR_SHAPE: return "inconsistent shape or stride";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported head_dim, scale group, dtype or extent";
+    case KVQ_ERR_ALIGN: return "misaligned pointer or stride";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int kvq_plan(const kvq_layout* layout, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+             int32_t window, int32_t n_cu, kvq_plan_t* out) {
+  int st = check_layout(layout);
+  if (st) return st;
+  if (!out) return KVQ_ERR_NULL;
+  const kvq_layout& L = *layout;
+  if ((st = check_heads(L, batch, n_q_heads))) return st;
+  if (max_seq_len < 0 || window < 0 || n_cu < 1) return KVQ_ERR_SHAPE;
+
+  const int64_t l_eff = effective_len(max_seq_len, window);
+  const int64_t G = n_q_heads / L.n_kv_heads;
+  const int64_t head_blocks = ceil_div(G, kHeadsPerBlock);
+  const int64_t units = (int64_t)(batch > 0 ? batch : 1) * L.n_kv_heads * head_blocks;
+  int64_t chunk;
+  if (l_eff < 64) {
+    // genie v1.3.0: a single block below 64 positions.
+    chunk = round_up(l_eff > 0 ? l_eff : 1, kTile);
+  } else {
+    // Bytes one position of one kv head costs to read (algorithmic).
+    int64_t kv_pos = 0;
+    for (int dt : {L.k_dtype, L.v_dtype})
+      kv_pos += dt == KVQ_STORE_INT8 ? L.head_dim + 2 * (L.head_dim / L.scale_group) : 4 * L.head_dim;
+    // Partial (m, l, O) bytes one split writes for its query heads.
+    const int64_t part = (G < kHeadsPerBlock ? G : kHeadsPerBlock) * (L.head_dim + 2) * 4;
+    // Long splits keep the partial traffic near 1 % of the KV bytes ...
+    chunk = ceil_div(part * 100, kv_pos);
+    if (chunk < 512) chunk = 512;
+    // ... unless that leaves fewer than two workgroups per compute unit; then
+    // the chip is filled first.
+    const int64_t want_wg = 2 * (int64_t)n_cu;
+    if (units * ceil_div(l_eff, chunk) < want_wg) chunk = ceil_div(units * l_eff, want_wg);
+    chunk = round_up(chunk < kTile ? kTile : chunk, kTile);
+    const int64_t cap = round_up(l_eff, kTile);
+    if (chunk > cap) chunk = cap;
+    // The reduce keeps one weight per split in LDS.
+    const int64_t min_chunk = round_up(ceil_div(l_eff, kMaxSplits), kTile);
+    if (chunk < min_chunk) chunk = min_chunk;
+  }
+  if (chunk > INT_MAX) return KVQ_ERR_UNSUPPORTED;
+  int64_t n_splits = l_eff > 0 ? ceil_div(l_eff, chunk) : 1;
+  out->chunk = (int32_t)chunk;
+  out->n_splits = (int32_t)n_splits;
+  out->ws_bytes = workspace_bytes(batch, n_q_heads, n_splits, L.head_dim);
+  return KVQ_OK;
+}
+
+int kv_quant_append(const kvq_layout* layout, void* k_store, void* v_store, uint16_t* k_scales,
+                    uint16_t* v_scales, const uint16_t* k_new, const uint16_t* v_new,
+                    const int32_t* d_start_pos, int32_t batch, int32_t n_tok, void* stream) {
+  int st = check_layout(layout);
+  if (st) return st;
+  const kvq_layout& L = *layout;
+  if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
+  if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
+  if (!k_new || !v_new || !d_start_pos) return KVQ_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(d_start_pos, 4)) return KVQ_ERR_ALIGN;
+  if (batch < 0 || n_tok < 0) return KVQ_ERR_SHAPE;
+  if ((int64_t)batch * n_tok * L.n_kv_heads > (int64_t)INT_MAX / 64) return KVQ_ERR_UNSUPPORTED;
+  if (batch == 0 || n_tok == 0) return KVQ_OK;
+  return launch_append(L, k_store, v_store, k_scales, v_scales, k_new, v_new, d_start_pos, batch,
+                       n_tok, stream);
+}
+
+int kv_decode_attn_splitk(const kvq_layout* layout, const void* k_store, const void* v_store,
+                          const uint16_t* k_scales, const uint16_t* v_scales, const uint16_t* q,
+                          int32_t batch, int32_t n_q_heads, const int32_t* d_seq_lens,
+                          int32_t window, float sm_scale, const kvq_plan_t* plan, void* ws,
+                          int64_t ws_bytes, void* stream) {
+  int st = check_layout(layout);
+  if (st) return st;
+  const kvq_layout& L = *layout;
+  if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
+  if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
+  if ((st = check_heads(L, batch, n_q_heads))) return st;
+  if ((st = check_plan(L, batch, n_q_heads, plan))) return st;
+  if (!q || !d_seq_lens) return KVQ_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(d_seq_lens, 4)) return KVQ_ERR_ALIGN;
+  if (window < 0) return KVQ_ERR_SHAPE;
+  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return KVQ_ERR_SHAPE;
+  if (!ws) return KVQ_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
+  if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
+  if (batch == 0) return KVQ_OK;
+  return launch_partial(L, k_store, v_store, k_scales, v_scales, q, batch, n_q_heads, d_seq_lens,
+                        window, sm_scale, *plan, ws, stream);
+}
+
+int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,
+                     const int32_t* d_seq_lens, int32_t batch, int32_t n_q_heads, int32_t window,
+                     const kvq_plan_t* plan, uint16_t* out, void* stream) {
+  int st = check_layout(layout);
+  if (st) return st;
+  const kvq_layout& L = *layout;
+  if ((st = check_heads(L, batch, n_q_heads))) return st;
+  if ((st = check_plan(L, batch, n_q_heads, plan))) return st;
+  if (!d_seq_lens || !out) return KVQ_ERR_NULL;
+  if (!aligned(d_seq_lens, 4) || !aligned(out, 16)) return KVQ_ERR_ALIGN;
+  if (window < 0) return KVQ_ERR_SHAPE;
+  if (!ws) return KVQ_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
+  if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
+  if (batch == 0) return KVQ_OK;
+  return launch_reduce(L, ws, d_seq_lens, batch, n_q_heads, window, *plan, out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal declarations shared by the host code and the HIP kernels of libkvq.
+// Nothing here is part of the C ABI (include/kvq.h is).
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kTile = 32;            // positions per MFMA tile step of a wave
+constexpr int kMaxSplits = 8192;     // bound on plan.n_splits (reduce keeps weights in LDS)
+constexpr int kHeadsPerBlock = 16;   // query heads one wave carries (MFMA M/N = 16)
+
+// Byte sizes of one store element.
+inline int store_elem_bytes(int dtype) { return dtype == KVQ_STORE_INT8 ? 1 : 4; }
+
+// Number of fp16 scales per row (0 for an fp32 store).
+inline int scales_per_row(const kvq_layout& L, int dtype) {
+  return dtype == KVQ_STORE_INT8 ? L.head_dim / L.scale_group : 0;
+}
+
+// Checks a layout on its own (no pointers). Returns KVQ_OK or an error code.
+int check_layout(const kvq_layout* L);
+
+// Checks pointer alignment of a store and its scale array for `L`.
+int check_store_ptrs(const kvq_layout& L, int dtype, const void* store, const void* scales);
+
+// Attended-range length bound used by the planner.
+inline int64_t effective_len(int64_t max_len, int32_t window) {
+  return window > 0 && window < max_len ? window : max_len;
+}
+
+// Workspace bytes for a plan.
+inline int64_t workspace_bytes(int64_t batch, int64_t n_q, int64_t n_splits, int64_t head_dim) {
+  return batch * n_q * n_splits * (head_dim + 2) * 4;
+}
+
+// Kernel launchers (defined in the .hip files). They assume validated input.
+int launch_append(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k_scales,
+                  uint16_t* v_scales, const uint16_t* k_new, const uint16_t* v_new,
+                  const int32_t* d_start_pos, int32_t batch, int32_t n_tok, void* stream);
+
+int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store,
+                   const uint16_t* k_scales, const uint16_t* v_scales, const uint16_t* q,
+                   int32_t batch, int32_t n_q_heads, const int32_t* d_seq_lens, int32_t window,
+                   float sm_scale, const kvq_plan_t& plan, void* ws, void* stream);
+
+int launch_reduce(const kvq_layout& L, const void* ws, const int32_t* d_seq_lens, int32_t batch,
+                  int32_t n_q_heads, int32_t window, const kvq_plan_t& plan, uint16_t* out,
+                  void* stream);
+
+}  // namespace kvq

@@ -1,0 +1,266 @@
+"""Decode attention (kv_decode_attn_splitk + kv_decode_reduce) on the GPU against
+the fp64 CPU oracle: max abs error <= 2e-3 (fp32 accumulation, fp16 output) on
+every workload, plus the method's invariants, split-count independence, poison
+and determinism checks."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import kvq_oracle as orc
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _ks():
+    import kvq_setup
+    return kvq_setup
+
+
+def _kvq():
+    import int8_quantized_kv_quant_amd as kvq
+    return kvq
+
+
+def _oracle_seq(w, b, L, q_b, window, sm, pos_from=0):
+    """fp64 oracle output [n_q][d] of sequence b over positions [0, L)."""
+    lo = max(0, L - window) if window else 0
+    lo = max(lo, pos_from)
+    cache = orc.Cache(1, L, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+    k = wl.kv_rows(w, "k", b, lo, L - lo)
+    v = wl.kv_rows(w, "v", b, lo, L - lo)
+    cache.append(k[None], v[None], [lo])   # positions before lo are never attended
+    return orc.attend(q_b[None], cache, [L], window, sm)[0]
+
+
+def _run(w, lay, cache, q, lens, window, plan=None, sm=None):
+    kvq = _kvq()
+    qd = torch.from_numpy(q).cuda()
+    ld = torch.from_numpy(lens.astype(np.int32)).cuda()
+    sm = sm if sm is not None else 1.0 / math.sqrt(w.head_dim)
+    out = kvq.decode(lay, cache, qd, ld, window, sm, plan=plan, n_cu=_ks().n_cu())
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _err(got, want):
+    e = np.abs(got - want)
+    i = np.unravel_index(np.argmax(e), e.shape)
+    return float(e[i]), float(want[i])
+
+
+def test_tiny_matches_oracle():
+    w = wl.WORKLOADS["tiny"]
+    lens = wl.seq_lens(w)
+    lay, cache = _ks().fill_cache(w, lens)
+    q = wl.queries(w)
+    got = _run(w, lay, cache, q, lens, 0)
+    want = _oracle_seq(w, 0, int(lens[0]), q[0], 0, 1 / 8)
+    e, at = _err(got[0], want)
+    print(f"tiny max abs err {e:.3g} (|out| {abs(at):.3g})")
+    assert e <= TOL
+
+
+@pytest.mark.parametrize("L", [512, 1024, 2048, 4096])
+def test_gemma_sliding_window(L):
+    """Head_dim 256 in a 512-wide slot, one scale per (position, kv head),
+    sliding window 512, automatic split count."""
+    w = wl.WORKLOADS["gemma"]
+    lens = np.array([L], dtype=np.int32)
+    lay, cache = _ks().fill_cache(w, lens)
+    q = wl.queries(w)
+    got = _run(w, lay, cache, q, lens, w.window)
+    want = _oracle_seq(w, 0, L, q[0], w.window, 1 / 16)
+    e, at = _err(got[0], want)
+    print(f"gemma L={L} max abs err {e:.3g}")
+    assert e <= TOL
+
+
+def test_long_context_128k():
+    w = wl.WORKLOADS["long"]
+    L = w.contexts[-1]
+    print("[decode] long 131072", flush=True)
+    lens = np.array([L], dtype=np.int32)
+    lay, cache = _ks().fill_cache(w, lens)
+    q = wl.queries(w)
+    got = _run(w, lay, cache, q, lens, 0)
+    want = _oracle_seq(w, 0, L, q[0], 0, 1 / 16)
+    e, at = _err(got[0], want)
+    print(f"long max abs err {e:.3g} (|out| at worst {abs(at):.3g})")
+    assert e <= TOL
+
+
+def test_batched_ragged_sampled_sequences():
+    w = wl.WORKLOADS["batched"]
+    lens = wl.seq_lens(w)
+    seqs = (int(np.argmin(lens)), int(np.argmax(lens)), 5, 40)
+    print(f"[decode] batched total {int(lens.sum())}, sampled {seqs}", flush=True)
+    # every sequence is attended at its real length; only the sampled ones hold
+    # generated rows (the rest keep zeros and are not compared)
+    lay, cache = _ks().fill_cache(w, lens, seqs=seqs)
+    q = wl.queries(w)
+    got = _run(w, lay, cache, q, lens, 0)
+    for b in seqs:
+        want = _oracle_seq(w, b, int(lens[b]), q[b], 0, 1 / math.sqrt(128))
+        e, _ = _err(got[b], want)
+        print(f"batched seq {b} L={lens[b]} err {e:.3g}")
+        assert e <= TOL
+
+
+@pytest.mark.parametrize("name", ["mixed_k8v32", "mixed_k32v8"])
+def test_mixed_stores_after_chunk_append(name):
+    w = wl.WORKLOADS[name]
+    ks = _ks()
+    L = w.contexts[-1]
+    lay, cache = ks.fill_cache(w, np.array([w.prefill]))
+    ks.append_rows(lay, cache, 0, w.prefill, wl.kv_rows(w, "k", 0, w.prefill, w.append),
+                   wl.kv_rows(w, "v", 0, w.prefill, w.append))
+    lens = np.array([L], dtype=np.int32)
+    q = wl.queries(w)
+    got = _run(w, lay, cache, q, lens, 0)
+    want = _oracle_seq(w, 0, L, q[0], 0, 1 / 16)
+    e, _ = _err(got[0], want)
+    print(f"{name} err {e:.3g}")
+    assert e <= TOL
+
+
+# ----------------------------------------------------------------- invariants
+
+def _small(name="inv", H=2, G=4, d=128, g=64, max_ctx=300, kdt="int8", vdt="int8", batch=1, seed=150):
+    return wl.Workload(name, batch, H * G, H, d, d, g, max_ctx, 0, seed, k_dtype=kdt, v_dtype=vdt,
+                       contexts=(max_ctx,))
+
+
+@pytest.mark.parametrize("kdt,vdt,g,d", [("int8", "int8", 64, 256), ("int8", "int8", 128, 128),
+                                         ("int8", "fp32", 64, 128), ("fp32", "int8", 64, 64),
+                                         ("fp32", "fp32", 256, 256)])
+def test_ragged_lengths_and_split_sweep(kdt, vdt, g, d):
+    """Lengths 0, 1, 31, 33, 64, 95, 300 in one batch; every split count from 1
+    to the maximum gives the oracle's result within tolerance."""
+    w = _small(d=d, g=g, kdt=kdt, vdt=vdt, batch=7, max_ctx=300)
+    lens = np.array([0, 1, 31, 33, 64, 95, 300], dtype=np.int32)
+    lay, cache = _ks().fill_cache(w, lens)
+    q = wl.queries(w)
+    sm = 1 / math.sqrt(d)
+    want = [(_oracle_seq(w, b, int(lens[b]), q[b], 0, sm) if lens[b] else np.zeros((8, d))) for b in range(7)]
+    kvq = _kvq()
+    outs = []
+    for chunk in (32, 64, 96, 320):
+        n = -(-300 // chunk)
+        plan = kvq.Plan(n, chunk, 7 * 8 * n * (d + 2) * 4)
+        got = _run(w, lay, cache, q, lens, 0, plan=plan)
+        outs.append(got)
+        for b in range(7):
+            e, _ = _err(got[b], want[b])
+            assert e <= TOL, (chunk, b, e)
+        assert not got[0].any()  # empty context -> zero row
+    # splits of one plan differ only by summation order
+    assert np.abs(outs[0] - outs[-1]).max() <= 2 * TOL
+
+
+def test_single_position_returns_the_value_row():
+    w = _small(max_ctx=64)
+    lens = np.array([1], dtype=np.int32)
+    lay, cache = _ks().fill_cache(w, lens)
+    q = wl.queries(w, 1) * np.float16(4)
+    got = _run(w, lay, cache, q.astype(np.float16), lens, 0)
+    c = orc.Cache(1, 1, 2, 128, 64)
+    c.append(wl.kv_rows(w, "k", 0, 0, 1)[None], wl.kv_rows(w, "v", 0, 0, 1)[None], [0])
+    for h in range(8):
+        v = c.values("v", 0, 0, 1, h // 4)[0]
+        assert np.abs(got[0, h] - v).max() <= TOL
+
+
+def test_constant_values_and_zero_query():
+    kvq = _kvq()
+    ks = _ks()
+    w = _small(max_ctx=200)
+    lay = ks.layout_for(w)
+    cache = kvq.alloc_cache(lay, 1)
+    k = wl.kv_rows(w, "k", 0, 0, 200)
+    v = np.broadcast_to(wl.kv_rows(w, "v", 0, 0, 1), (200, 2, 128)).copy()
+    ks.append_rows(lay, cache, 0, 0, k, v)
+    lens = np.array([200], dtype=np.int32)
+    q = wl.queries(w)
+    got = _run(w, lay, cache, q, lens, 0)
+    c = orc.Cache(1, 1, 2, 128, 64)
+    c.append(v[None, :1], v[None, :1], [0])
+    for h in range(8):
+        assert np.abs(got[0, h] - c.values("v", 0, 0, 1, h // 4)[0]).max() <= TOL
+    # zero query -> mean of the dequantized values over the window
+    lay2, cache2 = ks.fill_cache(w, lens)
+    got0 = _run(w, lay2, cache2, np.zeros_like(q), lens, 37)
+    want0 = _oracle_seq(w, 0, 200, np.zeros_like(q[0]), 37, 1 / math.sqrt(128))
+    assert np.abs(got0[0] - want0).max() <= TOL
+
+
+def test_window_at_least_context_equals_no_window():
+    w = _small(max_ctx=257)
+    lens = np.array([257], dtype=np.int32)
+    lay, cache = _ks().fill_cache(w, lens)
+    q = wl.queries(w)
+    a = _run(w, lay, cache, q, lens, 0)
+    b = _run(w, lay, cache, q, lens, 257)
+    c = _run(w, lay, cache, q, lens, 5000)
+    assert np.array_equal(b, c)
+    assert np.abs(a - b).max() <= TOL
+
+
+def test_head_major_layout_and_large_gqa_group():
+    """32 query heads on 1 kv head (two 16-head blocks) in a head-major cache
+    with a wider slot; compared with the oracle."""
+    w = wl.Workload("g32", 2, 32, 1, 128, 192, 64, 700, 0, 160, contexts=(700,))
+    lens = np.array([700, 333], dtype=np.int32)
+    ks = _ks()
+    lay = kvq_lay = ks.layout_for(w, order="head")
+    cache = _kvq().alloc_cache(lay, 2)
+    for b in range(2):
+        L = int(lens[b])
+        ks.append_rows(lay, cache, b, 0, wl.kv_rows(w, "k", b, 0, L), wl.kv_rows(w, "v", b, 0, L))
+    q = wl.queries(w)
+    got = _run(w, kvq_lay, cache, q, lens, 0)
+    for b in range(2):
+        want = _oracle_seq(w, b, int(lens[b]), q[b], 0, 1 / math.sqrt(128))
+        assert _err(got[b], want)[0] <= TOL
+
+
+def test_poison_outside_the_attended_range():
+    """NaN in fp32 stores beyond the context, inside the slot tail and before the
+    window; NaN scales beyond the context: none of it reaches the output."""
+    kvq = _kvq()
+    ks = _ks()
+    for kdt, vdt in (("fp32", "int8"), ("int8", "fp32")):
+        w = wl.Workload("poison", 1, 8, 2, 128, 160, 64, 256, 0, 170, k_dtype=kdt, v_dtype=vdt, contexts=(256,))
+        lay = ks.layout_for(w)
+        cache = kvq.alloc_cache(lay, 1)
+        for s in ("k", "v"):
+            if cache[s].dtype == torch.float32:
+                cache[s].fill_(float("nan"))
+            else:
+                cache[s + "_scales"].fill_(float("nan"))
+        L, W = 200, 150
+        ks.append_rows(lay, cache, 0, 0, wl.kv_rows(w, "k", 0, 0, L), wl.kv_rows(w, "v", 0, 0, L))
+        # NaN over the positions the window excludes, in the fp32 store
+        fp = "k" if kdt == "fp32" else "v"
+        idx = torch.arange(0, (L - W) * lay.s_pos, device="cuda")
+        cache[fp][idx] = float("nan")
+        lens = np.array([L], dtype=np.int32)
+        q = wl.queries(w)
+        got = _run(w, lay, cache, q, lens, W)
+        assert np.isfinite(got).all()
+        want = _oracle_seq(w, 0, L, q[0], W, 1 / math.sqrt(128))
+        assert _err(got[0], want)[0] <= TOL
+
+
+def test_run_twice_bitwise_identical():
+    w = wl.WORKLOADS["tiny"]
+    lens = wl.seq_lens(w)
+    lay, cache = _ks().fill_cache(w, lens)
+    q = wl.queries(w)
+    a = _run(w, lay, cache, q, lens, 0)
+    b = _run(w, lay, cache, q, lens, 0)
+    assert np.array_equal(a, b)

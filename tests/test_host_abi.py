@@ -1,0 +1,206 @@
+"""The C-ABI library on the host: it loads, exports every function that
+include/kvq.h declares, its planner keeps its stated properties, and every
+argument error is returned before any device call (no GPU needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import int8_quantized_kv_quant_amd as kvq
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(kvq.lib_path()), reason="libkvq.so not built")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^(?:const\s+)?(?:int|char\s*\*|const char\s*\*|void)\s*\*?\s*(\w+)\s*\(", src, re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert set(names) == set(kvq.EXPORTED_SYMBOLS), names
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kvq.lib_path())
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+@needs_lib
+def test_status_strings_and_version():
+    assert kvq.kvq_status_string(0) == "ok"
+    for st in range(-6, 0):
+        assert kvq.kvq_status_string(st) != "unknown status"
+    assert kvq.kvq_status_string(-99) == "unknown status"
+    assert kvq.kvq_version() > 0
+
+
+def _layout(w: wl.Workload, order="pos"):
+    return kvq.make_layout(w.n_kv_heads, w.head_dim, w.max_ctx, w.batch, slot_dim=w.slot_dim,
+                           k_dtype=w.k_dtype, v_dtype=w.v_dtype, scale_group=w.scale_group, order=order)
+
+
+@needs_lib
+@pytest.mark.parametrize("name", sorted(wl.WORKLOADS))
+@pytest.mark.parametrize("n_cu", [8, 256])
+def test_plan_covers_the_context(name, n_cu):
+    w = wl.WORKLOADS[name]
+    lay = _layout(w)
+    for L in (1, 63, 64, 100, w.max_ctx):
+        p = kvq.kvq_plan(lay, w.batch, w.n_q_heads, L, w.window, n_cu)
+        l_eff = min(L, w.window) if w.window else L
+        assert p.chunk % 32 == 0 and p.chunk >= 32
+        assert 1 <= p.n_splits <= 8192
+        assert p.n_splits * p.chunk >= l_eff
+        assert (p.n_splits - 1) * p.chunk < max(l_eff, 1)      # no split starts past the range
+        assert p.ws_bytes == w.batch * w.n_q_heads * p.n_splits * (w.head_dim + 2) * 4
+        if l_eff < 64:
+            assert p.n_splits == 1  # genie v1.3.0: single block below 64 positions
+
+
+@needs_lib
+def test_plan_long_context_fills_the_chip():
+    w = wl.WORKLOADS["long"]
+    p = kvq.kvq_plan(_layout(w), 1, 16, 131072, 0, 256)
+    assert (p.n_splits, p.chunk) == (256, 512)  # 2 kv heads x 256 splits = 2 workgroups per CU
+
+
+@needs_lib
+def test_plan_ragged_batch_keeps_partials_small():
+    w = wl.WORKLOADS["batched"]
+    p = kvq.kvq_plan(_layout(w), 64, 32, 32768, 0, 256)
+    kv_pos = 2 * (128 + 4)
+    part = 4 * (128 + 2) * 4
+    assert part / (p.chunk * kv_pos) <= 0.011
+
+
+# ---------------------------------------------------------------- validation
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _base():
+    return kvq.make_layout(2, 256, 1024, 1, scale_group=64)
+
+
+def _append(lay, **kw):
+    args = dict(k_store=FAKE, v_store=FAKE, k_scales=FAKE, v_scales=FAKE, k_new=FAKE, v_new=FAKE,
+                start_pos=FAKE, batch=1, n_tok=1)
+    args.update(kw)
+    return kvq.load().kv_quant_append(ctypes.byref(lay.c()), args["k_store"], args["v_store"],
+                                      args["k_scales"], args["v_scales"], args["k_new"], args["v_new"],
+                                      args["start_pos"], args["batch"], args["n_tok"], None)
+
+
+def _partial(lay, plan=None, **kw):
+    plan = plan or kvq.Plan(4, 256, 1 * 16 * 4 * 258 * 4)
+    args = dict(k_store=FAKE, v_store=FAKE, k_scales=FAKE, v_scales=FAKE, q=FAKE, batch=1, n_q=16,
+                seq_lens=FAKE, window=0, sm=0.0625, ws=FAKE, ws_bytes=plan.ws_bytes)
+    args.update(kw)
+    return kvq.load().kv_decode_attn_splitk(
+        ctypes.byref(lay.c()), args["k_store"], args["v_store"], args["k_scales"], args["v_scales"],
+        args["q"], args["batch"], args["n_q"], args["seq_lens"], args["window"], args["sm"],
+        ctypes.byref(plan.c()), args["ws"], args["ws_bytes"], None)
+
+
+def _reduce(lay, plan=None, **kw):
+    plan = plan or kvq.Plan(4, 256, 1 * 16 * 4 * 258 * 4)
+    args = dict(ws=FAKE, ws_bytes=plan.ws_bytes, seq_lens=FAKE, batch=1, n_q=16, window=0, out=FAKE)
+    args.update(kw)
+    return kvq.load().kv_decode_reduce(ctypes.byref(lay.c()), args["ws"], args["ws_bytes"], args["seq_lens"],
+                                       args["batch"], args["n_q"], args["window"], ctypes.byref(plan.c()),
+                                       args["out"], None)
+
+
+def _with(lay, **kw):
+    d = lay.__dict__.copy()
+    d.update(kw)
+    return kvq.Layout(**d)
+
+
+NULL_, SHAPE, UNSUP, ALIGN, WS = -1, -2, -3, -4, -5
+
+
+@needs_lib
+def test_null_scale_pointer_is_refused_not_read_as_one():
+    """genie v0.1.0-alpha.11 '--int8-kv triage': a null scale pointer became
+    scale 1.0; here it is an error for every int8 store, in every entry point."""
+    lay = _base()
+    assert _append(lay, k_scales=None) == NULL_
+    assert _append(lay, v_scales=None) == NULL_
+    assert _partial(lay, k_scales=None) == NULL_
+    assert _partial(lay, v_scales=None) == NULL_
+    mixed = _with(lay, v_dtype=kvq.KVQ_STORE_FP32)   # k8v32: V has no scales
+    assert _partial(mixed, v_scales=None, k_scales=None) == NULL_
+
+
+@needs_lib
+def test_shape_errors():
+    lay = _base()
+    assert _partial(lay, n_q=15) == SHAPE                    # n_q % n_kv != 0
+    assert _append(_with(lay, slot_dim=128)) == SHAPE         # slot narrower than head_dim
+    assert _append(_with(lay, s_pos=128)) == SHAPE            # rows of one head overlap
+    assert _partial(lay, window=-1) == SHAPE
+    assert _partial(lay, plan=kvq.Plan(4, 100, 10 ** 9)) == SHAPE   # chunk not a multiple of 32
+    assert _partial(lay, plan=kvq.Plan(0, 256, 10 ** 9)) == SHAPE
+    assert _partial(lay, plan=kvq.Plan(9000, 256, 10 ** 12)) == SHAPE
+    assert _partial(lay, sm=float("nan")) == SHAPE
+    assert _append(lay, batch=-1) == SHAPE
+
+
+@needs_lib
+def test_unsupported_requests_are_refused():
+    lay = _base()
+    # Strata PR 2698: head_dim must be a multiple of 64 for group-64 scales.
+    assert _append(_with(lay, head_dim=96, slot_dim=96, s_pos=192, s_head=96, s_seq=192 * 1024)) == UNSUP
+    assert _append(_with(lay, head_dim=512, slot_dim=512, s_pos=1024, s_head=512)) == UNSUP
+    assert _append(_with(lay, scale_group=32)) == UNSUP
+    assert _append(_with(lay, k_dtype=3)) == UNSUP
+    big = kvq.make_layout(2, 256, 5_000_000, 1, scale_group=64)   # > 2 GiB per sequence slice
+    assert _append(big) == UNSUP
+
+
+@needs_lib
+def test_alignment_errors():
+    lay = _base()
+    assert _append(lay, k_store=FAKE + 8) == ALIGN
+    assert _append(lay, k_new=FAKE + 2) == ALIGN
+    assert _partial(lay, q=FAKE + 4) == ALIGN
+    assert _partial(lay, k_scales=FAKE + 2) == ALIGN         # group-64 scale rows are 8-byte loads
+    assert _append(_with(lay, s_head=264, s_pos=528)) == ALIGN  # row offsets not multiples of 16 B
+    assert _reduce(lay, out=FAKE + 2) == ALIGN
+
+
+@needs_lib
+def test_workspace_errors():
+    lay = _base()
+    plan = kvq.Plan(4, 256, 1 * 16 * 4 * 258 * 4)
+    assert _partial(lay, plan=plan, ws=None) == WS
+    assert _partial(lay, plan=plan, ws_bytes=plan.ws_bytes - 1) == WS
+    assert _partial(lay, plan=kvq.Plan(4, 256, 100)) == WS
+    assert _reduce(lay, plan=plan, ws_bytes=16) == WS
+
+
+@needs_lib
+def test_empty_batch_is_a_no_op():
+    lay = _base()
+    assert _append(lay, batch=0) == 0
+    assert _append(lay, n_tok=0) == 0
+    assert _partial(lay, batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
+    assert _reduce(lay, batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kvq, "_lib", None)
+    monkeypatch.setattr(kvq, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(kvq.KvqLibraryMissing):
+        kvq.kvq_plan(_base(), 1, 16, 100, 0, 256)
