@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of one INT8-KV decode step on one MI355X.
+
+A step is the whole hot path for one new token of one sequence:
+  kv_quant_append (the token's K/V, 2 kv heads)  ->  kvq_plan (host)
+  ->  kv_decode_attn_splitk  ->  kv_decode_reduce
+on the long-context workload: batch 1, 16 query / 2 kv heads, head_dim 256,
+int8 codes with one fp16 scale per 64 values, context 131072 (K with 1 % outlier
+channels x20). Inputs are seeded synthetic data (workloads.py), resident in HBM
+before timing.
+
+The 132 MiB cache fits in the 256 MB Infinity Cache, so the timed steps rotate
+over 8 identical copies of the cache (1.1 GB): each step streams a copy that
+was not touched for 7 steps and has been evicted.
+
+Prints one JSON line: value = KV bytes read per step / step time (GB/s), the
+roofline of the partial kernel from HIP events over the timed region, and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+COPIES = 8
+TOL = 2e-3
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("kvq_decode.hip", "kvq_device.h"):
+        with open(os.path.join(ROOT, "int8_quantized_kv_quant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(digest: str):
+    """HBM bytes per partial launch measured with rocprofv3 counters, if they
+    were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "partial_long_128k_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_src_sha") != digest:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, lens, q, sm):
+    """The oracle as it stands, timed on the host: decode attention of the full
+    step (both kv heads, 131072 positions) over the dequantized cache in fp64."""
+    from oracle import kvq_oracle as orc
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    L = int(lens[0])
+    cache = orc.Cache(1, L, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+    cache.append(wl.kv_rows(w, "k", 0, 0, L)[None], wl.kv_rows(w, "v", 0, 0, L)[None], [0])
+    t0 = time.perf_counter()
+    want = orc.attend(q, cache, lens, 0, sm)
+    dt = time.perf_counter() - t0
+    return want, dt, cores
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--chunk", type=int, default=0, help="override the planner's split length")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this decode path has no multi-GPU mode "
+              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import int8_quantized_kv_quant_amd as kvq
+    import kvq_setup
+    import workloads as wl
+    from oracle import kvq_oracle as orc
+
+    kvq.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n_cu = kvq_setup.n_cu()
+    w = wl.WORKLOADS["long"]
+    L = w.contexts[-1]
+    lens = np.array([L], dtype=np.int32)
+    sm = 1.0 / math.sqrt(w.head_dim)
+
+    log(f"filling the {L}-position cache (quantize-append of {L - 1} tokens)")
+    lay, cache0 = kvq_setup.fill_cache(w, lens, upto=np.array([L - 1]))
+    k_new = torch.from_numpy(wl.kv_rows(w, "k", 0, L - 1, 1)).to(dev)
+    v_new = torch.from_numpy(wl.kv_rows(w, "v", 0, L - 1, 1)).to(dev)
+    start = torch.tensor([L - 1], dtype=torch.int32, device=dev)
+    q = wl.queries(w)
+    qd = torch.from_numpy(q).to(dev)
+    ld = torch.from_numpy(lens).to(dev)
+    caches = [cache0] + [{k: (None if t is None else t.clone()) for k, t in cache0.items()}
+                         for _ in range(COPIES - 1)]
+    plan0 = kvq.kvq_plan(lay, 1, w.n_q_heads, L, 0, n_cu)
+    if args.chunk:
+        n = -(-L // args.chunk)
+        plan0 = kvq.Plan(n, args.chunk, 1 * w.n_q_heads * n * (w.head_dim + 2) * 4)
+    ws = torch.empty(plan0.ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(c, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        kvq.kv_quant_append(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], k_new, v_new, start, 1, 1)
+        plan = plan0 if args.chunk else kvq.kvq_plan(lay, 1, w.n_q_heads, L, 0, n_cu)
+        if ev is not None:
+            ev[1].record(stream)
+        kvq.kv_decode_attn_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], qd, 1, w.n_q_heads,
+                                  ld, 0, sm, plan, ws, ws.numel())
+        if ev is not None:
+            ev[2].record(stream)
+        kvq.kv_decode_reduce(lay, ws, ws.numel(), ld, 1, w.n_q_heads, 0, plan, out)
+        if ev is not None:
+            ev[3].record(stream)
+
+    log(f"plan: n_splits={plan0.n_splits} chunk={plan0.chunk}; warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(caches[i % COPIES])
+    torch.cuda.synchronize()
+
+    # Parity of the state being timed: codes/scales of sampled rows bit-exact,
+    # and one step's output against the fp64 oracle.
+    log("checking codes and output against the oracle")
+    rng = np.random.default_rng(11)
+    pos = np.unique(np.concatenate([rng.integers(0, L, 2048), [L - 1]]))
+    k_all = wl.kv_rows(w, "k", 0, 0, L)
+    codes_ok = True
+    for h in range(w.n_kv_heads):
+        want_c, want_s = orc.quantize_rows(k_all[pos, h], w.scale_group)
+        got_c = kvq_setup.rows_of(lay, caches[3]["k"], 0, pos, h)
+        got_s = kvq_setup.scales_of(lay, caches[3]["k_scales"], 0, pos, h)
+        codes_ok &= bool(np.array_equal(got_c, want_c) and np.array_equal(got_s.view(np.uint16), want_s.view(np.uint16)))
+    step(caches[0])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the full step")
+        want, cpu_s, cores = cpu_baseline(w, lens, q, sm)
+        max_err = float(np.abs(got - want).max())
+        kv_bytes = wl.kv_bytes_per_step(w, lens)
+        cpu = {"value": round(kv_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+               "kind": "oracle", "seconds": round(cpu_s, 3),
+               "sample": "full step: numpy fp64 decode attention of 16 query heads over the "
+                         "dequantized 131072-position cache (both kv heads); cache set-up not timed"}
+    else:
+        max_err = None
+
+    log(f"timing {args.steps} steps over {COPIES} cache copies")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(caches[i % COPIES], evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    app = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    part = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    red = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    kv_bytes = wl.kv_bytes_per_step(w, lens)
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (part.mean() * 1e-3) / 1e9
+    digest = kernel_source_digest()
+    traffic = traffic_from_profiles(digest)
+
+    res = {
+        "metric": "int8-KV decode-attention HBM GB/s (% of peak) and us/step at 128K ctx",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 codes, fp16 MFMA operands, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) fp16, K outlier channels x20)",
+        "config": {"workload": "long_128k", "batch": 1, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "scale_group": w.scale_group, "context": L,
+                   "k_store": w.k_dtype, "v_store": w.v_dtype, "n_splits": plan0.n_splits,
+                   "chunk": plan0.chunk, "kv_bytes_per_step": kv_bytes, "cache_copies": COPIES},
+        "breakdown_us": {"append_plan": round(float(app.mean()) * 1e3, 2),
+                         "partial": round(float(part.mean()) * 1e3, 2),
+                         "reduce": round(float(red.mean()) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "kernel": "kvq_partial_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": kv_bytes,
+                     "avg_launch_us": round(float(part.mean()) * 1e3, 3), "kernel_src_sha": digest},
+        "parity": {"codes_scales_bitexact_sampled": codes_ok, "max_abs_err_vs_oracle": max_err,
+                   "tol": TOL},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0 if codes_ok and (max_err is None or max_err <= TOL) else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())
