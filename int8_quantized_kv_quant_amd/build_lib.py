@@ -5,7 +5,10 @@ Usage: python -m int8_quantized_kv_quant_amd.build_lib [--verbose]
 Every HIP source is compiled for gfx950 only. Flags that matter for results:
   -fhip-fp32-correctly-rounded-divide-sqrt  the quantizer's divisions must be
       IEEE correctly rounded (a reciprocal-multiply breaks exact .5 ties);
-  -Xclang -target-feature -Xclang -packed-fp32-ops  no packed fp32 VALU ops.
+  -Xclang -target-feature -Xclang -packed-fp32-ops  no packed fp32 VALU ops;
+  -mllvm -amdgpu-mfma-vgpr-form  MFMA accumulators in VGPRs: the decode kernels
+      scale MFMA results with VALU ops, and AGPR-resident accumulators cost a
+      copy per element each time.
 No fast-math flag is used anywhere.
 """
 from __future__ import annotations
@@ -28,7 +31,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
           "-I" + os.path.join(ROOT, "include")]
 HIP_FLAGS = ["--offload-arch=gfx950", "-fno-gpu-rdc",
              "-fhip-fp32-correctly-rounded-divide-sqrt",
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

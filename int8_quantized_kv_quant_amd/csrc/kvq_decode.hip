@@ -30,6 +30,14 @@
 // Partial output of a split: per query head its max m (log2 domain), l, and the
 // unnormalized O, after merging the wavefronts of the workgroup in LDS.
 //
+// Data movement. For int8 K and V the tiles are staged in LDS: each wavefront
+// owns two LDS stages and streams tile t+1 from HBM into one with direct-to-LDS
+// buffer loads (no registers held while in flight) while it computes tile t
+// from the other. Rows land as 16-byte chunks XOR-swizzled by row, so the
+// MFMA-layout reads are free of bank conflicts. A store with fp32 rows (k8v32,
+// k32v8, k32v32) is four times wider per position; those variants read their
+// operands straight from HBM into registers instead.
+//
 // Bounds. Every K/V/scale load goes through a buffer resource whose size ends
 // at the last row of the context, and positions outside the split get an
 // out-of-range offset, so they read as zero and are masked out of the softmax.
@@ -60,13 +68,396 @@ struct PartialArgs {
   float c2;  // sm_scale * log2(e)
 };
 
+// Compile-time shape of one kernel instance.
+template <int D_, bool KI8_, bool VI8_, bool G64_>
+struct Shape {
+  static constexpr int D = D_;
+  static constexpr bool KI8 = KI8_, VI8 = VI8_, G64 = G64_;
+  static constexpr int NJ = D / 64;          // 64-wide dim blocks per row (2 k-steps each)
+  static constexpr int NG = G64 ? NJ : 1;    // scales per row
+  static constexpr int SB = 2 * NG;          // scale bytes per row
+  static constexpr int NKS = (SB + 3) / 4;   // dwords holding one row's scales
+  static constexpr int VB = D / 16;          // V dims per lane per position = PV n-tiles
+  static constexpr int KE = KI8 ? 1 : 4;     // element bytes
+  static constexpr int VE = VI8 ? 1 : 4;
+  static constexpr int KW = KI8 ? 1 : 4;     // u32x4 of K per (C-tile, dim block)
+  static constexpr int VW = VB * VE / 4;     // dwords of V per lane per position
+  static constexpr int CH = D / 16;          // 16-byte chunks per int8 row
+};
+
+// Operand registers of one 32-position tile for one lane, in two halves that
+// are never live together in the LDS-staged kernel.
+//   k[ct][j]  A operand of S^T: row c16 of C-tile ct, dims 64j + 16*q4 + [0,16)
+//   ks[ct][i] the NG fp16 scales of position 16ct + 4*q4 + i (packed)
+//   v[e]      B operand of P.V: position kpos(e), dims VB*c16 + [0,VB)
+//   vs[e]     fp16 scale of v[e]'s group (low half)
+template <class S>
+struct KRegs {
+  u32x4 k[2][S::NJ][S::KW];
+  uint32_t ks[2][4][S::NKS];
+};
+template <class S>
+struct VRegs {
+  uint32_t v[8][S::VW];
+  uint32_t vs[8];
+};
+
+template <class S>
+struct WaveAcc {
+  f32x4 o[S::VB];
+  f32x4 l;
+  float m_ref;
+};
+
+// Position (within the tile) of element e of a lane's k-slice in P.V: the lane
+// of S^T with row group q4 holds positions 4*q4 + i of both 16-row C-tiles.
+__device__ __forceinline__ int kpos(int e, int q4) { return e < 4 ? 4 * q4 + e : 12 + 4 * q4 + e; }
+
+__device__ __forceinline__ float scale_of(const uint32_t* packed, int j) {
+  const uint32_t w = packed[j >> 1];
+  return h_bits_to_f32((j & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
+// K half of a tile: S^T = K.Q^T and the online-softmax update; returns the
+// tile's probabilities P (fp16) in the A-operand layout of P.V.
+// The query operand (B of S^T = K.Q^T) for lane (head c16, k-group q4) lives in
+// LDS, rows padded to break bank conflicts; k-step 2j+u covers dims
+// 64j + 16*q4 + 8u + [0, 8).
+template <class S>
+struct QOperand {
+  static constexpr int ROW = 2 * S::D + 16;  // bytes per padded head row
+  const uint8_t* p;                          // this lane's row + 32*q4
+  __device__ __forceinline__ f16x8 get(int j, int u) const {
+    return *reinterpret_cast<const f16x8*>(p + 128 * j + 16 * u);
+  }
+};
+
+template <class S>
+__device__ __forceinline__ f16x8 tile_qk(const KRegs<S>& t, int nvalid, WaveAcc<S>& acc,
+                                         const QOperand<S>& qb, const float (&corr)[S::NG],
+                                         float c2, int q4) {
+  float z[2][4];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    f32x4 zz = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (S::KI8 && S::G64) {
+#pragma unroll
+      for (int j = 0; j < S::NJ; ++j) {
+        const u32x4 c = t.k[ct][j][0];
+        f32x4 a = mfma16(codes8_biased(c.x, c.y), qb.get(j, 0), (f32x4){corr[j], corr[j], corr[j], corr[j]});
+        a = mfma16(codes8_biased(c.z, c.w), qb.get(j, 1), a);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zz[i] = fmaf(a[i], scale_of(t.ks[ct][i], j), zz[i]);
+      }
+    } else if constexpr (S::KI8) {
+      f32x4 a = {corr[0], corr[0], corr[0], corr[0]};
+#pragma unroll
+      for (int j = 0; j < S::NJ; ++j) {
+        const u32x4 c = t.k[ct][j][0];
+        a = mfma16(codes8_biased(c.x, c.y), qb.get(j, 0), a);
+        a = mfma16(codes8_biased(c.z, c.w), qb.get(j, 1), a);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zz[i] = a[i] * scale_of(t.ks[ct][i], 0);
+    } else {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < S::NJ; ++j) {
+        a = mfma16(f32x8_to_f16x8(t.k[ct][j][0], t.k[ct][j][S::KW > 1 ? 1 : 0]), qb.get(j, 0), a);
+        a = mfma16(f32x8_to_f16x8(t.k[ct][j][S::KW > 2 ? 2 : 0], t.k[ct][j][S::KW > 3 ? 3 : 0]), qb.get(j, 1), a);
+      }
+      zz = a;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[ct][i] = (16 * ct + 4 * q4 + i) < nvalid ? zz[i] * c2 : -INFINITY;
+  }
+
+  // ---- online softmax (base 2) -------------------------------------------------
+  float tmax = z[0][0];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, z[ct][i]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // tile max of head c16
+  const bool need = tmax > acc.m_ref + kTau;
+  if (__any(need)) {
+    const float m_new = need ? tmax : acc.m_ref;
+    const float alpha = need ? __builtin_amdgcn_exp2f(acc.m_ref - m_new) : 1.0f;
+    acc.m_ref = m_new;
+    // acc.o / acc.l rows are heads 4*q4 + i; lane h holds head h's alpha.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, 4 * q4 + i);
+#pragma unroll
+      for (int n = 0; n < S::VB; ++n) acc.o[n][i] *= ai;
+      acc.l[i] *= ai;
+    }
+  }
+  const float mu = acc.m_ref == -INFINITY ? 0.0f : acc.m_ref;
+  f16x8 pa;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pa[4 * ct + i] = (f16)__builtin_amdgcn_exp2f(z[ct][i] - mu);
+  return pa;
+}
+
+// V half of a tile: O += P . V_hat ;  l += P . 1.
+template <class S>
+__device__ __forceinline__ void tile_pv(const VRegs<S>& t, f16x8 pa, WaveAcc<S>& acc) {
+  if constexpr (S::VI8) {
+    constexpr uint32_t kNegBias = 0xE480E480u;  // fp16 pair (-1152, -1152)
+    f16x2 sv[4];
+#pragma unroll
+    for (int pi = 0; pi < 4; ++pi) sv[pi] = as_h2(__builtin_amdgcn_perm(t.vs[2 * pi + 1], t.vs[2 * pi], 0x05040100u));
+#pragma unroll
+    for (int w = 0; w < S::VW; ++w) {
+      uint32_t z01[4], z23[4];
+#pragma unroll
+      for (int pi = 0; pi < 4; ++pi) {
+        z01[pi] = zip_lo(t.v[2 * pi + 1][w], t.v[2 * pi][w]) ^ kCodeFlip;
+        z23[pi] = zip_hi(t.v[2 * pi + 1][w], t.v[2 * pi][w]) ^ kCodeFlip;
+      }
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        u32x4 r;
+#pragma unroll
+        for (int pi = 0; pi < 4; ++pi) {
+          const uint32_t src = bb < 2 ? z01[pi] : z23[pi];
+          const uint32_t biased = (bb & 1) ? biased_h2_hi(src) : biased_h2_lo(src);
+          const f16x2 c = as_h2(biased) + as_h2(kNegBias);  // exact code
+          r[pi] = as_u32(c * sv[pi]);                        // fp16(code * scale)
+        }
+        acc.o[4 * w + bb] = mfma16(pa, __builtin_bit_cast(f16x8, r), acc.o[4 * w + bb]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < S::VB; ++n) {
+      u32x4 r;
+#pragma unroll
+      for (int pi = 0; pi < 4; ++pi)
+        r[pi] = as_u32(__builtin_bit_cast(
+            f16x2, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, t.v[2 * pi][n]),
+                                              __builtin_bit_cast(float, t.v[2 * pi + 1][n]))));
+      acc.o[n] = mfma16(pa, __builtin_bit_cast(f16x8, r), acc.o[n]);
+    }
+  }
+  const f16x8 ones = {(f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1};
+  acc.l = mfma16(pa, ones, acc.l);
+}
+
+// ---- operand loads straight from HBM (any store dtype) --------------------------
+template <class S>
+__device__ __forceinline__ void load_tile_global(KRegs<S>& t, VRegs<S>& tv, __amdgpu_buffer_rsrc_t krs,
+                                                 __amdgpu_buffer_rsrc_t vrs, __amdgpu_buffer_rsrc_t ksrs,
+                                                 __amdgpu_buffer_rsrc_t vsrs, int p0, int end, uint32_t krow,
+                                                 uint32_t vrow, uint32_t srow, int c16, int q4) {
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int pk = p0 + 16 * ct + c16;
+    const uint32_t off = pk < end ? (uint32_t)pk * krow : kOOB;
+#pragma unroll
+    for (int j = 0; j < S::NJ; ++j)
+#pragma unroll
+      for (int m = 0; m < S::KW; ++m) t.k[ct][j][m] = ld128(krs, off + S::KE * (64 * j + 16 * q4) + 16 * m);
+  }
+  if constexpr (S::KI8) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ps = p0 + 16 * ct + 4 * q4 + i;
+        const uint32_t off = ps < end ? (uint32_t)ps * srow : kOOB;
+        if constexpr (S::SB == 8) {
+          const u32x2 v = ld64(ksrs, off);
+          t.ks[ct][i][0] = v.x;
+          t.ks[ct][i][S::NKS - 1] = v.y;
+        } else if constexpr (S::SB == 4) {
+          t.ks[ct][i][0] = ld32(ksrs, off);
+        } else {
+          t.ks[ct][i][0] = ld16(ksrs, off);
+        }
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int pv = p0 + kpos(e, q4);
+    const uint32_t off = pv < end ? (uint32_t)pv * vrow : kOOB;
+    const uint32_t base = off + S::VB * S::VE * c16;
+    if constexpr (S::VW == 1) {
+      tv.v[e][0] = ld32(vrs, base);
+    } else if constexpr (S::VW == 2) {
+      const u32x2 v = ld64(vrs, base);
+      tv.v[e][0] = v.x;
+      tv.v[e][S::VW - 1] = v.y;
+    } else {
+#pragma unroll
+      for (int m = 0; m < S::VW / 4; ++m) {
+        const u32x4 v = ld128(vrs, base + 16 * m);
+        tv.v[e][4 * m + 0] = v.x;
+        tv.v[e][4 * m + 1] = v.y;
+        tv.v[e][4 * m + 2] = v.z;
+        tv.v[e][4 * m + 3] = v.w;
+      }
+    }
+    if constexpr (S::VI8) {
+      const int grp = S::G64 ? (S::VB * c16) / 64 : 0;
+      tv.vs[e] = ld16(vsrs, pv < end ? (uint32_t)pv * srow + 2 * grp : kOOB);
+    }
+  }
+}
+
+// ---- LDS staging for int8 K and V --------------------------------------------------
+// Stage layout (bytes): K codes [0, 32D), V codes [32D, 64D), K scales
+// [64D, 64D+256), V scales [64D+256, 64D+512). Row r of a code tile holds its
+// 16-byte chunk c at chunk slot c ^ swz(r).
+template <class S>
+struct Stage {
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 32 * S::D;
+  static constexpr int KS_OFF = 64 * S::D;
+  static constexpr int VS_OFF = 64 * S::D + 256;
+  static constexpr int BYTES = 64 * S::D + 512;
+  // Rows per 256 bytes (the LDS bank width) = 16 / CH; spreading consecutive
+  // such row groups over distinct chunk slots keeps 16 lanes that read 16
+  // different rows at one column on 16 distinct bank groups.
+  static __device__ __forceinline__ int swz(int r) {
+    constexpr int SH = S::CH == 16 ? 0 : (S::CH == 8 ? 1 : 2);
+    return (r >> SH) & (S::CH - 1);
+  }
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <class S>
+__device__ __forceinline__ void stage_issue(uint8_t* st, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                            __amdgpu_buffer_rsrc_t ksrs, __amdgpu_buffer_rsrc_t vsrs, int p0,
+                                            int nvalid, uint32_t row, uint32_t srow, int lane) {
+  using T = Stage<S>;
+  constexpr int NI = 32 * S::D / 1024;  // 1 KiB direct-to-LDS loads per code tile
+  const uint32_t soff = (uint32_t)p0 * row;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int slot = i * 64 + lane;
+    const int r = slot / S::CH;
+    const int c = (slot % S::CH) ^ T::swz(r);
+    const uint32_t voff = r < nvalid ? (uint32_t)r * row + 16 * c : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(st + T::K_OFF + 1024 * i), 16, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(st + T::V_OFF + 1024 * i), 16, voff, soff, 0, 0);
+  }
+  const uint32_t ssoff = (uint32_t)p0 * srow;
+  const int nv = nvalid < 32 ? nvalid : 32;
+  if constexpr (S::SB >= 4) {
+    constexpr int PER = S::SB / 4;  // dwords per row
+    const int r = lane / PER;
+    const uint32_t voff = r < nv ? (uint32_t)r * srow + 4 * (lane % PER) : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrs, (lds_ptr_t)(st + T::KS_OFF), 4, voff, ssoff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vsrs, (lds_ptr_t)(st + T::VS_OFF), 4, voff, ssoff, 0, 0);
+  } else {
+    const uint32_t voff = lane < nv ? (uint32_t)lane * srow : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrs, (lds_ptr_t)(st + T::KS_OFF), 2, voff, ssoff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vsrs, (lds_ptr_t)(st + T::VS_OFF), 2, voff, ssoff, 0, 0);
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void stage_read_k(KRegs<S>& t, const uint8_t* st, int c16, int q4) {
+  using T = Stage<S>;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int r = 16 * ct + c16;
+#pragma unroll
+    for (int j = 0; j < S::NJ; ++j) {
+      const int slot = (4 * j + q4) ^ T::swz(r);
+      t.k[ct][j][0] = *reinterpret_cast<const u32x4*>(st + T::K_OFF + r * S::D + 16 * slot);
+    }
+    const uint8_t* ksp = st + T::KS_OFF + (16 * ct + 4 * q4) * S::SB;
+    if constexpr (S::SB == 8) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(ksp);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(ksp + 16);
+      t.ks[ct][0][0] = a.x; t.ks[ct][0][S::NKS - 1] = a.y;
+      t.ks[ct][1][0] = a.z; t.ks[ct][1][S::NKS - 1] = a.w;
+      t.ks[ct][2][0] = b.x; t.ks[ct][2][S::NKS - 1] = b.y;
+      t.ks[ct][3][0] = b.z; t.ks[ct][3][S::NKS - 1] = b.w;
+    } else if constexpr (S::SB == 4) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(ksp);
+      t.ks[ct][0][0] = a.x;
+      t.ks[ct][1][0] = a.y;
+      t.ks[ct][2][0] = a.z;
+      t.ks[ct][3][0] = a.w;
+    } else {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(ksp);
+      t.ks[ct][0][0] = a.x & 0xffffu;
+      t.ks[ct][1][0] = a.x >> 16;
+      t.ks[ct][2][0] = a.y & 0xffffu;
+      t.ks[ct][3][0] = a.y >> 16;
+    }
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void stage_read_v(VRegs<S>& t, const uint8_t* st, int c16, int q4) {
+  using T = Stage<S>;
+  const int byte = S::VB * c16;
+  const int grp = S::G64 ? byte / 64 : 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = kpos(e, q4);
+    const uint8_t* p = st + T::V_OFF + r * S::D + 16 * ((byte / 16) ^ T::swz(r)) + (byte % 16);
+    if constexpr (S::VW == 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+      t.v[e][0] = v.x;
+      t.v[e][1] = v.y;
+      t.v[e][2] = v.z;
+      t.v[e][3] = v.w;
+    } else if constexpr (S::VW == 2) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+      t.v[e][0] = v.x;
+      t.v[e][S::VW - 1] = v.y;
+    } else {
+      t.v[e][0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+    t.vs[e] = *reinterpret_cast<const uint16_t*>(st + T::VS_OFF + r * S::SB + 2 * grp);
+  }
+}
+
+// One tile from an LDS stage: K operands, QK + softmax, then V operands, P.V.
+// The scheduling barrier keeps the V reads after the K half, so only one half's
+// operands occupy registers at a time.
+template <class S>
+__device__ __forceinline__ void tile_staged(const uint8_t* st, int nvalid, WaveAcc<S>& acc,
+                                            const QOperand<S>& qb, const float (&corr)[S::NG],
+                                            float c2, int c16, int q4) {
+  f16x8 pa;
+  {
+    KRegs<S> tk;
+    stage_read_k<S>(tk, st, c16, q4);
+    pa = tile_qk<S>(tk, nvalid, acc, qb, corr, c2, q4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  VRegs<S> tv;
+  stage_read_v<S>(tv, st, c16, q4);
+  tile_pv<S>(tv, pa, acc);
+}
+
+// ---- kernel ----------------------------------------------------------------------
 template <int D, bool KI8, bool VI8, bool G64, int NW>
 __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
-  constexpr int NJ = D / 64;            // 64-wide dim blocks per row (2 k-steps each)
-  constexpr int NG = G64 ? NJ : 1;      // scales per row
-  constexpr int VB = D / 16;            // V elements per lane per position = PV n-tiles
-  constexpr int KE = KI8 ? 1 : 4;       // K element bytes
-  constexpr int VE = VI8 ? 1 : 4;       // V element bytes
+  using S = Shape<D, KI8, VI8, G64>;
+  constexpr bool kStaged = KI8 && VI8;
+  constexpr int STAGE_BYTES = kStaged ? Stage<S>::BYTES : 16;
+  // Two distinct LDS objects, one per pipeline stage, so that waiting for one
+  // stage's loads never waits for the other's.
+  // Stage 0 doubles as the output-merge buffer once every wavefront is done.
+  constexpr int S0_BYTES = NW * STAGE_BYTES > 16 * D * 4 ? NW * STAGE_BYTES : 16 * D * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s0[S0_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_s1[NW][STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_q[16 * QOperand<S>::ROW];
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  float* const sm_o = reinterpret_cast<float*>(lds_s0);
 
   const int split = blockIdx.x;
   const int hk = blockIdx.y / a.head_blocks;
@@ -82,281 +473,122 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   const int end = (split == a.n_splits - 1) ? L : (int)min((int64_t)L, start64 + a.chunk);
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15;
   const int q4 = lane >> 4;
   const int nh = min(16, a.G - hblk * 16);
   const int hq0 = hk * a.G + hblk * 16;
 
   // ---- buffer resources of this (sequence, kv head) slice -------------------
-  const uint32_t krow = (uint32_t)(a.s_pos * KE);
-  const uint32_t vrow = (uint32_t)(a.s_pos * VE);
+  const uint32_t krow = (uint32_t)(a.s_pos * S::KE);
+  const uint32_t vrow = (uint32_t)(a.s_pos * S::VE);
   const uint32_t srow = (uint32_t)(a.ss_pos * 2);
   const int64_t st_off = (int64_t)b * a.s_seq + (int64_t)hk * a.s_head;
   const int64_t sc_off = (int64_t)b * a.ss_seq + (int64_t)hk * a.ss_head;
-  const auto krs = make_rsrc(static_cast<const char*>(a.k_store) + st_off * KE,
-                             (uint32_t)(((int64_t)(L - 1) * a.s_pos + D) * KE));
-  const auto vrs = make_rsrc(static_cast<const char*>(a.v_store) + st_off * VE,
-                             (uint32_t)(((int64_t)(L - 1) * a.s_pos + D) * VE));
-  const uint32_t sc_bytes = (uint32_t)(((int64_t)(L - 1) * a.ss_pos + NG) * 2);
+  const auto krs = make_rsrc(static_cast<const char*>(a.k_store) + st_off * S::KE,
+                             (uint32_t)(((int64_t)(L - 1) * a.s_pos + D) * S::KE));
+  const auto vrs = make_rsrc(static_cast<const char*>(a.v_store) + st_off * S::VE,
+                             (uint32_t)(((int64_t)(L - 1) * a.s_pos + D) * S::VE));
+  const uint32_t sc_bytes = (uint32_t)(((int64_t)(L - 1) * a.ss_pos + S::NG) * 2);
   const auto ksrs = make_rsrc(KI8 ? static_cast<const void*>(a.k_scales + sc_off) : nullptr, KI8 ? sc_bytes : 0u);
   const auto vsrs = make_rsrc(VI8 ? static_cast<const void*>(a.v_scales + sc_off) : nullptr, VI8 ? sc_bytes : 0u);
 
-  // ---- query operand (B of S^T = K.Q^T): lane = (head c16, k-group q4) -------
-  // k-step 2j+u of the contraction covers dims 64j + 16*q4 + 8u + [0, 8).
-  f16x8 qb[NJ][2];
-  float qsum[NJ];
+  constexpr int STEP = NW * kTile;
+  int p0 = start + wv * kTile;
+  if constexpr (kStaged) {  // first tile in flight while the query is prepared
+    if (p0 < end) stage_issue<S>(lds_s0 + wv * STAGE_BYTES, krs, vrs, ksrs, vsrs, p0, end - p0, krow, srow, lane);
+  }
+
+  // ---- query operand: heads hq0.. of this block into LDS (zero rows beyond nh);
+  // per-group sums of q give the accumulator start values -1152 * sum(q) that
+  // cancel the +1152 code bias.
+  float corr[S::NG];
   {
+    float qsum[S::NJ];
     const bool has = c16 < nh;
     const uint16_t* qp = a.q + ((int64_t)b * a.n_q + hq0 + (has ? c16 : 0)) * D + 16 * q4;
+    uint8_t* qdst = lds_q + c16 * QOperand<S>::ROW + 32 * q4;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    for (int j = 0; j < S::NJ; ++j) {
       u32x4 x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
       if (has) {
         x0 = *reinterpret_cast<const u32x4*>(qp + 64 * j);
         x1 = *reinterpret_cast<const u32x4*>(qp + 64 * j + 8);
       }
-      qb[j][0] = __builtin_bit_cast(f16x8, x0);
-      qb[j][1] = __builtin_bit_cast(f16x8, x1);
+      if (wv == 0) {
+        *reinterpret_cast<u32x4*>(qdst + 128 * j) = x0;
+        *reinterpret_cast<u32x4*>(qdst + 128 * j + 16) = x1;
+      }
+      const f16x8 h0 = __builtin_bit_cast(f16x8, x0), h1 = __builtin_bit_cast(f16x8, x1);
       float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += (float)qb[j][0][e] + (float)qb[j][1][e];
+      for (int e = 0; e < 8; ++e) s += (float)h0[e] + (float)h1[e];
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
       qsum[j] = s;  // sum of q over the 64 dims of block j, for head c16
     }
-  }
-  // Accumulator start values that cancel the +1152 code bias (per scale group).
-  f32x4 cinit[NG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    float s = 0.0f;
-    if (G64) {
-      s = qsum[g];
-    } else {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) s += qsum[j];
-    }
-    const float v = KI8 ? -kCodeBias * s : 0.0f;
-    cinit[g] = (f32x4){v, v, v, v};
-  }
-
-  f32x4 acc_o[VB];
-#pragma unroll
-  for (int t = 0; t < VB; ++t) acc_o[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  f32x4 acc_l = {0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;
-  const f16x8 ones = {(f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1};
-
-  for (int p0 = start + wv * kTile; p0 < end; p0 += NW * kTile) {
-    // ---- issue all loads of the tile ----------------------------------------
-    // K rows for the A operand: row c16 of C-tile ct is position p0 + 16ct + c16.
-    u32x4 kr[2][NJ][KI8 ? 1 : 4];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int pk = p0 + 16 * ct + c16;
-      const uint32_t off = pk < end ? (uint32_t)pk * krow : kOOB;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if (KI8) {
-          kr[ct][j][0] = ld128(krs, off + 64 * j + 16 * q4);
-        } else {
-#pragma unroll
-          for (int m = 0; m < (KI8 ? 1 : 4); ++m) kr[ct][j][m] = ld128(krs, off + 4 * (64 * j + 16 * q4) + 16 * m);
-        }
-      }
-    }
-    // K scales for the C layout: lane (head c16, rows 4*q4+i) -> positions
-    // p0 + 16ct + 4q4 + i; all NG scales of the row.
-    uint32_t ks[2][4][NG > 1 ? NG / 2 : 1];
-    if (KI8) {
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ps = p0 + 16 * ct + 4 * q4 + i;
-          const uint32_t off = ps < end ? (uint32_t)ps * srow : kOOB;
-          if (NG == 4) {
-            const u32x2 v = ld64(ksrs, off);
-            ks[ct][i][0] = v.x;
-            ks[ct][i][NG > 1 ? 1 : 0] = v.y;
-          } else if (NG == 2) {
-            ks[ct][i][0] = ld32(ksrs, off);
-          } else {
-            ks[ct][i][0] = ld16(ksrs, off);
-          }
-        }
-    }
-    // V rows for the B operand of P.V: lane = (dim block c16, k-group q4);
-    // element e of the lane's k-slice is position p0 + kpos(e).
-    constexpr int VW = (VB * VE) / 4;  // dwords of V per lane per position
-    uint32_t vr[8][VW];
-    uint32_t vs[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pv = p0 + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4));
-      const uint32_t off = pv < end ? (uint32_t)pv * vrow : kOOB;
-      const uint32_t base = off + VB * VE * c16;
-      if (VW == 1) {
-        vr[e][0] = ld32(vrs, base);
-      } else if (VW == 2) {
-        const u32x2 v = ld64(vrs, base);
-        vr[e][0] = v.x;
-        vr[e][VW > 1 ? 1 : 0] = v.y;
+    for (int g = 0; g < S::NG; ++g) {
+      float t = 0.0f;
+      if (G64) {
+        t = qsum[g];
       } else {
 #pragma unroll
-        for (int m = 0; m < VW / 4; ++m) {
-          const u32x4 v = ld128(vrs, base + 16 * m);
-          vr[e][4 * m + 0] = v.x;
-          vr[e][4 * m + 1] = v.y;
-          vr[e][4 * m + 2] = v.z;
-          vr[e][4 * m + 3] = v.w;
-        }
+        for (int j = 0; j < S::NJ; ++j) t += qsum[j];
       }
-      if (VI8) {
-        const int grp = G64 ? (VB * c16) / 64 : 0;
-        const uint32_t soff = pv < end ? (uint32_t)pv * srow + 2 * grp : kOOB;
-        vs[e] = ld16(vsrs, soff);
-      }
+      corr[g] = KI8 ? -kCodeBias * t : 0.0f;
     }
+  }
+  __syncthreads();  // lds_q written by wavefront 0
+  const QOperand<S> qb{lds_q + c16 * QOperand<S>::ROW + 32 * q4};
 
-    // ---- S^T = K . Q^T ------------------------------------------------------
-    float z[2][4];
+  WaveAcc<S> acc;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      f32x4 zz = {0.f, 0.f, 0.f, 0.f};
-      if (KI8 && G64) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const u32x4 c = kr[ct][j][0];
-          f32x4 acc = mfma16(codes8_biased(c.x, c.y), qb[j][0], cinit[j]);
-          acc = mfma16(codes8_biased(c.z, c.w), qb[j][1], acc);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t pr = ks[ct][i][j / 2];
-            const float sc = h_bits_to_f32((j & 1) ? (pr >> 16) : (pr & 0xffffu));
-            zz[i] = fmaf(acc[i], sc, zz[i]);
-          }
-        }
-      } else if (KI8) {
-        f32x4 acc = cinit[0];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const u32x4 c = kr[ct][j][0];
-          acc = mfma16(codes8_biased(c.x, c.y), qb[j][0], acc);
-          acc = mfma16(codes8_biased(c.z, c.w), qb[j][1], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zz[i] = acc[i] * h_bits_to_f32(ks[ct][i][0] & 0xffffu);
-      } else {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          acc = mfma16(f32x8_to_f16x8(kr[ct][j][0], kr[ct][j][KI8 ? 0 : 1]), qb[j][0], acc);
-          acc = mfma16(f32x8_to_f16x8(kr[ct][j][KI8 ? 0 : 2], kr[ct][j][KI8 ? 0 : 3]), qb[j][1], acc);
-        }
-        zz = acc;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ps = p0 + 16 * ct + 4 * q4 + i;
-        z[ct][i] = ps < end ? zz[i] * a.c2 : -INFINITY;
-      }
-    }
+  for (int n = 0; n < S::VB; ++n) acc.o[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  acc.l = (f32x4){0.f, 0.f, 0.f, 0.f};
+  acc.m_ref = -INFINITY;
 
-    // ---- online softmax (base 2) over the tile --------------------------------
-    float tmax = z[0][0];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, z[ct][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // max over the tile for head c16
-    const bool need = tmax > m_ref + kTau;
-    if (__any(need)) {
-      const float m_new = need ? tmax : m_ref;
-      const float alpha = need ? exp2f(m_ref - m_new) : 1.0f;
-      m_ref = m_new;
-      // acc_o / acc_l rows are heads 4*q4 + i; lane h holds head h's alpha.
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, 4 * q4 + i);
-#pragma unroll
-        for (int t = 0; t < VB; ++t) acc_o[t][i] *= ai;
-        acc_l[i] *= ai;
-      }
+  if constexpr (kStaged) {
+    // Two-stage pipeline over this wavefront's tiles p0, p0 + STEP, ...
+    for (; p0 < end; p0 += 2 * STEP) {
+      const int p1 = p0 + STEP;
+      if (p1 < end) stage_issue<S>(lds_s1[wv], krs, vrs, ksrs, vsrs, p1, end - p1, krow, srow, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      tile_staged<S>(lds_s0 + wv * STAGE_BYTES, end - p0, acc, qb, corr, a.c2, c16, q4);
+      if (p1 >= end) break;
+      const int p2 = p1 + STEP;
+      if (p2 < end) stage_issue<S>(lds_s0 + wv * STAGE_BYTES, krs, vrs, ksrs, vsrs, p2, end - p2, krow, srow, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      tile_staged<S>(lds_s1[wv], end - p1, acc, qb, corr, a.c2, c16, q4);
     }
-    const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
-    f16x8 pa;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pa[4 * ct + i] = (f16)exp2f(z[ct][i] - mu);
-
-    // ---- O += P . V_hat ;  l += P . 1 --------------------------------------------
-    if (VI8) {
-      f16x2 sv[4];
-      constexpr uint32_t kNegBias = 0xE480E480u;  // fp16 pair (-1152, -1152)
-#pragma unroll
-      for (int pi = 0; pi < 4; ++pi) sv[pi] = as_h2((vs[2 * pi] & 0xffffu) | (vs[2 * pi + 1] << 16));
-#pragma unroll
-      for (int w = 0; w < VW; ++w) {
-        uint32_t z01[4], z23[4];
-#pragma unroll
-        for (int pi = 0; pi < 4; ++pi) {
-          z01[pi] = zip_lo(vr[2 * pi + 1][w], vr[2 * pi][w]) ^ kCodeFlip;
-          z23[pi] = zip_hi(vr[2 * pi + 1][w], vr[2 * pi][w]) ^ kCodeFlip;
-        }
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          u32x4 r;
-#pragma unroll
-          for (int pi = 0; pi < 4; ++pi) {
-            const uint32_t src = bb < 2 ? z01[pi] : z23[pi];
-            const uint32_t biased = (bb & 1) ? biased_h2_hi(src) : biased_h2_lo(src);
-            const f16x2 c = as_h2(biased) + as_h2(kNegBias);  // exact code
-            r[pi] = as_u32(c * sv[pi]);                        // fp16(code * scale)
-          }
-          acc_o[4 * w + bb] = mfma16(pa, __builtin_bit_cast(f16x8, r), acc_o[4 * w + bb]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < VB; ++t) {
-        u32x4 r;
-#pragma unroll
-        for (int pi = 0; pi < 4; ++pi)
-          r[pi] = as_u32(__builtin_bit_cast(
-              f16x2, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, vr[2 * pi][t]),
-                                                __builtin_bit_cast(float, vr[2 * pi + 1][t]))));
-        acc_o[t] = mfma16(pa, __builtin_bit_cast(f16x8, r), acc_o[t]);
-      }
+  } else {
+    for (; p0 < end; p0 += STEP) {
+      KRegs<S> tk;
+      VRegs<S> tv;
+      load_tile_global<S>(tk, tv, krs, vrs, ksrs, vsrs, p0, end, krow, vrow, srow, c16, q4);
+      const f16x8 pa = tile_qk<S>(tk, end - p0, acc, qb, corr, a.c2, q4);
+      tile_pv<S>(tv, pa, acc);
     }
-    acc_l = mfma16(pa, ones, acc_l);
   }
 
   // ---- merge the wavefronts of the workgroup -----------------------------------
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
-  __shared__ __attribute__((aligned(16))) float sm_o[16 * D];
-  if (q4 == 0) sm_m[wv][c16] = m_ref;
+  if (q4 == 0) sm_m[wv][c16] = acc.m_ref;
   if (c16 == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm_l[wv][4 * q4 + i] = acc_l[i];
+    for (int i = 0; i < 4; ++i) sm_l[wv][4 * q4 + i] = acc.l[i];
   }
   __syncthreads();
-  float mrow[4], frow[4];
+  float frow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * q4 + i;
     float M = -INFINITY;
 #pragma unroll
     for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
-    mrow[i] = M;
     const float mw = sm_m[wv][h];
-    frow[i] = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+    frow[i] = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
   }
-  // O rows of this lane: heads 4*q4+i, dims VB*c16 + t.
+  // O rows of this lane: heads 4*q4+i, dims VB*c16 + n. Wavefronts add in turn.
 #pragma unroll
   for (int k = 0; k < NW; ++k) {
     if (wv == k) {
@@ -364,12 +596,12 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int h = 4 * q4 + i;
         if (h < nh) {
-          float* dst = sm_o + h * D + VB * c16;
+          float* dst = sm_o + h * D + S::VB * c16;
 #pragma unroll
-          for (int t4 = 0; t4 < VB / 4; ++t4) {
-            float4 v = {acc_o[4 * t4 + 0][i] * frow[i], acc_o[4 * t4 + 1][i] * frow[i],
-                        acc_o[4 * t4 + 2][i] * frow[i], acc_o[4 * t4 + 3][i] * frow[i]};
-            float4* d4 = reinterpret_cast<float4*>(dst + 4 * t4);
+          for (int n4 = 0; n4 < S::VB / 4; ++n4) {
+            float4 v = {acc.o[4 * n4 + 0][i] * frow[i], acc.o[4 * n4 + 1][i] * frow[i],
+                        acc.o[4 * n4 + 2][i] * frow[i], acc.o[4 * n4 + 3][i] * frow[i]};
+            float4* d4 = reinterpret_cast<float4*>(dst + 4 * n4);
             if (k > 0) {
               const float4 o = *d4;
               v.x += o.x;
@@ -401,12 +633,11 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
       const float mk = sm_m[k][h];
-      if (mk != -INFINITY) l += sm_l[k][h] * exp2f(mk - M);
+      if (mk != -INFINITY) l += sm_l[k][h] * __builtin_amdgcn_exp2f(mk - M);
     }
     float2* ml = reinterpret_cast<float2*>(a.ws_ml) + row0 + (int64_t)h * a.n_splits;
     *ml = make_float2(M, l);
   }
-  (void)mrow;
 }
 
 template <int D, bool KI8, bool VI8, bool G64>

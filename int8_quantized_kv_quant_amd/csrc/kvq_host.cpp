@@ -123,9 +123,9 @@ int kvq_plan(const kvq_layout* layout, int32_t batch, int32_t n_q_heads, int32_t
     // Long splits keep the partial traffic near 1 % of the KV bytes ...
     chunk = ceil_div(part * 100, kv_pos);
     if (chunk < 512) chunk = 512;
-    // ... unless that leaves fewer than two workgroups per compute unit; then
-    // the chip is filled first.
-    const int64_t want_wg = 2 * (int64_t)n_cu;
+    // ... unless that leaves the chip less than one full wave of resident
+    // workgroups; then the chip is filled first.
+    const int64_t want_wg = (int64_t)resident_wgs_per_cu(L) * n_cu;
     if (units * ceil_div(l_eff, chunk) < want_wg) chunk = ceil_div(units * l_eff, want_wg);
     chunk = round_up(chunk < kTile ? kTile : chunk, kTile);
     const int64_t cap = round_up(l_eff, kTile);

@@ -26,6 +26,15 @@ int check_layout(const kvq_layout* L);
 // Checks pointer alignment of a store and its scale array for `L`.
 int check_store_ptrs(const kvq_layout& L, int dtype, const void* store, const void* scales);
 
+// Workgroups of the partial kernel that fit on one compute unit at once, for
+// this layout (from the kernels' LDS and register footprints on gfx950: the
+// LDS-staged int8 kernel holds two 32-position stages per wavefront).
+inline int resident_wgs_per_cu(const kvq_layout& L) {
+  if (L.head_dim == 256) return 1;
+  if (L.head_dim == 128) return 2;
+  return 3;
+}
+
 // Attended-range length bound used by the planner.
 inline int64_t effective_len(int64_t max_len, int32_t window) {
   return window > 0 && window < max_len ? window : max_len;
