@@ -312,7 +312,9 @@ __device__ __forceinline__ void load_tile_global(KRegs<S>& t, VRegs<S>& tv, __am
 // ---- LDS staging for int8 K and V --------------------------------------------------
 // Stage layout (bytes): K codes [0, 32D), V codes [32D, 64D), K scales
 // [64D, 64D+256), V scales [64D+256, 64D+512). Row r of a code tile holds its
-// 16-byte chunk c at chunk slot c ^ swz(r).
+// 16-byte chunk c at chunk slot c ^ swz(r). The scales of row r start at
+// r * SPITCH: a direct-to-LDS load places lane l's data at l * max(size, 4)
+// bytes, so 2-byte scale rows land 4 bytes apart.
 template <class S>
 struct Stage {
   static constexpr int K_OFF = 0;
@@ -320,6 +322,7 @@ struct Stage {
   static constexpr int KS_OFF = 64 * S::D;
   static constexpr int VS_OFF = 64 * S::D + 256;
   static constexpr int BYTES = 64 * S::D + 512;
+  static constexpr int SPITCH = S::SB >= 4 ? S::SB : 4;
   // Rows per 256 bytes (the LDS bank width) = 16 / CH; spreading consecutive
   // such row groups over distinct chunk slots keeps 16 lanes that read 16
   // different rows at one column on 16 distinct bank groups.
@@ -355,7 +358,7 @@ __device__ __forceinline__ void stage_issue(uint8_t* st, __amdgpu_buffer_rsrc_t 
     const uint32_t voff = r < nv ? (uint32_t)r * srow + 4 * (lane % PER) : kOOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrs, (lds_ptr_t)(st + T::KS_OFF), 4, voff, ssoff, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vsrs, (lds_ptr_t)(st + T::VS_OFF), 4, voff, ssoff, 0, 0);
-  } else {
+  } else {  // lane l = row l, written at byte 4l (see SPITCH); rows 32..63 read as 0
     const uint32_t voff = lane < nv ? (uint32_t)lane * srow : kOOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrs, (lds_ptr_t)(st + T::KS_OFF), 2, voff, ssoff, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vsrs, (lds_ptr_t)(st + T::VS_OFF), 2, voff, ssoff, 0, 0);
@@ -373,7 +376,7 @@ __device__ __forceinline__ void stage_read_k(KRegs<S>& t, const uint8_t* st, int
       const int slot = (4 * j + q4) ^ T::swz(r);
       t.k[ct][j][0] = *reinterpret_cast<const u32x4*>(st + T::K_OFF + r * S::D + 16 * slot);
     }
-    const uint8_t* ksp = st + T::KS_OFF + (16 * ct + 4 * q4) * S::SB;
+    const uint8_t* ksp = st + T::KS_OFF + (16 * ct + 4 * q4) * T::SPITCH;
     if constexpr (S::SB == 8) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(ksp);
       const u32x4 b = *reinterpret_cast<const u32x4*>(ksp + 16);
@@ -387,12 +390,12 @@ __device__ __forceinline__ void stage_read_k(KRegs<S>& t, const uint8_t* st, int
       t.ks[ct][1][0] = a.y;
       t.ks[ct][2][0] = a.z;
       t.ks[ct][3][0] = a.w;
-    } else {
-      const u32x2 a = *reinterpret_cast<const u32x2*>(ksp);
+    } else {  // one 2-byte scale per row, rows 4 bytes apart
+      const u32x4 a = *reinterpret_cast<const u32x4*>(ksp);
       t.ks[ct][0][0] = a.x & 0xffffu;
-      t.ks[ct][1][0] = a.x >> 16;
-      t.ks[ct][2][0] = a.y & 0xffffu;
-      t.ks[ct][3][0] = a.y >> 16;
+      t.ks[ct][1][0] = a.y & 0xffffu;
+      t.ks[ct][2][0] = a.z & 0xffffu;
+      t.ks[ct][3][0] = a.w & 0xffffu;
     }
   }
 }
@@ -419,7 +422,7 @@ __device__ __forceinline__ void stage_read_v(VRegs<S>& t, const uint8_t* st, int
     } else {
       t.v[e][0] = *reinterpret_cast<const uint32_t*>(p);
     }
-    t.vs[e] = *reinterpret_cast<const uint16_t*>(st + T::VS_OFF + r * S::SB + 2 * grp);
+    t.vs[e] = *reinterpret_cast<const uint16_t*>(st + T::VS_OFF + r * T::SPITCH + 2 * grp);
   }
 }
 
