@@ -13,6 +13,12 @@ The 132 MiB cache fits in the 256 MB Infinity Cache, so the timed steps rotate
 over 8 identical copies of the cache (1.1 GB): each step streams a copy that
 was not touched for 7 steps and has been evicted.
 
+Timing: the headline step time replays a HIP graph that holds one step per
+cache copy (split plan fixed at capture, context lengths read on the device),
+so kernels run back to back; per-kernel averages come from graphs of 8
+back-to-back launches of that kernel. Eager (per-launch, host-driven) step
+time is reported beside it.
+
 Prints one JSON line: value = KV bytes read per step / step time (GB/s), the
 roofline of the partial kernel from HIP events over the timed region, and the
 CPU oracle timed on a bounded sample of the same workload.
@@ -75,10 +81,14 @@ def cpu_baseline(w, lens, q, sm):
     L = int(lens[0])
     cache = orc.Cache(1, L, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
     cache.append(wl.kv_rows(w, "k", 0, 0, L)[None], wl.kv_rows(w, "v", 0, 0, L)[None], [0])
-    t0 = time.perf_counter()
-    want = orc.attend(q, cache, lens, 0, sm)
-    dt = time.perf_counter() - t0
-    return want, dt, cores
+    reps, t0 = 0, time.perf_counter()
+    while True:  # repeat the step until about 10 s of host work have been timed
+        want = orc.attend(q, cache, lens, 0, sm)
+        reps += 1
+        if time.perf_counter() - t0 >= 10.0:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    return want, dt, cores, reps
 
 
 def main() -> int:
@@ -88,6 +98,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--chunk", type=int, default=0, help="override the planner's split length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--order", choices=("pos", "head"), default="pos",
+                    help="cache layout: positions major (default) or heads major")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -111,7 +123,7 @@ def main() -> int:
     sm = 1.0 / math.sqrt(w.head_dim)
 
     log(f"filling the {L}-position cache (quantize-append of {L - 1} tokens)")
-    lay, cache0 = kvq_setup.fill_cache(w, lens, upto=np.array([L - 1]))
+    lay, cache0 = kvq_setup.fill_cache(w, lens, upto=np.array([L - 1]), order=args.order)
     k_new = torch.from_numpy(wl.kv_rows(w, "k", 0, L - 1, 1)).to(dev)
     v_new = torch.from_numpy(wl.kv_rows(w, "v", 0, L - 1, 1)).to(dev)
     start = torch.tensor([L - 1], dtype=torch.int32, device=dev)
@@ -144,6 +156,8 @@ def main() -> int:
             ev[3].record(stream)
 
     log(f"plan: n_splits={plan0.n_splits} chunk={plan0.chunk}; warmup {args.warmup} steps")
+    for c in caches:  # every copy holds the new token before anything is checked or timed
+        step(c)
     for i in range(args.warmup):
         step(caches[i % COPIES])
     torch.cuda.synchronize()
@@ -167,17 +181,18 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the full step")
-        want, cpu_s, cores = cpu_baseline(w, lens, q, sm)
+        want, cpu_s, cores, cpu_reps = cpu_baseline(w, lens, q, sm)
         max_err = float(np.abs(got - want).max())
         kv_bytes = wl.kv_bytes_per_step(w, lens)
         cpu = {"value": round(kv_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(cores),
                "kind": "oracle", "seconds": round(cpu_s, 3),
-               "sample": "full step: numpy fp64 decode attention of 16 query heads over the "
-                         "dequantized 131072-position cache (both kv heads); cache set-up not timed"}
+               "sample": f"full step repeated {cpu_reps}x (~10 s): numpy fp64 decode attention of 16 "
+                         "query heads over the dequantized 131072-position cache (both kv heads); "
+                         "cache set-up not timed"}
     else:
         max_err = None
 
-    log(f"timing {args.steps} steps over {COPIES} cache copies")
+    log(f"timing {args.steps} eager steps over {COPIES} cache copies")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -187,15 +202,55 @@ def main() -> int:
         step(caches[i % COPIES], evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    app = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    part = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    red = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    eager_ms = t_start.elapsed_time(t_end) / args.steps
+
+    # Graph-captured decode: one graph holds one step per cache copy (the split
+    # plan is fixed at capture; context lengths are read from device memory),
+    # so the kernels run back to back without host launch gaps.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in caches:
+                fn(c)
+        return g
+
+    def replay_ms(g, reps):
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * COPIES)
+
+    plan_g = plan0
+    reps = max(1, -(-args.steps // COPIES))
+    g_step = capture(lambda c: (
+        kvq.kv_quant_append(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], k_new, v_new, start, 1, 1),
+        kvq.kv_decode_attn_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], qd, 1, w.n_q_heads,
+                                  ld, 0, sm, plan_g, ws, ws.numel()),
+        kvq.kv_decode_reduce(lay, ws, ws.numel(), ld, 1, w.n_q_heads, 0, plan_g, out)))
+    log(f"timing {reps * COPIES} graph-replayed steps")
+    ms_per_step = replay_ms(g_step, reps)
+    graph_out = out.clone()
+    step(caches[COPIES - 1])  # eager step on the copy the graph ended with
+    torch.cuda.synchronize()
+    graph_matches_eager = bool(torch.equal(graph_out, out))
+    g_app = capture(lambda c: kvq.kv_quant_append(lay, c["k"], c["v"], c["k_scales"], c["v_scales"],
+                                                  k_new, v_new, start, 1, 1))
+    g_part = capture(lambda c: kvq.kv_decode_attn_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], qd, 1,
+                                                         w.n_q_heads, ld, 0, sm, plan_g, ws, ws.numel()))
+    g_red = capture(lambda c: kvq.kv_decode_reduce(lay, ws, ws.numel(), ld, 1, w.n_q_heads, 0, plan_g, out))
+    app_ms = replay_ms(g_app, reps)
+    part_ms = replay_ms(g_part, reps)
+    red_ms = replay_ms(g_red, reps)
 
     kv_bytes = wl.kv_bytes_per_step(w, lens)
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = kv_bytes / (part.mean() * 1e-3) / 1e9
+    achieved = kv_bytes / (part_ms * 1e-3) / 1e9
     digest = kernel_source_digest()
     traffic = traffic_from_profiles(digest)
 
@@ -217,20 +272,23 @@ def main() -> int:
         "config": {"workload": "long_128k", "batch": 1, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "scale_group": w.scale_group, "context": L,
                    "k_store": w.k_dtype, "v_store": w.v_dtype, "n_splits": plan0.n_splits,
-                   "chunk": plan0.chunk, "kv_bytes_per_step": kv_bytes, "cache_copies": COPIES},
-        "breakdown_us": {"append_plan": round(float(app.mean()) * 1e3, 2),
-                         "partial": round(float(part.mean()) * 1e3, 2),
-                         "reduce": round(float(red.mean()) * 1e3, 2)},
+                   "chunk": plan0.chunk, "kv_bytes_per_step": kv_bytes, "cache_copies": COPIES,
+                   "layout": "positions-major" if args.order == "pos" else "heads-major"},
+        "breakdown_us": {"append": round(app_ms * 1e3, 2), "partial": round(part_ms * 1e3, 2),
+                         "reduce": round(red_ms * 1e3, 2)},
+        "eager_us_per_step": round(eager_ms * 1e3, 2),
+        "graph": {"steps_per_graph": COPIES, "replays": reps, "matches_eager_bitwise": graph_matches_eager},
         "roofline": {"bound": "hbm", "kernel": "kvq_partial_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": kv_bytes,
-                     "avg_launch_us": round(float(part.mean()) * 1e3, 3), "kernel_src_sha": digest},
+                     "avg_launch_us": round(part_ms * 1e3, 3), "kernel_src_sha": digest},
         "parity": {"codes_scales_bitexact_sampled": codes_ok, "max_abs_err_vs_oracle": max_err,
                    "tol": TOL},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
-    return 0 if codes_ok and (max_err is None or max_err <= TOL) else 1
+    ok = codes_ok and graph_matches_eager and (max_err is None or max_err <= TOL)
+    return 0 if ok else 1
 
 
 if __name__ == "__main__":

@@ -122,19 +122,21 @@ __device__ __forceinline__ float scale_of(const uint32_t* packed, int j) {
 // tile's probabilities P (fp16) in the A-operand layout of P.V.
 // The query operand (B of S^T = K.Q^T) for lane (head c16, k-group q4) lives in
 // LDS, rows padded to break bank conflicts; k-step 2j+u covers dims
-// 64j + 16*q4 + 8u + [0, 8).
+// 64j + 16*q4 + 8u + [0, 8). `qp` points at the lane's row + 32*q4 bytes.
+// Every LDS pointer that the tile loop reads through is a __restrict__
+// parameter: the alias scopes this gives the reads let the compiler wait only
+// for the LDS stage being read, not for the stage that is still loading.
 template <class S>
 struct QOperand {
   static constexpr int ROW = 2 * S::D + 16;  // bytes per padded head row
-  const uint8_t* p;                          // this lane's row + 32*q4
-  __device__ __forceinline__ f16x8 get(int j, int u) const {
-    return *reinterpret_cast<const f16x8*>(p + 128 * j + 16 * u);
-  }
 };
+__device__ __forceinline__ f16x8 q_get(const uint8_t* __restrict__ qp, int j, int u) {
+  return *reinterpret_cast<const f16x8*>(qp + 128 * j + 16 * u);
+}
 
 template <class S>
 __device__ __forceinline__ f16x8 tile_qk(const KRegs<S>& t, int nvalid, WaveAcc<S>& acc,
-                                         const QOperand<S>& qb, const float (&corr)[S::NG],
+                                         const uint8_t* __restrict__ qb, const float (&corr)[S::NG],
                                          float c2, int q4) {
   float z[2][4];
 #pragma unroll
@@ -144,8 +146,8 @@ __device__ __forceinline__ f16x8 tile_qk(const KRegs<S>& t, int nvalid, WaveAcc<
 #pragma unroll
       for (int j = 0; j < S::NJ; ++j) {
         const u32x4 c = t.k[ct][j][0];
-        f32x4 a = mfma16(codes8_biased(c.x, c.y), qb.get(j, 0), (f32x4){corr[j], corr[j], corr[j], corr[j]});
-        a = mfma16(codes8_biased(c.z, c.w), qb.get(j, 1), a);
+        f32x4 a = mfma16(codes8_biased(c.x, c.y), q_get(qb, j, 0), (f32x4){corr[j], corr[j], corr[j], corr[j]});
+        a = mfma16(codes8_biased(c.z, c.w), q_get(qb, j, 1), a);
 #pragma unroll
         for (int i = 0; i < 4; ++i) zz[i] = fmaf(a[i], scale_of(t.ks[ct][i], j), zz[i]);
       }
@@ -154,8 +156,8 @@ __device__ __forceinline__ f16x8 tile_qk(const KRegs<S>& t, int nvalid, WaveAcc<
 #pragma unroll
       for (int j = 0; j < S::NJ; ++j) {
         const u32x4 c = t.k[ct][j][0];
-        a = mfma16(codes8_biased(c.x, c.y), qb.get(j, 0), a);
-        a = mfma16(codes8_biased(c.z, c.w), qb.get(j, 1), a);
+        a = mfma16(codes8_biased(c.x, c.y), q_get(qb, j, 0), a);
+        a = mfma16(codes8_biased(c.z, c.w), q_get(qb, j, 1), a);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) zz[i] = a[i] * scale_of(t.ks[ct][i], 0);
@@ -163,8 +165,8 @@ __device__ __forceinline__ f16x8 tile_qk(const KRegs<S>& t, int nvalid, WaveAcc<
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < S::NJ; ++j) {
-        a = mfma16(f32x8_to_f16x8(t.k[ct][j][0], t.k[ct][j][S::KW > 1 ? 1 : 0]), qb.get(j, 0), a);
-        a = mfma16(f32x8_to_f16x8(t.k[ct][j][S::KW > 2 ? 2 : 0], t.k[ct][j][S::KW > 3 ? 3 : 0]), qb.get(j, 1), a);
+        a = mfma16(f32x8_to_f16x8(t.k[ct][j][0], t.k[ct][j][S::KW > 1 ? 1 : 0]), q_get(qb, j, 0), a);
+        a = mfma16(f32x8_to_f16x8(t.k[ct][j][S::KW > 2 ? 2 : 0], t.k[ct][j][S::KW > 3 ? 3 : 0]), q_get(qb, j, 1), a);
       }
       zz = a;
     }
@@ -332,41 +334,92 @@ struct Stage {
   }
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) uint8_t* lds_u8_t;
 
+// Direct-to-LDS buffer loads, written as inline asm: the compiler's wait-count
+// insertion cannot tell which LDS bytes such a load writes and would make every
+// later LDS read wait for all of them, which serialises the two stages. Here
+// every wait for these loads is explicit (wait_vm below); the tile loop issues
+// no other vector-memory instruction, so counts are exact. Lane l's data lands
+// at M0 + l * max(bytes, 4). Writing M0 needs one wait state before the load.
+template <int BYTES>
+__device__ __forceinline__ void dma(u32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  if constexpr (BYTES == 16) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+  } else if constexpr (BYTES == 4) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+  } else {
+    static_assert(BYTES == 2, "direct-to-LDS load size");
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_ushort %1, %2, %3 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+  }
+}
+
+// Wait until at most N vector-memory operations of this wavefront are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// A raw buffer resource as four SGPRs: base, stride 0, size in bytes, flags.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r = {(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, kBufWord3};
+  r.x = __builtin_amdgcn_readfirstlane(r.x);
+  r.y = __builtin_amdgcn_readfirstlane(r.y);
+  r.z = __builtin_amdgcn_readfirstlane(r.z);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const uint8_t* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8_t)p);
+}
+
+// Direct-to-LDS loads that fill one half (K or V) of a stage: a code tile and
+// its scale rows.
 template <class S>
-__device__ __forceinline__ void stage_issue(uint8_t* st, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                            __amdgpu_buffer_rsrc_t ksrs, __amdgpu_buffer_rsrc_t vsrs, int p0,
-                                            int nvalid, uint32_t row, uint32_t srow, int lane) {
+constexpr int kHalfLoads = 32 * S::D / 1024 + 1;
+
+// Fill the K half (HALF = 0) or the V half (HALF = 1) of a stage with the tile
+// at position p0 (nvalid positions of it inside the split).
+template <class S, int HALF>
+__device__ __forceinline__ void stage_issue(uint8_t* st, const u32x4& rs, const u32x4& srs, int p0, int nvalid,
+                                            uint32_t row, uint32_t srow, int lane) {
   using T = Stage<S>;
   constexpr int NI = 32 * S::D / 1024;  // 1 KiB direct-to-LDS loads per code tile
-  const uint32_t soff = (uint32_t)p0 * row;
+  constexpr int CODE_OFF = HALF == 0 ? T::K_OFF : T::V_OFF;
+  constexpr int SCALE_OFF = HALF == 0 ? T::KS_OFF : T::VS_OFF;
+  // The half's previous contents were read by this wavefront: make sure those
+  // LDS reads have completed before new data can land.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const uint32_t base = lds_addr_of(st);
+  const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * row);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int slot = i * 64 + lane;
     const int r = slot / S::CH;
     const int c = (slot % S::CH) ^ T::swz(r);
     const uint32_t voff = r < nvalid ? (uint32_t)r * row + 16 * c : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(st + T::K_OFF + 1024 * i), 16, voff, soff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(st + T::V_OFF + 1024 * i), 16, voff, soff, 0, 0);
+    dma<16>(rs, base + CODE_OFF + 1024 * i, voff, soff);
   }
-  const uint32_t ssoff = (uint32_t)p0 * srow;
+  const uint32_t ssoff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * srow);
   const int nv = nvalid < 32 ? nvalid : 32;
   if constexpr (S::SB >= 4) {
     constexpr int PER = S::SB / 4;  // dwords per row
     const int r = lane / PER;
     const uint32_t voff = r < nv ? (uint32_t)r * srow + 4 * (lane % PER) : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrs, (lds_ptr_t)(st + T::KS_OFF), 4, voff, ssoff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vsrs, (lds_ptr_t)(st + T::VS_OFF), 4, voff, ssoff, 0, 0);
+    dma<4>(srs, base + SCALE_OFF, voff, ssoff);
   } else {  // lane l = row l, written at byte 4l (see SPITCH); rows 32..63 read as 0
     const uint32_t voff = lane < nv ? (uint32_t)lane * srow : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ksrs, (lds_ptr_t)(st + T::KS_OFF), 2, voff, ssoff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vsrs, (lds_ptr_t)(st + T::VS_OFF), 2, voff, ssoff, 0, 0);
+    dma<2>(srs, base + SCALE_OFF, voff, ssoff);
   }
 }
 
 template <class S>
-__device__ __forceinline__ void stage_read_k(KRegs<S>& t, const uint8_t* st, int c16, int q4) {
+__device__ __forceinline__ void stage_read_k(KRegs<S>& t, const uint8_t* __restrict__ st, int c16, int q4) {
   using T = Stage<S>;
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
@@ -401,7 +454,7 @@ __device__ __forceinline__ void stage_read_k(KRegs<S>& t, const uint8_t* st, int
 }
 
 template <class S>
-__device__ __forceinline__ void stage_read_v(VRegs<S>& t, const uint8_t* st, int c16, int q4) {
+__device__ __forceinline__ void stage_read_v(VRegs<S>& t, const uint8_t* __restrict__ st, int c16, int q4) {
   using T = Stage<S>;
   const int byte = S::VB * c16;
   const int grp = S::G64 ? byte / 64 : 0;
@@ -426,41 +479,23 @@ __device__ __forceinline__ void stage_read_v(VRegs<S>& t, const uint8_t* st, int
   }
 }
 
-// One tile from an LDS stage: K operands, QK + softmax, then V operands, P.V.
-// The scheduling barrier keeps the V reads after the K half, so only one half's
-// operands occupy registers at a time.
-template <class S>
-__device__ __forceinline__ void tile_staged(const uint8_t* st, int nvalid, WaveAcc<S>& acc,
-                                            const QOperand<S>& qb, const float (&corr)[S::NG],
-                                            float c2, int c16, int q4) {
-  f16x8 pa;
-  {
-    KRegs<S> tk;
-    stage_read_k<S>(tk, st, c16, q4);
-    pa = tile_qk<S>(tk, nvalid, acc, qb, corr, c2, q4);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  VRegs<S> tv;
-  stage_read_v<S>(tv, st, c16, q4);
-  tile_pv<S>(tv, pa, acc);
-}
-
 // ---- kernel ----------------------------------------------------------------------
 template <int D, bool KI8, bool VI8, bool G64, int NW>
 __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   using S = Shape<D, KI8, VI8, G64>;
   constexpr bool kStaged = KI8 && VI8;
   constexpr int STAGE_BYTES = kStaged ? Stage<S>::BYTES : 16;
-  // Two distinct LDS objects, one per pipeline stage, so that waiting for one
-  // stage's loads never waits for the other's.
-  // Stage 0 doubles as the output-merge buffer once every wavefront is done.
-  constexpr int S0_BYTES = NW * STAGE_BYTES > 16 * D * 4 ? NW * STAGE_BYTES : 16 * D * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s0[S0_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s1[NW][STAGE_BYTES];
+  // One stage per wavefront; the stages double as the output-merge buffer once
+  // every wavefront is done: one slot of 16 head rows per wavefront, rows padded
+  // by 16 bytes per 256 so that the lanes' float4 writes hit distinct banks.
+  constexpr int DP = D + D / 16;  // padded row length in floats
+  constexpr int MERGE_BYTES = NW * 16 * DP * 4;
+  constexpr int ST_BYTES = NW * STAGE_BYTES > MERGE_BYTES ? NW * STAGE_BYTES : MERGE_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_st[ST_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[16 * QOperand<S>::ROW];
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
-  float* const sm_o = reinterpret_cast<float*>(lds_s0);
+  float* const sm_o = reinterpret_cast<float*>(lds_st);
 
   const int split = blockIdx.x;
   const int hk = blockIdx.y / a.head_blocks;
@@ -498,8 +533,16 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
 
   constexpr int STEP = NW * kTile;
   int p0 = start + wv * kTile;
+  u32x4 krw = {0, 0, 0, 0}, vrw = krw, ksrw = krw, vsrw = krw;
   if constexpr (kStaged) {  // first tile in flight while the query is prepared
-    if (p0 < end) stage_issue<S>(lds_s0 + wv * STAGE_BYTES, krs, vrs, ksrs, vsrs, p0, end - p0, krow, srow, lane);
+    krw = rsrc_words(static_cast<const char*>(a.k_store) + st_off, (uint32_t)((int64_t)(L - 1) * a.s_pos + D));
+    vrw = rsrc_words(static_cast<const char*>(a.v_store) + st_off, (uint32_t)((int64_t)(L - 1) * a.s_pos + D));
+    ksrw = rsrc_words(a.k_scales + sc_off, sc_bytes);
+    vsrw = rsrc_words(a.v_scales + sc_off, sc_bytes);
+    if (p0 < end) {
+      stage_issue<S, 0>(lds_st + wv * STAGE_BYTES, krw, ksrw, p0, end - p0, krow, srow, lane);
+      stage_issue<S, 1>(lds_st + wv * STAGE_BYTES, vrw, vsrw, p0, end - p0, krow, srow, lane);
+    }
   }
 
   // ---- query operand: heads hq0.. of this block into LDS (zero rows beyond nh);
@@ -543,7 +586,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     }
   }
   __syncthreads();  // lds_q written by wavefront 0
-  const QOperand<S> qb{lds_q + c16 * QOperand<S>::ROW + 32 * q4};
+  const uint8_t* const qb = lds_q + c16 * QOperand<S>::ROW + 32 * q4;
 
   WaveAcc<S> acc;
 #pragma unroll
@@ -553,16 +596,28 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
 
   if constexpr (kStaged) {
     // Two-stage pipeline over this wavefront's tiles p0, p0 + STEP, ...
-    for (; p0 < end; p0 += 2 * STEP) {
-      const int p1 = p0 + STEP;
-      if (p1 < end) stage_issue<S>(lds_s1[wv], krs, vrs, ksrs, vsrs, p1, end - p1, krow, srow, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      tile_staged<S>(lds_s0 + wv * STAGE_BYTES, end - p0, acc, qb, corr, a.c2, c16, q4);
-      if (p1 >= end) break;
-      const int p2 = p1 + STEP;
-      if (p2 < end) stage_issue<S>(lds_s0 + wv * STAGE_BYTES, krs, vrs, ksrs, vsrs, p2, end - p2, krow, srow, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      tile_staged<S>(lds_s1[wv], end - p1, acc, qb, corr, a.c2, c16, q4);
+    // Per tile: K half landed -> K operands to registers -> next tile's K half
+    // starts loading -> S^T and softmax; then the same for the V half and P.V.
+    // Each half of the next tile is in flight for a whole tile of compute.
+    constexpr int NH = kHalfLoads<S>;
+    uint8_t* const st = lds_st + wv * STAGE_BYTES;
+    for (; p0 < end; p0 += STEP) {
+      const int pn = p0 + STEP;
+      const bool more = pn < end;
+      wait_vm<NH>();  // K half of this tile landed (its V half may still be loading)
+      f16x8 pa;
+      {
+        KRegs<S> tk;
+        stage_read_k<S>(tk, st, c16, q4);
+        if (more) stage_issue<S, 0>(st, krw, ksrw, pn, end - pn, krow, srow, lane);
+        pa = tile_qk<S>(tk, end - p0, acc, qb, corr, a.c2, q4);
+      }
+      if (more) wait_vm<NH>();  // V half landed; the next K half is in flight
+      else wait_vm<0>();
+      VRegs<S> tv;
+      stage_read_v<S>(tv, st, c16, q4);
+      if (more) stage_issue<S, 1>(st, vrw, vsrw, pn, end - pn, krow, srow, lane);
+      tile_pv<S>(tv, pa, acc);
     }
   } else {
     for (; p0 < end; p0 += STEP) {
@@ -591,41 +646,41 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     const float mw = sm_m[wv][h];
     frow[i] = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
   }
-  // O rows of this lane: heads 4*q4+i, dims VB*c16 + n. Wavefronts add in turn.
+  // Each wavefront writes its O rows (heads 4*q4+i, dims VB*c16 + n), scaled
+  // to the workgroup max, into its own slot; then all lanes sum the slots.
+  {
+    float* slot = sm_o + wv * 16 * DP;
 #pragma unroll
-  for (int k = 0; k < NW; ++k) {
-    if (wv == k) {
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * q4 + i;
+      if (h < nh) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 4 * q4 + i;
-        if (h < nh) {
-          float* dst = sm_o + h * D + S::VB * c16;
-#pragma unroll
-          for (int n4 = 0; n4 < S::VB / 4; ++n4) {
-            float4 v = {acc.o[4 * n4 + 0][i] * frow[i], acc.o[4 * n4 + 1][i] * frow[i],
-                        acc.o[4 * n4 + 2][i] * frow[i], acc.o[4 * n4 + 3][i] * frow[i]};
-            float4* d4 = reinterpret_cast<float4*>(dst + 4 * n4);
-            if (k > 0) {
-              const float4 o = *d4;
-              v.x += o.x;
-              v.y += o.y;
-              v.z += o.z;
-              v.w += o.w;
-            }
-            *d4 = v;
-          }
+        for (int n4 = 0; n4 < S::VB / 4; ++n4) {
+          const int d = S::VB * c16 + 4 * n4;
+          const float4 v = {acc.o[4 * n4 + 0][i] * frow[i], acc.o[4 * n4 + 1][i] * frow[i],
+                            acc.o[4 * n4 + 2][i] * frow[i], acc.o[4 * n4 + 3][i] * frow[i]};
+          *reinterpret_cast<float4*>(slot + h * DP + d + (d / 64) * 4) = v;
         }
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
   // ---- write the split's partial -----------------------------------------------
   const int64_t row0 = ((int64_t)b * a.n_q + hq0) * a.n_splits + split;
   for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
     const int h = idx / (D / 4);
-    const int d4 = idx % (D / 4);
-    const float4 v = reinterpret_cast<const float4*>(sm_o + h * D)[d4];
-    reinterpret_cast<float4*>(a.ws_o + (row0 + (int64_t)h * a.n_splits) * D)[d4] = v;
+    const int d = 4 * (idx % (D / 4));
+    const float* src = sm_o + h * DP + d + (d / 64) * 4;
+    float4 v = *reinterpret_cast<const float4*>(src);
+#pragma unroll
+    for (int k = 1; k < NW; ++k) {
+      const float4 u = *reinterpret_cast<const float4*>(src + k * 16 * DP);
+      v.x += u.x;
+      v.y += u.y;
+      v.z += u.z;
+      v.w += u.w;
+    }
+    reinterpret_cast<float4*>(a.ws_o + (row0 + (int64_t)h * a.n_splits) * D)[d / 4] = v;
   }
   if (threadIdx.x < nh) {
     const int h = threadIdx.x;
@@ -645,7 +700,9 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
 
 template <int D, bool KI8, bool VI8, bool G64>
 static void launch_partial_t(const PartialArgs& a, dim3 grid, hipStream_t s) {
-  constexpr int NW = 4;
+  // LDS-staged int8 kernels run 8 wavefronts (two per SIMD); the fp32-store
+  // variants keep their wider operands in registers and run 4.
+  constexpr int NW = (KI8 && VI8) ? 8 : 4;
   hipLaunchKernelGGL((kvq_partial_kernel<D, KI8, VI8, G64, NW>), grid, dim3(NW * 64), 0, s, a);
 }
 
