@@ -150,7 +150,10 @@ int kv_quant_append(const kvq_layout* layout, void* k_store, void* v_store,
  *   sm_scale    softmax scale applied to q.k (e.g. 1/sqrt(head_dim)).
  *   plan        from kvq_plan for at least this batch, n_q_heads and window.
  *   ws          device workspace of at least plan->ws_bytes bytes, 16-byte aligned;
- *               written here, read by kv_decode_reduce on the same stream.
+ *               written here, read by kv_decode_reduce on the same stream. Every
+ *               split records its (max, sum) pair, a split with no position in
+ *               the attended range as (-inf, 0); its output row is then left
+ *               unwritten. No initialization of ws is needed.
  * Device precondition: 0 <= d_seq_lens[b] <= max_ctx (larger values are clamped
  * to max_ctx). Keys are dequantized as code * scale; the fp32 store is read as
  * the fp16 values kv_quant_append widened into it. */
@@ -166,9 +169,12 @@ int kv_decode_attn_splitk(const kvq_layout* layout,
  * [G130: "a reduce kernel combines them"]. For each (b, hq): with split maxima
  * m_s, sums l_s and unnormalized outputs O_s, M = max m_s, w_s = exp(m_s - M),
  * out = sum_s w_s O_s / sum_s w_s l_s, rounded to fp16 (nearest even).
- * A sequence with no attended position (L_b = 0) gets an all-zero row.
+ * Splits recorded as empty add nothing; a sequence with no attended position
+ * (L_b = 0) gets an all-zero row.
  *   out  fp16 [batch][n_q_heads][head_dim], contiguous, 16-byte aligned.
- * The other arguments must equal those of the preceding kv_decode_attn_splitk. */
+ * The other arguments must equal those of the preceding kv_decode_attn_splitk
+ * (they are validated; the combine itself reads only ws, so it does not wait
+ * on d_seq_lens). */
 int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,
                      const int32_t* d_seq_lens, int32_t batch, int32_t n_q_heads,
                      int32_t window, const kvq_plan_t* plan, uint16_t* out,

@@ -50,10 +50,12 @@ __global__ __launch_bounds__(256) void kvq_append_kernel(AppendArgs a) {
   const int h = row % a.n_kv;
   const int t = (row / a.n_kv) % a.n_tok;
   const int b = row / (a.n_kv * a.n_tok);
+  // The row's values and its position are fetched together (neither waits for
+  // the other).
+  const u32x2 raw = *reinterpret_cast<const u32x2*>(S.src + (int64_t)row * D + 4 * lr);
   const int64_t pos = (int64_t)a.start_pos[b] + t;
   if (pos < 0 || pos >= a.max_ctx) return;
 
-  const u32x2 raw = *reinterpret_cast<const u32x2*>(S.src + (int64_t)row * D + 4 * lr);
   const uint32_t hb[4] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16};
   const int64_t row_off = b * a.s_seq + pos * a.s_pos + h * a.s_head;
 

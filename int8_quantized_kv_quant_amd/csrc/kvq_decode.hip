@@ -31,12 +31,14 @@
 // unnormalized O, after merging the wavefronts of the workgroup in LDS.
 //
 // Data movement. For int8 K and V the tiles are staged in LDS: each wavefront
-// owns two LDS stages and streams tile t+1 from HBM into one with direct-to-LDS
-// buffer loads (no registers held while in flight) while it computes tile t
-// from the other. Rows land as 16-byte chunks XOR-swizzled by row, so the
-// MFMA-layout reads are free of bank conflicts. A store with fp32 rows (k8v32,
-// k32v8, k32v32) is four times wider per position; those variants read their
-// operands straight from HBM into registers instead.
+// owns one stage with a K half and a V half, each refilled by direct-to-LDS
+// buffer loads (no registers held while in flight) as soon as the wavefront has
+// copied the half's current tile into registers, so every half is loading the
+// next tile for about one tile of compute. Rows land as 16-byte chunks
+// XOR-swizzled by row, so the MFMA-layout reads are free of bank conflicts. A
+// store with fp32 rows (k8v32, k32v8, k32v32) is four times wider per
+// position; those variants read their operands straight from HBM into
+// registers instead.
 //
 // Bounds. Every K/V/scale load goes through a buffer resource whose size ends
 // at the last row of the context, and positions outside the split get an
@@ -118,8 +120,6 @@ __device__ __forceinline__ float scale_of(const uint32_t* packed, int j) {
   return h_bits_to_f32((j & 1) ? (w >> 16) : (w & 0xffffu));
 }
 
-// K half of a tile: S^T = K.Q^T and the online-softmax update; returns the
-// tile's probabilities P (fp16) in the A-operand layout of P.V.
 // The query operand (B of S^T = K.Q^T) for lane (head c16, k-group q4) lives in
 // LDS, rows padded to break bank conflicts; k-step 2j+u covers dims
 // 64j + 16*q4 + 8u + [0, 8). `qp` points at the lane's row + 32*q4 bytes.
@@ -134,11 +134,22 @@ __device__ __forceinline__ f16x8 q_get(const uint8_t* __restrict__ qp, int j, in
   return *reinterpret_cast<const f16x8*>(qp + 128 * j + 16 * u);
 }
 
+// K half of a tile: the scaled, masked scores z (log2 domain) of the 32
+// positions x 16 heads of S^T = K.Q^T; lane (c16, q4) gets positions
+// 16*ct + 4*q4 + i of head c16.
 template <class S>
-__device__ __forceinline__ f16x8 tile_qk(const KRegs<S>& t, int nvalid, WaveAcc<S>& acc,
-                                         const uint8_t* __restrict__ qb, const float (&corr)[S::NG],
-                                         float c2, int q4) {
-  float z[2][4];
+__device__ __forceinline__ void tile_scores(const KRegs<S>& t, int nvalid, float (&z)[2][4],
+                                            const uint8_t* __restrict__ qb, const float (&corr)[S::NG],
+                                            float c2, int q4) {
+  // All query operand reads are issued before the first MFMA so that their LDS
+  // latency is paid once per tile.
+  f16x8 qv[S::NJ][2];
+#pragma unroll
+  for (int j = 0; j < S::NJ; ++j) {
+    qv[j][0] = q_get(qb, j, 0);
+    qv[j][1] = q_get(qb, j, 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     f32x4 zz = {0.f, 0.f, 0.f, 0.f};
@@ -146,8 +157,8 @@ __device__ __forceinline__ f16x8 tile_qk(const KRegs<S>& t, int nvalid, WaveAcc<
 #pragma unroll
       for (int j = 0; j < S::NJ; ++j) {
         const u32x4 c = t.k[ct][j][0];
-        f32x4 a = mfma16(codes8_biased(c.x, c.y), q_get(qb, j, 0), (f32x4){corr[j], corr[j], corr[j], corr[j]});
-        a = mfma16(codes8_biased(c.z, c.w), q_get(qb, j, 1), a);
+        f32x4 a = mfma16(codes8_biased(c.x, c.y), qv[j][0], (f32x4){corr[j], corr[j], corr[j], corr[j]});
+        a = mfma16(codes8_biased(c.z, c.w), qv[j][1], a);
 #pragma unroll
         for (int i = 0; i < 4; ++i) zz[i] = fmaf(a[i], scale_of(t.ks[ct][i], j), zz[i]);
       }
@@ -156,8 +167,8 @@ __device__ __forceinline__ f16x8 tile_qk(const KRegs<S>& t, int nvalid, WaveAcc<
 #pragma unroll
       for (int j = 0; j < S::NJ; ++j) {
         const u32x4 c = t.k[ct][j][0];
-        a = mfma16(codes8_biased(c.x, c.y), q_get(qb, j, 0), a);
-        a = mfma16(codes8_biased(c.z, c.w), q_get(qb, j, 1), a);
+        a = mfma16(codes8_biased(c.x, c.y), qv[j][0], a);
+        a = mfma16(codes8_biased(c.z, c.w), qv[j][1], a);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) zz[i] = a[i] * scale_of(t.ks[ct][i], 0);
@@ -165,8 +176,8 @@ __device__ __forceinline__ f16x8 tile_qk(const KRegs<S>& t, int nvalid, WaveAcc<
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < S::NJ; ++j) {
-        a = mfma16(f32x8_to_f16x8(t.k[ct][j][0], t.k[ct][j][S::KW > 1 ? 1 : 0]), q_get(qb, j, 0), a);
-        a = mfma16(f32x8_to_f16x8(t.k[ct][j][S::KW > 2 ? 2 : 0], t.k[ct][j][S::KW > 3 ? 3 : 0]), q_get(qb, j, 1), a);
+        a = mfma16(f32x8_to_f16x8(t.k[ct][j][0], t.k[ct][j][S::KW > 1 ? 1 : 0]), qv[j][0], a);
+        a = mfma16(f32x8_to_f16x8(t.k[ct][j][S::KW > 2 ? 2 : 0], t.k[ct][j][S::KW > 3 ? 3 : 0]), qv[j][1], a);
       }
       zz = a;
     }
@@ -174,14 +185,36 @@ __device__ __forceinline__ f16x8 tile_qk(const KRegs<S>& t, int nvalid, WaveAcc<
     for (int i = 0; i < 4; ++i) z[ct][i] = (16 * ct + 4 * q4 + i) < nvalid ? zz[i] * c2 : -INFINITY;
   }
 
+}
+
+// Maximum over lanes l, l ^ 16 and l ^ 32 without going through LDS:
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with
+// the even rows of its second, v_permlane32_swap the upper 32 lanes of the
+// first with the lower 32 of the second. With x in both operands, every lane
+// ends up holding its own value and that of its partner lane, one in each.
+__device__ __forceinline__ float max_xor16_xor32(float x) {
+  float y;
+  asm volatile("" : "=v"(y) : "0"(x));  // a second register holding x
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y), false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  x = fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+  asm volatile("" : "=v"(y) : "0"(x));
+  const auto u = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, y), false, false);
+  const uint32_t u0 = u[0], u1 = u[1];
+  return fmaxf(__builtin_bit_cast(float, u0), __builtin_bit_cast(float, u1));
+}
+
+// Online-softmax update for one tile's scores; returns the tile's
+// probabilities P (fp16) in the A-operand layout of P.V.
+template <class S>
+__device__ __forceinline__ f16x8 tile_softmax(const float (&z)[2][4], WaveAcc<S>& acc, int q4) {
   // ---- online softmax (base 2) -------------------------------------------------
   float tmax = z[0][0];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
     for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, z[ct][i]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));  // tile max of head c16
+  tmax = max_xor16_xor32(tmax);  // tile max of head c16
   const bool need = tmax > acc.m_ref + kTau;
   if (__any(need)) {
     const float m_new = need ? tmax : acc.m_ref;
@@ -205,16 +238,20 @@ __device__ __forceinline__ f16x8 tile_qk(const KRegs<S>& t, int nvalid, WaveAcc<
   return pa;
 }
 
-// V half of a tile: O += P . V_hat ;  l += P . 1.
-template <class S>
+// V half of a tile: O += P . V_hat ;  l += P . 1. PART 1 and 2 split the work
+// in two halves of the output columns (l goes with PART 2), so that a wait can
+// sit between them; PART 0 does all of it.
+template <class S, int PART = 0>
 __device__ __forceinline__ void tile_pv(const VRegs<S>& t, f16x8 pa, WaveAcc<S>& acc) {
+  constexpr int W0 = PART == 2 ? S::VW / 2 : 0, W1 = PART == 1 ? S::VW / 2 : S::VW;
+  constexpr int N0 = PART == 2 ? S::VB / 2 : 0, N1 = PART == 1 ? S::VB / 2 : S::VB;
   if constexpr (S::VI8) {
     constexpr uint32_t kNegBias = 0xE480E480u;  // fp16 pair (-1152, -1152)
     f16x2 sv[4];
 #pragma unroll
     for (int pi = 0; pi < 4; ++pi) sv[pi] = as_h2(__builtin_amdgcn_perm(t.vs[2 * pi + 1], t.vs[2 * pi], 0x05040100u));
 #pragma unroll
-    for (int w = 0; w < S::VW; ++w) {
+    for (int w = W0; w < W1; ++w) {
       uint32_t z01[4], z23[4];
 #pragma unroll
       for (int pi = 0; pi < 4; ++pi) {
@@ -236,7 +273,7 @@ __device__ __forceinline__ void tile_pv(const VRegs<S>& t, f16x8 pa, WaveAcc<S>&
     }
   } else {
 #pragma unroll
-    for (int n = 0; n < S::VB; ++n) {
+    for (int n = N0; n < N1; ++n) {
       u32x4 r;
 #pragma unroll
       for (int pi = 0; pi < 4; ++pi)
@@ -246,8 +283,10 @@ __device__ __forceinline__ void tile_pv(const VRegs<S>& t, f16x8 pa, WaveAcc<S>&
       acc.o[n] = mfma16(pa, __builtin_bit_cast(f16x8, r), acc.o[n]);
     }
   }
-  const f16x8 ones = {(f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1};
-  acc.l = mfma16(pa, ones, acc.l);
+  if constexpr (PART != 1) {
+    const f16x8 ones = {(f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1};
+    acc.l = mfma16(pa, ones, acc.l);
+  }
 }
 
 // ---- operand loads straight from HBM (any store dtype) --------------------------
@@ -385,6 +424,12 @@ constexpr int kHalfLoads = 32 * S::D / 1024 + 1;
 
 // Fill the K half (HALF = 0) or the V half (HALF = 1) of a stage with the tile
 // at position p0 (nvalid positions of it inside the split).
+//
+// Bounds: a row the tile does not own gets the out-of-range offset kOOB in its
+// lane offset, so it reads as zeros. The lane offset is the only part of the
+// address that the buffer range check is sure to cover (the uniform soffset
+// may not be), so no row beyond the split is ever fetched from memory; a full
+// tile (nvalid >= 32) has no such row and skips the selects.
 template <class S, int HALF>
 __device__ __forceinline__ void stage_issue(uint8_t* st, const u32x4& rs, const u32x4& srs, int p0, int nvalid,
                                             uint32_t row, uint32_t srow, int lane) {
@@ -397,16 +442,24 @@ __device__ __forceinline__ void stage_issue(uint8_t* st, const u32x4& rs, const 
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   const uint32_t base = lds_addr_of(st);
   const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * row);
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
+  auto code_off = [&](int i) {
     const int slot = i * 64 + lane;
     const int r = slot / S::CH;
     const int c = (slot % S::CH) ^ T::swz(r);
-    const uint32_t voff = r < nvalid ? (uint32_t)r * row + 16 * c : kOOB;
-    dma<16>(rs, base + CODE_OFF + 1024 * i, voff, soff);
+    return (uint32_t)r * row + 16 * c;
+  };
+  if (nvalid >= kTile) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma<16>(rs, base + CODE_OFF + 1024 * i, code_off(i), soff);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (i * 64 + lane) / S::CH;
+      dma<16>(rs, base + CODE_OFF + 1024 * i, r < nvalid ? code_off(i) : kOOB, soff);
+    }
   }
   const uint32_t ssoff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * srow);
-  const int nv = nvalid < 32 ? nvalid : 32;
+  const int nv = nvalid < kTile ? nvalid : kTile;
   if constexpr (S::SB >= 4) {
     constexpr int PER = S::SB / 4;  // dwords per row
     const int r = lane / PER;
@@ -479,34 +532,47 @@ __device__ __forceinline__ void stage_read_v(VRegs<S>& t, const uint8_t* __restr
   }
 }
 
+// Float4 position of float4 f of a merge-slot row. The 16 lanes that write one
+// row at a time hold f = 4c + n for c = 0..15: XOR-ing bits 0-1 with bits 4-5
+// spreads them over the 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int merge_swz(int f) { return f ^ ((f >> 4) & 3); }
+
 // ---- kernel ----------------------------------------------------------------------
 template <int D, bool KI8, bool VI8, bool G64, int NW>
 __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   using S = Shape<D, KI8, VI8, G64>;
   constexpr bool kStaged = KI8 && VI8;
   constexpr int STAGE_BYTES = kStaged ? Stage<S>::BYTES : 16;
-  // One stage per wavefront; the stages double as the output-merge buffer once
-  // every wavefront is done: one slot of 16 head rows per wavefront, rows padded
-  // by 16 bytes per 256 so that the lanes' float4 writes hit distinct banks.
-  constexpr int DP = D + D / 16;  // padded row length in floats
-  constexpr int MERGE_BYTES = NW * 16 * DP * 4;
-  constexpr int ST_BYTES = NW * STAGE_BYTES > MERGE_BYTES ? NW * STAGE_BYTES : MERGE_BYTES;
+  // One stage per wavefront. After its last tile a wavefront reuses its own
+  // stage as its slot of the output merge (16 head rows of D floats, which fit
+  // in a stage), so no wavefront waits for another before writing its slot.
+  constexpr int SLOT_BYTES = 16 * D * 4;
+  constexpr int SLOT_PITCH = kStaged ? STAGE_BYTES : SLOT_BYTES;
+  static_assert(!kStaged || SLOT_BYTES <= STAGE_BYTES, "merge slot must fit in a stage");
+  constexpr int ST_BYTES = NW * SLOT_PITCH;
   __shared__ __attribute__((aligned(16))) uint8_t lds_st[ST_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[16 * QOperand<S>::ROW];
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
-  float* const sm_o = reinterpret_cast<float*>(lds_st);
 
   const int split = blockIdx.x;
   const int hk = blockIdx.y / a.head_blocks;
   const int hblk = blockIdx.y % a.head_blocks;
   const int b = blockIdx.z;
 
+  const int nh = min(16, a.G - hblk * 16);
+  const int hq0 = hk * a.G + hblk * 16;
+  const int64_t row0 = ((int64_t)b * a.n_q + hq0) * a.n_splits + split;
+  float2* const ml_out = reinterpret_cast<float2*>(a.ws_ml) + row0;
+
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
   const int lo = a.window > 0 ? max(0, L - a.window) : 0;
   const int64_t start64 = (int64_t)lo + (int64_t)split * a.chunk;
-  if (start64 >= L) return;  // empty split: the reduce never reads it
+  if (start64 >= L) {  // empty split: recorded as (m, l) = (-inf, 0), O not written
+    if (threadIdx.x < nh) ml_out[(int64_t)threadIdx.x * a.n_splits] = make_float2(-INFINITY, 0.0f);
+    return;
+  }
   const int start = (int)start64;
   const int end = (split == a.n_splits - 1) ? L : (int)min((int64_t)L, start64 + a.chunk);
 
@@ -514,8 +580,6 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15;
   const int q4 = lane >> 4;
-  const int nh = min(16, a.G - hblk * 16);
-  const int hq0 = hk * a.G + hblk * 16;
 
   // ---- buffer resources of this (sequence, kv head) slice -------------------
   const uint32_t krow = (uint32_t)(a.s_pos * S::KE);
@@ -595,90 +659,96 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   acc.m_ref = -INFINITY;
 
   if constexpr (kStaged) {
-    // Two-stage pipeline over this wavefront's tiles p0, p0 + STEP, ...
-    // Per tile: K half landed -> K operands to registers -> next tile's K half
-    // starts loading -> S^T and softmax; then the same for the V half and P.V.
-    // Each half of the next tile is in flight for a whole tile of compute.
+    // Pipeline over this wavefront's tiles p0, p0 + STEP, ... For tile t:
+    //   S^T from the K operands already in registers;
+    //   V half of t landed -> V operands to registers; softmax;
+    //   the V half starts loading tile t+1; first half of P.V;
+    //   K half of t+1 landed -> K operands to registers; second half of P.V;
+    //   the K half starts loading tile t+2.
+    // Every half is in flight for about one tile of compute, and the LDS reads
+    // of each half overlap the arithmetic that precedes their use.
     constexpr int NH = kHalfLoads<S>;
     uint8_t* const st = lds_st + wv * STAGE_BYTES;
+    KRegs<S> tk;
+    if (p0 < end) {
+      wait_vm<NH>();  // K half of the first tile landed (its V half may still be loading)
+      stage_read_k<S>(tk, st, c16, q4);
+      if (p0 + STEP < end) stage_issue<S, 0>(st, krw, ksrw, p0 + STEP, end - p0 - STEP, krow, srow, lane);
+    }
     for (; p0 < end; p0 += STEP) {
       const int pn = p0 + STEP;
       const bool more = pn < end;
-      wait_vm<NH>();  // K half of this tile landed (its V half may still be loading)
-      f16x8 pa;
-      {
-        KRegs<S> tk;
-        stage_read_k<S>(tk, st, c16, q4);
-        if (more) stage_issue<S, 0>(st, krw, ksrw, pn, end - pn, krow, srow, lane);
-        pa = tile_qk<S>(tk, end - p0, acc, qb, corr, a.c2, q4);
-      }
-      if (more) wait_vm<NH>();  // V half landed; the next K half is in flight
+      const bool more2 = pn + STEP < end;
+      float z[2][4];
+      tile_scores<S>(tk, end - p0, z, qb, corr, a.c2, q4);
+      if (more) wait_vm<NH>();  // V half of this tile landed; the next K half is in flight
       else wait_vm<0>();
       VRegs<S> tv;
       stage_read_v<S>(tv, st, c16, q4);
+      const f16x8 pa = tile_softmax<S>(z, acc, q4);
       if (more) stage_issue<S, 1>(st, vrw, vsrw, pn, end - pn, krow, srow, lane);
-      tile_pv<S>(tv, pa, acc);
+      tile_pv<S, 1>(tv, pa, acc);
+      if (more) {
+        wait_vm<NH>();  // K half of the next tile landed; its V half is in flight
+        stage_read_k<S>(tk, st, c16, q4);
+      }
+      tile_pv<S, 2>(tv, pa, acc);
+      if (more2) stage_issue<S, 0>(st, krw, ksrw, pn + STEP, end - pn - STEP, krow, srow, lane);
     }
   } else {
     for (; p0 < end; p0 += STEP) {
       KRegs<S> tk;
       VRegs<S> tv;
       load_tile_global<S>(tk, tv, krs, vrs, ksrs, vsrs, p0, end, krow, vrow, srow, c16, q4);
-      const f16x8 pa = tile_qk<S>(tk, end - p0, acc, qb, corr, a.c2, q4);
+      float z[2][4];
+      tile_scores<S>(tk, end - p0, z, qb, corr, a.c2, q4);
+      const f16x8 pa = tile_softmax<S>(z, acc, q4);
       tile_pv<S>(tv, pa, acc);
     }
   }
 
   // ---- merge the wavefronts of the workgroup -----------------------------------
+  // Each wavefront stores its unscaled O rows (in its own stage), its max and
+  // its sum; after one barrier every lane combines the wavefronts for one
+  // (head, 4 dims) with weights 2^(m_k - M).
   if (q4 == 0) sm_m[wv][c16] = acc.m_ref;
   if (c16 == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sm_l[wv][4 * q4 + i] = acc.l[i];
   }
-  __syncthreads();
-  float frow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * q4 + i;
-    float M = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
-    const float mw = sm_m[wv][h];
-    frow[i] = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
-  }
-  // Each wavefront writes its O rows (heads 4*q4+i, dims VB*c16 + n), scaled
-  // to the workgroup max, into its own slot; then all lanes sum the slots.
   {
-    float* slot = sm_o + wv * 16 * DP;
+    float* slot = reinterpret_cast<float*>(lds_st + wv * SLOT_PITCH);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * q4 + i;
       if (h < nh) {
 #pragma unroll
         for (int n4 = 0; n4 < S::VB / 4; ++n4) {
-          const int d = S::VB * c16 + 4 * n4;
-          const float4 v = {acc.o[4 * n4 + 0][i] * frow[i], acc.o[4 * n4 + 1][i] * frow[i],
-                            acc.o[4 * n4 + 2][i] * frow[i], acc.o[4 * n4 + 3][i] * frow[i]};
-          *reinterpret_cast<float4*>(slot + h * DP + d + (d / 64) * 4) = v;
+          const int f = (S::VB * c16 + 4 * n4) / 4;  // float4 index within the row
+          const float4 v = {acc.o[4 * n4 + 0][i], acc.o[4 * n4 + 1][i], acc.o[4 * n4 + 2][i], acc.o[4 * n4 + 3][i]};
+          reinterpret_cast<float4*>(slot + h * D)[merge_swz(f)] = v;
         }
       }
     }
   }
   __syncthreads();
-  // ---- write the split's partial -----------------------------------------------
-  const int64_t row0 = ((int64_t)b * a.n_q + hq0) * a.n_splits + split;
   for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
     const int h = idx / (D / 4);
     const int d = 4 * (idx % (D / 4));
-    const float* src = sm_o + h * DP + d + (d / 64) * 4;
-    float4 v = *reinterpret_cast<const float4*>(src);
+    float M = -INFINITY;
 #pragma unroll
-    for (int k = 1; k < NW; ++k) {
-      const float4 u = *reinterpret_cast<const float4*>(src + k * 16 * DP);
-      v.x += u.x;
-      v.y += u.y;
-      v.z += u.z;
-      v.w += u.w;
+    for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
+    const int f = merge_swz(d / 4);
+    float4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const float mk = sm_m[k][h];
+      const float wk = mk == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk - M);
+      const float4 u = reinterpret_cast<const float4*>(lds_st + k * SLOT_PITCH)[h * (D / 4) + f];
+      v.x = fmaf(wk, u.x, v.x);
+      v.y = fmaf(wk, u.y, v.y);
+      v.z = fmaf(wk, u.z, v.z);
+      v.w = fmaf(wk, u.w, v.w);
     }
     reinterpret_cast<float4*>(a.ws_o + (row0 + (int64_t)h * a.n_splits) * D)[d / 4] = v;
   }
@@ -693,8 +763,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       const float mk = sm_m[k][h];
       if (mk != -INFINITY) l += sm_l[k][h] * __builtin_amdgcn_exp2f(mk - M);
     }
-    float2* ml = reinterpret_cast<float2*>(a.ws_ml) + row0 + (int64_t)h * a.n_splits;
-    *ml = make_float2(M, l);
+    ml_out[(int64_t)h * a.n_splits] = make_float2(M, l);
   }
 }
 

@@ -198,7 +198,7 @@ int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,
   if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
   if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
   if (batch == 0) return KVQ_OK;
-  return launch_reduce(L, ws, d_seq_lens, batch, n_q_heads, window, *plan, out, stream);
+  return launch_reduce(L, ws, batch, n_q_heads, *plan, out, stream);
 }
 
 }  // extern "C"

@@ -55,8 +55,7 @@ int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store
                    int32_t batch, int32_t n_q_heads, const int32_t* d_seq_lens, int32_t window,
                    float sm_scale, const kvq_plan_t& plan, void* ws, void* stream);
 
-int launch_reduce(const kvq_layout& L, const void* ws, const int32_t* d_seq_lens, int32_t batch,
-                  int32_t n_q_heads, int32_t window, const kvq_plan_t& plan, uint16_t* out,
-                  void* stream);
+int launch_reduce(const kvq_layout& L, const void* ws, int32_t batch, int32_t n_q_heads,
+                  const kvq_plan_t& plan, uint16_t* out, void* stream);
 
 }  // namespace kvq

@@ -230,10 +230,12 @@ def test_head_major_layout_and_large_gqa_group():
 
 def test_poison_outside_the_attended_range():
     """NaN in fp32 stores beyond the context, inside the slot tail and before the
-    window; NaN scales beyond the context: none of it reaches the output."""
+    window; NaN scales beyond the context and before the window: none of it
+    reaches the output (k8v8 streams tiles through LDS, the mixed stores load
+    them into registers; both must leave such rows unread)."""
     kvq = _kvq()
     ks = _ks()
-    for kdt, vdt in (("fp32", "int8"), ("int8", "fp32")):
+    for kdt, vdt in (("fp32", "int8"), ("int8", "fp32"), ("int8", "int8")):
         w = wl.Workload("poison", 1, 8, 2, 128, 160, 64, 256, 0, 170, k_dtype=kdt, v_dtype=vdt, contexts=(256,))
         lay = ks.layout_for(w)
         cache = kvq.alloc_cache(lay, 1)
@@ -244,10 +246,16 @@ def test_poison_outside_the_attended_range():
                 cache[s + "_scales"].fill_(float("nan"))
         L, W = 200, 150
         ks.append_rows(lay, cache, 0, 0, wl.kv_rows(w, "k", 0, 0, L), wl.kv_rows(w, "v", 0, 0, L))
-        # NaN over the positions the window excludes, in the fp32 store
-        fp = "k" if kdt == "fp32" else "v"
-        idx = torch.arange(0, (L - W) * lay.s_pos, device="cuda")
-        cache[fp][idx] = float("nan")
+        # NaN over the positions the window excludes: the fp32 store's values,
+        # or the int8 stores' scales
+        if "fp32" in (kdt, vdt):
+            fp = "k" if kdt == "fp32" else "v"
+            idx = torch.arange(0, (L - W) * lay.s_pos, device="cuda")
+            cache[fp][idx] = float("nan")
+        else:
+            for s in ("k", "v"):
+                idx = torch.arange(0, (L - W) * lay.ss_pos, device="cuda")
+                cache[s + "_scales"][idx] = float("nan")
         lens = np.array([L], dtype=np.int32)
         q = wl.queries(w)
         got = _run(w, lay, cache, q, lens, W)
