@@ -2,8 +2,8 @@
 """Benchmark of one INT8-KV decode step on one MI355X.
 
 A step is the whole hot path for one new token of one sequence:
-  kv_quant_append (the token's K/V, 2 kv heads)  ->  kvq_plan (host)
-  ->  kv_decode_attn_splitk  ->  kv_decode_reduce
+  kvq_plan (host)  ->  kv_append_decode_splitk (the token's K/V quantized and
+  written into the cache, fused with the split-K partials)  ->  kv_decode_reduce
 on the long-context workload: batch 1, 16 query / 2 kv heads, head_dim 256,
 int8 codes with one fp16 scale per 64 values, context 131072 (K with 1 % outlier
 channels x20). Inputs are seeded synthetic data (workloads.py), resident in HBM
@@ -17,7 +17,8 @@ Timing: the headline step time replays a HIP graph that holds one step per
 cache copy (split plan fixed at capture, context lengths read on the device),
 so kernels run back to back; per-kernel averages come from graphs of 8
 back-to-back launches of that kernel. Eager (per-launch, host-driven) step
-time is reported beside it.
+time, and the same step as three calls (kv_quant_append, kv_decode_attn_splitk,
+kv_decode_reduce), are reported beside it.
 
 Prints one JSON line: value = KV bytes read per step / step time (GB/s), the
 roofline of the partial kernel from HIP events over the timed region, and the
@@ -96,7 +97,6 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--chunk", type=int, default=0, help="override the planner's split length")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--order", choices=("pos", "head"), default="pos",
                     help="cache layout: positions major (default) or heads major")
@@ -133,27 +133,31 @@ def main() -> int:
     caches = [cache0] + [{k: (None if t is None else t.clone()) for k, t in cache0.items()}
                          for _ in range(COPIES - 1)]
     plan0 = kvq.kvq_plan(lay, 1, w.n_q_heads, L, 0, n_cu)
-    if args.chunk:
-        n = -(-L // args.chunk)
-        plan0 = kvq.Plan(n, args.chunk, 1 * w.n_q_heads * n * (w.head_dim + 2) * 4)
-    ws = torch.empty(plan0.ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(plan0.ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(c, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    # The timed step: the new token's quantize-append fused into the split-K
+    # partials, then the reduce. The plan is made on the host every step.
+    def fused_partial(c, plan):
+        kvq.kv_append_decode_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], k_new, v_new, qd, 1,
+                                    w.n_q_heads, ld, 0, sm, plan, ws, ws.numel())
+
+    def reduce(plan):
+        kvq.kv_decode_reduce(lay, ws, ws.numel(), ld, 1, w.n_q_heads, 0, plan, out)
+
+    def step(c):
+        plan = kvq.kvq_plan(lay, 1, w.n_q_heads, L, 0, n_cu)
+        fused_partial(c, plan)
+        reduce(plan)
+
+    # The same step as three calls (append, partials, reduce), reported beside it.
+    def append(c):
         kvq.kv_quant_append(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], k_new, v_new, start, 1, 1)
-        plan = plan0 if args.chunk else kvq.kvq_plan(lay, 1, w.n_q_heads, L, 0, n_cu)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def partial(c, plan):
         kvq.kv_decode_attn_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], qd, 1, w.n_q_heads,
                                   ld, 0, sm, plan, ws, ws.numel())
-        if ev is not None:
-            ev[2].record(stream)
-        kvq.kv_decode_reduce(lay, ws, ws.numel(), ld, 1, w.n_q_heads, 0, plan, out)
-        if ev is not None:
-            ev[3].record(stream)
 
     log(f"plan: n_splits={plan0.n_splits} chunk={plan0.chunk}; warmup {args.warmup} steps")
     for c in caches:  # every copy holds the new token before anything is checked or timed
@@ -162,18 +166,21 @@ def main() -> int:
         step(caches[i % COPIES])
     torch.cuda.synchronize()
 
-    # Parity of the state being timed: codes/scales of sampled rows bit-exact,
-    # and one step's output against the fp64 oracle.
+    # Parity of the state being timed: codes/scales of sampled rows bit-exact
+    # (the last row is the one the fused step wrote), and one step's output
+    # against the fp64 oracle.
     log("checking codes and output against the oracle")
     rng = np.random.default_rng(11)
     pos = np.unique(np.concatenate([rng.integers(0, L, 2048), [L - 1]]))
-    k_all = wl.kv_rows(w, "k", 0, 0, L)
     codes_ok = True
-    for h in range(w.n_kv_heads):
-        want_c, want_s = orc.quantize_rows(k_all[pos, h], w.scale_group)
-        got_c = kvq_setup.rows_of(lay, caches[3]["k"], 0, pos, h)
-        got_s = kvq_setup.scales_of(lay, caches[3]["k_scales"], 0, pos, h)
-        codes_ok &= bool(np.array_equal(got_c, want_c) and np.array_equal(got_s.view(np.uint16), want_s.view(np.uint16)))
+    for kind in ("k", "v"):
+        rows = wl.kv_rows(w, kind, 0, 0, L)
+        for h in range(w.n_kv_heads):
+            want_c, want_s = orc.quantize_rows(rows[pos, h], w.scale_group)
+            got_c = kvq_setup.rows_of(lay, caches[3][kind], 0, pos, h)
+            got_s = kvq_setup.scales_of(lay, caches[3][kind + "_scales"], 0, pos, h)
+            codes_ok &= bool(np.array_equal(got_c, want_c) and
+                             np.array_equal(got_s.view(np.uint16), want_s.view(np.uint16)))
     step(caches[0])
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
@@ -193,13 +200,12 @@ def main() -> int:
         max_err = None
 
     log(f"timing {args.steps} eager steps over {COPIES} cache copies")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(caches[i % COPIES], evs[i])
+        step(caches[i % COPIES])
     t_end.record(stream)
     torch.cuda.synchronize()
     eager_ms = t_start.elapsed_time(t_end) / args.steps
@@ -228,29 +234,24 @@ def main() -> int:
 
     plan_g = plan0
     reps = max(1, -(-args.steps // COPIES))
-    g_step = capture(lambda c: (
-        kvq.kv_quant_append(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], k_new, v_new, start, 1, 1),
-        kvq.kv_decode_attn_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], qd, 1, w.n_q_heads,
-                                  ld, 0, sm, plan_g, ws, ws.numel()),
-        kvq.kv_decode_reduce(lay, ws, ws.numel(), ld, 1, w.n_q_heads, 0, plan_g, out)))
+    g_step = capture(lambda c: (fused_partial(c, plan_g), reduce(plan_g)))
     log(f"timing {reps * COPIES} graph-replayed steps")
     ms_per_step = replay_ms(g_step, reps)
     graph_out = out.clone()
     step(caches[COPIES - 1])  # eager step on the copy the graph ended with
     torch.cuda.synchronize()
     graph_matches_eager = bool(torch.equal(graph_out, out))
-    g_app = capture(lambda c: kvq.kv_quant_append(lay, c["k"], c["v"], c["k_scales"], c["v_scales"],
-                                                  k_new, v_new, start, 1, 1))
-    g_part = capture(lambda c: kvq.kv_decode_attn_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], qd, 1,
-                                                         w.n_q_heads, ld, 0, sm, plan_g, ws, ws.numel()))
-    g_red = capture(lambda c: kvq.kv_decode_reduce(lay, ws, ws.numel(), ld, 1, w.n_q_heads, 0, plan_g, out))
-    app_ms = replay_ms(g_app, reps)
-    part_ms = replay_ms(g_part, reps)
-    red_ms = replay_ms(g_red, reps)
+    # Per-kernel graphs (8 back-to-back launches each) for the breakdown and the
+    # roofline of the partial kernel; then the unfused three-call step.
+    fpart_ms = replay_ms(capture(lambda c: fused_partial(c, plan_g)), reps)
+    red_ms = replay_ms(capture(lambda c: reduce(plan_g)), reps)
+    unfused_ms = replay_ms(capture(lambda c: (append(c), partial(c, plan_g), reduce(plan_g))), reps)
+    app_ms = replay_ms(capture(append), reps)
+    part_ms = replay_ms(capture(lambda c: partial(c, plan_g)), reps)
 
     kv_bytes = wl.kv_bytes_per_step(w, lens)
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = kv_bytes / (part_ms * 1e-3) / 1e9
+    achieved = kv_bytes / (fpart_ms * 1e-3) / 1e9
     digest = kernel_source_digest()
     traffic = traffic_from_profiles(digest)
 
@@ -274,14 +275,17 @@ def main() -> int:
                    "k_store": w.k_dtype, "v_store": w.v_dtype, "n_splits": plan0.n_splits,
                    "chunk": plan0.chunk, "kv_bytes_per_step": kv_bytes, "cache_copies": COPIES,
                    "layout": "positions-major" if args.order == "pos" else "heads-major"},
-        "breakdown_us": {"append": round(app_ms * 1e3, 2), "partial": round(part_ms * 1e3, 2),
-                         "reduce": round(red_ms * 1e3, 2)},
+        "step": "kv_append_decode_splitk + kv_decode_reduce (quantize-append fused into the partials)",
+        "breakdown_us": {"append_and_partial": round(fpart_ms * 1e3, 2), "reduce": round(red_ms * 1e3, 2)},
+        "unfused_step_us": {"step": round(unfused_ms * 1e3, 2), "append": round(app_ms * 1e3, 2),
+                            "partial": round(part_ms * 1e3, 2), "reduce": round(red_ms * 1e3, 2)},
         "eager_us_per_step": round(eager_ms * 1e3, 2),
         "graph": {"steps_per_graph": COPIES, "replays": reps, "matches_eager_bitwise": graph_matches_eager},
-        "roofline": {"bound": "hbm", "kernel": "kvq_partial_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "kvq_partial_kernel (with the fused append)",
+                     "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": kv_bytes,
-                     "avg_launch_us": round(part_ms * 1e3, 3), "kernel_src_sha": digest},
+                     "avg_launch_us": round(fpart_ms * 1e3, 3), "kernel_src_sha": digest},
         "parity": {"codes_scales_bitexact_sampled": codes_ok, "max_abs_err_vs_oracle": max_err,
                    "tol": TOL},
         "cpu_baseline": cpu,

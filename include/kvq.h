@@ -7,6 +7,8 @@
  *   kv_quant_append        quantize new K/V rows and write them into the cache
  *   kv_decode_attn_splitk  split-K partial attention of one query token per
  *                          sequence (online-softmax partials per split)
+ *   kv_append_decode_splitk  the decode step's one-token quantize-append fused
+ *                          into kv_decode_attn_splitk
  *   kv_decode_reduce       combine the split partials into the fp16 output
  *   kvq_plan               host-only choice of the split count and workspace
  *
@@ -164,6 +166,32 @@ int kv_decode_attn_splitk(const kvq_layout* layout,
                           const int32_t* d_seq_lens, int32_t window, float sm_scale,
                           const kvq_plan_t* plan, void* ws, int64_t ws_bytes,
                           void* stream);
+
+/* kv_append_decode_splitk -- one decode step's quantize-append fused into the
+ * split-K partials. [G12 #64, #65], [G130], [S2698 "What it does"].
+ * For each sequence b with 1 <= L_b = d_seq_lens[b] <= max_ctx, the new token's
+ * K and V rows of every kv head are quantized exactly as kv_quant_append does
+ * (d_start_pos[b] = L_b - 1, n_tok = 1) and written to row L_b - 1 of the
+ * stores and scales; the partials are those of kv_decode_attn_splitk over
+ * [lo, L_b) with that row in place. The workgroup whose range holds position
+ * L_b - 1 takes the new row from its own quantizer, so within the call nothing
+ * reads that row from memory. A sequence with L_b = 0 or L_b > max_ctx gets
+ * no append (as kv_quant_append drops such rows) and the partials of
+ * kv_decode_attn_splitk.
+ *   k_new, v_new  fp16 [batch][n_kv_heads][head_dim] (one token per sequence),
+ *                 contiguous, 16-byte aligned.
+ *   other arguments as for kv_decode_attn_splitk; the stores and scales are
+ *   written, so they are not const here. Combine with kv_decode_reduce.
+ * Codes and scales are bit-identical to kv_quant_append's; the output of the
+ * reduce differs from the unfused pair only in the order in which the new
+ * position's term is summed. */
+int kv_append_decode_splitk(const kvq_layout* layout, void* k_store, void* v_store,
+                            uint16_t* k_scales, uint16_t* v_scales,
+                            const uint16_t* k_new, const uint16_t* v_new,
+                            const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                            const int32_t* d_seq_lens, int32_t window, float sm_scale,
+                            const kvq_plan_t* plan, void* ws, int64_t ws_bytes,
+                            void* stream);
 
 /* kv_decode_reduce -- combine the partials of kv_decode_attn_splitk.
  * [G130: "a reduce kernel combines them"]. For each (b, hq): with split maxima

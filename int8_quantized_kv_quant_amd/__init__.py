@@ -18,7 +18,8 @@ from dataclasses import dataclass
 __all__ = [
     "KVQ_STORE_INT8", "KVQ_STORE_FP32", "KvqError", "KvqLibraryMissing", "Layout", "Plan",
     "lib_path", "load", "kvq_version", "kvq_status_string", "kvq_plan", "kv_quant_append",
-    "kv_decode_attn_splitk", "kv_decode_reduce", "make_layout", "alloc_cache", "decode",
+    "kv_decode_attn_splitk", "kv_append_decode_splitk", "kv_decode_reduce", "make_layout",
+    "alloc_cache", "decode",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -26,8 +27,8 @@ KVQ_STORE_INT8 = 1
 KVQ_STORE_FP32 = 2
 _DT = {"int8": KVQ_STORE_INT8, "fp32": KVQ_STORE_FP32}
 
-EXPORTED_SYMBOLS = ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_decode_reduce",
-                    "kvq_status_string", "kvq_version")
+EXPORTED_SYMBOLS = ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
+                    "kv_decode_reduce", "kvq_status_string", "kvq_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -111,11 +112,14 @@ def load():
     lib.kvq_plan.argtypes = [LP, i32, i32, i32, i32, i32, PP]
     lib.kv_quant_append.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
     lib.kv_decode_attn_splitk.argtypes = [LP, vp, vp, vp, vp, vp, i32, i32, vp, i32, f32, PP, vp, i64, vp]
+    lib.kv_append_decode_splitk.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, f32, PP, vp,
+                                            i64, vp]
     lib.kv_decode_reduce.argtypes = [LP, vp, i64, vp, i32, i32, i32, PP, vp, vp]
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_version.argtypes = []
-    for fn in ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_decode_reduce", "kvq_version"):
+    for fn in ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
+               "kv_decode_reduce", "kvq_version"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -178,6 +182,15 @@ def kv_decode_attn_splitk(layout: Layout, k_store, v_store, k_scales, v_scales, 
         _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def kv_append_decode_splitk(layout: Layout, k_store, v_store, k_scales, v_scales, k_new, v_new, q,
+                            batch: int, n_q_heads: int, seq_lens, window: int, sm_scale: float,
+                            plan: Plan, ws, ws_bytes: int, stream=None) -> None:
+    _check("kv_append_decode_splitk", load().kv_append_decode_splitk(
+        ctypes.byref(layout.c()), _ptr(k_store), _ptr(v_store), _ptr(k_scales), _ptr(v_scales),
+        _ptr(k_new), _ptr(v_new), _ptr(q), batch, n_q_heads, _ptr(seq_lens), window, sm_scale,
+        ctypes.byref(plan.c()), _ptr(ws), ws_bytes, _stream(stream)))
+
+
 def kv_decode_reduce(layout: Layout, ws, ws_bytes: int, seq_lens, batch: int, n_q_heads: int,
                      window: int, plan: Plan, out, stream=None) -> None:
     _check("kv_decode_reduce", load().kv_decode_reduce(
@@ -227,9 +240,12 @@ def alloc_cache(layout: Layout, batch: int, device="cuda", fill=0):
 
 
 def decode(layout: Layout, cache: dict, q, seq_lens, window: int, sm_scale: float | None = None,
-           plan: Plan | None = None, ws=None, out=None, n_cu: int | None = None, stream=None):
-    """One decode step over an already-filled cache: kv_decode_attn_splitk then
-    kv_decode_reduce on the current stream. q: fp16 [batch][n_q][head_dim] on the
+           plan: Plan | None = None, ws=None, out=None, n_cu: int | None = None, stream=None,
+           new_kv=None):
+    """One decode step: kv_decode_attn_splitk then kv_decode_reduce on the
+    current stream; with new_kv = (k_new, v_new) (fp16 [batch][n_kv][head_dim] on
+    the device) the token's quantize-append is fused in (kv_append_decode_splitk,
+    appending at position seq_lens[b] - 1). q: fp16 [batch][n_q][head_dim] on the
     device; seq_lens: int32 [batch] on the device. Returns the fp16 output."""
     import torch
     batch, n_q, d = q.shape
@@ -243,7 +259,12 @@ def decode(layout: Layout, cache: dict, q, seq_lens, window: int, sm_scale: floa
         ws = torch.empty(max(plan.ws_bytes, 16), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((batch, n_q, d), dtype=torch.float16, device=q.device)
-    kv_decode_attn_splitk(layout, cache["k"], cache["v"], cache["k_scales"], cache["v_scales"], q,
-                          batch, n_q, seq_lens, window, sm_scale, plan, ws, ws.numel(), stream)
+    if new_kv is None:
+        kv_decode_attn_splitk(layout, cache["k"], cache["v"], cache["k_scales"], cache["v_scales"], q,
+                              batch, n_q, seq_lens, window, sm_scale, plan, ws, ws.numel(), stream)
+    else:
+        kv_append_decode_splitk(layout, cache["k"], cache["v"], cache["k_scales"], cache["v_scales"],
+                                new_kv[0], new_kv[1], q, batch, n_q, seq_lens, window, sm_scale, plan,
+                                ws, ws.numel(), stream)
     kv_decode_reduce(layout, ws, ws.numel(), seq_lens, batch, n_q, window, plan, out, stream)
     return out

@@ -10,11 +10,7 @@
 // 4, 2 or 1 rows. A 64-value scale group is 16 lanes; a per-row group is the
 // whole row. The group absmax is a butterfly max over those lanes.
 //
-// Arithmetic (bit-exact with the CPU definition): absmax is exact on the fp16
-// bit patterns; scale = fp16_rne(a / 127.0f) with a correctly rounded fp32
-// division; code = clamp(rint(x / scale), -127, 127) with a correctly rounded
-// fp32 division (x and scale are fp16, so the fp32 quotient rounds to the same
-// integer as the exact quotient, ties to even); code 0 where scale == 0.
+// Arithmetic: quantize4 (kvq_device.h), bit-exact with the CPU definition.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -66,30 +62,12 @@ __global__ __launch_bounds__(256) void kvq_append_kernel(AppendArgs a) {
     return;
   }
 
-  // |x| ordering of finite fp16 values equals the integer ordering of the
-  // bit patterns with the sign cleared.
-  uint32_t amax = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) amax = max(amax, hb[e] & 0x7fffu);
-  for (int o = 1; o < a.group_lanes; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
-
-  const float absmax = h_bits_to_f32(amax);
-  const f16 scale_h = (f16)(absmax / 127.0f);  // fp32 IEEE division, then fp16 RNE
-  const float scale = (float)scale_h;
-  uint32_t packed = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float c = 0.0f;
-    if (scale > 0.0f) {
-      c = __builtin_rintf(h_bits_to_f32(hb[e]) / scale);
-      c = fminf(fmaxf(c, -127.0f), 127.0f);
-    }
-    packed |= ((uint32_t)(int32_t)c & 0xffu) << (8 * e);
-  }
+  uint16_t scale_bits;
+  const uint32_t packed = quantize4(hb, a.group_lanes, &scale_bits);
   *reinterpret_cast<uint32_t*>(static_cast<int8_t*>(S.store) + row_off + 4 * lr) = packed;
   if (lr % a.group_lanes == 0) {
     const int64_t soff = b * a.ss_seq + pos * a.ss_pos + h * a.ss_head + lr / a.group_lanes;
-    S.scales[soff] = __builtin_bit_cast(uint16_t, scale_h);
+    S.scales[soff] = scale_bits;
   }
 }
 

@@ -58,6 +58,12 @@ struct PartialArgs {
   const void* v_store;
   const uint16_t* k_scales;
   const uint16_t* v_scales;
+  // Fused append: the new token's K and V rows, fp16 [B][n_kv][D] (null: none).
+  // Row L - 1 of the stores and scales is then written (through the pointers
+  // above, which the fused entry point receives writable).
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int32_t group_lanes;  // lanes of one scale group for the quantizer (4 values each)
   const uint16_t* q;
   const int32_t* seq_lens;
   float* ws_o;   // [B][Hq][n_splits][D]
@@ -554,6 +560,14 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[16 * QOperand<S>::ROW];
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
+  // The new token's rows when the append is fused ([0] = K, [1] = V): the fp16
+  // input (landing place of its direct-to-LDS load), the dequantized values,
+  // the codes and scales (for the cache), and the new position's scores.
+  __shared__ __attribute__((aligned(16))) uint16_t nw_in[2][D];
+  __shared__ __attribute__((aligned(16))) float nw_val[2][D];
+  __shared__ __attribute__((aligned(16))) uint32_t nw_code[2][D / 4];
+  __shared__ uint16_t nw_scale[2][S::NG];
+  __shared__ float nw_z[16];
 
   const int split = blockIdx.x;
   const int hk = blockIdx.y / a.head_blocks;
@@ -565,8 +579,8 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   const int64_t row0 = ((int64_t)b * a.n_q + hq0) * a.n_splits + split;
   float2* const ml_out = reinterpret_cast<float2*>(a.ws_ml) + row0;
 
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
+  const int L_in = a.seq_lens[b];
+  const int L = L_in < 0 ? 0 : (L_in > a.max_ctx ? a.max_ctx : L_in);
   const int lo = a.window > 0 ? max(0, L - a.window) : 0;
   const int64_t start64 = (int64_t)lo + (int64_t)split * a.chunk;
   if (start64 >= L) {  // empty split: recorded as (m, l) = (-inf, 0), O not written
@@ -574,7 +588,11 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     return;
   }
   const int start = (int)start64;
-  const int end = (split == a.n_splits - 1) ? L : (int)min((int64_t)L, start64 + a.chunk);
+  int end = (split == a.n_splits - 1) ? L : (int)min((int64_t)L, start64 + a.chunk);
+  // Fused append: the workgroup whose range holds position L - 1 takes the new
+  // row from the quantizer instead of the cache, and its tiles stop before it.
+  const bool own_new = a.k_new != nullptr && L_in == L && L - 1 < end;
+  if (own_new) end = L - 1;
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -597,6 +615,27 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
 
   constexpr int STEP = NW * kTile;
   int p0 = start + wv * kTile;
+  // Loads into LDS before the first tile's, counted like them (compiler-visible
+  // loads here would make the compiler wait for every load in flight before
+  // their first use): the new K (wavefront 0) or V (wavefront 1) row when the
+  // append is fused, then 16 / NW query rows per wavefront (rows past nh read
+  // as zeros). A query row lands as D consecutive fp16 values at the start of
+  // its padded LDS row.
+  constexpr int QROWS = 16 / NW;
+  if (own_new && wv < 2) {
+    const uint16_t* src = (wv == 0 ? a.k_new : a.v_new) + ((int64_t)b * a.n_kv + hk) * D;
+    if (lane < D / 8) dma<16>(rsrc_words(src, 2 * D), lds_addr_of(reinterpret_cast<const uint8_t*>(nw_in[wv])),
+                              16u * lane, 0u);
+  }
+  {
+    const u32x4 qrs = rsrc_words(a.q + ((int64_t)b * a.n_q + hq0) * D, (uint32_t)(nh * D * 2));
+#pragma unroll
+    for (int i = 0; i < QROWS; ++i) {
+      const int r = wv * QROWS + i;
+      if (lane < D / 8)
+        dma<16>(qrs, lds_addr_of(lds_q + r * QOperand<S>::ROW), r < nh ? (uint32_t)(r * 2 * D + 16 * lane) : kOOB, 0u);
+    }
+  }
   u32x4 krw = {0, 0, 0, 0}, vrw = krw, ksrw = krw, vsrw = krw;
   if constexpr (kStaged) {  // first tile in flight while the query is prepared
     krw = rsrc_words(static_cast<const char*>(a.k_store) + st_off, (uint32_t)((int64_t)(L - 1) * a.s_pos + D));
@@ -609,27 +648,44 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     }
   }
 
-  // ---- query operand: heads hq0.. of this block into LDS (zero rows beyond nh);
-  // per-group sums of q give the accumulator start values -1152 * sum(q) that
-  // cancel the +1152 code bias.
+  // ---- this wavefront's LDS loads have landed (the first tile's two halves may
+  // still be loading); after the barrier every query row is in LDS.
+  if (kStaged && p0 < end) wait_vm<2 * kHalfLoads<S>>();
+  else wait_vm<0>();
+  if (own_new && wv < 2) {
+    const bool i8 = wv == 0 ? KI8 : VI8;
+    uint32_t hb[4] = {0, 0, 0, 0};
+    if (lane < D / 4) {
+      const u32x2 raw = *reinterpret_cast<const u32x2*>(&nw_in[wv][4 * lane]);
+      hb[0] = raw.x & 0xffffu; hb[1] = raw.x >> 16; hb[2] = raw.y & 0xffffu; hb[3] = raw.y >> 16;
+    }
+    float4 val;
+    if (i8) {
+      uint16_t sb;
+      const uint32_t code = quantize4(hb, a.group_lanes, &sb);  // as kv_quant_append
+      const float sc = h_bits_to_f32(sb);
+      val = make_float4((float)(int8_t)(code & 0xff) * sc, (float)(int8_t)((code >> 8) & 0xff) * sc,
+                        (float)(int8_t)((code >> 16) & 0xff) * sc, (float)(int8_t)(code >> 24) * sc);
+      if (lane < D / 4) {
+        nw_code[wv][lane] = code;
+        if (lane % a.group_lanes == 0) nw_scale[wv][lane / a.group_lanes] = sb;
+      }
+    } else {  // an fp32 store holds the fp16 value widened
+      val = make_float4(h_bits_to_f32(hb[0]), h_bits_to_f32(hb[1]), h_bits_to_f32(hb[2]), h_bits_to_f32(hb[3]));
+    }
+    if (lane < D / 4) *reinterpret_cast<float4*>(&nw_val[wv][4 * lane]) = val;
+  }
+  __syncthreads();  // query rows (and the new rows) in LDS
+  const uint8_t* const qb = lds_q + c16 * QOperand<S>::ROW + 32 * q4;
+
+  // ---- per-group sums of q: the accumulator start values -1152 * sum(q) that
+  // cancel the +1152 code bias (rows beyond nh are zero).
   float corr[S::NG];
   {
     float qsum[S::NJ];
-    const bool has = c16 < nh;
-    const uint16_t* qp = a.q + ((int64_t)b * a.n_q + hq0 + (has ? c16 : 0)) * D + 16 * q4;
-    uint8_t* qdst = lds_q + c16 * QOperand<S>::ROW + 32 * q4;
 #pragma unroll
     for (int j = 0; j < S::NJ; ++j) {
-      u32x4 x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-      if (has) {
-        x0 = *reinterpret_cast<const u32x4*>(qp + 64 * j);
-        x1 = *reinterpret_cast<const u32x4*>(qp + 64 * j + 8);
-      }
-      if (wv == 0) {
-        *reinterpret_cast<u32x4*>(qdst + 128 * j) = x0;
-        *reinterpret_cast<u32x4*>(qdst + 128 * j + 16) = x1;
-      }
-      const f16x8 h0 = __builtin_bit_cast(f16x8, x0), h1 = __builtin_bit_cast(f16x8, x1);
+      const f16x8 h0 = q_get(qb, j, 0), h1 = q_get(qb, j, 1);
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += (float)h0[e] + (float)h1[e];
@@ -649,8 +705,27 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       corr[g] = KI8 ? -kCodeBias * t : 0.0f;
     }
   }
-  __syncthreads();  // lds_q written by wavefront 0
-  const uint8_t* const qb = lds_q + c16 * QOperand<S>::ROW + 32 * q4;
+  if (own_new && wv == 0) {
+    // Scores of the new position for the 16 heads (rows beyond nh are zero):
+    // lane 4h + r sums a quarter of the dims of head h; lds_q row h holds
+    // q[h][0..D) as consecutive fp16 values.
+    const int h = lane >> 2, r = lane & 3;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(lds_q + h * QOperand<S>::ROW);
+    float zs = 0.0f;
+#pragma unroll 4
+    for (int d = r * (D / 4); d < (r + 1) * (D / 4); d += 8) {
+      const f16x8 qv = *reinterpret_cast<const f16x8*>(qrow + d);
+      const float4 k0 = *reinterpret_cast<const float4*>(&nw_val[0][d]);
+      const float4 k1 = *reinterpret_cast<const float4*>(&nw_val[0][d + 4]);
+      zs = fmaf((float)qv[0], k0.x, zs); zs = fmaf((float)qv[1], k0.y, zs);
+      zs = fmaf((float)qv[2], k0.z, zs); zs = fmaf((float)qv[3], k0.w, zs);
+      zs = fmaf((float)qv[4], k1.x, zs); zs = fmaf((float)qv[5], k1.y, zs);
+      zs = fmaf((float)qv[6], k1.z, zs); zs = fmaf((float)qv[7], k1.w, zs);
+    }
+    zs += __shfl_xor(zs, 1);
+    zs += __shfl_xor(zs, 2);
+    if (r == 0) nw_z[h] = zs * a.c2;  // read in the epilogue, after its barrier
+  }
 
   WaveAcc<S> acc;
 #pragma unroll
@@ -735,11 +810,17 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
     const int h = idx / (D / 4);
     const int d = 4 * (idx % (D / 4));
-    float M = -INFINITY;
+    const float zn = own_new ? nw_z[h] : -INFINITY;  // the fused new position
+    float M = zn;
 #pragma unroll
     for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
     const int f = merge_swz(d / 4);
     float4 v = {0.f, 0.f, 0.f, 0.f};
+    if (own_new) {
+      const float wn = __builtin_amdgcn_exp2f(zn - M);
+      const float4 u = *reinterpret_cast<const float4*>(&nw_val[1][d]);
+      v = make_float4(wn * u.x, wn * u.y, wn * u.z, wn * u.w);
+    }
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
       const float mk = sm_m[k][h];
@@ -754,16 +835,34 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   }
   if (threadIdx.x < nh) {
     const int h = threadIdx.x;
-    float M = -INFINITY;
+    const float zn = own_new ? nw_z[h] : -INFINITY;
+    float M = zn;
 #pragma unroll
     for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
-    float l = 0.0f;
+    float l = own_new ? __builtin_amdgcn_exp2f(zn - M) : 0.0f;
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
       const float mk = sm_m[k][h];
       if (mk != -INFINITY) l += sm_l[k][h] * __builtin_amdgcn_exp2f(mk - M);
     }
     ml_out[(int64_t)h * a.n_splits] = make_float2(M, l);
+  }
+  // ---- fused append: the new row into the cache (one head block writes it) --
+  if (own_new && hblk == 0 && wv < 2 && lane < D / 4) {
+    const int64_t r = (int64_t)b * a.s_seq + (int64_t)(L - 1) * a.s_pos + (int64_t)hk * a.s_head;
+    const bool i8 = wv == 0 ? KI8 : VI8;
+    void* store = const_cast<void*>(wv == 0 ? a.k_store : a.v_store);
+    if (i8) {
+      reinterpret_cast<uint32_t*>(static_cast<int8_t*>(store) + r)[lane] = nw_code[wv][lane];
+      if (lane % a.group_lanes == 0) {
+        uint16_t* sc = const_cast<uint16_t*>(wv == 0 ? a.k_scales : a.v_scales);
+        sc[(int64_t)b * a.ss_seq + (int64_t)(L - 1) * a.ss_pos + (int64_t)hk * a.ss_head + lane / a.group_lanes] =
+            nw_scale[wv][lane / a.group_lanes];
+      }
+    } else {
+      reinterpret_cast<float4*>(static_cast<float*>(store) + r)[lane] =
+          *reinterpret_cast<const float4*>(&nw_val[wv][4 * lane]);
+    }
   }
 }
 
@@ -795,14 +894,18 @@ static int dispatch_dtypes(const kvq_layout& L, const PartialArgs& a, dim3 grid,
 }
 
 int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store,
-                   const uint16_t* k_scales, const uint16_t* v_scales, const uint16_t* q,
-                   int32_t batch, int32_t n_q_heads, const int32_t* d_seq_lens, int32_t window,
-                   float sm_scale, const kvq_plan_t& plan, void* ws, void* stream) {
+                   const uint16_t* k_scales, const uint16_t* v_scales, const uint16_t* k_new,
+                   const uint16_t* v_new, const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                   const int32_t* d_seq_lens, int32_t window, float sm_scale, const kvq_plan_t& plan,
+                   void* ws, void* stream) {
   PartialArgs a{};
   a.k_store = k_store;
   a.v_store = v_store;
   a.k_scales = k_scales;
   a.v_scales = v_scales;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.group_lanes = L.scale_group == 64 ? 16 : L.head_dim / 4;
   a.q = q;
   a.seq_lens = d_seq_lens;
   const int64_t rows = (int64_t)batch * n_q_heads * plan.n_splits;

@@ -88,4 +88,37 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Quantizer of one group of values spread over `group_lanes` consecutive lanes
+// (a power of two, groups aligned to it), 4 fp16 values (bit patterns hb) per
+// lane. Strata PR 2698, "What it does": the FP16 scale of a group is its absmax
+// / 127; each value becomes the int8 code of x / scale.
+//   absmax: exact, on the fp16 bit patterns (for finite values the ordering
+//           of |x| is the integer ordering of the bits with the sign cleared);
+//   scale = fp16_rne(absmax / 127.0f), the division correctly rounded in fp32;
+//   code  = clamp(rint(x / scale), -127, 127), a correctly rounded fp32
+//           division (x and scale are fp16, so the quotient rounds to the same
+//           integer as the exact one, ties to even); 0 where scale == 0.
+// Returns the 4 codes packed little-endian; *scale_bits gets the fp16 scale.
+__device__ __forceinline__ uint32_t quantize4(const uint32_t (&hb)[4], int group_lanes, uint16_t* scale_bits) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) amax = max(amax, hb[e] & 0x7fffu);
+  for (int o = 1; o < group_lanes; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
+  const float absmax = h_bits_to_f32(amax);
+  const f16 scale_h = (f16)(absmax / 127.0f);  // fp32 IEEE division, then fp16 RNE
+  const float scale = (float)scale_h;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float c = 0.0f;
+    if (scale > 0.0f) {
+      c = __builtin_rintf(h_bits_to_f32(hb[e]) / scale);
+      c = fminf(fmaxf(c, -127.0f), 127.0f);
+    }
+    packed |= ((uint32_t)(int32_t)c & 0xffu) << (8 * e);
+  }
+  *scale_bits = __builtin_bit_cast(uint16_t, scale_h);
+  return packed;
+}
+
 }  // namespace kvq

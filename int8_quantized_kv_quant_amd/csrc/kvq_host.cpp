@@ -179,8 +179,33 @@ int kv_decode_attn_splitk(const kvq_layout* layout, const void* k_store, const v
   if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
   if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
   if (batch == 0) return KVQ_OK;
-  return launch_partial(L, k_store, v_store, k_scales, v_scales, q, batch, n_q_heads, d_seq_lens,
-                        window, sm_scale, *plan, ws, stream);
+  return launch_partial(L, k_store, v_store, k_scales, v_scales, nullptr, nullptr, q, batch, n_q_heads,
+                        d_seq_lens, window, sm_scale, *plan, ws, stream);
+}
+
+int kv_append_decode_splitk(const kvq_layout* layout, void* k_store, void* v_store, uint16_t* k_scales,
+                            uint16_t* v_scales, const uint16_t* k_new, const uint16_t* v_new,
+                            const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                            const int32_t* d_seq_lens, int32_t window, float sm_scale,
+                            const kvq_plan_t* plan, void* ws, int64_t ws_bytes, void* stream) {
+  int st = check_layout(layout);
+  if (st) return st;
+  const kvq_layout& L = *layout;
+  if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
+  if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
+  if ((st = check_heads(L, batch, n_q_heads))) return st;
+  if ((st = check_plan(L, batch, n_q_heads, plan))) return st;
+  if (!k_new || !v_new || !q || !d_seq_lens) return KVQ_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(q, 16) || !aligned(d_seq_lens, 4))
+    return KVQ_ERR_ALIGN;
+  if (window < 0) return KVQ_ERR_SHAPE;
+  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return KVQ_ERR_SHAPE;
+  if (!ws) return KVQ_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
+  if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
+  if (batch == 0) return KVQ_OK;
+  return launch_partial(L, k_store, v_store, k_scales, v_scales, k_new, v_new, q, batch, n_q_heads,
+                        d_seq_lens, window, sm_scale, *plan, ws, stream);
 }
 
 int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,

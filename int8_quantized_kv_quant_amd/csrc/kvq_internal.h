@@ -50,10 +50,12 @@ int launch_append(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k
                   uint16_t* v_scales, const uint16_t* k_new, const uint16_t* v_new,
                   const int32_t* d_start_pos, int32_t batch, int32_t n_tok, void* stream);
 
+// k_new / v_new non-null: the fused append of kv_append_decode_splitk.
 int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store,
-                   const uint16_t* k_scales, const uint16_t* v_scales, const uint16_t* q,
-                   int32_t batch, int32_t n_q_heads, const int32_t* d_seq_lens, int32_t window,
-                   float sm_scale, const kvq_plan_t& plan, void* ws, void* stream);
+                   const uint16_t* k_scales, const uint16_t* v_scales, const uint16_t* k_new,
+                   const uint16_t* v_new, const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                   const int32_t* d_seq_lens, int32_t window, float sm_scale, const kvq_plan_t& plan,
+                   void* ws, void* stream);
 
 int launch_reduce(const kvq_layout& L, const void* ws, int32_t batch, int32_t n_q_heads,
                   const kvq_plan_t& plan, uint16_t* out, void* stream);

@@ -112,6 +112,17 @@ def _partial(lay, plan=None, **kw):
         ctypes.byref(plan.c()), args["ws"], args["ws_bytes"], None)
 
 
+def _fused(lay, plan=None, **kw):
+    plan = plan or kvq.Plan(4, 256, 1 * 16 * 4 * 258 * 4)
+    args = dict(k_store=FAKE, v_store=FAKE, k_scales=FAKE, v_scales=FAKE, k_new=FAKE, v_new=FAKE, q=FAKE,
+                batch=1, n_q=16, seq_lens=FAKE, window=0, sm=0.0625, ws=FAKE, ws_bytes=plan.ws_bytes)
+    args.update(kw)
+    return kvq.load().kv_append_decode_splitk(
+        ctypes.byref(lay.c()), args["k_store"], args["v_store"], args["k_scales"], args["v_scales"],
+        args["k_new"], args["v_new"], args["q"], args["batch"], args["n_q"], args["seq_lens"], args["window"],
+        args["sm"], ctypes.byref(plan.c()), args["ws"], args["ws_bytes"], None)
+
+
 def _reduce(lay, plan=None, **kw):
     plan = plan or kvq.Plan(4, 256, 1 * 16 * 4 * 258 * 4)
     args = dict(ws=FAKE, ws_bytes=plan.ws_bytes, seq_lens=FAKE, batch=1, n_q=16, window=0, out=FAKE)
@@ -141,6 +152,22 @@ def test_null_scale_pointer_is_refused_not_read_as_one():
     assert _partial(lay, v_scales=None) == NULL_
     mixed = _with(lay, v_dtype=kvq.KVQ_STORE_FP32)   # k8v32: V has no scales
     assert _partial(mixed, v_scales=None, k_scales=None) == NULL_
+    assert _fused(lay, k_scales=None) == NULL_
+    assert _fused(lay, v_scales=None) == NULL_
+
+
+@needs_lib
+def test_fused_append_refuses_what_either_part_refuses():
+    lay = _base()
+    assert _fused(lay, k_new=None) == NULL_
+    assert _fused(lay, v_new=None) == NULL_
+    assert _fused(lay, q=None) == NULL_
+    assert _fused(lay, k_new=FAKE + 2) == ALIGN
+    assert _fused(lay, v_new=FAKE + 8) == ALIGN
+    assert _fused(lay, n_q=15) == SHAPE
+    assert _fused(lay, window=-1) == SHAPE
+    assert _fused(lay, ws=None) == WS
+    assert _fused(lay, batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
 
 
 @needs_lib
