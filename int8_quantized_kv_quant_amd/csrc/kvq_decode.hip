@@ -868,9 +868,11 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
 
 template <int D, bool KI8, bool VI8, bool G64>
 static void launch_partial_t(const PartialArgs& a, dim3 grid, hipStream_t s) {
-  // LDS-staged int8 kernels run 8 wavefronts (two per SIMD); the fp32-store
-  // variants keep their wider operands in registers and run 4.
-  constexpr int NW = (KI8 && VI8) ? 8 : 4;
+  // Four wavefronts per workgroup, and several workgroups per compute unit
+  // (two at D = 256, three at D = 128): one workgroup's start (query load,
+  // first tiles in flight) and end (merge, partial stores) overlap another's
+  // streaming, which measured faster than one 8-wavefront workgroup per unit.
+  constexpr int NW = 4;
   hipLaunchKernelGGL((kvq_partial_kernel<D, KI8, VI8, G64, NW>), grid, dim3(NW * 64), 0, s, a);
 }
 

@@ -31,7 +31,7 @@ struct ReduceArgs {
   int32_t n_splits;
 };
 
-constexpr int kReduceBatch = 8;  // splits per lane per round of loads
+constexpr int kReduceBatch = 16;  // splits per lane per round of loads (256 splits: one round)
 
 template <int D>
 __global__ __launch_bounds__(256) void kvq_reduce_kernel(ReduceArgs a) {
