@@ -872,7 +872,7 @@ static void launch_partial_t(const PartialArgs& a, dim3 grid, hipStream_t s) {
   // (two at D = 256, three at D = 128): one workgroup's start (query load,
   // first tiles in flight) and end (merge, partial stores) overlap another's
   // streaming, which measured faster than one 8-wavefront workgroup per unit.
-  constexpr int NW = 4;
+  constexpr int NW = kPartialWaves;
   hipLaunchKernelGGL((kvq_partial_kernel<D, KI8, VI8, G64, NW>), grid, dim3(NW * 64), 0, s, a);
 }
 

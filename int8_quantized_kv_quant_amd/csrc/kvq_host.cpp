@@ -127,7 +127,8 @@ int kvq_plan(const kvq_layout* layout, int32_t batch, int32_t n_q_heads, int32_t
     // workgroups; then the chip is filled first.
     const int64_t want_wg = (int64_t)resident_wgs_per_cu(L) * n_cu;
     if (units * ceil_div(l_eff, chunk) < want_wg) chunk = ceil_div(units * l_eff, want_wg);
-    chunk = round_up(chunk < kTile ? kTile : chunk, kTile);
+    // A split gets at least one tile per wavefront of its workgroup.
+    chunk = round_up(chunk < kMinSplitChunk ? kMinSplitChunk : chunk, kTile);
     const int64_t cap = round_up(l_eff, kTile);
     if (chunk > cap) chunk = cap;
     // The reduce keeps one weight per split in LDS.

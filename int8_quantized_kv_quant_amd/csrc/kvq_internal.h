@@ -9,8 +9,10 @@
 namespace kvq {
 
 constexpr int kTile = 32;            // positions per MFMA tile step of a wave
-constexpr int kMaxSplits = 8192;     // bound on plan.n_splits (reduce keeps weights in LDS)
+constexpr int kMaxSplits = 8192;     // bound on plan.n_splits
 constexpr int kHeadsPerBlock = 16;   // query heads one wave carries (MFMA M/N = 16)
+constexpr int kPartialWaves = 4;     // wavefronts per partial-kernel workgroup
+constexpr int kMinSplitChunk = kPartialWaves * kTile;  // planner: one tile per wavefront at least
 
 // Byte sizes of one store element.
 inline int store_elem_bytes(int dtype) { return dtype == KVQ_STORE_INT8 ? 1 : 4; }

@@ -64,6 +64,8 @@ def test_plan_covers_the_context(name, n_cu):
         assert p.n_splits * p.chunk >= l_eff
         assert (p.n_splits - 1) * p.chunk < max(l_eff, 1)      # no split starts past the range
         assert p.ws_bytes == w.batch * w.n_q_heads * p.n_splits * (w.head_dim + 2) * 4
+        if l_eff >= 128:
+            assert p.chunk >= 128  # at least one 32-position tile per wavefront of a split
         if l_eff < 64:
             assert p.n_splits == 1  # genie v1.3.0: single block below 64 positions
 
