@@ -92,6 +92,88 @@ def cpu_baseline(w, lens, q, sm):
     return want, dt, cores, reps
 
 
+def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
+    """The decode step (kv_append_decode_splitk + kv_decode_reduce, graph-replayed)
+    on the other two shapes the metric is quoted on:
+      gemma_4k  -- 8 query / 1 kv head, head_dim 256 in a 512-wide slot, one scale
+                   per (position, kv head), context 4096 with a 512-key window;
+      batched   -- 64 sequences of lengths U[1024, 32768], 32 query / 8 kv heads,
+                   head_dim 128, group-64 scales (2.2 GB of KV per step).
+    Gemma rows come from workloads.py; the batched cache (1.1 G values) is filled
+    through kv_quant_append from rows drawn on the device with a seeded
+    torch.Generator (timing only: its parity is covered by the GPU tests)."""
+    import torch
+    dev = torch.device("cuda:0")
+    res = {}
+
+    def timed(w, lens, lay, caches, k_new, v_new):
+        B = w.batch
+        qd = torch.from_numpy(wl.queries(w)).to(dev)
+        ld = torch.from_numpy(lens.astype(np.int32)).to(dev)
+        sm = 1.0 / math.sqrt(w.head_dim)
+        plan = kvq.kvq_plan(lay, B, w.n_q_heads, w.max_ctx, w.window, n_cu)
+        ws = torch.zeros(plan.ws_bytes, dtype=torch.uint8, device=dev)
+        out = torch.empty((B, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+
+        def step(c):
+            kvq.kv_append_decode_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], k_new, v_new, qd, B,
+                                        w.n_q_heads, ld, w.window, sm, plan, ws, ws.numel())
+            kvq.kv_decode_reduce(lay, ws, ws.numel(), ld, B, w.n_q_heads, w.window, plan, out)
+
+        for c in caches:
+            step(c)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in caches:
+                step(c)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(2, steps // len(caches))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * len(caches))
+        kvb = wl.kv_bytes_per_step(w, lens)
+        return {"us_per_step": round(us, 2), "kv_bytes_per_step": int(kvb), "GB_s": round(kvb / us / 1e3, 1),
+                "pct_hbm_peak": round(100 * kvb / us / 1e3 / HBM_PEAK_GBS, 2), "n_splits": plan.n_splits,
+                "chunk": plan.chunk, "steps": reps * len(caches)}
+
+    w = wl.WORKLOADS["gemma"]
+    L = 4096
+    lens = np.array([L], dtype=np.int32)
+    lay, c0 = kvq_setup.fill_cache(w, lens, upto=np.array([L - 1]))
+    caches = [c0] + [{k: (None if t is None else t.clone()) for k, t in c0.items()} for _ in range(COPIES - 1)]
+    k_new = torch.from_numpy(wl.kv_rows(w, "k", 0, L - 1, 1)).to(dev)
+    v_new = torch.from_numpy(wl.kv_rows(w, "v", 0, L - 1, 1)).to(dev)
+    res["gemma_4k"] = {"context": L, "window": w.window, "cache_copies": COPIES,
+                       **timed(w, lens, lay, caches, k_new, v_new)}
+    del caches, c0
+
+    w = wl.WORKLOADS["batched"]
+    lens = wl.seq_lens(w)
+    lay = kvq_setup.layout_for(w)
+    cache = kvq.alloc_cache(lay, w.batch, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    for b in range(w.batch):
+        p, n_fill = 0, int(lens[b]) - 1
+        while p < n_fill:
+            n = min(16384, n_fill - p)
+            rows = torch.randn((2, n, w.n_kv_heads, w.head_dim), generator=gen, device=dev).half()
+            kvq_setup.append_rows_device(lay, cache, b, p, rows[0], rows[1])
+            p += n
+    new = torch.randn((2, w.batch, w.n_kv_heads, w.head_dim), generator=gen, device=dev).half()
+    res["batched"] = {"batch": w.batch, "contexts": "U[1024, 32768]", "total_positions": int(lens.sum()),
+                      **timed(w, lens, lay, [cache], new[0].contiguous(), new[1].contiguous())}
+    del cache
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +182,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--order", choices=("pos", "head"), default="pos",
                     help="cache layout: positions major (default) or heads major")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the Gemma 4K and batched-serving timings (profiling runs of the 128K step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (the reference for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run to bytes)")
@@ -262,6 +346,13 @@ def main() -> int:
     app_ms = replay_ms(capture(append), reps)
     part_ms = replay_ms(capture(lambda c: partial(c, plan_g)), reps)
 
+    others = None
+    if not args.no_other_workloads:
+        log("timing the decode step on the Gemma 4K and batched-serving workloads")
+        del caches, cache0
+        torch.cuda.empty_cache()
+        others = secondary_workloads(kvq, kvq_setup, wl, n_cu, args.steps)
+
     kv_bytes = wl.kv_bytes_per_step(w, lens)
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (fpart_ms * 1e-3) / 1e9
@@ -302,6 +393,7 @@ def main() -> int:
         "parity": {"codes_scales_bitexact_sampled": codes_ok, "max_abs_err_vs_oracle": max_err,
                    "tol": TOL},
         "cpu_baseline": cpu,
+        "other_workloads": others,
     }
     print(json.dumps(res), flush=True)
     ok = codes_ok and graph_matches_eager and (max_err is None or max_err <= TOL)

@@ -3,7 +3,7 @@
 // genie-ai-runtime releases, v1.3.0 "split-K decode attention": a reduce kernel
 // combines the per-split online-softmax partials of each head. Strata PR 2698
 // notes the merge cost grows with context, so the merge is spread wide: one
-// workgroup per (sequence, query head, 64-dim slice).
+// workgroup per (sequence, query head, slice of 16, 32 or 64 dims).
 //
 // For (b, hq) over its splits s:
 //   M = max_s m_s;  w_s = 2^(m_s - M);  out = sum_s w_s O_s / sum_s w_s l_s
@@ -13,10 +13,13 @@
 // m = -inf contributes nothing and its O is never used in arithmetic. A head
 // whose splits are all empty (context length 0) gets an all-zero row.
 //
-// Latency, not bandwidth, bounds this kernel (a few MB in total), so each lane
-// issues all loads of a batch of splits at once and folds them into a running
-// (max, sum, output) triple; the 16 lanes that share a 4-dim column then merge
-// their triples through LDS.
+// Latency, not bandwidth, bounds this kernel (a few MB in total, and at batch
+// 1 only n_q_heads rows), so the work is spread over many lanes: a workgroup
+// covers SLICE dims of one (b, hq) row; lane (column c, split phase p) folds the
+// splits p, p + P, ... of its 4-dim column into a running (max, sum, output)
+// triple, issuing a batch of loads at once; the P phases of a column are P
+// consecutive lanes of one wavefront and combine by a shuffle butterfly (no
+// LDS, no barrier). Narrow slices give small batches many workgroups.
 #include <math.h>
 
 #include "kvq_device.h"
@@ -31,26 +34,46 @@ struct ReduceArgs {
   int32_t n_splits;
 };
 
-constexpr int kReduceBatch = 16;  // splits per lane per round of loads (256 splits: one round)
+constexpr int kReduceBatch = 8;  // splits per lane per round of loads
 
-template <int D>
+struct Triple {
+  float m, l;
+  float4 o;
+};
+
+// (m, l, o) of two disjoint sets of positions -> that of their union.
+__device__ __forceinline__ Triple combine(const Triple& a, const Triple& b) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == -INFINITY) return a;  // both empty
+  const float wa = a.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a.m - M);
+  const float wb = b.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(b.m - M);
+  Triple r;
+  r.m = M;
+  r.l = wa * a.l + wb * b.l;
+  r.o = make_float4(wa * a.o.x + wb * b.o.x, wa * a.o.y + wb * b.o.y, wa * a.o.z + wb * b.o.z,
+                    wa * a.o.w + wb * b.o.w);
+  return r;
+}
+
+template <int D, int SLICE>
 __global__ __launch_bounds__(256) void kvq_reduce_kernel(ReduceArgs a) {
-  const int bh = blockIdx.x;     // b * n_q + hq
-  const int slice = blockIdx.y;  // 64-dim slice
+  constexpr int C = SLICE / 4;  // 4-dim columns per workgroup
+  constexpr int P = 256 / C;    // split phases per column (16, 32 or 64 lanes)
+  const int bh = blockIdx.x;    // b * n_q + hq
+  const int slice = blockIdx.y;
   const int tid = threadIdx.x;
-  const int sp = tid >> 4;       // split phase 0..15: splits sp, sp + 16, ...
-  const int d4 = tid & 15;       // 4-dim column of the slice
+  const int p = tid % P;
+  const int c = tid / P;
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + (int64_t)bh * a.n_splits;
-  const float* O = a.ws_o + (int64_t)bh * a.n_splits * D + slice * 64 + 4 * d4;
+  const float* O = a.ws_o + (int64_t)bh * a.n_splits * D + slice * SLICE + 4 * c;
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  float4 o_run = {0.f, 0.f, 0.f, 0.f};
-  for (int base = sp; base < a.n_splits; base += 16 * kReduceBatch) {
+  Triple run = {-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
+  for (int base = p; base < a.n_splits; base += P * kReduceBatch) {
     float2 v[kReduceBatch];
     float4 o[kReduceBatch];
 #pragma unroll
     for (int k = 0; k < kReduceBatch; ++k) {
-      const int s = base + 16 * k;
+      const int s = base + P * k;
       v[k] = make_float2(-INFINITY, 0.0f);
       o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (s < a.n_splits) {
@@ -58,80 +81,82 @@ __global__ __launch_bounds__(256) void kvq_reduce_kernel(ReduceArgs a) {
         o[k] = *reinterpret_cast<const float4*>(O + (int64_t)s * D);
       }
     }
-    float bm = m_run;
+    float bm = run.m;
 #pragma unroll
     for (int k = 0; k < kReduceBatch; ++k) bm = fmaxf(bm, v[k].x);
     if (bm == -INFINITY) continue;  // nothing recorded yet
-    const float r = m_run == -INFINITY ? 0.0f : exp2f(m_run - bm);
-    l_run *= r;
-    o_run.x *= r;
-    o_run.y *= r;
-    o_run.z *= r;
-    o_run.w *= r;
-    m_run = bm;
+    // An empty split (m = -inf) has its O row unwritten: it must not enter the
+    // arithmetic, so it is skipped rather than weighted by 0.
+    const float r = run.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(run.m - bm);
+    run.l *= r;
+    run.o.x *= r;
+    run.o.y *= r;
+    run.o.z *= r;
+    run.o.w *= r;
+    run.m = bm;
 #pragma unroll
     for (int k = 0; k < kReduceBatch; ++k) {
       if (v[k].x != -INFINITY) {
-        const float w = exp2f(v[k].x - bm);
-        l_run = fmaf(w, v[k].y, l_run);
-        o_run.x = fmaf(w, o[k].x, o_run.x);
-        o_run.y = fmaf(w, o[k].y, o_run.y);
-        o_run.z = fmaf(w, o[k].z, o_run.z);
-        o_run.w = fmaf(w, o[k].w, o_run.w);
+        const float w = __builtin_amdgcn_exp2f(v[k].x - bm);
+        run.l = fmaf(w, v[k].y, run.l);
+        run.o.x = fmaf(w, o[k].x, run.o.x);
+        run.o.y = fmaf(w, o[k].y, run.o.y);
+        run.o.z = fmaf(w, o[k].z, run.o.z);
+        run.o.w = fmaf(w, o[k].w, run.o.w);
       }
     }
   }
 
-  __shared__ float4 part_o[16][16];
-  __shared__ float part_m[16][16];
-  __shared__ float part_l[16][16];
-  part_o[sp][d4] = o_run;
-  part_m[sp][d4] = m_run;
-  part_l[sp][d4] = l_run;
-  __syncthreads();
-  if (tid < 16) {
-    float M = -INFINITY;
+  // Butterfly over the P lanes of the column: after log2(P) exchanges every
+  // lane holds the column's total (the same on both sides of each exchange).
 #pragma unroll
-    for (int k = 0; k < 16; ++k) M = fmaxf(M, part_m[k][tid]);
-    float4 t = {0.f, 0.f, 0.f, 0.f};
-    float l = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float mk = part_m[k][tid];
-        if (mk != -INFINITY) {
-          const float w = exp2f(mk - M);
-          const float4 u = part_o[k][tid];
-          l = fmaf(w, part_l[k][tid], l);
-          t.x = fmaf(w, u.x, t.x);
-          t.y = fmaf(w, u.y, t.y);
-          t.z = fmaf(w, u.z, t.z);
-          t.w = fmaf(w, u.w, t.w);
-        }
-      }
-    }
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const f16 r0 = (f16)(t.x * inv), r1 = (f16)(t.y * inv), r2 = (f16)(t.z * inv), r3 = (f16)(t.w * inv);
+  for (int off = P / 2; off; off >>= 1) {
+    Triple q;
+    q.m = __shfl_xor(run.m, off);
+    q.l = __shfl_xor(run.l, off);
+    q.o = make_float4(__shfl_xor(run.o.x, off), __shfl_xor(run.o.y, off), __shfl_xor(run.o.z, off),
+                      __shfl_xor(run.o.w, off));
+    run = (p & off) ? combine(q, run) : combine(run, q);
+  }
+  if (p == 0) {
+    const float inv = run.l > 0.0f ? 1.0f / run.l : 0.0f;
+    const f16 r0 = (f16)(run.o.x * inv), r1 = (f16)(run.o.y * inv), r2 = (f16)(run.o.z * inv),
+              r3 = (f16)(run.o.w * inv);
     u32x2 pk = {(uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16),
                 (uint32_t)__builtin_bit_cast(uint16_t, r2) | ((uint32_t)__builtin_bit_cast(uint16_t, r3) << 16)};
-    *reinterpret_cast<u32x2*>(a.out + (int64_t)bh * D + slice * 64 + 4 * tid) = pk;
+    *reinterpret_cast<u32x2*>(a.out + (int64_t)bh * D + slice * SLICE + 4 * c) = pk;
+  }
+}
+
+template <int D>
+static void launch_reduce_d(const ReduceArgs& a, int64_t rows, hipStream_t s) {
+  // Narrower slices (more split phases per column) when there are few (b, hq)
+  // rows and more than one split per lane at 16 phases, so that the grid still
+  // spreads over the chip and each lane waits on few loads; with at most 16
+  // splits the longer butterfly of a narrow slice would cost more than it saves.
+  if (a.n_splits <= 16 || rows * (D / 64) >= 256) {
+    hipLaunchKernelGGL((kvq_reduce_kernel<D, 64>), dim3(rows, D / 64), dim3(256), 0, s, a);
+  } else if (rows * (D / 32) >= 256) {
+    hipLaunchKernelGGL((kvq_reduce_kernel<D, 32>), dim3(rows, D / 32), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((kvq_reduce_kernel<D, 16>), dim3(rows, D / 16), dim3(256), 0, s, a);
   }
 }
 
 int launch_reduce(const kvq_layout& L, const void* ws, int32_t batch, int32_t n_q_heads,
                   const kvq_plan_t& plan, uint16_t* out, void* stream) {
   ReduceArgs a{};
-  const int64_t rows = (int64_t)batch * n_q_heads * plan.n_splits;
+  const int64_t bh = (int64_t)batch * n_q_heads;
+  const int64_t rows = bh * plan.n_splits;
   a.ws_o = static_cast<const float*>(ws);
   a.ws_ml = static_cast<const float*>(ws) + rows * L.head_dim;
   a.out = out;
   a.n_splits = plan.n_splits;
-  dim3 grid(batch * n_q_heads, L.head_dim / 64);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (L.head_dim) {
-    case 64: hipLaunchKernelGGL(kvq_reduce_kernel<64>, grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(kvq_reduce_kernel<128>, grid, dim3(256), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(kvq_reduce_kernel<256>, grid, dim3(256), 0, s, a); break;
+    case 64: launch_reduce_d<64>(a, bh, s); break;
+    case 128: launch_reduce_d<128>(a, bh, s); break;
+    case 256: launch_reduce_d<256>(a, bh, s); break;
     default: return KVQ_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;

@@ -40,6 +40,18 @@ def append_rows(lay: kvq.Layout, cache: dict, b: int, start: int, k_rows: np.nda
         kn, vn, sp, 1, n)
 
 
+def append_rows_device(lay: kvq.Layout, cache: dict, b: int, start: int, k_rows, v_rows) -> None:
+    """kv_quant_append of device fp16 rows [n][n_kv][d] of sequence b at `start`."""
+    sp = torch.tensor([start], dtype=torch.int32, device=k_rows.device)
+    ks = cache["k_scales"]
+    vs = cache["v_scales"]
+    kvq.kv_quant_append(
+        lay, _store_view(cache["k"], b * lay.s_seq), _store_view(cache["v"], b * lay.s_seq),
+        None if ks is None else _store_view(ks, b * lay.ss_seq),
+        None if vs is None else _store_view(vs, b * lay.ss_seq),
+        k_rows.contiguous(), v_rows.contiguous(), sp, 1, k_rows.shape[0])
+
+
 def fill_cache(w: wl.Workload, lens: np.ndarray, order: str = "pos", device="cuda",
                block: int = 16384, upto=None, fill: int = 0, seqs=None):
     """Allocate the cache of workload w and append positions [0, upto_b) of every
