@@ -1,4 +1,5 @@
-"""CPU oracle for the INT8 KV cache: quantize-append and single-token decode attention.
+"""CPU oracle for the INT8 KV cache: quantize-append, single-token decode attention
+and chunk (several query tokens, causal) attention.
 
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this module. The library
@@ -196,6 +197,45 @@ def attend(q, cache: Cache, seq_lens, window: int, sm_scale: float, heads=None) 
             K = cache.values("k", b, lo, hi, hk)
             V = cache.values("v", b, lo, hi, hk)
             out[b, hq] = attend_one(q[b, hq].astype(np.float64), K, V, sm_scale)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Chunk attention: several consecutive query tokens per sequence
+# --------------------------------------------------------------------------
+
+def attend_chunk(q, cache: Cache, start_pos, window: int, sm_scale: float, tokens=None) -> np.ndarray:
+    """Attention of a chunk of n_tok consecutive query tokens per sequence over
+    the cache: q float16 [batch][n_tok][n_q][d]; token t of sequence b sits at
+    position P = start_pos[b] + t, its own K/V row already in the cache, and
+    attends to the keys p with lo <= p <= P, lo = max(0, P + 1 - window) when
+    window > 0 (causal inside the chunk; the decode reading applied to each
+    token as if it were the last of a context of P + 1 positions).
+
+    Strata PR 2698, "What it does": the prompt chunk and the verify windows
+    read the same int8 cache, dequantized on the fly; genie-ai-runtime release
+    v0.1.0-alpha.11, "--int8-kv triage": the batched prefill attention must read
+    the scales as decode does. Query head h reads kv head h // G (G = n_q /
+    n_kv). Returns float64 [batch][n_tok][n_q][d]. ``tokens`` optionally
+    restricts the work to a list of (b, t) pairs (the other rows stay 0)."""
+    q = np.asarray(q, dtype=np.float16)
+    B, T, Hq, d = q.shape
+    Hkv = cache.n_kv_heads
+    G = Hq // Hkv
+    out = np.zeros((B, T, Hq, d), dtype=np.float64)
+    want = None if tokens is None else set((int(b), int(t)) for b, t in tokens)
+    for b in range(B):
+        for t in range(T):
+            if want is not None and (b, t) not in want:
+                continue
+            P = int(start_pos[b]) + t
+            lo = max(0, P + 1 - window) if window > 0 else 0
+            for hk in range(Hkv):
+                K = cache.values("k", b, lo, P + 1, hk)
+                V = cache.values("v", b, lo, P + 1, hk)
+                z = sm_scale * (q[b, t, hk * G:(hk + 1) * G].astype(np.float64) @ K.T)
+                e = np.exp(z - z.max(axis=1, keepdims=True))
+                out[b, t, hk * G:(hk + 1) * G] = (e @ V) / e.sum(axis=1, keepdims=True)
     return out
 
 
