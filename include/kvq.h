@@ -10,7 +10,11 @@
  *   kv_append_decode_splitk  the decode step's one-token quantize-append fused
  *                          into kv_decode_attn_splitk
  *   kv_decode_reduce       combine the split partials into the fp16 output
+ *   kv_chunk_attn          attention of a chunk of consecutive query tokens per
+ *                          sequence (prompt chunk, verify window): causal
+ *                          inside the chunk, partials + combine in one call
  *   kvq_plan               host-only choice of the split count and workspace
+ *   kvq_plan_chunk         the same for kv_chunk_attn
  *
  * Sources of the method (web pages; cited by title and section):
  *   [G12]  genie-ai-runtime release v0.1.0-alpha.12, "Path I: INT8 KV cache",
@@ -207,6 +211,44 @@ int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,
                      const int32_t* d_seq_lens, int32_t batch, int32_t n_q_heads,
                      int32_t window, const kvq_plan_t* plan, uint16_t* out,
                      void* stream);
+
+/* kvq_plan_chunk -- host only, no device call. Split plan of kv_chunk_attn
+ * for `batch` sequences of `n_tok` query tokens whose last token sits below
+ * position max_seq_len (the largest start + n_tok). Chunks with many query
+ * rows run one split per (sequence, kv head, 64-row block); a few tokens over
+ * a long prefix (a verify window) get their keys split so that the grid covers
+ * the chip. ws_bytes = batch * n_tok * n_q_heads * n_splits * (head_dim + 2) * 4.
+ * Writes *out; returns KVQ_OK or an error for invalid layout/sizes. */
+int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32_t n_q_heads,
+                   int32_t max_seq_len, int32_t window, int32_t n_cu, kvq_plan_t* out);
+
+/* kv_chunk_attn -- attention of a chunk of n_tok consecutive query tokens per
+ * sequence over the int8 cache, into `out`. [S2698 "What it does": the prompt
+ * chunk and the verify windows read the same int8 cache, dequantized on the
+ * fly], [G11 "--int8-kv triage": the batched prefill attention reads the
+ * scales as decode does], [G130 "split-K decode attention"].
+ * Token t of sequence b sits at position P = d_start_pos[b] + t; its own K and
+ * V rows must already be in the cache (kv_quant_append of the chunk first). It
+ * attends to the keys lo <= p <= P with lo = max(0, P + 1 - window) when
+ * window > 0, else 0 (causal inside the chunk). Keys are dequantized as code *
+ * scale, exactly as in kv_decode_attn_splitk; query head hq reads kv head
+ * hq / (n_q_heads / n_kv_heads).
+ *   q            fp16 [batch][n_tok][n_q_heads][head_dim], contiguous, 16-byte aligned.
+ *   d_start_pos  device int32 [batch].
+ *   plan         from kvq_plan_chunk for at least this batch, n_tok and n_q_heads.
+ *   ws           device workspace of at least plan->ws_bytes bytes, 16-byte
+ *                aligned (split partials of rows (b, t, hq); no initialization).
+ *   out          fp16 [batch][n_tok][n_q_heads][head_dim], contiguous, 16-byte aligned.
+ * Both stores must be int8 (KVQ_ERR_UNSUPPORTED otherwise). Two kernels are
+ * enqueued on `stream`: the partials and the combine of kv_decode_reduce.
+ * Device precondition: 0 <= d_start_pos[b] and d_start_pos[b] + n_tok <= max_ctx;
+ * a token that would sit at or beyond max_ctx sees no key and gets a zero row. */
+int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_store,
+                  const uint16_t* k_scales, const uint16_t* v_scales,
+                  const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
+                  const int32_t* d_start_pos, int32_t window, float sm_scale,
+                  const kvq_plan_t* plan, void* ws, int64_t ws_bytes, uint16_t* out,
+                  void* stream);
 
 /* Text for a kvq_status value (static storage). */
 const char* kvq_status_string(int status);

@@ -18,8 +18,8 @@ from dataclasses import dataclass
 __all__ = [
     "KVQ_STORE_INT8", "KVQ_STORE_FP32", "KvqError", "KvqLibraryMissing", "Layout", "Plan",
     "lib_path", "load", "kvq_version", "kvq_status_string", "kvq_plan", "kv_quant_append",
-    "kv_decode_attn_splitk", "kv_append_decode_splitk", "kv_decode_reduce", "make_layout",
-    "alloc_cache", "decode",
+    "kv_decode_attn_splitk", "kv_append_decode_splitk", "kv_decode_reduce", "kvq_plan_chunk",
+    "kv_chunk_attn", "make_layout", "alloc_cache", "decode", "chunk_attn",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -28,7 +28,7 @@ KVQ_STORE_FP32 = 2
 _DT = {"int8": KVQ_STORE_INT8, "fp32": KVQ_STORE_FP32}
 
 EXPORTED_SYMBOLS = ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
-                    "kv_decode_reduce", "kvq_status_string", "kvq_version")
+                    "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_status_string", "kvq_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -115,11 +115,13 @@ def load():
     lib.kv_append_decode_splitk.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, f32, PP, vp,
                                             i64, vp]
     lib.kv_decode_reduce.argtypes = [LP, vp, i64, vp, i32, i32, i32, PP, vp, vp]
+    lib.kvq_plan_chunk.argtypes = [LP, i32, i32, i32, i32, i32, i32, PP]
+    lib.kv_chunk_attn.argtypes = [LP, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, f32, PP, vp, i64, vp, vp]
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_version.argtypes = []
     for fn in ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
-               "kv_decode_reduce", "kvq_version"):
+               "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_version"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -198,6 +200,23 @@ def kv_decode_reduce(layout: Layout, ws, ws_bytes: int, seq_lens, batch: int, n_
         ctypes.byref(plan.c()), _ptr(out), _stream(stream)))
 
 
+def kvq_plan_chunk(layout: Layout, batch: int, n_tok: int, n_q_heads: int, max_seq_len: int, window: int,
+                   n_cu: int) -> Plan:
+    out = _Plan()
+    _check("kvq_plan_chunk", load().kvq_plan_chunk(ctypes.byref(layout.c()), batch, n_tok, n_q_heads,
+                                                   max_seq_len, window, n_cu, ctypes.byref(out)))
+    return Plan(out.n_splits, out.chunk, out.ws_bytes)
+
+
+def kv_chunk_attn(layout: Layout, k_store, v_store, k_scales, v_scales, q, batch: int, n_tok: int,
+                  n_q_heads: int, start_pos, window: int, sm_scale: float, plan: Plan, ws, ws_bytes: int, out,
+                  stream=None) -> None:
+    _check("kv_chunk_attn", load().kv_chunk_attn(
+        ctypes.byref(layout.c()), _ptr(k_store), _ptr(v_store), _ptr(k_scales), _ptr(v_scales), _ptr(q),
+        batch, n_tok, n_q_heads, _ptr(start_pos), window, sm_scale, ctypes.byref(plan.c()), _ptr(ws), ws_bytes,
+        _ptr(out), _stream(stream)))
+
+
 # --------------------------------------------------------------------------
 # Allocation helpers (memory plumbing; no arithmetic of the method)
 # --------------------------------------------------------------------------
@@ -267,4 +286,27 @@ def decode(layout: Layout, cache: dict, q, seq_lens, window: int, sm_scale: floa
                                 new_kv[0], new_kv[1], q, batch, n_q, seq_lens, window, sm_scale, plan,
                                 ws, ws.numel(), stream)
     kv_decode_reduce(layout, ws, ws.numel(), seq_lens, batch, n_q, window, plan, out, stream)
+    return out
+
+
+def chunk_attn(layout: Layout, cache: dict, q, start_pos, window: int, sm_scale: float | None = None,
+               plan: Plan | None = None, max_seq_len: int | None = None, ws=None, out=None,
+               n_cu: int | None = None, stream=None):
+    """Chunk attention (kv_chunk_attn) of q fp16 [batch][n_tok][n_q][head_dim]
+    at device positions start_pos (int32 [batch]) over the cache. Returns the
+    fp16 output [batch][n_tok][n_q][head_dim]."""
+    import torch
+    batch, n_tok, n_q, d = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if plan is None:
+        if n_cu is None:
+            n_cu = torch.cuda.get_device_properties(q.device).multi_processor_count
+        plan = kvq_plan_chunk(layout, batch, n_tok, n_q, max_seq_len or layout.max_ctx, window, n_cu)
+    if ws is None:
+        ws = torch.empty(max(plan.ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((batch, n_tok, n_q, d), dtype=torch.float16, device=q.device)
+    kv_chunk_attn(layout, cache["k"], cache["v"], cache["k_scales"], cache["v_scales"], q, batch, n_tok, n_q,
+                  start_pos, window, sm_scale, plan, ws, ws.numel(), out, stream)
     return out

@@ -2,6 +2,7 @@
 // entry points. Validation always runs before any HIP call, so every error path
 // can be exercised without a device.
 #include <limits.h>
+#include <algorithm>
 #include <stddef.h>
 
 #include "kvq_internal.h"
@@ -207,6 +208,68 @@ int kv_append_decode_splitk(const kvq_layout* layout, void* k_store, void* v_sto
   if (batch == 0) return KVQ_OK;
   return launch_partial(L, k_store, v_store, k_scales, v_scales, k_new, v_new, q, batch, n_q_heads,
                         d_seq_lens, window, sm_scale, *plan, ws, stream);
+}
+
+int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32_t n_q_heads,
+                   int32_t max_seq_len, int32_t window, int32_t n_cu, kvq_plan_t* out) {
+  int st = check_layout(layout);
+  if (st) return st;
+  if (!out) return KVQ_ERR_NULL;
+  const kvq_layout& L = *layout;
+  if ((st = check_heads(L, batch, n_q_heads))) return st;
+  if (n_tok < 0 || max_seq_len < 0 || window < 0 || n_cu < 1) return KVQ_ERR_SHAPE;
+  const int64_t G = n_q_heads / L.n_kv_heads;
+  // Keys one workgroup may walk: the whole prefix, or the window plus the chunk.
+  const int64_t l_eff = window > 0 ? std::min<int64_t>(max_seq_len, (int64_t)window + n_tok) : max_seq_len;
+  const int64_t units = (int64_t)(batch > 0 ? batch : 1) * L.n_kv_heads * chunk_row_blocks(n_tok > 0 ? n_tok : 1, G);
+  const int64_t want = (int64_t)resident_chunk_wgs_per_cu(L) * n_cu;
+  int64_t n_splits = 1, chunk = round_up(l_eff > 0 ? l_eff : 1, kTile);
+  if (units < want && l_eff > kMinSplitChunk) {
+    // Few query rows over a long prefix (a verify window): split the keys so
+    // that the grid still covers the chip, at least 4 tiles per split.
+    n_splits = std::min(ceil_div(want, units), ceil_div(l_eff, kMinSplitChunk));
+    chunk = round_up(ceil_div(l_eff, n_splits), kTile);
+    n_splits = ceil_div(l_eff, chunk);
+  }
+  if (n_splits > kMaxSplits || chunk > INT_MAX) return KVQ_ERR_UNSUPPORTED;
+  out->n_splits = (int32_t)n_splits;
+  out->chunk = (int32_t)chunk;
+  out->ws_bytes = workspace_bytes((int64_t)batch * n_tok, n_q_heads, n_splits, L.head_dim);
+  return KVQ_OK;
+}
+
+int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_store, const uint16_t* k_scales,
+                  const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
+                  const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t* plan, void* ws,
+                  int64_t ws_bytes, uint16_t* out, void* stream) {
+  int st = check_layout(layout);
+  if (st) return st;
+  const kvq_layout& L = *layout;
+  if (L.k_dtype != KVQ_STORE_INT8 || L.v_dtype != KVQ_STORE_INT8) return KVQ_ERR_UNSUPPORTED;
+  if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
+  if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
+  if ((st = check_heads(L, batch, n_q_heads))) return st;
+  if (n_tok < 0) return KVQ_ERR_SHAPE;
+  if (!plan) return KVQ_ERR_NULL;
+  if (plan->n_splits < 1 || plan->n_splits > kMaxSplits) return KVQ_ERR_SHAPE;
+  if (plan->chunk < kTile || plan->chunk % kTile) return KVQ_ERR_SHAPE;
+  const int64_t rows = (int64_t)batch * n_tok;
+  if (rows * n_q_heads > INT_MAX / 8 || (int64_t)L.n_kv_heads * chunk_row_blocks(n_tok, n_q_heads / L.n_kv_heads) > 65535)
+    return KVQ_ERR_UNSUPPORTED;  // grid limits
+  if (plan->ws_bytes < workspace_bytes(rows, n_q_heads, plan->n_splits, L.head_dim)) return KVQ_ERR_WORKSPACE;
+  if (!q || !d_start_pos || !out) return KVQ_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(d_start_pos, 4) || !aligned(out, 16)) return KVQ_ERR_ALIGN;
+  if (window < 0) return KVQ_ERR_SHAPE;
+  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return KVQ_ERR_SHAPE;
+  if (!ws) return KVQ_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
+  if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
+  if (batch == 0 || n_tok == 0) return KVQ_OK;
+  st = launch_chunk(L, k_store, v_store, k_scales, v_scales, q, batch, n_tok, n_q_heads, d_start_pos, window,
+                    sm_scale, *plan, ws, stream);
+  if (st) return st;
+  // The partial rows are (b, t, hq): the reduce treats batch * n_tok rows of n_q_heads.
+  return launch_reduce(L, ws, (int32_t)rows, n_q_heads, *plan, out, stream);
 }
 
 int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,

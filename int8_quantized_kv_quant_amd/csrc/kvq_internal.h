@@ -13,6 +13,23 @@ constexpr int kMaxSplits = 8192;     // bound on plan.n_splits
 constexpr int kHeadsPerBlock = 16;   // query heads one wave carries (MFMA M/N = 16)
 constexpr int kPartialWaves = 4;     // wavefronts per partial-kernel workgroup
 constexpr int kMinSplitChunk = kPartialWaves * kTile;  // planner: one tile per wavefront at least
+constexpr int kChunkWaves = 4;       // wavefronts per chunk-attention workgroup
+constexpr int kChunkRows = 16 * kChunkWaves;  // (token, head) query rows per chunk workgroup
+
+// Row blocks of a chunk of n_tok tokens whose G query heads share a kv head.
+inline int chunk_row_blocks(int64_t n_tok, int64_t G) {
+  return (int)((n_tok * G + kChunkRows - 1) / kChunkRows);
+}
+
+// Chunk-attention workgroups that fit on one compute unit at once, from the
+// kernel's footprint on gfx950 (three LDS stages per workgroup): ~225 VGPRs and
+// 50 KB at D = 256 (two), ~150 VGPRs and 26 KB at D = 128 (three), ~100 VGPRs
+// and 14 KB at D = 64 (four or more).
+inline int resident_chunk_wgs_per_cu(const kvq_layout& L) {
+  if (L.head_dim == 256) return 2;
+  if (L.head_dim == 128) return 3;
+  return 4;
+}
 
 // Byte sizes of one store element.
 inline int store_elem_bytes(int dtype) { return dtype == KVQ_STORE_INT8 ? 1 : 4; }
@@ -62,6 +79,11 @@ int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store
                    const uint16_t* v_new, const uint16_t* q, int32_t batch, int32_t n_q_heads,
                    const int32_t* d_seq_lens, int32_t window, float sm_scale, const kvq_plan_t& plan,
                    void* ws, void* stream);
+
+int launch_chunk(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
+                 const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
+                 const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
+                 void* stream);
 
 int launch_reduce(const kvq_layout& L, const void* ws, int32_t batch, int32_t n_q_heads,
                   const kvq_plan_t& plan, uint16_t* out, void* stream);

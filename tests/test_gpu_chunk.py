@@ -1,0 +1,138 @@
+"""Chunk attention (kv_chunk_attn: several consecutive query tokens per
+sequence, causal inside the chunk) on the GPU against the fp64 oracle
+(oracle.attend_chunk): max abs error <= 2e-3 (fp32 accumulation, fp16 output)
+on prompt chunks and verify windows, windows, every GQA grouping and the
+ragged row blocks of a chunk.
+
+Strata PR 2698, "What it does": the prompt chunk and the verify windows read
+the same int8 cache as decode, dequantized on the fly.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import kvq_oracle as orc
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _run(w, starts, n_tok, window, plan=None, tokens=None):
+    """Fill positions [0, start_b + n_tok) of every sequence, run the chunk
+    attention on the GPU and the oracle on the host (all tokens, or the listed
+    (b, t) pairs); returns (gpu [B][T][Hq][d], oracle, plan)."""
+    import int8_quantized_kv_quant_amd as kvq
+    import kvq_setup as ks
+    starts = np.asarray(starts, dtype=np.int64)
+    ends = np.minimum(starts + n_tok, w.max_ctx)
+    lay, cache = ks.fill_cache(w, ends)
+    q = wl.chunk_queries(w, n_tok)
+    sm = 1.0 / math.sqrt(w.head_dim)
+    if plan is None:
+        plan = kvq.kvq_plan_chunk(lay, w.batch, n_tok, w.n_q_heads, int(ends.max()), window, ks.n_cu())
+    got = kvq.chunk_attn(lay, cache, torch.from_numpy(q).cuda(),
+                         torch.from_numpy(starts.astype(np.int32)).cuda(), window, sm, plan=plan)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().astype(np.float64)
+    oc = orc.Cache(w.batch, w.max_ctx, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+    for b in range(w.batch):
+        lo = max(0, int(starts[b]) + 1 - window) if window else 0
+        n = int(ends[b]) - lo
+        if n > 0:
+            one = np.array([lo])
+            rows_k = wl.kv_rows(w, "k", b, lo, n)[None]
+            rows_v = wl.kv_rows(w, "v", b, lo, n)[None]
+            sub = orc.Cache(1, w.max_ctx, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+            sub.append(rows_k, rows_v, one)
+            for s in ("k", "v"):
+                oc.data[s][b] = sub.data[s][0]
+                if oc.scales[s] is not None:
+                    oc.scales[s][b] = sub.scales[s][0]
+    want = orc.attend_chunk(q, oc, starts, window, sm, tokens=tokens)
+    return got, want, plan
+
+
+def _check(got, want, tokens=None, label=""):
+    pairs = tokens if tokens is not None else [(b, t) for b in range(got.shape[0]) for t in range(got.shape[1])]
+    worst = 0.0
+    for b, t in pairs:
+        worst = max(worst, float(np.abs(got[b, t] - want[b, t]).max()))
+    print(f"[chunk] {label} max abs err {worst:.3g}", flush=True)
+    assert worst <= TOL, label
+
+
+CASES = {
+    # name: (workload, starts, n_tok, window)
+    "tiny_prompt": (wl.WORKLOADS["tiny"].with_(batch=2, max_ctx=512), [0, 37], 5, 0),
+    "gemma_window_chunk": (wl.WORKLOADS["gemma"].with_(max_ctx=1024), [600], 40, 512),
+    "long_prompt_ragged_blocks": (wl.WORKLOADS["long"].with_(max_ctx=4096), [3000], 130, 0),
+    "batched_three": (wl.WORKLOADS["batched"].with_(batch=3, max_ctx=2304), [100, 2000, 0], 33, 0),
+    "verify_window_long": (wl.WORKLOADS["long"].with_(max_ctx=8192), [6000], 4, 0),
+    "mha_g1": (wl.Workload("mha", 1, 4, 4, 128, 128, 64, 1024, 0, 170), [300], 70, 0),
+    "g16_d64": (wl.Workload("g16", 1, 32, 2, 64, 64, 64, 1024, 0, 171), [500], 9, 0),
+    "window_smaller_than_chunk": (wl.WORKLOADS["long"].with_(max_ctx=2048), [1000], 100, 64),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_chunk_matches_oracle(case):
+    w, starts, n_tok, window = CASES[case]
+    print(f"[chunk] {case}: B={w.batch} T={n_tok} starts={starts} W={window}", flush=True)
+    got, want, plan = _run(w, starts, n_tok, window)
+    print(f"[chunk] {case}: plan {plan.n_splits} x {plan.chunk}", flush=True)
+    _check(got, want, label=case)
+
+
+def test_forced_splits_equal_one_split():
+    """The same chunk with the keys split 1, 3 and 17 ways: every result within
+    the tolerance of the oracle (the combine of kv_decode_reduce per row)."""
+    import int8_quantized_kv_quant_amd as kvq
+    w = wl.WORKLOADS["long"].with_(max_ctx=2048)
+    T = 24
+    for ns, chunk in ((1, 2048), (3, 704), (17, 128)):
+        plan = kvq.Plan(ns, chunk, w.batch * T * w.n_q_heads * ns * (w.head_dim + 2) * 4)
+        got, want, _ = _run(w, [1500], T, 0, plan=plan)
+        _check(got, want, label=f"splits {ns}")
+
+
+def test_single_token_chunk_equals_decode():
+    """n_tok = 1 at start L - 1 is decode attention at context L."""
+    import int8_quantized_kv_quant_amd as kvq
+    import kvq_setup as ks
+    w = wl.WORKLOADS["long"].with_(max_ctx=4096)
+    L = 3333
+    lay, cache = ks.fill_cache(w, np.array([L]))
+    q1 = wl.chunk_queries(w, 1)
+    sm = 1 / 16
+    got = kvq.chunk_attn(lay, cache, torch.from_numpy(q1).cuda(), torch.tensor([L - 1], dtype=torch.int32).cuda(),
+                         0, sm, max_seq_len=L)
+    dec = kvq.decode(lay, cache, torch.from_numpy(q1[:, 0].copy()).cuda(),
+                     torch.tensor([L], dtype=torch.int32).cuda(), 0, sm, n_cu=ks.n_cu())
+    torch.cuda.synchronize()
+    assert np.abs(got[:, 0].float().cpu().numpy() - dec.float().cpu().numpy()).max() <= TOL
+
+
+def test_tokens_past_the_cache_end_get_zero_rows():
+    """A chunk that would run past max_ctx (a device precondition violation):
+    tokens at or beyond max_ctx see no key and get zero rows; the others are
+    exact; nothing outside the cache is read."""
+    w = wl.WORKLOADS["long"].with_(max_ctx=1024)
+    got, want, _ = _run(w, [1000], 40, 0)
+    _check(got[:, :24], want[:, :24], label="inside")
+    assert not got[:, 24:].any()
+
+
+def test_full_size_prompt_chunk_sampled():
+    """The bench's prefill shape: 2048 tokens at position 30000 over the 128K
+    layout of the long workload (16 query / 2 kv heads, head_dim 256, group-64
+    scales); sampled tokens against the oracle."""
+    w = wl.WORKLOADS["long"].with_(max_ctx=32768)
+    T, start = 2048, 30000
+    toks = [(0, 0), (0, 1), (0, 777), (0, 1500), (0, 2046), (0, 2047)]
+    got, want, plan = _run(w, [start], T, 0, tokens=toks)
+    print(f"[chunk] full-size plan {plan.n_splits} x {plan.chunk}", flush=True)
+    _check(got, want, tokens=toks, label="full-size")

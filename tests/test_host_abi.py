@@ -125,6 +125,17 @@ def _fused(lay, plan=None, **kw):
         args["sm"], ctypes.byref(plan.c()), args["ws"], args["ws_bytes"], None)
 
 
+def _chunk(lay, plan=None, **kw):
+    plan = plan or kvq.Plan(2, 256, 1 * 8 * 16 * 2 * 258 * 4)
+    args = dict(k_store=FAKE, v_store=FAKE, k_scales=FAKE, v_scales=FAKE, q=FAKE, batch=1, n_tok=8, n_q=16,
+                start=FAKE, window=0, sm=0.0625, ws=FAKE, ws_bytes=plan.ws_bytes, out=FAKE)
+    args.update(kw)
+    return kvq.load().kv_chunk_attn(
+        ctypes.byref(lay.c()), args["k_store"], args["v_store"], args["k_scales"], args["v_scales"], args["q"],
+        args["batch"], args["n_tok"], args["n_q"], args["start"], args["window"], args["sm"],
+        ctypes.byref(plan.c()), args["ws"], args["ws_bytes"], args["out"], None)
+
+
 def _reduce(lay, plan=None, **kw):
     plan = plan or kvq.Plan(4, 256, 1 * 16 * 4 * 258 * 4)
     args = dict(ws=FAKE, ws_bytes=plan.ws_bytes, seq_lens=FAKE, batch=1, n_q=16, window=0, out=FAKE)
@@ -170,6 +181,43 @@ def test_fused_append_refuses_what_either_part_refuses():
     assert _fused(lay, window=-1) == SHAPE
     assert _fused(lay, ws=None) == WS
     assert _fused(lay, batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
+
+
+@needs_lib
+def test_chunk_attention_refusals():
+    lay = _base()
+    assert _chunk(_with(lay, v_dtype=kvq.KVQ_STORE_FP32)) == UNSUP   # int8 K and V only
+    assert _chunk(lay, k_scales=None) == NULL_
+    assert _chunk(lay, q=None) == NULL_
+    assert _chunk(lay, start=None) == NULL_
+    assert _chunk(lay, out=None) == NULL_
+    assert _chunk(lay, q=FAKE + 8) == ALIGN
+    assert _chunk(lay, out=FAKE + 2) == ALIGN
+    assert _chunk(lay, n_q=15) == SHAPE
+    assert _chunk(lay, n_tok=-1) == SHAPE
+    assert _chunk(lay, window=-1) == SHAPE
+    assert _chunk(lay, plan=kvq.Plan(2, 100, 10 ** 9)) == SHAPE
+    assert _chunk(lay, plan=kvq.Plan(2, 256, 1000)) == WS           # smaller than the partials
+    assert _chunk(lay, ws_bytes=16) == WS
+    assert _chunk(lay, ws=None) == WS
+    assert _chunk(lay, batch=0) == 0 and _chunk(lay, n_tok=0) == 0
+
+
+@needs_lib
+@pytest.mark.parametrize("n_tok,start,window", [(2048, 30000, 0), (4, 131068, 0), (1024, 3072, 512), (1, 63, 0)])
+def test_chunk_plan_covers_every_key_range(n_tok, start, window):
+    w = wl.WORKLOADS["long"]
+    lay = _layout(w)
+    p = kvq.kvq_plan_chunk(lay, 1, n_tok, 16, start + n_tok, window, 256)
+    l_eff = min(start + n_tok, window + n_tok) if window else start + n_tok
+    assert p.chunk % 32 == 0 and 1 <= p.n_splits <= 8192
+    assert p.n_splits * p.chunk >= l_eff
+    assert p.ws_bytes == n_tok * 16 * p.n_splits * (256 + 2) * 4
+    rows = n_tok * 8
+    if rows >= 64 * 256:     # enough 64-row blocks to fill the chip: one split
+        assert p.n_splits == 1
+    if n_tok == 4:           # a verify window over 128K keys is split
+        assert p.n_splits > 16
 
 
 @needs_lib

@@ -116,6 +116,13 @@ def queries(w: Workload, seed_offset: int = 0) -> np.ndarray:
     return _normal_f16(_rng(w.seed + seed_offset, "q"), (w.batch, w.n_q_heads, w.head_dim))
 
 
+def chunk_queries(w: Workload, n_tok: int, seed_offset: int = 0) -> np.ndarray:
+    """float16 [batch][n_tok][n_q_heads][head_dim]: query rows of a chunk of
+    n_tok consecutive tokens per sequence (its own stream, apart from the
+    single-token queries)."""
+    return _normal_f16(_rng(w.seed + seed_offset, "q", 1), (w.batch, n_tok, w.n_q_heads, w.head_dim))
+
+
 def outlier_channels(w: Workload) -> np.ndarray:
     """int64 [n_kv_heads][n_out]: K channels scaled by outlier_gain (per kv head)."""
     n_out = int(round(w.outlier_frac * w.head_dim))
