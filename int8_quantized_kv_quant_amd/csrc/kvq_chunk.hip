@@ -58,18 +58,98 @@ struct ChunkArgs {
 
 constexpr int kChunkStages = 3;
 
-template <int D, bool G64>
+// The fp16 value tile of the chunk kernel is stored transposed: row d holds the
+// 32 positions of dim d, position p at slot vt_slot(p), so that the P.V
+// contraction index 8*q4 + e (position kpos(e, q4)) is contiguous per lane.
+__device__ __forceinline__ int vt_slot(int p) { return 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3); }
+constexpr int kVtPitch = 64;  // bytes per dim row: 32 fp16
+
+// Accumulators of one block of 16 query rows in the O^T layout: lane (c16, q4)
+// holds O^T[dim 16*mt + 4*q4 + i][row c16], i.e. only values of its own row.
+template <int D>
+struct RowAcc {
+  f32x4 o[D / 16];
+  f32x4 l;       // the row sum (all four elements equal)
+  float m_ref;   // lazily raised reference max of the row (log2 domain)
+};
+
+// Online-softmax update of one tile's scores for the lane's own row; returns
+// P (fp16) in the B-operand layout of O^T += V_hat^T . P^T.
+template <int D>
+__device__ __forceinline__ f16x8 row_softmax(const float (&z)[2][4], RowAcc<D>& acc) {
+  float tmax = z[0][0];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, z[ct][i]);
+  tmax = max_xor16_xor32(tmax);
+  const bool need = tmax > acc.m_ref + kTau;
+  if (__any(need)) {
+    const float m_new = need ? tmax : acc.m_ref;
+    const float alpha = need ? __builtin_amdgcn_exp2f(acc.m_ref - m_new) : 1.0f;
+    acc.m_ref = m_new;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) acc.o[mt] *= alpha;
+    acc.l *= alpha;
+  }
+  const float mu = acc.m_ref == -INFINITY ? 0.0f : acc.m_ref;
+  f16x8 pa;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pa[4 * ct + i] = (f16)__builtin_amdgcn_exp2f(z[ct][i] - mu);
+  return pa;
+}
+
+// This wavefront's quarter of the value tile in stage `st`, dequantized to
+// fp16(code * scale) (the decode kernel's rounding) and stored transposed:
+// lane (dim quad, slot block qb) converts 4 dims x 8 positions.
+template <class S, int NW>
+__device__ __forceinline__ void convert_v(const uint8_t* __restrict__ st, uint8_t* __restrict__ vt, int wv, int lane) {
+  using ST = Stage<S>;
+  constexpr int QPW = S::D / 4 / NW;  // dim quads per wavefront
+  if (lane >= 4 * QPW) return;
+  const int qb = lane / QPW;
+  const int d0 = 4 * (wv * QPW + lane % QPW);
+  const int grp = S::G64 ? d0 / 64 : 0;
+  constexpr uint32_t kNegBias = 0xE480E480u;  // fp16 pair (-1152, -1152)
+  uint32_t v01[8], v23[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = kpos(e, qb);
+    const uint32_t codes =
+        *reinterpret_cast<const uint32_t*>(st + ST::V_OFF + r * S::D + 16 * ((d0 / 16) ^ ST::swz(r)) + (d0 % 16));
+    const uint32_t sb = *reinterpret_cast<const uint16_t*>(st + ST::VS_OFF + r * ST::SPITCH + 2 * grp);
+    const f16x2 s2 = as_h2(sb | (sb << 16));
+    const uint32_t fl = codes ^ kCodeFlip;
+    v01[e] = as_u32((as_h2(biased_h2_lo(fl)) + as_h2(kNegBias)) * s2);
+    v23[e] = as_u32((as_h2(biased_h2_hi(fl)) + as_h2(kNegBias)) * s2);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t* src = k < 2 ? v01 : v23;
+    const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 w;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) w[e2] = __builtin_amdgcn_perm(src[2 * e2 + 1], src[2 * e2], sel);
+    *reinterpret_cast<u32x4*>(vt + (d0 + k) * kVtPitch + 16 * qb) = w;
+  }
+}
+
+template <int D, bool G64, int RB>
 __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a) {
   using S = Shape<D, true, true, G64>;
   using ST = Stage<S>;
   constexpr int NI = 32 * D / 1024;  // 1 KiB code loads per half tile
   constexpr int NL = 2 * NI + 2;     // direct-to-LDS loads per tile (codes + scale rows)
   constexpr int NW = kChunkWaves;
+  constexpr int ROWS = 16 * RB * NW;  // query rows of the workgroup
   __shared__ __attribute__((aligned(16))) uint8_t lds_st[kChunkStages][ST::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_vt[D * kVtPitch];
 
   const int split = blockIdx.x;
   const int hk = blockIdx.y / a.row_blocks;
-  const int rb = blockIdx.y % a.row_blocks;
+  const int rblk = blockIdx.y % a.row_blocks;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -78,9 +158,9 @@ __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a
   const int G = a.G;
 
   // ---- rows of the workgroup and the keys they may see ------------------------
-  const int fr0 = rb * kChunkRows;                     // first flat row (t * G + h)
+  const int fr0 = rblk * ROWS;                         // first flat row (t * G + h)
   const int t_first = fr0 / G;
-  const int t_last = min(a.T - 1, (fr0 + kChunkRows - 1) / G);
+  const int t_last = min(a.T - 1, (fr0 + ROWS - 1) / G);
   int s0 = a.start_pos[b];
   s0 = s0 < 0 ? 0 : (s0 > a.max_ctx ? a.max_ctx : s0);
   // Keys [lo_all, hi_all): up to the last token's own position (tokens that
@@ -90,15 +170,11 @@ __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a
   const int start = lo_all + split * a.chunk;
   const int end = (split == a.n_splits - 1) ? hi_all : min(hi_all, start + a.chunk);
 
-  // This lane's row as the S^T column c16, and as O rows 4*q4 + i.
-  const int my_fr = fr0 + wv * 16 + c16;
-  const int my_t = my_fr / G;
-  const bool my_valid = my_t < a.T;
-  const int my_P = s0 + my_t;
-  const int my_hi = (my_valid && my_P < a.max_ctx) ? my_P + 1 : 0;  // keys p < my_hi
-  const int my_lo = a.window > 0 ? max(0, my_P + 1 - a.window) : 0;
-  auto row_id = [&](int r) -> int64_t {  // partial row of wave row r, or -1
-    const int fr = fr0 + wv * 16 + r;
+  // Row block rb of this wavefront: flat rows fr0 + 16 * (RB * wv + rb) + c16.
+  // The lane's row is the S^T column c16 and the O^T column c16.
+  auto flat_row = [&](int rb) { return fr0 + 16 * (RB * wv + rb) + c16; };
+  auto row_id = [&](int rb) -> int64_t {  // partial row of the lane's row in block rb, or -1
+    const int fr = flat_row(rb);
     const int t = fr / G;
     if (t >= a.T) return -1;
     return (((int64_t)b * a.T + t) * a.n_q + hk * G + fr % G) * a.n_splits + split;
@@ -106,49 +182,58 @@ __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a
 
   float2* const ml = reinterpret_cast<float2*>(a.ws_ml);
   if (start >= end) {  // nothing to attend in this split: empty partials
-    if (lane < 16) {
-      const int64_t id = row_id(lane);
-      if (id >= 0) ml[id] = make_float2(-INFINITY, 0.0f);
+    if (q4 == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int64_t id = row_id(rb);
+        if (id >= 0) ml[id] = make_float2(-INFINITY, 0.0f);
+      }
     }
     return;
   }
 
-  // ---- query operands of the lane's row, in registers (before any LDS load, so
-  // the compiler's wait for them does not include the key tiles) ---------------
-  f16x8 qv[S::NJ][2];
-  {
-    const uint16_t* qrow = a.q + (((int64_t)b * a.T + my_t) * a.n_q + hk * G + my_fr % G) * D;
+  // ---- query operands of the lane's rows, in registers (loaded and used before
+  // any direct-to-LDS load, so the compiler's wait for them covers nothing else)
+  f16x8 qv[RB][S::NJ][2];
+  float corr[RB][S::NG];
+  int vlo[RB], vhi[RB];  // keys [vlo, vhi) of the lane's row in block rb
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int fr = flat_row(rb);
+    const int t = fr / G;
+    const bool valid = t < a.T;
+    const int P = s0 + t;
+    vhi[rb] = (valid && P < a.max_ctx) ? P + 1 : 0;
+    vlo[rb] = a.window > 0 ? max(0, P + 1 - a.window) : 0;
+    const uint16_t* qrow = a.q + (((int64_t)b * a.T + t) * a.n_q + hk * G + fr % G) * D;
 #pragma unroll
     for (int j = 0; j < S::NJ; ++j)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (my_valid) v = *reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * q4 + 8 * u);
-        qv[j][u] = __builtin_bit_cast(f16x8, v);
+        if (valid) v = *reinterpret_cast<const u32x4*>(qrow + 64 * j + 16 * q4 + 8 * u);
+        qv[rb][j][u] = __builtin_bit_cast(f16x8, v);
       }
-  }
-  float corr[S::NG];
-  {
     float qsum[S::NJ];
 #pragma unroll
     for (int j = 0; j < S::NJ; ++j) {
       float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += (float)qv[j][0][e] + (float)qv[j][1][e];
+      for (int e = 0; e < 8; ++e) s += (float)qv[rb][j][0][e] + (float)qv[rb][j][1][e];
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
       qsum[j] = s;
     }
 #pragma unroll
     for (int g = 0; g < S::NG; ++g) {
-      float t = 0.0f;
+      float t2 = 0.0f;
       if (G64) {
-        t = qsum[g];
+        t2 = qsum[g];
       } else {
 #pragma unroll
-        for (int j = 0; j < S::NJ; ++j) t += qsum[j];
+        for (int j = 0; j < S::NJ; ++j) t2 += qsum[j];
       }
-      corr[g] = -kCodeBias * t;
+      corr[rb][g] = -kCodeBias * t2;
     }
   }
 
@@ -163,10 +248,10 @@ __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a
   const u32x4 ksrw = rsrc_words(a.k_scales + sc_off, sc_bytes);
   const u32x4 vsrw = rsrc_words(a.v_scales + sc_off, sc_bytes);
 
-  // Load i of the NL loads of the tile at p0 into stage `st` (wavefront wv
-  // issues loads wv, wv + NW, ...): K codes, V codes, K scale rows, V scale
-  // rows, laid out as the decode kernel's stage. Rows beyond the split read as
-  // zeros through an out-of-range lane offset.
+  // The NL loads of the tile at p0 into stage `stage`, spread over the
+  // wavefronts (wavefront wv issues loads wv, wv + NW, ...): K codes, V codes,
+  // K scale rows, V scale rows, in the decode kernel's stage layout. Rows
+  // beyond the split read as zeros through an out-of-range lane offset.
   auto issue_tile = [&](int stage, int p0) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int nvalid = min(kTile, end - p0);
@@ -200,11 +285,15 @@ __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a
     else wait_vm<NL / NW>();
   };
 
-  WaveAcc<S> acc;
+  RowAcc<D> acc[RB];
 #pragma unroll
-  for (int n = 0; n < S::VB; ++n) acc.o[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  acc.l = (f32x4){0.f, 0.f, 0.f, 0.f};
-  acc.m_ref = -INFINITY;
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) acc[rb].o[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    acc[rb].l = (f32x4){0.f, 0.f, 0.f, 0.f};
+    acc[rb].m_ref = -INFINITY;
+  }
+  const f16x8 ones = {(f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1};
 
   const int n_tiles = (end - start + kTile - 1) / kTile;
   issue_tile(0, start);
@@ -213,54 +302,64 @@ __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a
     if (t + 1 < n_tiles) wait_all_but_next();  // own share of tile t landed; tile t+1 may still load
     else wait_vm<0>();
     // Every wavefront's share of tile t is in LDS, and every wavefront is done
-    // with tile t-1, whose stage the tile t+2 loads now reuse.
+    // with tile t-1 (its stage, which the tile t+2 loads reuse, and the value
+    // tile, which is rewritten next).
     asm volatile("s_barrier" ::: "memory");
     if (t + 2 < n_tiles) issue_tile((t + 2) % kChunkStages, start + (t + 2) * kTile);
     const uint8_t* st = &lds_st[t % kChunkStages][0];
     const int p0 = start + t * kTile;
+    convert_v<S, NW>(st, lds_vt, wv, lane);
+    // Scores and softmax of the wavefront's rows while the value tile fills.
     KRegs<S> tk;
     stage_read_k<S>(tk, st, c16, q4);
-    float z[2][4];
-    tile_scores_q<S>(tk, max(my_lo, p0) - p0, min(my_hi, end) - p0, z, qv, corr, a.c2, q4);
-    VRegs<S> tv;
-    stage_read_v<S>(tv, st, c16, q4);
-    const f16x8 pa = tile_softmax<S>(z, acc, q4);
-    tile_pv<S>(tv, pa, acc);
+    f16x8 pa[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float z[2][4];
+      tile_scores_q<S>(tk, max(vlo[rb], p0) - p0, min(vhi[rb], end) - p0, z, qv[rb], corr[rb], a.c2, q4);
+      pa[rb] = row_softmax<D>(z, acc[rb]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the value tile is complete
+    // O^T (dims x rows) += V_hat^T (dims x 32 positions) . P^T; A operand: 8
+    // positions of one dim, contiguous in the transposed tile.
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
+      const f16x8 v = *reinterpret_cast<const f16x8*>(lds_vt + (16 * mt + c16) * kVtPitch + 16 * q4);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb].o[mt] = mfma16(v, pa[rb], acc[rb].o[mt]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb].l = mfma16(ones, pa[rb], acc[rb].l);
   }
 
-  // ---- partials of this wavefront's 16 rows --------------------------------------
-  // O rows 4*q4 + i, dims VB*c16 + [0, VB); the max of row r is held by the lanes
-  // with c16 = r, its sum by the lanes with q4 = r / 4 (element r % 4).
+  // ---- partials of the wavefront's rows: lane (c16, q4) writes dims
+  // 16*mt + 4*q4 + [0, 4) of its row c16, and lanes q4 = 0 its (max, sum) ------
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t id = row_id(4 * q4 + i);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int64_t id = row_id(rb);
     if (id >= 0) {
-      float* o = a.ws_o + id * D + S::VB * c16;
+      float* o = a.ws_o + id * D + 4 * q4;
 #pragma unroll
-      for (int n4 = 0; n4 < S::VB / 4; ++n4)
-        *reinterpret_cast<float4*>(o + 4 * n4) =
-            make_float4(acc.o[4 * n4 + 0][i], acc.o[4 * n4 + 1][i], acc.o[4 * n4 + 2][i], acc.o[4 * n4 + 3][i]);
-    }
-  }
-  {
-    const int r = c16;
-    const int src = 16 * (r >> 2);
-    const float l0 = __shfl(acc.l[0], src), l1 = __shfl(acc.l[1], src);
-    const float l2 = __shfl(acc.l[2], src), l3 = __shfl(acc.l[3], src);
-    const float l = (r & 3) == 0 ? l0 : (r & 3) == 1 ? l1 : (r & 3) == 2 ? l2 : l3;
-    if (q4 == 0) {
-      const int64_t id = row_id(r);
-      if (id >= 0) ml[id] = make_float2(acc.m_ref, l);
+      for (int mt = 0; mt < D / 16; ++mt)
+        *reinterpret_cast<float4*>(o + 16 * mt) =
+            make_float4(acc[rb].o[mt][0], acc[rb].o[mt][1], acc[rb].o[mt][2], acc[rb].o[mt][3]);
+      if (q4 == 0) ml[id] = make_float2(acc[rb].m_ref, acc[rb].l[0]);
     }
   }
 }
 
-template <int D>
-static void launch_chunk_d(const kvq_layout& L, const ChunkArgs& a, dim3 grid, hipStream_t s) {
+template <int D, int RB>
+static void launch_chunk_rb(const kvq_layout& L, const ChunkArgs& a, dim3 grid, hipStream_t s) {
   if (L.scale_group == 64 && L.head_dim != 64)
-    hipLaunchKernelGGL((kvq_chunk_kernel<D, true>), grid, dim3(kChunkWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((kvq_chunk_kernel<D, true, RB>), grid, dim3(kChunkWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((kvq_chunk_kernel<D, false>), grid, dim3(kChunkWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((kvq_chunk_kernel<D, false, RB>), grid, dim3(kChunkWaves * 64), 0, s, a);
+}
+
+template <int D>
+static void launch_chunk_d(const kvq_layout& L, const ChunkArgs& a, int rows_per_wg, dim3 grid, hipStream_t s) {
+  if (rows_per_wg == 32 * kChunkWaves) launch_chunk_rb<D, 2>(L, a, grid, s);
+  else launch_chunk_rb<D, 1>(L, a, grid, s);
 }
 
 int launch_chunk(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
@@ -288,7 +387,8 @@ int launch_chunk(const kvq_layout& L, const void* k_store, const void* v_store, 
   a.G = n_q_heads / L.n_kv_heads;
   a.n_q = n_q_heads;
   a.T = n_tok;
-  a.row_blocks = chunk_row_blocks(n_tok, a.G);
+  const int rows_per_wg = chunk_rows_per_wg(n_tok, a.G, L.head_dim);
+  a.row_blocks = chunk_row_blocks(n_tok, a.G, L.head_dim);
   a.n_splits = plan.n_splits;
   a.chunk = plan.chunk;
   a.window = window;
@@ -296,9 +396,9 @@ int launch_chunk(const kvq_layout& L, const void* k_store, const void* v_store, 
   dim3 grid(plan.n_splits, L.n_kv_heads * a.row_blocks, batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (L.head_dim) {
-    case 64: launch_chunk_d<64>(L, a, grid, s); break;
-    case 128: launch_chunk_d<128>(L, a, grid, s); break;
-    case 256: launch_chunk_d<256>(L, a, grid, s); break;
+    case 64: launch_chunk_d<64>(L, a, rows_per_wg, grid, s); break;
+    case 128: launch_chunk_d<128>(L, a, rows_per_wg, grid, s); break;
+    case 256: launch_chunk_d<256>(L, a, rows_per_wg, grid, s); break;
     default: return KVQ_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;

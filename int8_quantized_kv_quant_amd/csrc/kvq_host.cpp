@@ -221,8 +221,8 @@ int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32
   const int64_t G = n_q_heads / L.n_kv_heads;
   // Keys one workgroup may walk: the whole prefix, or the window plus the chunk.
   const int64_t l_eff = window > 0 ? std::min<int64_t>(max_seq_len, (int64_t)window + n_tok) : max_seq_len;
-  const int64_t units = (int64_t)(batch > 0 ? batch : 1) * L.n_kv_heads * chunk_row_blocks(n_tok > 0 ? n_tok : 1, G);
-  const int64_t want = (int64_t)resident_chunk_wgs_per_cu(L) * n_cu;
+  const int64_t units = (int64_t)(batch > 0 ? batch : 1) * L.n_kv_heads * chunk_row_blocks(n_tok > 0 ? n_tok : 1, G, L.head_dim);
+  const int64_t want = (int64_t)resident_chunk_wgs_per_cu(L, chunk_rows_per_wg(n_tok > 0 ? n_tok : 1, G, L.head_dim)) * n_cu;
   int64_t n_splits = 1, chunk = round_up(l_eff > 0 ? l_eff : 1, kTile);
   if (units < want && l_eff > kMinSplitChunk) {
     // Few query rows over a long prefix (a verify window): split the keys so
@@ -254,7 +254,7 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
   if (plan->n_splits < 1 || plan->n_splits > kMaxSplits) return KVQ_ERR_SHAPE;
   if (plan->chunk < kTile || plan->chunk % kTile) return KVQ_ERR_SHAPE;
   const int64_t rows = (int64_t)batch * n_tok;
-  if (rows * n_q_heads > INT_MAX / 8 || (int64_t)L.n_kv_heads * chunk_row_blocks(n_tok, n_q_heads / L.n_kv_heads) > 65535)
+  if (rows * n_q_heads > INT_MAX / 8 || (int64_t)L.n_kv_heads * chunk_row_blocks(n_tok, n_q_heads / L.n_kv_heads, L.head_dim) > 65535)
     return KVQ_ERR_UNSUPPORTED;  // grid limits
   if (plan->ws_bytes < workspace_bytes(rows, n_q_heads, plan->n_splits, L.head_dim)) return KVQ_ERR_WORKSPACE;
   if (!q || !d_start_pos || !out) return KVQ_ERR_NULL;

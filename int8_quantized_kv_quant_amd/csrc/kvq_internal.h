@@ -14,21 +14,32 @@ constexpr int kHeadsPerBlock = 16;   // query heads one wave carries (MFMA M/N =
 constexpr int kPartialWaves = 4;     // wavefronts per partial-kernel workgroup
 constexpr int kMinSplitChunk = kPartialWaves * kTile;  // planner: one tile per wavefront at least
 constexpr int kChunkWaves = 4;       // wavefronts per chunk-attention workgroup
-constexpr int kChunkRows = 16 * kChunkWaves;  // (token, head) query rows per chunk workgroup
+
+// (token, head) query rows per chunk-attention workgroup: 16 per wavefront,
+// or 32 (two row blocks sharing each key and value operand) for head_dim <= 128
+// when the chunk has rows enough; at head_dim 256 two row blocks exceed the
+// register file (measured slower).
+inline int chunk_rows_per_wg(int64_t n_tok, int64_t G, int head_dim) {
+  return (head_dim <= 128 && n_tok * G >= 1024) ? 32 * kChunkWaves : 16 * kChunkWaves;
+}
 
 // Row blocks of a chunk of n_tok tokens whose G query heads share a kv head.
-inline int chunk_row_blocks(int64_t n_tok, int64_t G) {
-  return (int)((n_tok * G + kChunkRows - 1) / kChunkRows);
+inline int chunk_row_blocks(int64_t n_tok, int64_t G, int head_dim) {
+  const int64_t r = chunk_rows_per_wg(n_tok, G, head_dim);
+  return (int)((n_tok * G + r - 1) / r);
 }
 
 // Chunk-attention workgroups that fit on one compute unit at once, from the
-// kernel's footprint on gfx950 (three LDS stages per workgroup): ~225 VGPRs and
-// 50 KB at D = 256 (two), ~150 VGPRs and 26 KB at D = 128 (three), ~100 VGPRs
-// and 14 KB at D = 64 (four or more).
-inline int resident_chunk_wgs_per_cu(const kvq_layout& L) {
-  if (L.head_dim == 256) return 2;
-  if (L.head_dim == 128) return 3;
-  return 4;
+// kernel's footprint on gfx950 (three LDS stages and the fp16 value tile per
+// workgroup): with one row block per wavefront ~250 VGPRs and 67 KB at D = 256
+// (two), ~150 VGPRs and 34 KB at D = 128 (three), ~110 VGPRs at D = 64 (four);
+// with two row blocks 256 VGPRs + AGPRs at D = 256 (one), ~230 at D = 128
+// (two), ~150 at D = 64 (three).
+inline int resident_chunk_wgs_per_cu(const kvq_layout& L, int rows_per_wg) {
+  const bool two = rows_per_wg == 32 * kChunkWaves;
+  if (L.head_dim == 256) return two ? 1 : 2;
+  if (L.head_dim == 128) return two ? 2 : 3;
+  return two ? 3 : 4;
 }
 
 // Byte sizes of one store element.

@@ -75,6 +75,9 @@ CASES = {
     "mha_g1": (wl.Workload("mha", 1, 4, 4, 128, 128, 64, 1024, 0, 170), [300], 70, 0),
     "g16_d64": (wl.Workload("g16", 1, 32, 2, 64, 64, 64, 1024, 0, 171), [500], 9, 0),
     "window_smaller_than_chunk": (wl.WORKLOADS["long"].with_(max_ctx=2048), [1000], 100, 64),
+    # head_dim <= 128 with >= 1024 rows per kv head: two row blocks per wavefront
+    "batched_two_row_blocks": (wl.WORKLOADS["batched"].with_(batch=2, max_ctx=2048), [500, 1400], 300, 0),
+    "g16_d64_two_row_blocks": (wl.Workload("g16b", 1, 32, 2, 64, 64, 64, 1024, 0, 172), [600], 80, 100),
 }
 
 
