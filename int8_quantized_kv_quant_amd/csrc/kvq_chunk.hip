@@ -62,7 +62,10 @@ constexpr int kChunkStages = 3;
 // 32 positions of dim d, position p at slot vt_slot(p), so that the P.V
 // contraction index 8*q4 + e (position kpos(e, q4)) is contiguous per lane.
 __device__ __forceinline__ int vt_slot(int p) { return 8 * ((p & 15) >> 2) + 4 * (p >> 4) + (p & 3); }
-constexpr int kVtPitch = 64;  // bytes per dim row: 32 fp16
+// Bytes per dim row: 32 fp16 and 16 bytes of padding, so that the rows four
+// apart that one conversion store writes (and the 16 consecutive rows one
+// operand read covers) fall on distinct LDS banks.
+constexpr int kVtPitch = 80;
 
 // Accumulators of one block of 16 query rows in the O^T layout: lane (c16, q4)
 // holds O^T[dim 16*mt + 4*q4 + i][row c16], i.e. only values of its own row.
@@ -249,36 +252,50 @@ __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a
   const u32x4 vsrw = rsrc_words(a.v_scales + sc_off, sc_bytes);
 
   // The NL loads of the tile at p0 into stage `stage`, spread over the
-  // wavefronts (wavefront wv issues loads wv, wv + NW, ...): K codes, V codes,
-  // K scale rows, V scale rows, in the decode kernel's stage layout. Rows
-  // beyond the split read as zeros through an out-of-range lane offset.
+  // wavefronts (wavefront w issues loads w, w + NW, ..., a compile-time set):
+  // K codes, V codes, K scale rows, V scale rows, in the decode kernel's stage
+  // layout. Rows beyond the split read as zeros through an out-of-range lane
+  // offset.
+  auto issue_one = [&](int i, uint32_t base, uint32_t soff, uint32_t ssoff, int nvalid) {
+    if (i < 2 * NI) {
+      const int ci = i < NI ? i : i - NI;
+      const int slot = ci * 64 + lane;
+      const int r = slot / S::CH;
+      const int c = (slot % S::CH) ^ ST::swz(r);
+      const uint32_t voff = r < nvalid ? (uint32_t)r * row + 16 * c : kOOB;
+      dma<16>(i < NI ? krw : vrw, base + (i < NI ? ST::K_OFF : ST::V_OFF) + 1024 * ci, voff, soff);
+    } else {
+      const uint32_t dst = base + (i == 2 * NI ? ST::KS_OFF : ST::VS_OFF);
+      if constexpr (S::SB >= 4) {
+        constexpr int PER = S::SB / 4;  // dwords per row
+        const int r = lane / PER;
+        dma<4>(i == 2 * NI ? ksrw : vsrw, dst, r < nvalid ? (uint32_t)r * srow + 4 * (lane % PER) : kOOB, ssoff);
+      } else {  // lane l = row l, written at byte 4l; rows 32..63 read as zero
+        dma<2>(i == 2 * NI ? ksrw : vsrw, dst, lane < nvalid ? (uint32_t)lane * srow : kOOB, ssoff);
+      }
+    }
+  };
+  // Role w: loads w, w + NW, ... With w a constant in each case below, the
+  // unrolled indices are constants and every branch above folds away.
+  auto issue_role = [&](const int w, uint32_t base, uint32_t soff, uint32_t ssoff, int nvalid) {
+#pragma unroll
+    for (int k = 0; k < (NL + NW - 1) / NW; ++k)
+      if (w + NW * k < NL) issue_one(w + NW * k, base, soff, ssoff, nvalid);
+  };
   auto issue_tile = [&](int stage, int p0) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int nvalid = min(kTile, end - p0);
     const uint32_t base = lds_addr_of(&lds_st[stage][0]);
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * row);
     const uint32_t ssoff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * srow);
-    for (int i = wv; i < NL; i += NW) {
-      if (i < 2 * NI) {
-        const int ci = i < NI ? i : i - NI;
-        const int slot = ci * 64 + lane;
-        const int r = slot / S::CH;
-        const int c = (slot % S::CH) ^ ST::swz(r);
-        const uint32_t voff = r < nvalid ? (uint32_t)r * row + 16 * c : kOOB;
-        dma<16>(i < NI ? krw : vrw, base + (i < NI ? ST::K_OFF : ST::V_OFF) + 1024 * ci, voff, soff);
-      } else {
-        const u32x4 srs = i == 2 * NI ? ksrw : vsrw;
-        const uint32_t dst = base + (i == 2 * NI ? ST::KS_OFF : ST::VS_OFF);
-        if constexpr (S::SB >= 4) {
-          constexpr int PER = S::SB / 4;  // dwords per row
-          const int r = lane / PER;
-          dma<4>(srs, dst, r < nvalid ? (uint32_t)r * srow + 4 * (lane % PER) : kOOB, ssoff);
-        } else {  // lane l = row l, written at byte 4l; rows 32..63 read as zero
-          dma<2>(srs, dst, lane < nvalid ? (uint32_t)lane * srow : kOOB, ssoff);
-        }
-      }
+    switch (wv) {
+      case 0: issue_role(0, base, soff, ssoff, nvalid); break;
+      case 1: issue_role(1, base, soff, ssoff, nvalid); break;
+      case 2: issue_role(2, base, soff, ssoff, nvalid); break;
+      default: issue_role(3, base, soff, ssoff, nvalid); break;
     }
   };
+  static_assert(NW == 4, "issue_tile assigns four wavefront roles");
   // Loads this wavefront issues per tile (NL spread round-robin over NW).
   auto wait_all_but_next = [&]() {
     if (wv < NL % NW) wait_vm<NL / NW + 1>();
