@@ -106,14 +106,16 @@ __device__ __forceinline__ f16x8 row_softmax(const float (&z)[2][4], RowAcc<D>& 
 
 // This wavefront's quarter of the value tile in stage `st`, dequantized to
 // fp16(code * scale) (the decode kernel's rounding) and stored transposed:
-// lane (dim quad, slot block qb) converts 4 dims x 8 positions.
+// lane (dim quad, slot block qb) converts 4 dims x 8 positions. The slot block
+// is the fast lane index, so the 16 lanes of one LDS pass store to 16 distinct
+// 16-byte bank groups (rows 80 bytes apart) and read 16 distinct dwords.
 template <class S, int NW>
 __device__ __forceinline__ void convert_v(const uint8_t* __restrict__ st, uint8_t* __restrict__ vt, int wv, int lane) {
   using ST = Stage<S>;
   constexpr int QPW = S::D / 4 / NW;  // dim quads per wavefront
   if (lane >= 4 * QPW) return;
-  const int qb = lane / QPW;
-  const int d0 = 4 * (wv * QPW + lane % QPW);
+  const int qb = lane & 3;
+  const int d0 = 4 * (wv * QPW + (lane >> 2));
   const int grp = S::G64 ? d0 / 64 : 0;
   constexpr uint32_t kNegBias = 0xE480E480u;  // fp16 pair (-1152, -1152)
   uint32_t v01[8], v23[8];
