@@ -51,7 +51,7 @@ def log(msg: str) -> None:
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("kvq_decode.hip", "kvq_device.h"):
+    for f in ("kvq_decode.hip", "kvq_tile.h", "kvq_device.h"):
         with open(os.path.join(ROOT, "int8_quantized_kv_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -94,7 +94,8 @@ def cpu_baseline(w, lens, q, sm):
 
 def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
     """The decode step (kv_append_decode_splitk + kv_decode_reduce, graph-replayed)
-    on the other two shapes the metric is quoted on:
+    on the other two shapes the metric is quoted on, and the chunk attention of
+    a prompt chunk (chunk_workload):
       gemma_4k  -- 8 query / 1 kv head, head_dim 256 in a 512-wide slot, one scale
                    per (position, kv head), context 4096 with a 512-key window;
       batched   -- 64 sequences of lengths U[1024, 32768], 32 query / 8 kv heads,
@@ -153,6 +154,8 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
                        **timed(w, lens, lay, caches, k_new, v_new)}
     del caches, c0
 
+    res["prefill_chunk"] = chunk_workload(kvq, kvq_setup, wl, n_cu)
+
     w = wl.WORKLOADS["batched"]
     lens = wl.seq_lens(w)
     lay = kvq_setup.layout_for(w)
@@ -172,6 +175,59 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
     del cache
     torch.cuda.empty_cache()
     return res
+
+
+def chunk_workload(kvq, kvq_setup, wl, n_cu):
+    """kv_chunk_attn (partials + combine) on a 2048-token prompt chunk at
+    position 30000 of the long-context layout (16 query / 2 kv heads, head_dim
+    256, group-64 scales; keys 0..32047 in the cache, causal inside the chunk).
+    Algorithmic work: 4 * head_dim flops per (token, query head, attended key)
+    (Q.K and P.V); bound by the matrix cores (fp16 MFMA peak 2.5 PFLOP/s).
+    Two sampled tokens are checked against the fp64 oracle."""
+    import torch
+    from oracle import kvq_oracle as orc
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS["long"].with_(max_ctx=32768)
+    T, start = 2048, 30000
+    end = start + T
+    lay, cache = kvq_setup.fill_cache(w, np.array([end]))
+    qh = wl.chunk_queries(w, T)
+    q = torch.from_numpy(qh).to(dev)
+    sp = torch.tensor([start], dtype=torch.int32, device=dev)
+    sm = 1.0 / math.sqrt(w.head_dim)
+    plan = kvq.kvq_plan_chunk(lay, 1, T, w.n_q_heads, end, 0, n_cu)
+    ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((1, T, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+
+    def call():
+        kvq.kv_chunk_attn(lay, cache["k"], cache["v"], cache["k_scales"], cache["v_scales"], q, 1, T, w.n_q_heads,
+                          sp, 0, sm, plan, ws, ws.numel(), out)
+
+    call()
+    torch.cuda.synchronize()
+    reps = 10
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    toks = [(0, 5), (0, T - 1)]
+    oc = orc.Cache(1, end, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+    oc.append(wl.kv_rows(w, "k", 0, 0, end)[None], wl.kv_rows(w, "v", 0, 0, end)[None], [0])
+    want = orc.attend_chunk(qh, oc, np.array([start]), 0, sm, tokens=toks)
+    got = out.cpu().numpy().astype(np.float64)
+    err = max(float(np.abs(got[b, t] - want[b, t]).max()) for b, t in toks)
+    keys = sum(start + t + 1 for t in range(T))
+    flops = keys * w.n_q_heads * 4 * w.head_dim
+    del cache
+    torch.cuda.empty_cache()
+    return {"tokens": T, "start": start, "context_end": end, "us": round(us, 1),
+            "tflops": round(flops / us / 1e6, 1), "bound": "mfma", "peak_tflops": 2500.0,
+            "frac": round(flops / us / 1e6 / 2500.0, 4), "algorithmic_flops": int(flops),
+            "n_splits": plan.n_splits, "chunk": plan.chunk, "max_abs_err_sampled": err,
+            "kernel": "kvq_chunk_kernel + kvq_reduce_kernel"}
 
 
 def main() -> int:

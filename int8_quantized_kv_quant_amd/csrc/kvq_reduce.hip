@@ -128,8 +128,61 @@ __global__ __launch_bounds__(256) void kvq_reduce_kernel(ReduceArgs a) {
   }
 }
 
+// Few splits (n_splits <= P, P = 1, 2 or 4): a workgroup covers whole rows,
+// lane (row, 4-dim column, split phase p) loads split p of its column, and the
+// P phases (consecutive lanes) combine by the same butterfly. With one split
+// this is the normalization out = O / l, one float4 per lane.
+template <int D, int P>
+__global__ __launch_bounds__(256) void kvq_reduce_few_kernel(ReduceArgs a, int64_t rows) {
+  constexpr int C = D / 4;            // 4-dim columns per row
+  constexpr int R = 256 / (C * P);    // rows per workgroup
+  static_assert(R >= 1 && R * C * P == 256, "reduce tiling");
+  const int tid = threadIdx.x;
+  const int p = tid % P;
+  const int c = (tid / P) % C;
+  const int64_t bh = (int64_t)blockIdx.x * R + tid / (P * C);
+  if (bh >= rows) return;  // whole P-groups leave together, so the butterfly below stays closed
+  Triple run = {-INFINITY, 0.0f, make_float4(0.f, 0.f, 0.f, 0.f)};
+  if (p < a.n_splits) {
+    const float2 v = reinterpret_cast<const float2*>(a.ws_ml)[bh * a.n_splits + p];
+    if (v.x != -INFINITY) {  // an empty split's O row was never written
+      run.m = v.x;
+      run.l = v.y;
+      run.o = *reinterpret_cast<const float4*>(a.ws_o + (bh * a.n_splits + p) * D + 4 * c);
+    }
+  }
+#pragma unroll
+  for (int off = P / 2; off; off >>= 1) {
+    Triple q;
+    q.m = __shfl_xor(run.m, off);
+    q.l = __shfl_xor(run.l, off);
+    q.o = make_float4(__shfl_xor(run.o.x, off), __shfl_xor(run.o.y, off), __shfl_xor(run.o.z, off),
+                      __shfl_xor(run.o.w, off));
+    run = (p & off) ? combine(q, run) : combine(run, q);
+  }
+  if (p == 0) {
+    // the value at max m is exp2(0) = 1: out = O / l with O, l taken at the same reference
+    const float inv = run.l > 0.0f ? 1.0f / run.l : 0.0f;
+    const f16 r0 = (f16)(run.o.x * inv), r1 = (f16)(run.o.y * inv), r2 = (f16)(run.o.z * inv),
+              r3 = (f16)(run.o.w * inv);
+    u32x2 pk = {(uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16),
+                (uint32_t)__builtin_bit_cast(uint16_t, r2) | ((uint32_t)__builtin_bit_cast(uint16_t, r3) << 16)};
+    *reinterpret_cast<u32x2*>(a.out + bh * D + 4 * c) = pk;
+  }
+}
+
 template <int D>
 static void launch_reduce_d(const ReduceArgs& a, int64_t rows, hipStream_t s) {
+  // One to four splits: whole rows per workgroup.
+  if (a.n_splits <= 4) {
+    const int P = a.n_splits == 1 ? 1 : (a.n_splits == 2 ? 2 : 4);
+    const int64_t R = 256 / ((D / 4) * P);
+    const dim3 grid((unsigned)((rows + R - 1) / R));
+    if (P == 1) hipLaunchKernelGGL((kvq_reduce_few_kernel<D, 1>), grid, dim3(256), 0, s, a, rows);
+    else if (P == 2) hipLaunchKernelGGL((kvq_reduce_few_kernel<D, 2>), grid, dim3(256), 0, s, a, rows);
+    else hipLaunchKernelGGL((kvq_reduce_few_kernel<D, 4>), grid, dim3(256), 0, s, a, rows);
+    return;
+  }
   // Narrower slices (more split phases per column) when there are few (b, hq)
   // rows and more than one split per lane at 16 phases, so that the grid still
   // spreads over the chip and each lane waits on few loads; with at most 16
