@@ -307,3 +307,67 @@ def pool_bytes(n_layers: int, ctx: int, n_kv_heads: int, head_dim: int, dtype: s
     body = 2 * n_layers * ctx * n_kv_heads * head_dim * _DTYPE_BYTES[dtype]
     scales = 2 * n_layers * ctx * n_kv_heads * scale_bytes if dtype == "int8" else 0
     return body, scales
+
+
+# --------------------------------------------------------------------------
+# Cache blob: codes with their scales and the layout facts they need
+# --------------------------------------------------------------------------
+
+BLOB_MAGIC = 0x3151564B   # "KVQ1" read as a little-endian uint32
+BLOB_VERSION = 1
+
+
+def blob_payload(cache: Cache, b: int, pos0: int, n_pos: int) -> bytes:
+    """Payload of the cache blob of positions [pos0, pos0 + n_pos) of
+    sequence b: K values, V values, then for each int8 store its fp16 scales,
+    every region positions-major ([position][kv head][...]) and padded to a
+    multiple of 16 bytes.
+
+    genie-ai-runtime release v0.1.0-alpha.11, "--int8-kv triage": a saved
+    cache must carry the scales region too; release v0.1.0-alpha.12, "Path F
+    (#45) interop guard": int8 bytes saved without their per-head scales give
+    garbage when read back. The blob therefore always holds, for an int8
+    store, the scales next to the codes."""
+    def pad(x: bytes) -> bytes:
+        return x + b"\0" * (-len(x) % 16)
+    parts = []
+    for s in ("k", "v"):
+        parts.append(pad(np.ascontiguousarray(cache.data[s][b, pos0:pos0 + n_pos]).tobytes()))
+    for s in ("k", "v"):
+        if cache.dtypes[s] == "int8":
+            parts.append(pad(np.ascontiguousarray(cache.scales[s][b, pos0:pos0 + n_pos]).tobytes()))
+    return b"".join(parts)
+
+
+def blob_header(cache: Cache, n_pos: int) -> dict:
+    """The facts a reader must match before it may place the payload: format
+    magic and version, kv heads, head_dim, both store types, scale group and
+    the number of positions, plus the payload size."""
+    dt = {"int8": 1, "fp32": 2}
+    return {"magic": BLOB_MAGIC, "version": BLOB_VERSION, "n_kv_heads": cache.n_kv_heads,
+            "head_dim": cache.head_dim, "k_dtype": dt[cache.dtypes["k"]], "v_dtype": dt[cache.dtypes["v"]],
+            "scale_group": cache.group, "n_pos": n_pos}
+
+
+def blob_restore(cache: Cache, header: dict, payload: bytes, b: int, pos0: int) -> None:
+    """Place a blob's payload at positions [pos0, pos0 + n_pos) of sequence b,
+    refusing (ValueError) a blob whose layout facts differ from the cache's."""
+    want = blob_header(cache, header["n_pos"])
+    for k, v in want.items():
+        if header.get(k) != v:
+            raise ValueError(f"blob {k} {header.get(k)} does not match the cache ({v})")
+    n = header["n_pos"]
+    off = 0
+    for s in ("k", "v"):
+        arr = cache.data[s][b, pos0:pos0 + n]
+        nb = arr.nbytes
+        cache.data[s][b, pos0:pos0 + n] = np.frombuffer(payload[off:off + nb], dtype=arr.dtype).reshape(arr.shape)
+        off += nb + (-nb % 16)
+    for s in ("k", "v"):
+        if cache.dtypes[s] == "int8":
+            arr = cache.scales[s][b, pos0:pos0 + n]
+            nb = arr.nbytes
+            cache.scales[s][b, pos0:pos0 + n] = np.frombuffer(payload[off:off + nb], dtype=np.float16).reshape(arr.shape)
+            off += nb + (-nb % 16)
+    if off != len(payload):
+        raise ValueError("blob payload size does not match its header")
