@@ -230,6 +230,38 @@ def chunk_workload(kvq, kvq_setup, wl, n_cu):
             "kernel": "kvq_chunk_kernel + kvq_reduce_kernel"}
 
 
+def blob_workload(kvq, lay, cache, L):
+    """kv_cache_pack / kv_cache_unpack of all L positions of the 128K cache
+    (codes with their scales: 138.4 MB of payload). Each direction reads and
+    writes the payload once: bound by HBM at 2 x payload bytes per call. The
+    unpacked copy is checked bit-identical to the original."""
+    import torch
+    size = kvq.kvq_blob_size(lay, L)
+    blob = torch.empty(size, dtype=torch.uint8, device="cuda:0")
+    other = {k: (None if t is None else torch.zeros_like(t)) for k, t in cache.items()}
+    hdr = kvq.kv_cache_pack(lay, cache["k"], cache["v"], cache["k_scales"], cache["v_scales"], 0, 0, L, blob, size)
+    kvq.kv_cache_unpack(lay, other["k"], other["v"], other["k_scales"], other["v_scales"], 0, 0, hdr, blob, size)
+    torch.cuda.synchronize()
+    same = all(torch.equal(cache[k], other[k]) for k in cache if cache[k] is not None)
+    res = {"payload_bytes": size, "roundtrip_bitexact": same}
+    for name, f in (("pack", lambda: kvq.kv_cache_pack(lay, cache["k"], cache["v"], cache["k_scales"],
+                                                        cache["v_scales"], 0, 0, L, blob, size)),
+                    ("unpack", lambda: kvq.kv_cache_unpack(lay, other["k"], other["v"], other["k_scales"],
+                                                            other["v_scales"], 0, 0, hdr, blob, size))):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 10
+        res[name] = {"us": round(us, 1), "GB_s": round(2 * size / us / 1e3, 1),
+                     "frac_hbm": round(2 * size / us / 1e3 / HBM_PEAK_GBS, 3)}
+    del other, blob
+    torch.cuda.empty_cache()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -404,10 +436,13 @@ def main() -> int:
 
     others = None
     if not args.no_other_workloads:
+        log("timing the cache blob (pack / unpack of the 128K cache)")
+        blob = blob_workload(kvq, lay, caches[0], L)
         log("timing the decode step on the Gemma 4K and batched-serving workloads")
         del caches, cache0
         torch.cuda.empty_cache()
         others = secondary_workloads(kvq, kvq_setup, wl, n_cu, args.steps)
+        others["cache_blob"] = blob
 
     kv_bytes = wl.kv_bytes_per_step(w, lens)
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9

@@ -13,6 +13,8 @@
  *   kv_chunk_attn          attention of a chunk of consecutive query tokens per
  *                          sequence (prompt chunk, verify window): causal
  *                          inside the chunk, partials + combine in one call
+ *   kv_cache_pack / kv_cache_unpack  a sequence's cache positions as one
+ *                          contiguous blob (codes with their scales) and back
  *   kvq_plan               host-only choice of the split count and workspace
  *   kvq_plan_chunk         the same for kv_chunk_attn
  *
@@ -65,7 +67,8 @@ typedef enum {
   KVQ_ERR_UNSUPPORTED = -3, /* a valid request this build does not implement (e.g. head_dim 96) */
   KVQ_ERR_ALIGN = -4,       /* a pointer or stride breaks the alignment the loads need */
   KVQ_ERR_WORKSPACE = -5,   /* workspace missing or smaller than kvq_plan_t.ws_bytes */
-  KVQ_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+  KVQ_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
+  KVQ_ERR_MISMATCH = -7     /* a cache blob whose layout facts differ from the target cache's */
 } kvq_status;
 
 /* Store element types ([S2698]: fp32 = the unquantized store). */
@@ -249,6 +252,52 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
                   const int32_t* d_start_pos, int32_t window, float sm_scale,
                   const kvq_plan_t* plan, void* ws, int64_t ws_bytes, uint16_t* out,
                   void* stream);
+
+/* Cache blob: positions [pos0, pos0 + n_pos) of one sequence as one
+ * contiguous payload that carries, for every int8 store, the fp16 scales next
+ * to the codes ([G11 "--int8-kv triage": a saved cache must persist the scales
+ * region too], [G12 "Path F (#45) interop guard": int8 bytes saved without
+ * their per-head scales read back as garbage]).
+ * Payload (device memory): K values, V values, then the K scales and the V
+ * scales of int8 stores; each region positions-major ([position][kv head]
+ * [head_dim values] or [head_dim / scale_group scales]) and padded to a
+ * multiple of 16 bytes. The header (host memory) holds the facts a reader must
+ * match; it is independent of the strides, so a blob can be placed into a
+ * cache with another layout order. */
+#define KVQ_BLOB_MAGIC 0x3151564Bu /* "KVQ1" */
+#define KVQ_BLOB_VERSION 1u
+typedef struct {
+  uint32_t magic;
+  uint32_t version;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t k_dtype;
+  int32_t v_dtype;
+  int32_t scale_group;
+  int32_t n_pos;
+  int64_t payload_bytes;
+} kvq_blob_header;
+
+/* kvq_blob_size -- host only: payload bytes of a blob of n_pos positions. */
+int kvq_blob_size(const kvq_layout* layout, int32_t n_pos, int64_t* payload_bytes);
+
+/* kv_cache_pack -- copy positions [pos0, pos0 + n_pos) of sequence `seq` into
+ * the payload `dst` (device, 16-byte aligned, at least the payload size) and
+ * fill *header. Requires 0 <= pos0, pos0 + n_pos <= max_ctx; `seq` must be a
+ * sequence of the stores (not checkable here). Scales must be non-NULL for
+ * int8 stores. Enqueued on `stream`; the header is valid on return. */
+int kv_cache_pack(const kvq_layout* layout, const void* k_store, const void* v_store,
+                  const uint16_t* k_scales, const uint16_t* v_scales, int32_t seq, int32_t pos0,
+                  int32_t n_pos, void* dst, int64_t dst_bytes, kvq_blob_header* header, void* stream);
+
+/* kv_cache_unpack -- place a blob at positions [pos0, pos0 + header->n_pos) of
+ * sequence `seq`. Returns KVQ_ERR_MISMATCH, with nothing enqueued, when the
+ * header's magic, version, kv heads, head_dim, store types, scale group or
+ * payload size differ from this layout's (e.g. an int8 blob for an fp32
+ * cache); KVQ_ERR_WORKSPACE when src_bytes is smaller than the payload. */
+int kv_cache_unpack(const kvq_layout* layout, void* k_store, void* v_store, uint16_t* k_scales,
+                    uint16_t* v_scales, int32_t seq, int32_t pos0, const kvq_blob_header* header,
+                    const void* src, int64_t src_bytes, void* stream);
 
 /* Text for a kvq_status value (static storage). */
 const char* kvq_status_string(int status);

@@ -19,7 +19,8 @@ __all__ = [
     "KVQ_STORE_INT8", "KVQ_STORE_FP32", "KvqError", "KvqLibraryMissing", "Layout", "Plan",
     "lib_path", "load", "kvq_version", "kvq_status_string", "kvq_plan", "kv_quant_append",
     "kv_decode_attn_splitk", "kv_append_decode_splitk", "kv_decode_reduce", "kvq_plan_chunk",
-    "kv_chunk_attn", "make_layout", "alloc_cache", "decode", "chunk_attn",
+    "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack", "kv_cache_unpack", "BlobHeader", "make_layout",
+    "alloc_cache", "decode", "chunk_attn",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -28,7 +29,8 @@ KVQ_STORE_FP32 = 2
 _DT = {"int8": KVQ_STORE_INT8, "fp32": KVQ_STORE_FP32}
 
 EXPORTED_SYMBOLS = ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
-                    "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_status_string", "kvq_version")
+                    "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack",
+                    "kv_cache_unpack", "kvq_status_string", "kvq_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -116,12 +118,17 @@ def load():
                                             i64, vp]
     lib.kv_decode_reduce.argtypes = [LP, vp, i64, vp, i32, i32, i32, PP, vp, vp]
     lib.kvq_plan_chunk.argtypes = [LP, i32, i32, i32, i32, i32, i32, PP]
+    HP = ctypes.POINTER(BlobHeader)
+    lib.kvq_blob_size.argtypes = [LP, i32, ctypes.POINTER(i64)]
+    lib.kv_cache_pack.argtypes = [LP, vp, vp, vp, vp, i32, i32, i32, vp, i64, HP, vp]
+    lib.kv_cache_unpack.argtypes = [LP, vp, vp, vp, vp, i32, i32, HP, vp, i64, vp]
     lib.kv_chunk_attn.argtypes = [LP, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, f32, PP, vp, i64, vp, vp]
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_version.argtypes = []
     for fn in ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
-               "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_version"):
+               "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack",
+               "kv_cache_unpack", "kvq_version"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -215,6 +222,35 @@ def kv_chunk_attn(layout: Layout, k_store, v_store, k_scales, v_scales, q, batch
         ctypes.byref(layout.c()), _ptr(k_store), _ptr(v_store), _ptr(k_scales), _ptr(v_scales), _ptr(q),
         batch, n_tok, n_q_heads, _ptr(start_pos), window, sm_scale, ctypes.byref(plan.c()), _ptr(ws), ws_bytes,
         _ptr(out), _stream(stream)))
+
+
+class BlobHeader(ctypes.Structure):
+    """kvq_blob_header: the layout facts a cache blob carries."""
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("k_dtype", ctypes.c_int32), ("v_dtype", ctypes.c_int32),
+                ("scale_group", ctypes.c_int32), ("n_pos", ctypes.c_int32), ("payload_bytes", ctypes.c_int64)]
+
+
+def kvq_blob_size(layout: Layout, n_pos: int) -> int:
+    out = ctypes.c_int64()
+    _check("kvq_blob_size", load().kvq_blob_size(ctypes.byref(layout.c()), n_pos, ctypes.byref(out)))
+    return out.value
+
+
+def kv_cache_pack(layout: Layout, k_store, v_store, k_scales, v_scales, seq: int, pos0: int, n_pos: int, dst,
+                  dst_bytes: int, stream=None) -> BlobHeader:
+    hdr = BlobHeader()
+    _check("kv_cache_pack", load().kv_cache_pack(
+        ctypes.byref(layout.c()), _ptr(k_store), _ptr(v_store), _ptr(k_scales), _ptr(v_scales), seq, pos0, n_pos,
+        _ptr(dst), dst_bytes, ctypes.byref(hdr), _stream(stream)))
+    return hdr
+
+
+def kv_cache_unpack(layout: Layout, k_store, v_store, k_scales, v_scales, seq: int, pos0: int,
+                    header: BlobHeader, src, src_bytes: int, stream=None) -> None:
+    _check("kv_cache_unpack", load().kv_cache_unpack(
+        ctypes.byref(layout.c()), _ptr(k_store), _ptr(v_store), _ptr(k_scales), _ptr(v_scales), seq, pos0,
+        ctypes.byref(header), _ptr(src), src_bytes, _stream(stream)))
 
 
 # --------------------------------------------------------------------------

@@ -93,6 +93,7 @@ const char* kvq_status_string(int s) {
     case KVQ_ERR_ALIGN: return "misaligned pointer or stride";
     case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
     case KVQ_ERR_HIP: return "HIP runtime error at launch";
+    case KVQ_ERR_MISMATCH: return "cache blob does not match the cache layout (store types, scale group, heads)";
     default: return "unknown status";
   }
 }
@@ -270,6 +271,63 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
   if (st) return st;
   // The partial rows are (b, t, hq): the reduce treats batch * n_tok rows of n_q_heads.
   return launch_reduce(L, ws, (int32_t)rows, n_q_heads, *plan, out, stream);
+}
+
+int kvq_blob_size(const kvq_layout* layout, int32_t n_pos, int64_t* payload_bytes) {
+  int st = check_layout(layout);
+  if (st) return st;
+  if (!payload_bytes) return KVQ_ERR_NULL;
+  if (n_pos < 0) return KVQ_ERR_SHAPE;
+  *payload_bytes = blob_payload_bytes(*layout, n_pos);
+  return KVQ_OK;
+}
+
+static int check_blob_range(const kvq_layout& L, int32_t seq, int32_t pos0, int32_t n_pos) {
+  if (seq < 0 || pos0 < 0 || n_pos < 0 || (int64_t)pos0 + n_pos > L.max_ctx) return KVQ_ERR_SHAPE;
+  if ((int64_t)n_pos * L.n_kv_heads > INT_MAX / 64) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+int kv_cache_pack(const kvq_layout* layout, const void* k_store, const void* v_store, const uint16_t* k_scales,
+                  const uint16_t* v_scales, int32_t seq, int32_t pos0, int32_t n_pos, void* dst,
+                  int64_t dst_bytes, kvq_blob_header* header, void* stream) {
+  int st = check_layout(layout);
+  if (st) return st;
+  const kvq_layout& L = *layout;
+  if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
+  if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
+  if (!dst || !header) return KVQ_ERR_NULL;
+  if (!aligned(dst, 16)) return KVQ_ERR_ALIGN;
+  if ((st = check_blob_range(L, seq, pos0, n_pos))) return st;
+  const int64_t bytes = blob_payload_bytes(L, n_pos);
+  if (dst_bytes < bytes) return KVQ_ERR_WORKSPACE;
+  *header = kvq_blob_header{KVQ_BLOB_MAGIC, KVQ_BLOB_VERSION, L.n_kv_heads, L.head_dim, L.k_dtype, L.v_dtype,
+                            L.scale_group, n_pos, bytes};
+  if (n_pos == 0) return KVQ_OK;
+  return launch_blob(L, const_cast<void*>(k_store), const_cast<void*>(v_store), const_cast<uint16_t*>(k_scales),
+                     const_cast<uint16_t*>(v_scales), seq, pos0, n_pos, dst, false, stream);
+}
+
+int kv_cache_unpack(const kvq_layout* layout, void* k_store, void* v_store, uint16_t* k_scales, uint16_t* v_scales,
+                    int32_t seq, int32_t pos0, const kvq_blob_header* header, const void* src, int64_t src_bytes,
+                    void* stream) {
+  int st = check_layout(layout);
+  if (st) return st;
+  const kvq_layout& L = *layout;
+  if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
+  if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
+  if (!src || !header) return KVQ_ERR_NULL;
+  if (!aligned(src, 16)) return KVQ_ERR_ALIGN;
+  const kvq_blob_header& h = *header;
+  if (h.magic != KVQ_BLOB_MAGIC || h.version != KVQ_BLOB_VERSION || h.n_kv_heads != L.n_kv_heads ||
+      h.head_dim != L.head_dim || h.k_dtype != L.k_dtype || h.v_dtype != L.v_dtype ||
+      h.scale_group != L.scale_group || h.n_pos < 0 || h.payload_bytes != blob_payload_bytes(L, h.n_pos))
+    return KVQ_ERR_MISMATCH;
+  if ((st = check_blob_range(L, seq, pos0, h.n_pos))) return st;
+  if (src_bytes < h.payload_bytes) return KVQ_ERR_WORKSPACE;
+  if (h.n_pos == 0) return KVQ_OK;
+  return launch_blob(L, k_store, v_store, k_scales, v_scales, seq, pos0, h.n_pos, const_cast<void*>(src), true,
+                     stream);
 }
 
 int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,

@@ -69,6 +69,20 @@ inline int resident_wgs_per_cu(const kvq_layout& L) {
   return 4;
 }
 
+// Bytes of one region of a cache blob: padded to 16.
+inline int64_t blob_region_bytes(int64_t bytes) { return (bytes + 15) / 16 * 16; }
+
+// Payload bytes of a cache blob of n_pos positions: K values, V values, then
+// the fp16 scales of each int8 store, every region padded to 16 bytes.
+inline int64_t blob_payload_bytes(const kvq_layout& L, int64_t n_pos) {
+  const int64_t rows = n_pos * L.n_kv_heads;
+  int64_t b = 0;
+  for (int dt : {L.k_dtype, L.v_dtype}) b += blob_region_bytes(rows * L.head_dim * store_elem_bytes(dt));
+  for (int dt : {L.k_dtype, L.v_dtype})
+    if (dt == KVQ_STORE_INT8) b += blob_region_bytes(rows * (L.head_dim / L.scale_group) * 2);
+  return b;
+}
+
 // Attended-range length bound used by the planner.
 inline int64_t effective_len(int64_t max_len, int32_t window) {
   return window > 0 && window < max_len ? window : max_len;
@@ -95,6 +109,9 @@ int launch_chunk(const kvq_layout& L, const void* k_store, const void* v_store, 
                  const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
                  const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
                  void* stream);
+
+int launch_blob(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k_scales, uint16_t* v_scales,
+                int32_t seq, int32_t pos0, int32_t n_pos, void* blob, bool unpack, void* stream);
 
 int launch_reduce(const kvq_layout& L, const void* ws, int32_t batch, int32_t n_q_heads,
                   const kvq_plan_t& plan, uint16_t* out, void* stream);

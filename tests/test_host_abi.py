@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_status_strings_and_version():
     assert kvq.kvq_status_string(0) == "ok"
-    for st in range(-6, 0):
+    for st in range(-7, 0):
         assert kvq.kvq_status_string(st) != "unknown status"
     assert kvq.kvq_status_string(-99) == "unknown status"
     assert kvq.kvq_version() > 0
@@ -218,6 +218,70 @@ def test_chunk_plan_covers_every_key_range(n_tok, start, window):
         assert p.n_splits == 1
     if n_tok == 4:           # a verify window over 128K keys is split
         assert p.n_splits > 16
+
+
+def _blob(lay, unpack=False, **kw):
+    hdr = kw.pop("header", None)
+    args = dict(k_store=FAKE, v_store=FAKE, k_scales=FAKE, v_scales=FAKE, seq=0, pos0=0, n_pos=8, buf=FAKE,
+                buf_bytes=1 << 30)
+    args.update(kw)
+    lib = kvq.load()
+    if not unpack:
+        h = kvq.BlobHeader()
+        return lib.kv_cache_pack(ctypes.byref(lay.c()), args["k_store"], args["v_store"], args["k_scales"],
+                                 args["v_scales"], args["seq"], args["pos0"], args["n_pos"], args["buf"],
+                                 args["buf_bytes"], ctypes.byref(h), None)
+    return lib.kv_cache_unpack(ctypes.byref(lay.c()), args["k_store"], args["v_store"], args["k_scales"],
+                               args["v_scales"], args["seq"], args["pos0"],
+                               None if hdr is None else ctypes.byref(hdr), args["buf"], args["buf_bytes"], None)
+
+
+def _header(lay, n_pos=8, **kw):
+    h = kvq.BlobHeader(0x3151564B, 1, lay.n_kv_heads, lay.head_dim, lay.k_dtype, lay.v_dtype, lay.scale_group,
+                       n_pos, kvq.kvq_blob_size(lay, n_pos))
+    for k, v in kw.items():
+        setattr(h, k, v)
+    return h
+
+
+MISMATCH = -7
+
+
+@needs_lib
+def test_blob_size_matches_the_oracle_payload():
+    from oracle import kvq_oracle as orc
+    for kdt, vdt, g, H in (("int8", "int8", 64, 2), ("int8", "fp32", 256, 2), ("fp32", "int8", 64, 8),
+                           ("fp32", "fp32", 256, 1)):
+        lay = kvq.make_layout(H, 256, 64, 1, k_dtype=kdt, v_dtype=vdt, scale_group=g)
+        c = orc.Cache(1, 64, H, 256, g, kdt, vdt)
+        for n in (0, 1, 7, 64):
+            assert kvq.kvq_blob_size(lay, n) == len(orc.blob_payload(c, 0, 0, n))
+
+
+@needs_lib
+def test_blob_refusals():
+    lay = _base()
+    assert _blob(lay, k_scales=None) == NULL_
+    assert _blob(lay, buf=None) == NULL_
+    assert _blob(lay, buf=FAKE + 8) == ALIGN
+    assert _blob(lay, pos0=1020, n_pos=8) == SHAPE          # past max_ctx
+    assert _blob(lay, seq=-1) == SHAPE
+    assert _blob(lay, buf_bytes=100) == WS
+    assert _blob(lay, n_pos=0) == 0
+    # unpack: the header must describe this layout
+    assert _blob(lay, unpack=True, header=None) == NULL_
+    assert _blob(lay, unpack=True, header=_header(lay, magic=0)) == MISMATCH
+    assert _blob(lay, unpack=True, header=_header(lay, version=2)) == MISMATCH
+    assert _blob(lay, unpack=True, header=_header(lay, k_dtype=kvq.KVQ_STORE_FP32)) == MISMATCH
+    assert _blob(lay, unpack=True, header=_header(lay, scale_group=256)) == MISMATCH
+    assert _blob(lay, unpack=True, header=_header(lay, head_dim=128)) == MISMATCH
+    assert _blob(lay, unpack=True, header=_header(lay, n_kv_heads=4)) == MISMATCH
+    assert _blob(lay, unpack=True, header=_header(lay, payload_bytes=123)) == MISMATCH
+    # an int8 blob into an fp32 cache (the kv_int8 toggle of the pages)
+    f32 = _with(lay, k_dtype=kvq.KVQ_STORE_FP32, v_dtype=kvq.KVQ_STORE_FP32)
+    assert _blob(f32, unpack=True, header=_header(lay), k_scales=None, v_scales=None) == MISMATCH
+    assert _blob(lay, unpack=True, header=_header(lay), buf_bytes=16) == WS
+    assert _blob(lay, unpack=True, header=_header(lay, n_pos=0, payload_bytes=0)) == 0
 
 
 @needs_lib
