@@ -23,6 +23,10 @@ written to be checked by eye against the pages:
 * Strata pull request 2698, "What it does": int8 codes with one FP16 scale per
   64 values, the scale being the group absmax / 127; k8v32 / k32v8 quantize
   one store only; the fp32 store is plain attention.
+* Strata pull request 2698, "Not in this PR": the 4-bit stores (q4_0 for both,
+  k8v4 for V only) use a Hadamard rotation over head_dim 256 with Q4_0
+  blocks; K is rotated together with the queries, V is rotated and the output
+  is rotated back.
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
@@ -34,7 +38,12 @@ design notes of the repository):
   * query head h uses kv head h // (n_q_heads / n_kv_heads);
   * with window W > 0 the query at position L-1 sees keys p with
     L - W <= p < L (exactly W keys once L >= W);
-  * an empty context (L = 0) yields an all-zero output row.
+  * an empty context (L = 0) yields an all-zero output row;
+  * a 4-bit store is the published Q4_0 block format (32 values, one fp16
+    scale d = the value of largest magnitude / -8, codes 0..15 with offset 8)
+    over the row after the orthonormal Walsh-Hadamard rotation H / 16, the
+    rotation evaluated in float32 butterflies so that codes are decided in
+    float32 on both sides.
 The GQA mapping, the softmax scale and the window inequality are not fixed by
 the pages (parity unpinned against the pages; pinned only against this
 module's stated definition by brute force).
@@ -99,6 +108,94 @@ def dequantize_rows(codes, scales, group: int) -> np.ndarray:
     return (cg * s).reshape(c.shape)
 
 
+# --------------------------------------------------------------------------
+# 4-bit stores (Q4_0 blocks after a 256-point Hadamard rotation)
+# --------------------------------------------------------------------------
+# Strata PR 2698, "Not in this PR": --kv q4_0 and k8v4 use a Hadamard rotation
+# over head_dim 256 (FWHT-256) with Q4_0 blocks; keys are rotated (and the
+# queries with them), values are rotated and the output is rotated back. The
+# pages name the pieces but do not spell them out; this oracle takes the
+# published definitions of the Q4_0 block and of the Walsh-Hadamard transform.
+
+Q4_BLOCK = 32
+ROT_DIM = 256
+
+
+def hadamard(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix: H[i, j] = (-1)^popcount(i & j), float64."""
+    i = np.arange(n)
+    bits = np.bitwise_and.outer(i, i)
+    par = np.zeros_like(bits)
+    while bits.any():
+        par ^= bits & 1
+        bits >>= 1
+    return np.where(par == 1, -1.0, 1.0)
+
+
+def rotate_exact(x) -> np.ndarray:
+    """Orthonormal rotation y = H x / 16 over the last axis (256), in float64.
+    H / 16 is symmetric and its own inverse."""
+    x = np.asarray(x, dtype=np.float64)
+    return x @ hadamard(ROT_DIM) / 16.0
+
+
+def rotate_f32(x) -> np.ndarray:
+    """The same rotation as the quantizer computes it: float32 butterflies
+    (a, b) -> (a + b, a - b) at strides 1, 2, 4, ..., 128, then * (1/16)
+    (exact). Both the oracle and the kernel decide Q4_0 codes from these
+    float32 values."""
+    y = np.asarray(x, dtype=np.float16).astype(np.float32)
+    shape = y.shape
+    y = y.reshape(-1, ROT_DIM)
+    h = 1
+    while h < ROT_DIM:
+        v = y.reshape(y.shape[0], ROT_DIM // (2 * h), 2, h)
+        a, b = v[:, :, 0, :], v[:, :, 1, :]
+        y = np.stack([a + b, a - b], axis=2).reshape(-1, ROT_DIM)
+        h *= 2
+    return (y * np.float32(1.0 / 16.0)).reshape(shape)
+
+
+def quantize_q4_0(y):
+    """Q4_0 blocks of 32 float32 values (the published block format): m = the
+    value of largest magnitude (the first one on ties), d = m / -8 in float32,
+    stored as fp16 (round to nearest even); codes q = min(15, trunc(x * (1/d) +
+    8.5)) with 1/d, the product and the sum in float32 (1/d = 0 when d = 0, so a
+    zero block has codes 8); value = (q - 8) * d_fp16.
+
+    y: float32 [..., n] (n % 32 == 0). Returns (codes uint8 [..., n] in 0..15,
+    scales float16 [..., n // 32])."""
+    y = np.asarray(y, dtype=np.float32)
+    n = y.shape[-1]
+    yb = y.reshape(y.shape[:-1] + (n // Q4_BLOCK, Q4_BLOCK))
+    idx = np.argmax(np.abs(yb), axis=-1)  # first index of the largest magnitude
+    m = np.take_along_axis(yb, idx[..., None], axis=-1)[..., 0]
+    d = (m / np.float32(-8.0)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(d != 0, np.float32(1.0) / d, np.float32(0.0)).astype(np.float32)
+    x0 = (yb * inv[..., None]).astype(np.float32)
+    t = (x0 + np.float32(8.5)).astype(np.float32)
+    q = np.minimum(15, np.trunc(t).astype(np.int32)).astype(np.uint8)
+    return q.reshape(y.shape), d.astype(np.float16)
+
+
+def dequantize_q4_0(codes, scales) -> np.ndarray:
+    """(q - 8) * d in float64 (exact)."""
+    c = np.asarray(codes).astype(np.float64) - 8.0
+    n = c.shape[-1]
+    cb = c.reshape(c.shape[:-1] + (n // Q4_BLOCK, Q4_BLOCK))
+    return (cb * np.asarray(scales, dtype=np.float16).astype(np.float64)[..., None]).reshape(c.shape)
+
+
+def pack_q4(codes) -> np.ndarray:
+    """Bytes of Q4_0 blocks: in each block of 32, byte j (j < 16) holds value j
+    in its low nibble and value j + 16 in its high nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    n = c.shape[-1]
+    cb = c.reshape(c.shape[:-1] + (n // Q4_BLOCK, 2, Q4_BLOCK // 2))
+    return (cb[..., 0, :] | (cb[..., 1, :] << 4)).reshape(c.shape[:-1] + (n // 2,)).astype(np.uint8)
+
+
 class Cache:
     """Logical KV cache of one layer: per store either int8 codes + fp16 scales
     or fp32 values, indexed [seq][position][kv head][element] (positions
@@ -122,6 +219,11 @@ class Cache:
             elif self.dtypes[s] == "fp32":
                 self.data[s] = np.zeros(shape, dtype=np.float32)
                 self.scales[s] = None
+            elif self.dtypes[s] == "q4":
+                if head_dim != ROT_DIM:
+                    raise ValueError("4-bit stores rotate over head_dim 256")
+                self.data[s] = np.zeros(shape, dtype=np.uint8)  # codes 0..15, unpacked
+                self.scales[s] = np.zeros(shape[:-1] + (head_dim // Q4_BLOCK,), dtype=np.float16)
             else:
                 raise ValueError(self.dtypes[s])
 
@@ -141,14 +243,26 @@ class Cache:
                     c, sc = quantize_rows(new[b], self.group)
                     self.data[s][b, p0:p0 + n_tok] = c
                     self.scales[s][b, p0:p0 + n_tok] = sc
+                elif self.dtypes[s] == "q4":
+                    c, sc = quantize_q4_0(rotate_f32(new[b]))
+                    self.data[s][b, p0:p0 + n_tok] = c
+                    self.scales[s][b, p0:p0 + n_tok] = sc
                 else:
                     self.data[s][b, p0:p0 + n_tok] = new[b].astype(np.float32)
 
     def values(self, s, b, lo, hi, h):
-        """float64 [hi-lo][d]: dequantized (or widened) rows of store s."""
+        """float64 [hi-lo][d]: dequantized (or widened) rows of store s; rows of a
+        4-bit store stay in the rotated basis (see rotated())."""
         if self.dtypes[s] == "int8":
             return dequantize_rows(self.data[s][b, lo:hi, h], self.scales[s][b, lo:hi, h], self.group)
+        if self.dtypes[s] == "q4":
+            return dequantize_q4_0(self.data[s][b, lo:hi, h], self.scales[s][b, lo:hi, h])
         return self.data[s][b, lo:hi, h].astype(np.float64)
+
+    def rotated(self, s) -> bool:
+        """A 4-bit store holds rotated rows: a rotated K store needs rotated
+        queries, a rotated V store a rotated-back output."""
+        return self.dtypes[s] == "q4"
 
 
 # --------------------------------------------------------------------------
@@ -196,7 +310,11 @@ def attend(q, cache: Cache, seq_lens, window: int, sm_scale: float, heads=None) 
                 continue
             K = cache.values("k", b, lo, hi, hk)
             V = cache.values("v", b, lo, hi, hk)
-            out[b, hq] = attend_one(q[b, hq].astype(np.float64), K, V, sm_scale)
+            qq = q[b, hq].astype(np.float64)
+            if cache.rotated("k"):
+                qq = rotate_exact(qq)
+            o = attend_one(qq, K, V, sm_scale)
+            out[b, hq] = rotate_exact(o) if cache.rotated("v") else o
     return out
 
 
@@ -233,9 +351,13 @@ def attend_chunk(q, cache: Cache, start_pos, window: int, sm_scale: float, token
             for hk in range(Hkv):
                 K = cache.values("k", b, lo, P + 1, hk)
                 V = cache.values("v", b, lo, P + 1, hk)
-                z = sm_scale * (q[b, t, hk * G:(hk + 1) * G].astype(np.float64) @ K.T)
+                qq = q[b, t, hk * G:(hk + 1) * G].astype(np.float64)
+                if cache.rotated("k"):
+                    qq = rotate_exact(qq)
+                z = sm_scale * (qq @ K.T)
                 e = np.exp(z - z.max(axis=1, keepdims=True))
-                out[b, t, hk * G:(hk + 1) * G] = (e @ V) / e.sum(axis=1, keepdims=True)
+                o = (e @ V) / e.sum(axis=1, keepdims=True)
+                out[b, t, hk * G:(hk + 1) * G] = rotate_exact(o) if cache.rotated("v") else o
     return out
 
 
@@ -293,6 +415,8 @@ def cell_bytes(n_kv_heads: int, head_dim: int, group: int, dtype: str,
     values plus, for int8, one scale per group. Strata PR 2698 "What it does"
     counts 528 B per cell for int8 + FP16 group-64 scales against 2048 B for
     FP32 at head_dim 256."""
+    if dtype == "q4":  # two codes per byte and one fp16 scale per 32 values
+        return n_kv_heads * (head_dim // 2 + (head_dim // Q4_BLOCK) * 2)
     b = n_kv_heads * head_dim * _DTYPE_BYTES[dtype]
     if dtype == "int8":
         b += n_kv_heads * (head_dim // group) * scale_bytes
@@ -344,6 +468,8 @@ def blob_header(cache: Cache, n_pos: int) -> dict:
     magic and version, kv heads, head_dim, both store types, scale group and
     the number of positions, plus the payload size."""
     dt = {"int8": 1, "fp32": 2}
+    if any(cache.dtypes[s] not in dt for s in ("k", "v")):
+        raise ValueError("the blob format holds int8 and fp32 stores")
     return {"magic": BLOB_MAGIC, "version": BLOB_VERSION, "n_kv_heads": cache.n_kv_heads,
             "head_dim": cache.head_dim, "k_dtype": dt[cache.dtypes["k"]], "v_dtype": dt[cache.dtypes["v"]],
             "scale_group": cache.group, "n_pos": n_pos}
