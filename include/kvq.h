@@ -37,6 +37,10 @@
  *          codes with one FP16 scale per 64 values equal to the group absmax /
  *          127; head_dim must be a multiple of 64 or the host refuses; k8v32 and
  *          k32v8 quantize one store only; the fp32 store is plain attention.
+ *          "Not in this PR": 4-bit stores (q4_0 for K and V, k8v4 for V only)
+ *          use a Hadamard rotation over head_dim 256 with Q4_0 blocks; K is
+ *          rotated after RoPE together with the queries, V is rotated and the
+ *          output rotated back.
  *
  * Conventions for every entry point:
  *   - All tensors are caller-owned device memory unless stated; the library
@@ -71,29 +75,43 @@ typedef enum {
   KVQ_ERR_MISMATCH = -7     /* a cache blob whose layout facts differ from the target cache's */
 } kvq_status;
 
-/* Store element types ([S2698]: fp32 = the unquantized store). */
-enum { KVQ_STORE_INT8 = 1, KVQ_STORE_FP32 = 2 };
+/* Store element types ([S2698]: fp32 = the unquantized store; q4 = the 4-bit
+ * store of [S2698 "Not in this PR"]).
+ * KVQ_STORE_Q4 holds each row rotated, y = H x / 16 with H the 256 x 256
+ * Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i & j); H / 16 is
+ * orthonormal and its own inverse), as Q4_0 blocks: per 32 values one fp16
+ * scale d and 32 4-bit codes q (value (q - 8) * d), byte j of a block's 16
+ * bytes holding value j in its low nibble and value j + 16 in its high one.
+ * Requires head_dim 256. */
+enum { KVQ_STORE_INT8 = 1, KVQ_STORE_FP32 = 2, KVQ_STORE_Q4 = 3 };
 
 /* Layout of one layer's KV cache.
  *
  * Each store (K and V) is an array of rows; the row of (sequence b, position p,
  * kv head h) starts at element  b*s_seq + p*s_pos + h*s_head  and holds
- * head_dim contiguous elements (int8 codes or fp32 values). A row may sit in a
- * wider slot (slot_dim >= head_dim, [G121]); elements [head_dim, slot_dim) are
- * never read or written. K and V use the same element strides.
+ * head_dim contiguous elements (int8 codes, fp32 values, or 4-bit codes: a q4
+ * element is half a byte, so element e sits at byte e / 2). A row may sit in
+ * a wider slot (slot_dim >= head_dim, [G121]); elements [head_dim, slot_dim)
+ * are never read or written. K and V use the same element strides.
  *
  * Each int8 store has an fp16 scale array: the scales of row (b, p, h) start at
  * element  b*ss_seq + p*ss_pos + h*ss_head  and are head_dim/scale_group
  * consecutive values, scale j covering elements [j*g, (j+1)*g) of the row.
  * scale_group == head_dim gives one scale per (position, kv head) [G12 #64];
- * scale_group == 64 gives one scale per 64 values [S2698]. Both scale arrays use
- * the same strides. An fp32 store has no scales.
+ * scale_group == 64 gives one scale per 64 values [S2698]. A q4 store has
+ * head_dim / 32 scales per row, one per Q4_0 block (scale_group applies to
+ * int8 stores only). Both scale arrays use the same strides, which must leave
+ * room for the larger of the two stores' scale rows. An fp32 store has no
+ * scales.
  *
  * Supported: head_dim in {64, 128, 256}; scale_group in {64, head_dim}; every
  * combination of k_dtype/v_dtype in {KVQ_STORE_INT8, KVQ_STORE_FP32}
- * (k8v8, k8v32, k32v8, k32v32). Row offsets in bytes must be multiples of 16;
- * scale-row offsets in bytes multiples of 2*(head_dim/scale_group); the byte
- * extent of one sequence (max_ctx positions) must stay below 2^31.
+ * (k8v8, k8v32, k32v8, k32v32); at head_dim 256 also q4 K and V (q4_0) and
+ * int8 K with q4 V (k8v4) -- the other combinations with a q4 store are
+ * refused (KVQ_ERR_UNSUPPORTED). Row offsets in bytes must be multiples of 16;
+ * scale-row offsets in bytes multiples of 2 * (scales per row) of each store
+ * that has scales; the byte extent of one sequence (max_ctx positions) must
+ * stay below 2^31.
  */
 typedef struct {
   int32_t n_kv_heads;
@@ -141,6 +159,14 @@ int kvq_plan(const kvq_layout* layout, int32_t batch, int32_t n_q_heads,
  * round-to-nearest-even fp16 value of a/127 (fp32 division, correctly rounded);
  * code = clamp(round-half-even(x / scale), -127, 127), 0 when the scale is 0.
  * An fp32 store receives the fp16 values widened exactly.
+ * A q4 store ([S2698 "Not in this PR"]) receives the rotated row as Q4_0
+ * blocks: the rotation is evaluated in fp32 as butterflies (a, b) -> (a + b,
+ * a - b) over index pairs at distance 1, 2, 4, ..., 128 in that order, then
+ * multiplied by 1/16; per block of 32 rotated values y, m is the value of
+ * largest magnitude (the first one on ties), d = m / -8 (fp32), stored as its
+ * round-to-nearest-even fp16 value, and q = min(15, trunc(y * r + 8.5)) with
+ * r = 1/d (0 when d = 0), the reciprocal, product and sum each rounded to fp32
+ * (no fused multiply-add), as the published Q4_0 quantizer does.
  * Device precondition: 0 <= d_start_pos[b] and d_start_pos[b] + n_tok <= max_ctx;
  * rows that would land outside [0, max_ctx) are not written. */
 int kv_quant_append(const kvq_layout* layout, void* k_store, void* v_store,
@@ -165,7 +191,10 @@ int kv_quant_append(const kvq_layout* layout, void* k_store, void* v_store,
  *               unwritten. No initialization of ws is needed.
  * Device precondition: 0 <= d_seq_lens[b] <= max_ctx (larger values are clamped
  * to max_ctx). Keys are dequantized as code * scale; the fp32 store is read as
- * the fp16 values kv_quant_append widened into it. */
+ * the fp16 values kv_quant_append widened into it. With a q4 K store the query
+ * is rotated the same way (H q / 16, rounded to fp16) before q.k; with a q4 V
+ * store each split's partial output is rotated back (H o / 16, fp32), so the
+ * reduced output is in the original basis ([S2698 "Not in this PR"]). */
 int kv_decode_attn_splitk(const kvq_layout* layout,
                           const void* k_store, const void* v_store,
                           const uint16_t* k_scales, const uint16_t* v_scales,
@@ -191,7 +220,9 @@ int kv_decode_attn_splitk(const kvq_layout* layout,
  *   written, so they are not const here. Combine with kv_decode_reduce.
  * Codes and scales are bit-identical to kv_quant_append's; the output of the
  * reduce differs from the unfused pair only in the order in which the new
- * position's term is summed. */
+ * position's term is summed. A layout with a q4 store is refused
+ * (KVQ_ERR_UNSUPPORTED): such a step is kv_quant_append followed by
+ * kv_decode_attn_splitk. */
 int kv_append_decode_splitk(const kvq_layout* layout, void* k_store, void* v_store,
                             uint16_t* k_scales, uint16_t* v_scales,
                             const uint16_t* k_new, const uint16_t* v_new,
@@ -278,7 +309,9 @@ typedef struct {
   int64_t payload_bytes;
 } kvq_blob_header;
 
-/* kvq_blob_size -- host only: payload bytes of a blob of n_pos positions. */
+/* kvq_blob_size -- host only: payload bytes of a blob of n_pos positions.
+ * The blob format holds int8 and fp32 stores; the pack, unpack and size calls
+ * refuse a layout with a q4 store (KVQ_ERR_UNSUPPORTED). */
 int kvq_blob_size(const kvq_layout* layout, int32_t n_pos, int64_t* payload_bytes);
 
 /* kv_cache_pack -- copy positions [pos0, pos0 + n_pos) of sequence `seq` into

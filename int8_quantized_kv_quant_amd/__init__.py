@@ -16,7 +16,7 @@ import os
 from dataclasses import dataclass
 
 __all__ = [
-    "KVQ_STORE_INT8", "KVQ_STORE_FP32", "KvqError", "KvqLibraryMissing", "Layout", "Plan",
+    "KVQ_STORE_INT8", "KVQ_STORE_FP32", "KVQ_STORE_Q4", "KvqError", "KvqLibraryMissing", "Layout", "Plan",
     "lib_path", "load", "kvq_version", "kvq_status_string", "kvq_plan", "kv_quant_append",
     "kv_decode_attn_splitk", "kv_append_decode_splitk", "kv_decode_reduce", "kvq_plan_chunk",
     "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack", "kv_cache_unpack", "BlobHeader", "make_layout",
@@ -26,7 +26,9 @@ __all__ = [
 
 KVQ_STORE_INT8 = 1
 KVQ_STORE_FP32 = 2
-_DT = {"int8": KVQ_STORE_INT8, "fp32": KVQ_STORE_FP32}
+KVQ_STORE_Q4 = 3
+_DT = {"int8": KVQ_STORE_INT8, "fp32": KVQ_STORE_FP32, "q4": KVQ_STORE_Q4}
+Q4_BLOCK = 32  # values per Q4_0 block (one fp16 scale each)
 
 EXPORTED_SYMBOLS = ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
                     "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack",
@@ -84,7 +86,14 @@ class Layout:
 
     @property
     def n_groups(self) -> int:
+        """Scales per row of an int8 store."""
         return self.head_dim // self.scale_group
+
+    def groups_of(self, dtype: int) -> int:
+        """Scales per row of a store of this type (0: none)."""
+        if dtype == KVQ_STORE_Q4:
+            return self.head_dim // Q4_BLOCK
+        return self.n_groups if dtype == KVQ_STORE_INT8 else 0
 
 
 @dataclass(frozen=True)
@@ -264,7 +273,8 @@ def make_layout(n_kv_heads: int, head_dim: int, max_ctx: int, batch: int = 1, sl
     as the genie pool indexes its scales); order="head": [seq][head][pos][slot]."""
     slot = slot_dim or head_dim
     g = scale_group or head_dim
-    ng = head_dim // g
+    # the scale arrays share their strides: room for the longer scale row
+    ng = max(head_dim // Q4_BLOCK if dt == "q4" else head_dim // g for dt in (k_dtype, v_dtype))
     if order == "pos":
         s_head, s_pos, s_seq = slot, n_kv_heads * slot, max_ctx * n_kv_heads * slot
         ss_head, ss_pos, ss_seq = ng, n_kv_heads * ng, max_ctx * n_kv_heads * ng
@@ -279,7 +289,8 @@ def make_layout(n_kv_heads: int, head_dim: int, max_ctx: int, batch: int = 1, sl
 
 def alloc_cache(layout: Layout, batch: int, device="cuda", fill=0):
     """Torch tensors for a dense cache of `batch` sequences: dict with k, v
-    (int8 or float32, flat) and k_scales, v_scales (float16 flat or None)."""
+    (int8, float32, or uint8 holding two 4-bit codes per byte; flat) and
+    k_scales, v_scales (float16 flat or None)."""
     import torch
     n = batch * layout.s_seq
     ns = batch * layout.ss_seq
@@ -287,6 +298,9 @@ def alloc_cache(layout: Layout, batch: int, device="cuda", fill=0):
     for s, dt in (("k", layout.k_dtype), ("v", layout.v_dtype)):
         if dt == KVQ_STORE_INT8:
             out[s] = torch.full((n,), fill, dtype=torch.int8, device=device)
+            out[s + "_scales"] = torch.zeros((ns,), dtype=torch.float16, device=device)
+        elif dt == KVQ_STORE_Q4:
+            out[s] = torch.full((n // 2,), fill, dtype=torch.uint8, device=device)
             out[s + "_scales"] = torch.zeros((ns,), dtype=torch.float16, device=device)
         else:
             out[s] = torch.full((n,), fill, dtype=torch.float32, device=device)

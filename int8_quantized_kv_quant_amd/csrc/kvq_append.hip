@@ -11,8 +11,14 @@
 // whole row. The group absmax is a butterfly max over those lanes.
 //
 // Arithmetic: quantize4 (kvq_device.h), bit-exact with the CPU definition.
+//
+// A q4 store (head_dim 256, Strata PR 2698 "Not in this PR"): the row's
+// wavefront rotates it (fwht256) and quantizes each 32-value block to Q4_0
+// (q4_quantize, kvq_q4.h); lanes 8k .. 8k+3 write block k's 16 bytes and lane
+// 8k its fp16 scale.
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_q4.h"
 
 namespace kvq {
 
@@ -20,7 +26,7 @@ struct AppendStore {
   void* store;
   uint16_t* scales;
   const uint16_t* src;
-  int32_t is_int8;
+  int32_t dtype;  // KVQ_STORE_*
   int32_t pad_;
 };
 
@@ -55,7 +61,20 @@ __global__ __launch_bounds__(256) void kvq_append_kernel(AppendArgs a) {
   const uint32_t hb[4] = {raw.x & 0xffffu, raw.x >> 16, raw.y & 0xffffu, raw.y >> 16};
   const int64_t row_off = b * a.s_seq + pos * a.s_pos + h * a.s_head;
 
-  if (!S.is_int8) {
+  if (S.dtype == KVQ_STORE_Q4) {
+    if constexpr (D == 256) {  // one row per wavefront (TPR == 64)
+      float y[4] = {h_bits_to_f32(hb[0]), h_bits_to_f32(hb[1]), h_bits_to_f32(hb[2]), h_bits_to_f32(hb[3])};
+      fwht256(y, lr);
+      uint16_t scale_bits;
+      const uint32_t packed = q4_quantize(y, lr, &scale_bits);
+      if ((lr & 7) < 4)
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(S.store) + row_off / 2 + 16 * (lr >> 3) + 4 * (lr & 7)) =
+            packed;
+      if ((lr & 7) == 0) S.scales[b * a.ss_seq + pos * a.ss_pos + h * a.ss_head + (lr >> 3)] = scale_bits;
+    }
+    return;
+  }
+  if (S.dtype == KVQ_STORE_FP32) {
     // fp32 store: the fp16 values widened exactly.
     float4 v = {h_bits_to_f32(hb[0]), h_bits_to_f32(hb[1]), h_bits_to_f32(hb[2]), h_bits_to_f32(hb[3])};
     *reinterpret_cast<float4*>(static_cast<float*>(S.store) + row_off + 4 * lr) = v;
@@ -75,8 +94,8 @@ int launch_append(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k
                   uint16_t* v_scales, const uint16_t* k_new, const uint16_t* v_new,
                   const int32_t* d_start_pos, int32_t batch, int32_t n_tok, void* stream) {
   AppendArgs a{};
-  a.st[0] = {k_store, k_scales, k_new, L.k_dtype == KVQ_STORE_INT8, 0};
-  a.st[1] = {v_store, v_scales, v_new, L.v_dtype == KVQ_STORE_INT8, 0};
+  a.st[0] = {k_store, k_scales, k_new, L.k_dtype, 0};
+  a.st[1] = {v_store, v_scales, v_new, L.v_dtype, 0};
   a.start_pos = d_start_pos;
   a.s_seq = L.s_seq;
   a.s_pos = L.s_pos;

@@ -20,7 +20,9 @@ int check_layout(const kvq_layout* L) {
   if (L->head_dim != 64 && L->head_dim != 128 && L->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
   if (L->slot_dim < L->head_dim) return KVQ_ERR_SHAPE;  // genie v1.2.1: slot >= head_dim
   for (int dt : {L->k_dtype, L->v_dtype})
-    if (dt != KVQ_STORE_INT8 && dt != KVQ_STORE_FP32) return KVQ_ERR_UNSUPPORTED;
+    if (dt != KVQ_STORE_INT8 && dt != KVQ_STORE_FP32 && dt != KVQ_STORE_Q4) return KVQ_ERR_UNSUPPORTED;
+  // Strata PR 2698 "Not in this PR": the 4-bit stores rotate over head_dim 256.
+  if (has_q4(*L) && L->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
   const bool any_i8 = L->k_dtype == KVQ_STORE_INT8 || L->v_dtype == KVQ_STORE_INT8;
   if (any_i8 && L->scale_group != 64 && L->scale_group != L->head_dim) return KVQ_ERR_UNSUPPORTED;
   if (L->s_seq < 0 || L->s_pos < 0 || L->s_head < 0) return KVQ_ERR_SHAPE;
@@ -29,14 +31,21 @@ int check_layout(const kvq_layout* L) {
   // rely on it to make positions past the context read as zero.
   if (L->s_pos < L->head_dim) return KVQ_ERR_SHAPE;
   for (int dt : {L->k_dtype, L->v_dtype}) {
-    const int64_t eb = store_elem_bytes(dt);
-    if ((L->s_seq * eb) % 16 || (L->s_pos * eb) % 16 || (L->s_head * eb) % 16) return KVQ_ERR_ALIGN;
+    // Row offsets in bytes are multiples of 16 (for a q4 store, whose element
+    // is half a byte: element offsets multiples of 32).
+    if (dt == KVQ_STORE_Q4) {
+      if ((L->s_seq | L->s_pos | L->s_head) & 31) return KVQ_ERR_ALIGN;
+    } else {
+      const int64_t eb = store_elem_bytes(dt);
+      if ((L->s_seq * eb) % 16 || (L->s_pos * eb) % 16 || (L->s_head * eb) % 16) return KVQ_ERR_ALIGN;
+    }
     // One (sequence, head) slice is addressed with 32-bit offsets.
-    const int64_t extent = ((L->max_ctx - 1) * L->s_pos + L->head_dim) * eb;
+    const int64_t extent = store_bytes((L->max_ctx - 1) * L->s_pos + L->head_dim, dt);
     if (extent > (int64_t)INT_MAX) return KVQ_ERR_UNSUPPORTED;
   }
-  if (any_i8) {
-    const int64_t ng = L->head_dim / L->scale_group;
+  for (int dt : {L->k_dtype, L->v_dtype}) {
+    const int64_t ng = scales_per_row(*L, dt);
+    if (!ng) continue;
     if (L->ss_pos < ng) return KVQ_ERR_SHAPE;
     const int64_t a = 2 * ng;
     if ((L->ss_seq * 2) % a || (L->ss_pos * 2) % a || (L->ss_head * 2) % a) return KVQ_ERR_ALIGN;
@@ -49,11 +58,11 @@ int check_layout(const kvq_layout* L) {
 int check_store_ptrs(const kvq_layout& L, int dtype, const void* store, const void* scales) {
   if (!store) return KVQ_ERR_NULL;
   if (!aligned(store, 16)) return KVQ_ERR_ALIGN;
-  if (dtype == KVQ_STORE_INT8) {
+  if (const int ng = scales_per_row(L, dtype)) {
     // genie v0.1.0-alpha.11 "--int8-kv triage": a missing scale pointer must be
     // refused, never read as scale 1.0.
     if (!scales) return KVQ_ERR_NULL;
-    if (!aligned(scales, 2 * (L.head_dim / L.scale_group))) return KVQ_ERR_ALIGN;
+    if (!aligned(scales, 2 * ng)) return KVQ_ERR_ALIGN;
   }
   return KVQ_OK;
 }
@@ -119,7 +128,7 @@ int kvq_plan(const kvq_layout* layout, int32_t batch, int32_t n_q_heads, int32_t
     // Bytes one position of one kv head costs to read (algorithmic).
     int64_t kv_pos = 0;
     for (int dt : {L.k_dtype, L.v_dtype})
-      kv_pos += dt == KVQ_STORE_INT8 ? L.head_dim + 2 * (L.head_dim / L.scale_group) : 4 * L.head_dim;
+      kv_pos += store_bytes(L.head_dim, dt) + 2 * scales_per_row(L, dt);
     // Partial (m, l, O) bytes one split writes for its query heads.
     const int64_t part = (G < kHeadsPerBlock ? G : kHeadsPerBlock) * (L.head_dim + 2) * 4;
     // Long splits keep the partial traffic near 1 % of the KV bytes ...
@@ -181,7 +190,11 @@ int kv_decode_attn_splitk(const kvq_layout* layout, const void* k_store, const v
   if (!ws) return KVQ_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
   if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
+  if (has_q4(L) && !q4_decode_supported(L)) return KVQ_ERR_UNSUPPORTED;
   if (batch == 0) return KVQ_OK;
+  if (has_q4(L))
+    return launch_partial_q4(L, k_store, v_store, k_scales, v_scales, q, batch, n_q_heads, d_seq_lens, window,
+                             sm_scale, *plan, ws, stream);
   return launch_partial(L, k_store, v_store, k_scales, v_scales, nullptr, nullptr, q, batch, n_q_heads,
                         d_seq_lens, window, sm_scale, *plan, ws, stream);
 }
@@ -194,6 +207,7 @@ int kv_append_decode_splitk(const kvq_layout* layout, void* k_store, void* v_sto
   int st = check_layout(layout);
   if (st) return st;
   const kvq_layout& L = *layout;
+  if (has_q4(L)) return KVQ_ERR_UNSUPPORTED;  // kv_quant_append + kv_decode_attn_splitk
   if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
   if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
   if ((st = check_heads(L, batch, n_q_heads))) return st;
@@ -276,6 +290,7 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
 int kvq_blob_size(const kvq_layout* layout, int32_t n_pos, int64_t* payload_bytes) {
   int st = check_layout(layout);
   if (st) return st;
+  if (has_q4(*layout)) return KVQ_ERR_UNSUPPORTED;  // the blob format holds int8 and fp32 stores
   if (!payload_bytes) return KVQ_ERR_NULL;
   if (n_pos < 0) return KVQ_ERR_SHAPE;
   *payload_bytes = blob_payload_bytes(*layout, n_pos);
@@ -294,6 +309,7 @@ int kv_cache_pack(const kvq_layout* layout, const void* k_store, const void* v_s
   int st = check_layout(layout);
   if (st) return st;
   const kvq_layout& L = *layout;
+  if (has_q4(L)) return KVQ_ERR_UNSUPPORTED;
   if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
   if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
   if (!dst || !header) return KVQ_ERR_NULL;
@@ -314,6 +330,7 @@ int kv_cache_unpack(const kvq_layout* layout, void* k_store, void* v_store, uint
   int st = check_layout(layout);
   if (st) return st;
   const kvq_layout& L = *layout;
+  if (has_q4(L)) return KVQ_ERR_UNSUPPORTED;
   if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
   if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
   if (!src || !header) return KVQ_ERR_NULL;

@@ -42,12 +42,29 @@ inline int resident_chunk_wgs_per_cu(const kvq_layout& L, int rows_per_wg) {
   return two ? 3 : 4;
 }
 
-// Byte sizes of one store element.
+// Byte sizes of one store element (int8 and fp32 stores).
 inline int store_elem_bytes(int dtype) { return dtype == KVQ_STORE_INT8 ? 1 : 4; }
+
+// Bytes of `elems` consecutive elements of a store (a q4 element is half a byte).
+inline int64_t store_bytes(int64_t elems, int dtype) {
+  return dtype == KVQ_STORE_Q4 ? elems / 2 : elems * store_elem_bytes(dtype);
+}
+
+// Values per Q4_0 block (one fp16 scale each).
+constexpr int kQ4Block = 32;
 
 // Number of fp16 scales per row (0 for an fp32 store).
 inline int scales_per_row(const kvq_layout& L, int dtype) {
+  if (dtype == KVQ_STORE_Q4) return L.head_dim / kQ4Block;
   return dtype == KVQ_STORE_INT8 ? L.head_dim / L.scale_group : 0;
+}
+
+inline bool has_q4(const kvq_layout& L) { return L.k_dtype == KVQ_STORE_Q4 || L.v_dtype == KVQ_STORE_Q4; }
+
+// Store combinations with a q4 store that the decode kernels implement: q4 K
+// and V (q4_0), int8 K with q4 V (k8v4).
+inline bool q4_decode_supported(const kvq_layout& L) {
+  return L.v_dtype == KVQ_STORE_Q4 && (L.k_dtype == KVQ_STORE_Q4 || L.k_dtype == KVQ_STORE_INT8);
 }
 
 // Checks a layout on its own (no pointers). Returns KVQ_OK or an error code.
@@ -63,6 +80,7 @@ int check_store_ptrs(const kvq_layout& L, int dtype, const void* store, const vo
 // (four). Stores with fp32 rows keep their operands in registers: 256 VGPRs at
 // D = 256 (one), ~200 at D = 128 (two), ~125 at D = 64 (four).
 inline int resident_wgs_per_cu(const kvq_layout& L) {
+  if (has_q4(L)) return 2;  // the 4-bit kernel: ~72 KB of LDS per workgroup
   const bool staged = L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8;
   if (L.head_dim == 256) return staged ? 2 : 1;
   if (L.head_dim == 128) return staged ? 3 : 2;
@@ -112,6 +130,12 @@ int launch_chunk(const kvq_layout& L, const void* k_store, const void* v_store, 
 
 int launch_blob(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k_scales, uint16_t* v_scales,
                 int32_t seq, int32_t pos0, int32_t n_pos, void* blob, bool unpack, void* stream);
+
+// Partials of a layout with a q4 store (q4_decode_supported).
+int launch_partial_q4(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
+                      const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                      const int32_t* d_seq_lens, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
+                      void* stream);
 
 int launch_reduce(const kvq_layout& L, const void* ws, int32_t batch, int32_t n_q_heads,
                   const kvq_plan_t& plan, uint16_t* out, void* stream);

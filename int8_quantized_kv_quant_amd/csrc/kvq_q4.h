@@ -1,0 +1,84 @@
+// Device helpers of the 4-bit stores: the 256-point Walsh-Hadamard rotation of
+// one row held by a whole wavefront (4 values per lane) and the Q4_0 block
+// quantizer of the rotated row.
+//
+// Strata PR 2698, "Not in this PR": q4_0 and k8v4 use a Hadamard rotation over
+// head_dim 256 with Q4_0 blocks; K is rotated together with the queries, V is
+// rotated and the output rotated back. Q4_0 is the published 4-bit block
+// format: 32 values share one fp16 scale d = (value of largest magnitude) / -8,
+// codes q = min(15, trunc(x / d + 8.5)) stand for (q - 8) * d.
+#pragma once
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+// y = H x / 16 for the 256 values of one row, lane l holding elements
+// 4l .. 4l+3 in v[0..3] (all 64 lanes of the wavefront take part). fp32
+// butterflies (a, b) -> (a + b, a - b) over index pairs at distance 1, 2, 4,
+// ..., 128, in that order, then * 1/16 (exact): every step is one correctly
+// rounded fp32 addition or subtraction, so the result does not depend on how
+// the pairs are assigned to lanes.
+__device__ __forceinline__ void fwht256(float (&v)[4], int lane) {
+#pragma clang fp contract(off)
+  float a = v[0] + v[1], b = v[0] - v[1], c = v[2] + v[3], d = v[2] - v[3];
+  v[0] = a + c;
+  v[2] = a - c;
+  v[1] = b + d;
+  v[3] = b - d;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {  // distance 4m between the paired elements
+    const bool lower = (lane & m) == 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float p = __shfl_xor(v[k], m);
+      v[k] = lower ? v[k] + p : p - v[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] *= 0.0625f;
+}
+
+// Q4_0 quantization of a rotated row held as by fwht256: lanes 8k .. 8k+7 hold
+// block k (32 values). Returns, for lanes with (lane & 7) < 4, the dword of
+// the block's bytes 4 * (lane & 7) .. +3 (byte j = code j | code (j+16) << 4);
+// *scale_bits gets the block's fp16 scale (every lane of the block).
+//   m: the value of largest magnitude, the first one on ties;
+//   d = m * -0.125 (= m / -8, exact), r = 1/d correctly rounded (0 if d = 0);
+//   q = min(15, trunc(fp32(fp32(y * r) + 8.5))), no fused multiply-add.
+__device__ __forceinline__ uint32_t q4_quantize(const float (&y)[4], int lane, uint16_t* scale_bits) {
+#pragma clang fp contract(off)  // y * r and + 8.5 are two roundings, as in the published quantizer
+  const int lb = lane & 7;
+  float am = fabsf(y[0]), m = y[0];
+  int idx = 4 * lb;
+#pragma unroll
+  for (int k = 1; k < 4; ++k)
+    if (fabsf(y[k]) > am) {
+      am = fabsf(y[k]);
+      m = y[k];
+      idx = 4 * lb + k;
+    }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    const float pam = __shfl_xor(am, o), pm = __shfl_xor(m, o);
+    const int pidx = __shfl_xor(idx, o);
+    if (pam > am || (pam == am && pidx < idx)) {
+      am = pam;
+      m = pm;
+      idx = pidx;
+    }
+  }
+  const float d = m * -0.125f;
+  const float r = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
+  uint32_t codes = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float t = y[k] * r + 8.5f;  // not contracted (pragma above)
+    codes |= (uint32_t)min(15, (int)t) << (8 * k);
+  }
+  *scale_bits = __builtin_bit_cast(uint16_t, (f16)d);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)codes, 4);  // codes of values 16 + 4 * (lane & 3) + k
+  return codes | (hi << 4);
+}
+
+}  // namespace kvq

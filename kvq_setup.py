@@ -79,10 +79,21 @@ def rows_of(lay: kvq.Layout, store: torch.Tensor, b: int, positions, h: int, wid
     return store[idx].cpu().numpy()
 
 
-def scales_of(lay: kvq.Layout, scales: torch.Tensor, b: int, positions, h: int):
+def q4_rows_of(lay: kvq.Layout, store: torch.Tensor, b: int, positions, h: int):
+    """Host copy of the packed bytes of rows (b, positions, h) of a q4 store
+    (a uint8 tensor, two codes per byte): [n][head_dim / 2]."""
+    pos = torch.as_tensor(np.asarray(positions, dtype=np.int64), device=store.device)
+    base = (b * lay.s_seq + h * lay.s_head + pos * lay.s_pos) // 2
+    idx = base[:, None] + torch.arange(lay.head_dim // 2, device=store.device)[None, :]
+    return store[idx].cpu().numpy()
+
+
+def scales_of(lay: kvq.Layout, scales: torch.Tensor, b: int, positions, h: int, n: int | None = None):
+    """Host copy of the n (default: an int8 store's count) fp16 scales of rows
+    (b, positions, h): [len(positions)][n]."""
     pos = torch.as_tensor(np.asarray(positions, dtype=np.int64), device=scales.device)
     base = b * lay.ss_seq + h * lay.ss_head + pos * lay.ss_pos
-    idx = base[:, None] + torch.arange(lay.n_groups, device=scales.device)[None, :]
+    idx = base[:, None] + torch.arange(n or lay.n_groups, device=scales.device)[None, :]
     return scales[idx].cpu().numpy()
 
 

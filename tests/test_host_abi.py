@@ -305,7 +305,7 @@ def test_unsupported_requests_are_refused():
     assert _append(_with(lay, head_dim=96, slot_dim=96, s_pos=192, s_head=96, s_seq=192 * 1024)) == UNSUP
     assert _append(_with(lay, head_dim=512, slot_dim=512, s_pos=1024, s_head=512)) == UNSUP
     assert _append(_with(lay, scale_group=32)) == UNSUP
-    assert _append(_with(lay, k_dtype=3)) == UNSUP
+    assert _append(_with(lay, k_dtype=4)) == UNSUP
     big = kvq.make_layout(2, 256, 5_000_000, 1, scale_group=64)   # > 2 GiB per sequence slice
     assert _append(big) == UNSUP
 
@@ -345,3 +345,48 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kvq, "lib_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(kvq.KvqLibraryMissing):
         kvq.kvq_plan(_base(), 1, 16, 100, 0, 256)
+
+
+def _q4_layout(k="q4", v="q4", **kw):
+    return kvq.make_layout(2, 256, 1024, 1, k_dtype=k, v_dtype=v, scale_group=64, **kw)
+
+
+@needs_lib
+def test_q4_layout_rules():
+    """Strata PR 2698 'Not in this PR': the 4-bit stores rotate over head_dim
+    256. A q4 element is half a byte, so row offsets in elements are multiples
+    of 32; a q4 row has 8 fp16 scales (one per 32-value block), so the shared
+    scale strides leave room for 8."""
+    for k, v in (("q4", "q4"), ("int8", "q4"), ("q4", "int8"), ("fp32", "q4")):
+        lay = _q4_layout(k, v)
+        assert lay.ss_pos >= 8 * 2 and lay.ss_head == 8
+        assert _append(lay, batch=0) == 0                     # a valid layout (nothing launched)
+    q4 = _q4_layout()
+    assert _append(_with(q4, head_dim=128, slot_dim=128, s_head=128, s_pos=256)) == UNSUP
+    assert _append(_with(q4, slot_dim=272, s_head=272, s_pos=544, s_seq=544 * 1024), batch=0) == ALIGN
+    assert _append(_with(q4, ss_pos=4, ss_head=2, ss_seq=4096), batch=0) == SHAPE   # no room for 8 scales
+    assert _append(_with(q4, ss_head=4), batch=0) == ALIGN    # 8-scale rows are 16-byte aligned
+    assert _append(q4, v_scales=None) == NULL_                 # a q4 store has scales too
+    assert _append(q4, k_scales=FAKE + 8) == ALIGN
+    k8v4 = _q4_layout("int8", "q4")
+    assert _append(_with(k8v4, ss_pos=8, ss_head=4, ss_seq=8192), batch=0) == ALIGN
+
+
+@needs_lib
+def test_q4_entry_point_refusals():
+    """Decode takes q4_0 and k8v4; every other combination with a q4 store is
+    refused before any device call, as are the fused step, chunk attention and
+    the blob calls."""
+    assert _partial(_q4_layout("q4", "int8")) == UNSUP
+    assert _partial(_q4_layout("q4", "fp32")) == UNSUP
+    assert _partial(_q4_layout("fp32", "q4")) == UNSUP
+    assert _partial(_q4_layout(), batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
+    assert _partial(_q4_layout("int8", "q4"), batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
+    assert _partial(_q4_layout(), k_scales=None) == NULL_
+    assert _fused(_q4_layout()) == UNSUP
+    assert _fused(_q4_layout("int8", "q4")) == UNSUP
+    assert _chunk(_q4_layout()) == UNSUP
+    out = ctypes.c_int64(0)
+    assert kvq.load().kvq_blob_size(ctypes.byref(_q4_layout().c()), 4, ctypes.byref(out)) == UNSUP
+    assert _blob(_q4_layout()) == UNSUP
+    assert _blob(_q4_layout("int8", "q4"), unpack=True) == UNSUP

@@ -50,7 +50,7 @@ class Workload:
     max_ctx: int              # positions allocated per sequence
     window: int               # 0 = no sliding window
     seed: int
-    k_dtype: str = "int8"     # "int8" or "fp32"
+    k_dtype: str = "int8"     # "int8", "fp32" or "q4" (rotated Q4_0 blocks, head_dim 256)
     v_dtype: str = "int8"
     contexts: Sequence[int] = field(default_factory=tuple)  # decode contexts (batch 1)
     outlier_frac: float = 0.0  # fraction of K channels scaled by outlier_gain
@@ -91,6 +91,12 @@ WORKLOADS = {
     "mixed_k32v8": Workload("mixed_k32v8", 1, 16, 2, 256, 256, 64, 32768, 0, 4,
                             k_dtype="fp32", v_dtype="int8", contexts=(32048,),
                             prefill=30000, append=2048),
+    # the long-context shape with the 4-bit stores (Strata PR 2698, "Not in
+    # this PR": q4_0 for K and V, k8v4 for V only, head_dim 256)
+    "long_q4": Workload("long_q4", 1, 16, 2, 256, 256, 64, 131072, 0, 2, k_dtype="q4", v_dtype="q4",
+                        contexts=(131072,), outlier_frac=0.01, outlier_gain=20.0),
+    "long_k8v4": Workload("long_k8v4", 1, 16, 2, 256, 256, 64, 131072, 0, 2, k_dtype="int8", v_dtype="q4",
+                          contexts=(131072,), outlier_frac=0.01, outlier_gain=20.0),
 }
 
 
@@ -166,13 +172,16 @@ def uniform_rows(seed: int, shape, scale: float = 1.0) -> np.ndarray:
 
 
 def kv_bytes_per_step(w: Workload, lens: np.ndarray) -> int:
-    """Algorithmic bytes the decode step must read: codes (1 B) or fp32 values
-    (4 B) for every attended position, plus the fp16 scales of int8 stores.
+    """Algorithmic bytes the decode step must read: codes (1 B, or 1/2 B for a
+    q4 store) or fp32 values (4 B) for every attended position, plus the fp16
+    scales of int8 and q4 stores.
     The slot tail beyond head_dim is not read and not counted."""
     per_pos = 0
     for dt in (w.k_dtype, w.v_dtype):
         if dt == "int8":
             per_pos += w.head_dim + 2 * w.n_groups
+        elif dt == "q4":  # two codes per byte, one fp16 scale per 32 values
+            per_pos += w.head_dim // 2 + 2 * (w.head_dim // 32)
         else:
             per_pos += 4 * w.head_dim
     total = 0
