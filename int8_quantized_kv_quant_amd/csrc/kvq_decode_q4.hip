@@ -1,12 +1,607 @@
-// kv_decode_attn_splitk for layouts with a 4-bit store (q4_0, k8v4).
+// kv_decode_attn_splitk for the 4-bit layouts: q4 K and V (q4_0) and int8 K with
+// q4 V (k8v4), head_dim 256, on the gfx950 matrix cores.
+//
+// Strata PR 2698, "Not in this PR": the 4-bit stores hold Q4_0 blocks of rows
+// rotated by the 256-point Hadamard transform; K is rotated together with the
+// queries and V's output is rotated back. genie-ai-runtime v1.3.0 "split-K
+// decode attention": per-split online-softmax partials, combined by the reduce.
+//
+// Mapping as in the int8 kernel (kvq_decode.hip): a workgroup of four
+// wavefronts = (sequence, kv head, up to 16 query heads, split); wavefronts take
+// 32-position tiles round-robin, each staging its tiles' K and V halves in LDS
+// with direct-to-LDS loads, one half refilling while the other is computed.
+//
+// Query. A q4 K store holds rotated keys, so the query rows are rotated the
+// same way in LDS (fwht256 in fp32, rounded to fp16) before any score; with
+// H / 16 orthonormal, q_rot . k_rot = q . k.
+// Keys (q4). One MFMA v_mfma_f32_16x16x32_f16 contracts one Q4_0 block (32
+// dims) of 16 positions. The A operand is the dequantized key K_hat =
+// fp16((code - 8) * d) of the lane's own position (its row of S^T), built from
+// the exact fp16 value 1024 + code (0x64 above the nibble, by byte permutes)
+// minus 1032 (exact) times the block scale (one rounding, as the values are),
+// so the eight blocks of a row accumulate in one MFMA chain.
+// Keys (int8, k8v4): the int8 kernel's operands and scores, unrotated.
+// Values (q4). Lane (column c16) holds dims 16 c16 .. +15, i.e. the low
+// (c16 even) or high (c16 odd) nibbles of 16 bytes of block c16 / 2; after a
+// shift and mask they are bytes holding the codes, transposed per position
+// pair by byte permutes into the fp16 operand (code - 8) * d_b, one rounding,
+// exactly as the int8 kernel builds code * scale.
+// Output. O of each split stays in the rotated basis through the softmax; the
+// merged partial rows are rotated back (fwht256, fp32) before they are
+// written, so the reduce (linear in O) combines unrotated rows.
+#include <math.h>
+
+#include <type_traits>
+
+#include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_q4.h"
+#include "kvq_tile.h"
 
 namespace kvq {
 
-int launch_partial_q4(const kvq_layout&, const void*, const void*, const uint16_t*, const uint16_t*,
-                      const uint16_t*, int32_t, int32_t, const int32_t*, int32_t, float, const kvq_plan_t&, void*,
-                      void*) {
-  return KVQ_ERR_UNSUPPORTED;
+struct Q4Args {
+  const void* k_store;
+  const void* v_store;
+  const uint16_t* k_scales;
+  const uint16_t* v_scales;
+  const uint16_t* q;
+  const int32_t* seq_lens;
+  float* ws_o;   // [B][Hq][n_splits][D]
+  float* ws_ml;  // [B][Hq][n_splits][2]
+  int64_t s_seq, s_pos, s_head;     // element strides (a q4 element is half a byte)
+  int64_t ss_seq, ss_pos, ss_head;  // fp16 scale strides
+  int32_t max_ctx;
+  int32_t n_kv, G, n_q, head_blocks;
+  int32_t n_splits, chunk, window;
+  float c2;  // sm_scale * log2(e)
+};
+
+// Stage of one wavefront (bytes): K codes, V codes (128 bytes per q4 row),
+// K scale rows, V scale rows. Code rows hold their 16-byte chunk c at slot
+// c ^ swz(r); a scale region is 1 KiB for 16-byte rows (a 64-lane
+// direct-to-LDS load writes 16 bytes per lane, lanes past row 31 zeros).
+template <bool KQ4, bool KG64>
+struct Q4Stage {
+  static constexpr int D = 256;
+  static constexpr int KRB = KQ4 ? D / 2 : D;  // bytes per K row
+  static constexpr int VRB = D / 2;
+  static constexpr int KNG = KQ4 ? D / kQ4Block : (KG64 ? D / 64 : 1);  // K scales per row
+  static constexpr int KSB = 2 * KNG;
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 32 * KRB;
+  static constexpr int KS_OFF = V_OFF + 32 * VRB;
+  static constexpr int KS_SPITCH = KSB >= 4 ? KSB : 4;
+  static constexpr int KS_BYTES = KQ4 ? 1024 : 256;
+  static constexpr int VS_OFF = KS_OFF + KS_BYTES;
+  static constexpr int BYTES = VS_OFF + 1024;
+  static constexpr int NK = 32 * KRB / 1024 + 1;  // direct-to-LDS loads of a K half
+  static constexpr int NV = 32 * VRB / 1024 + 1;  // of a V half
+};
+
+// Rows per 256-byte LDS line = 16 / CH; consecutive such row groups get
+// distinct chunk slots, so 16 rows read at one chunk hit 16 distinct banks.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  constexpr int SH = CH == 16 ? 0 : (CH == 8 ? 1 : 2);
+  return (r >> SH) & (CH - 1);
+}
+
+// Direct-to-LDS loads of a 32-row code tile with ROWB bytes per row at byte
+// `lds` (rows >= nvalid read as zeros: out-of-range lane offset).
+template <int ROWB>
+__device__ __forceinline__ void issue_codes(uint32_t lds, const u32x4& rs, uint32_t soff, int nvalid, uint32_t row,
+                                            int lane) {
+  constexpr int CH = ROWB / 16;
+  constexpr int NI = 32 * ROWB / 1024;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int slot = 64 * i + lane;
+    const int r = slot / CH;
+    const int c = (slot % CH) ^ swz<CH>(r);
+    dma<16>(rs, lds + 1024 * i, (nvalid >= kTile || r < nvalid) ? (uint32_t)r * row + 16 * c : kOOB, soff);
+  }
+}
+
+// Direct-to-LDS load of the scale rows (SB bytes each) of a 32-row tile.
+template <int SB>
+__device__ __forceinline__ void issue_scales(uint32_t lds, const u32x4& rs, uint32_t soff, int nvalid, uint32_t srow,
+                                             int lane) {
+  const int nv = nvalid < kTile ? nvalid : kTile;
+  if constexpr (SB == 16) {  // lane l = row l, 16 bytes at 16 l
+    dma<16>(rs, lds, lane < nv ? (uint32_t)lane * srow : kOOB, soff);
+  } else if constexpr (SB == 8) {  // two lanes per row, 8 bytes at 8 r
+    const int r = lane >> 1;
+    dma<4>(rs, lds, r < nv ? (uint32_t)r * srow + 4 * (lane & 1) : kOOB, soff);
+  } else {  // one 2-byte scale per row, at 4 r
+    static_assert(SB == 2, "scale row size");
+    dma<2>(rs, lds, lane < nv ? (uint32_t)lane * srow : kOOB, soff);
+  }
+}
+
+// Fill the K half (HALF = 0) or the V half (HALF = 1) of a stage with the tile
+// at position p0. The half's previous contents were read by this wavefront:
+// those LDS reads complete before new data can land.
+template <bool KQ4, bool KG64, int HALF>
+__device__ __forceinline__ void issue_half(uint8_t* st, const u32x4& rs, const u32x4& srs, int p0, int nvalid,
+                                           uint32_t row, uint32_t srow, int lane) {
+  using T = Q4Stage<KQ4, KG64>;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const uint32_t base = lds_addr_of(st);
+  const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * row);
+  const uint32_t ssoff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * srow);
+  if constexpr (HALF == 0) {
+    issue_codes<T::KRB>(base + T::K_OFF, rs, soff, nvalid, row, lane);
+    issue_scales<T::KSB>(base + T::KS_OFF, srs, ssoff, nvalid, srow, lane);
+  } else {
+    issue_codes<T::VRB>(base + T::V_OFF, rs, soff, nvalid, row, lane);
+    issue_scales<16>(base + T::VS_OFF, srs, ssoff, nvalid, srow, lane);
+  }
+}
+
+// ---- keys ---------------------------------------------------------------------------
+// q4 K operands of one tile for lane (c16, q4): k[ct][j] = bytes 8 (q4 & 1) .. +7
+// of block j of row 16 ct + c16 (dims 32 j + 8 q4 .. +7 after the nibble
+// select); ks[ct] = the 8 block scales of that row's position.
+struct KQ4Regs {
+  u32x2 k[2][8];
+  u32x4 ks[2];
+};
+
+template <bool KG64>
+__device__ __forceinline__ void read_k_q4(KQ4Regs& t, const uint8_t* __restrict__ st, int c16, int q4) {
+  using T = Q4Stage<true, KG64>;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int r = 16 * ct + c16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      t.k[ct][j] = *reinterpret_cast<const u32x2*>(st + T::K_OFF + r * T::KRB + 16 * (j ^ swz<8>(r)) + 8 * (q4 & 1));
+    t.ks[ct] = *reinterpret_cast<const u32x4*>(st + T::KS_OFF + r * 16);
+  }
+}
+
+constexpr uint32_t kQ4NegBias = 0xE408E408u;  // fp16 pair (-1032, -1032)
+
+// Scores of a q4 K tile: z[ct][i] for positions 16 ct + 4 q4 + i of query row
+// c16 (log2 domain), positions >= nvalid masked. qv[j] = the rotated query's
+// dims 32 j + 8 q4 .. +7 (fp16).
+__device__ __forceinline__ void scores_q4(const KQ4Regs& t, int nvalid, float (&z)[2][4], const f16x8 (&qv)[8],
+                                          float c2, int q4) {
+  const uint32_t sh = 4u * (uint32_t)(q4 >> 1);  // q4 = 2, 3: the high nibbles (dims 16..31 of the block)
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    f32x4 zz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w0 = (t.k[ct][j].x >> sh) & 0x0F0F0F0Fu;
+      const uint32_t w1 = (t.k[ct][j].y >> sh) & 0x0F0F0F0Fu;
+      const uint32_t sw = t.ks[ct][j >> 1];
+      const f16x2 d2 = as_h2(__builtin_amdgcn_perm(sw, sw, (j & 1) ? 0x07060706u : 0x05040504u));  // (d_j, d_j)
+      u32x4 a4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = e < 2 ? w0 : w1;
+        const uint32_t biased = (e & 1) ? biased_h2_hi(w) : biased_h2_lo(w);  // 1024 + code
+        a4[e] = as_u32((as_h2(biased) + as_h2(kQ4NegBias)) * d2);           // fp16((code - 8) * d)
+      }
+      zz = mfma16(__builtin_bit_cast(f16x8, a4), qv[j], zz);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[ct][i] = (16 * ct + 4 * q4 + i < nvalid) ? zz[i] * c2 : -INFINITY;
+  }
+}
+
+// int8 K operands (k8v4) from this stage layout, as stage_read_k reads them.
+template <bool KG64>
+__device__ __forceinline__ void read_k_i8(KRegs<Shape<256, true, true, KG64>>& t, const uint8_t* __restrict__ st,
+                                          int c16, int q4) {
+  using S = Shape<256, true, true, KG64>;
+  using T = Q4Stage<false, KG64>;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int r = 16 * ct + c16;
+#pragma unroll
+    for (int j = 0; j < S::NJ; ++j)
+      t.k[ct][j][0] = *reinterpret_cast<const u32x4*>(st + T::K_OFF + r * 256 + 16 * ((4 * j + q4) ^ swz<16>(r)));
+    const uint8_t* ksp = st + T::KS_OFF + (16 * ct + 4 * q4) * T::KS_SPITCH;
+    if constexpr (KG64) {  // 8-byte rows
+      const u32x4 a = *reinterpret_cast<const u32x4*>(ksp);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(ksp + 16);
+      t.ks[ct][0][0] = a.x; t.ks[ct][0][1] = a.y;
+      t.ks[ct][1][0] = a.z; t.ks[ct][1][1] = a.w;
+      t.ks[ct][2][0] = b.x; t.ks[ct][2][1] = b.y;
+      t.ks[ct][3][0] = b.z; t.ks[ct][3][1] = b.w;
+    } else {  // one 2-byte scale per row, rows 4 bytes apart
+      const u32x4 a = *reinterpret_cast<const u32x4*>(ksp);
+      t.ks[ct][0][0] = a.x & 0xffffu;
+      t.ks[ct][1][0] = a.y & 0xffffu;
+      t.ks[ct][2][0] = a.z & 0xffffu;
+      t.ks[ct][3][0] = a.w & 0xffffu;
+    }
+  }
+}
+
+// Scores of an int8 K tile (k8v4): as the int8 kernel's, with the bias
+// correction added after each MFMA instead of preloaded into its accumulator
+// (one register per group instead of four).
+template <bool KG64>
+__device__ __forceinline__ void scores_i8(const KRegs<Shape<256, true, true, KG64>>& t, int nvalid, float (&z)[2][4],
+                                          const uint8_t* __restrict__ qb, const float (&corr)[KG64 ? 4 : 1], float c2,
+                                          int q4) {
+  f16x8 qv[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    qv[j][0] = q_get(qb, j, 0);
+    qv[j][1] = q_get(qb, j, 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    f32x4 zz = zero;
+    if constexpr (KG64) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 c = t.k[ct][j][0];
+        f32x4 a = mfma16(codes8_biased(c.x, c.y), qv[j][0], zero);
+        a = mfma16(codes8_biased(c.z, c.w), qv[j][1], a);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zz[i] = fmaf(a[i] + corr[j], scale_of(t.ks[ct][i], j), zz[i]);
+      }
+    } else {
+      f32x4 a = zero;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 c = t.k[ct][j][0];
+        a = mfma16(codes8_biased(c.x, c.y), qv[j][0], a);
+        a = mfma16(codes8_biased(c.z, c.w), qv[j][1], a);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zz[i] = (a[i] + corr[0]) * scale_of(t.ks[ct][i], 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[ct][i] = (16 * ct + 4 * q4 + i < nvalid) ? zz[i] * c2 : -INFINITY;
+  }
+}
+
+// ---- values ---------------------------------------------------------------------------
+// v[e][w]: bytes holding the codes of dims 16 c16 + 4 w .. +3 at position
+// kpos(e, q4); vs[e]: that position's scale of block c16 / 2.
+struct VQ4Regs {
+  uint32_t v[8][4];
+  uint32_t vs[8];
+};
+
+template <bool KQ4, bool KG64>
+__device__ __forceinline__ void read_v_q4(VQ4Regs& t, const uint8_t* __restrict__ st, int c16, int q4) {
+  using T = Q4Stage<KQ4, KG64>;
+  const uint32_t sh = 4u * (uint32_t)(c16 & 1);
+  const int blk = c16 >> 1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = kpos(e, q4);
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(st + T::V_OFF + r * T::VRB + 16 * (blk ^ swz<8>(r)));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) t.v[e][w] = (raw[w] >> sh) & 0x0F0F0F0Fu;
+    t.vs[e] = *reinterpret_cast<const uint16_t*>(st + T::VS_OFF + r * 16 + 2 * blk);
+  }
+}
+
+// O += P . V_hat with V_hat = fp16((code - 8) * d) and l += P . 1; PART 1 and 2
+// split the output columns in halves (l with PART 2) so that a wait can sit
+// between them.
+template <int PART>
+__device__ __forceinline__ void pv_q4(const VQ4Regs& t, f16x8 pa, WaveAcc<Shape<256, true, true, true>>& acc) {
+  constexpr int W0 = PART == 2 ? 2 : 0, W1 = PART == 1 ? 2 : 4;
+  f16x2 sv[4];
+#pragma unroll
+  for (int pi = 0; pi < 4; ++pi) sv[pi] = as_h2(__builtin_amdgcn_perm(t.vs[2 * pi + 1], t.vs[2 * pi], 0x05040100u));
+#pragma unroll
+  for (int w = W0; w < W1; ++w) {
+    uint32_t z01[4], z23[4];
+#pragma unroll
+    for (int pi = 0; pi < 4; ++pi) {
+      z01[pi] = zip_lo(t.v[2 * pi + 1][w], t.v[2 * pi][w]);
+      z23[pi] = zip_hi(t.v[2 * pi + 1][w], t.v[2 * pi][w]);
+    }
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      u32x4 r;
+#pragma unroll
+      for (int pi = 0; pi < 4; ++pi) {
+        const uint32_t src = bb < 2 ? z01[pi] : z23[pi];
+        const uint32_t biased = (bb & 1) ? biased_h2_hi(src) : biased_h2_lo(src);  // 1024 + code
+        const f16x2 c = as_h2(biased) + as_h2(kQ4NegBias);                         // code - 8, exact
+        r[pi] = as_u32(c * sv[pi]);                                                 // fp16((code - 8) * d)
+      }
+      acc.o[4 * w + bb] = mfma16(pa, __builtin_bit_cast(f16x8, r), acc.o[4 * w + bb]);
+    }
+  }
+  if constexpr (PART != 1) {
+    const f16x8 ones = {(f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1};
+    acc.l = mfma16(pa, ones, acc.l);
+  }
+}
+
+// Float4 position of float4 f of a merge-slot row: the 16 lanes that write one
+// row at a time hold f = 4c + n for c = 0..15; XOR-ing bits 0-1 with bits 4-5
+// spreads them over the 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int slot_swz(int f) { return f ^ ((f >> 4) & 3); }
+
+// ---- kernel ------------------------------------------------------------------------
+template <bool KQ4, bool KG64>
+__global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
+  constexpr int D = 256, NW = 4;
+  using T = Q4Stage<KQ4, KG64>;
+  using SA = Shape<256, true, true, true>;  // accumulators (16 heads x 256 dims per wavefront)
+  using SK = Shape<256, true, true, KG64>;  // int8 keys (k8v4)
+  constexpr int SLOT_BYTES = 16 * D * 4;    // merge slot: 16 head rows of D floats
+  constexpr int PITCH = T::BYTES > SLOT_BYTES ? T::BYTES : SLOT_BYTES;
+  constexpr int QROW = QOperand<SA>::ROW;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_st[NW * PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_q[16 * QROW];
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+
+  const int split = blockIdx.x;
+  const int hk = blockIdx.y / a.head_blocks;
+  const int hblk = blockIdx.y % a.head_blocks;
+  const int b = blockIdx.z;
+  const int nh = min(16, a.G - hblk * 16);
+  const int hq0 = hk * a.G + hblk * 16;
+  const int64_t row0 = ((int64_t)b * a.n_q + hq0) * a.n_splits + split;
+  float2* const ml_out = reinterpret_cast<float2*>(a.ws_ml) + row0;
+
+  const int L_in = a.seq_lens[b];
+  const int L = L_in < 0 ? 0 : (L_in > a.max_ctx ? a.max_ctx : L_in);
+  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+  const int64_t start64 = (int64_t)lo + (int64_t)split * a.chunk;
+  if (start64 >= L) {  // empty split: (m, l) = (-inf, 0), O not written
+    if (threadIdx.x < nh) ml_out[(int64_t)threadIdx.x * a.n_splits] = make_float2(-INFINITY, 0.0f);
+    return;
+  }
+  const int start = (int)start64;
+  const int end = (split == a.n_splits - 1) ? L : (int)min((int64_t)L, start64 + a.chunk);
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15;
+  const int q4 = lane >> 4;
+
+  // ---- buffer resources of this (sequence, kv head) slice: each ends at the
+  // last row of the context.
+  const int64_t st_off = (int64_t)b * a.s_seq + (int64_t)hk * a.s_head;  // elements
+  const int64_t sc_off = (int64_t)b * a.ss_seq + (int64_t)hk * a.ss_head;
+  const int64_t last = (int64_t)(L - 1) * a.s_pos + D;
+  const uint32_t krow = (uint32_t)(KQ4 ? a.s_pos / 2 : a.s_pos);
+  const uint32_t vrow = (uint32_t)(a.s_pos / 2);
+  const uint32_t srow = (uint32_t)(a.ss_pos * 2);
+  const u32x4 krw = rsrc_words(static_cast<const char*>(a.k_store) + (KQ4 ? st_off / 2 : st_off),
+                               (uint32_t)(KQ4 ? last / 2 : last));
+  const u32x4 vrw = rsrc_words(static_cast<const char*>(a.v_store) + st_off / 2, (uint32_t)(last / 2));
+  const u32x4 ksrw = rsrc_words(a.k_scales + sc_off, (uint32_t)(((int64_t)(L - 1) * a.ss_pos + T::KNG) * 2));
+  const u32x4 vsrw = rsrc_words(a.v_scales + sc_off, (uint32_t)(((int64_t)(L - 1) * a.ss_pos + D / kQ4Block) * 2));
+
+  constexpr int STEP = NW * kTile;
+  int p0 = start + wv * kTile;
+  // The query rows (4 per wavefront; rows past nh read as zeros), then this
+  // wavefront's first tile, all as counted direct-to-LDS loads.
+  {
+    const u32x4 qrs = rsrc_words(a.q + ((int64_t)b * a.n_q + hq0) * D, (uint32_t)(nh * D * 2));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wv * 4 + i;
+      if (lane < D / 8) dma<16>(qrs, lds_addr_of(lds_q + r * QROW), r < nh ? (uint32_t)(r * 2 * D + 16 * lane) : kOOB, 0u);
+    }
+  }
+  uint8_t* const st = lds_st + wv * PITCH;
+  if (p0 < end) {
+    issue_half<KQ4, KG64, 0>(st, krw, ksrw, p0, end - p0, krow, srow, lane);
+    issue_half<KQ4, KG64, 1>(st, vrw, vsrw, p0, end - p0, vrow, srow, lane);
+    wait_vm<T::NK + T::NV>();  // the query rows landed
+  } else {
+    wait_vm<0>();
+  }
+  if constexpr (KQ4) {
+    // Rotate this wavefront's 4 query rows in place: lane l holds dims 4l .. 4l+3.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint8_t* qr = lds_q + (wv * 4 + i) * QROW + 8 * lane;
+      const u32x2 raw = *reinterpret_cast<const u32x2*>(qr);
+      float v[4] = {h_bits_to_f32(raw.x & 0xffffu), h_bits_to_f32(raw.x >> 16), h_bits_to_f32(raw.y & 0xffffu),
+                    h_bits_to_f32(raw.y >> 16)};
+      fwht256(v, lane);
+      const f16x2 h01 = {(f16)v[0], (f16)v[1]}, h23 = {(f16)v[2], (f16)v[3]};
+      *reinterpret_cast<u32x2*>(qr) = (u32x2){as_u32(h01), as_u32(h23)};
+    }
+  }
+  __syncthreads();  // every query row in LDS (rotated for a q4 K store)
+  const uint8_t* const qrow = lds_q + c16 * QROW;
+
+  // ---- int8 keys: accumulator start values -1152 * (group sum of q) that
+  // cancel the code bias (q4 keys are dequantized into the operand instead).
+  constexpr int NC = KQ4 ? 1 : SK::NG;
+  float corr[NC];
+  if constexpr (!KQ4) {
+    const uint8_t* qb = qrow + 32 * q4;
+    float qsum[SK::NJ];
+#pragma unroll
+    for (int j = 0; j < SK::NJ; ++j) {
+      const f16x8 h0 = q_get(qb, j, 0), h1 = q_get(qb, j, 1);
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += (float)h0[e] + (float)h1[e];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      qsum[j] = s;
+    }
+#pragma unroll
+    for (int g = 0; g < NC; ++g) {
+      float t = 0.0f;
+      if (KG64) {
+        t = qsum[g];
+      } else {
+#pragma unroll
+        for (int j = 0; j < SK::NJ; ++j) t += qsum[j];
+      }
+      corr[g] = -kCodeBias * t;
+    }
+  }
+
+  WaveAcc<SA> acc;
+#pragma unroll
+  for (int n = 0; n < SA::VB; ++n) acc.o[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  acc.l = (f32x4){0.f, 0.f, 0.f, 0.f};
+  acc.m_ref = -INFINITY;
+
+  // ---- pipeline over this wavefront's tiles (as in the int8 kernel): for tile
+  // t, scores from the K operands in registers; V half of t landed -> V
+  // operands; softmax; V half starts loading t+1; first half of P.V; K half of
+  // t+1 landed -> K operands; second half of P.V; K half starts loading t+2.
+  using KR = typename std::conditional<KQ4, KQ4Regs, KRegs<SK>>::type;
+  KR tk;
+  auto read_k = [&](KR& t) {
+    if constexpr (KQ4) read_k_q4<KG64>(t, st, c16, q4);
+    else read_k_i8<KG64>(t, st, c16, q4);
+  };
+  if (p0 < end) {
+    wait_vm<T::NV>();  // K half of the first tile landed (its V half may still be loading)
+    read_k(tk);
+    if (p0 + STEP < end) issue_half<KQ4, KG64, 0>(st, krw, ksrw, p0 + STEP, end - p0 - STEP, krow, srow, lane);
+  }
+  for (; p0 < end; p0 += STEP) {
+    const int pn = p0 + STEP;
+    const bool more = pn < end;
+    const bool more2 = pn + STEP < end;
+    float z[2][4];
+    if constexpr (KQ4) {
+      f16x8 qv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qv[j] = *reinterpret_cast<const f16x8*>(qrow + 64 * j + 16 * q4);
+      __builtin_amdgcn_sched_barrier(0);
+      scores_q4(tk, end - p0, z, qv, a.c2, q4);
+    } else {
+      scores_i8<KG64>(tk, end - p0, z, qrow + 32 * q4, corr, a.c2, q4);
+    }
+    if (more) wait_vm<T::NK>();  // V half of this tile landed; the next K half is in flight
+    else wait_vm<0>();
+    VQ4Regs tv;
+    read_v_q4<KQ4, KG64>(tv, st, c16, q4);
+    const f16x8 pa = tile_softmax<SA>(z, acc, q4);
+    if (more) issue_half<KQ4, KG64, 1>(st, vrw, vsrw, pn, end - pn, vrow, srow, lane);
+    pv_q4<1>(tv, pa, acc);
+    if (more) {
+      wait_vm<T::NV>();  // K half of the next tile landed; its V half is in flight
+      read_k(tk);
+    }
+    pv_q4<2>(tv, pa, acc);
+    if (more2) issue_half<KQ4, KG64, 0>(st, krw, ksrw, pn + STEP, end - pn - STEP, krow, srow, lane);
+  }
+
+  // ---- merge the wavefronts: slots, one barrier, the weighted sum written back
+  // into slot 0, a barrier, then each head row rotated back and stored.
+  if (q4 == 0) sm_m[wv][c16] = acc.m_ref;
+  if (c16 == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_l[wv][4 * q4 + i] = acc.l[i];
+  }
+  {
+    float* slot = reinterpret_cast<float*>(lds_st + wv * PITCH);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * q4 + i;
+      if (h < nh) {
+#pragma unroll
+        for (int n4 = 0; n4 < SA::VB / 4; ++n4) {
+          const int f = (SA::VB * c16 + 4 * n4) / 4;
+          const float4 v = {acc.o[4 * n4 + 0][i], acc.o[4 * n4 + 1][i], acc.o[4 * n4 + 2][i], acc.o[4 * n4 + 3][i]};
+          reinterpret_cast<float4*>(slot + h * D)[slot_swz(f)] = v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
+    const int h = idx / (D / 4);
+    const int f = slot_swz(idx % (D / 4));
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
+    float4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const float mk = sm_m[k][h];
+      const float wk = mk == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk - M);
+      const float4 u = reinterpret_cast<const float4*>(lds_st + k * PITCH)[h * (D / 4) + f];
+      v.x = fmaf(wk, u.x, v.x);
+      v.y = fmaf(wk, u.y, v.y);
+      v.z = fmaf(wk, u.z, v.z);
+      v.w = fmaf(wk, u.w, v.w);
+    }
+    reinterpret_cast<float4*>(lds_st)[h * (D / 4) + f] = v;  // same element, same thread: no race
+  }
+  if (threadIdx.x < nh) {
+    const int h = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
+    float l = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const float mk = sm_m[k][h];
+      if (mk != -INFINITY) l += sm_l[k][h] * __builtin_amdgcn_exp2f(mk - M);
+    }
+    ml_out[(int64_t)h * a.n_splits] = make_float2(M, l);
+  }
+  __syncthreads();
+  for (int h = wv; h < nh; h += NW) {
+    const float4 u = reinterpret_cast<const float4*>(lds_st)[h * (D / 4) + slot_swz(lane)];
+    float v[4] = {u.x, u.y, u.z, u.w};
+    fwht256(v, lane);  // back to the original basis (H / 16 is its own inverse)
+    reinterpret_cast<float4*>(a.ws_o + (row0 + (int64_t)h * a.n_splits) * D)[lane] = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+int launch_partial_q4(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
+                      const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                      const int32_t* d_seq_lens, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
+                      void* stream) {
+  if (L.head_dim != 256 || !q4_decode_supported(L)) return KVQ_ERR_UNSUPPORTED;
+  Q4Args a{};
+  a.k_store = k_store;
+  a.v_store = v_store;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.q = q;
+  a.seq_lens = d_seq_lens;
+  const int64_t rows = (int64_t)batch * n_q_heads * plan.n_splits;
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_ml = static_cast<float*>(ws) + rows * L.head_dim;
+  a.s_seq = L.s_seq;
+  a.s_pos = L.s_pos;
+  a.s_head = L.s_head;
+  a.ss_seq = L.ss_seq;
+  a.ss_pos = L.ss_pos;
+  a.ss_head = L.ss_head;
+  a.max_ctx = L.max_ctx > 0x7fffffff ? 0x7fffffff : (int32_t)L.max_ctx;
+  a.n_kv = L.n_kv_heads;
+  a.G = n_q_heads / L.n_kv_heads;
+  a.n_q = n_q_heads;
+  a.head_blocks = (a.G + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  a.n_splits = plan.n_splits;
+  a.chunk = plan.chunk;
+  a.window = window;
+  a.c2 = sm_scale * kLog2e;
+  const dim3 grid(plan.n_splits, L.n_kv_heads * a.head_blocks, batch);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L.k_dtype == KVQ_STORE_Q4)
+    hipLaunchKernelGGL((kvq_partial_q4_kernel<true, false>), grid, dim3(256), 0, s, a);
+  else if (L.scale_group == 64)
+    hipLaunchKernelGGL((kvq_partial_q4_kernel<false, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((kvq_partial_q4_kernel<false, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 }  // namespace kvq

@@ -24,6 +24,12 @@ def _store_view(t: torch.Tensor, off: int) -> torch.Tensor:
     return t[off:]
 
 
+def _seq_store(lay: kvq.Layout, t: torch.Tensor, dtype: int, b: int) -> torch.Tensor:
+    """View of a flat store from sequence b on (a q4 store holds two elements per byte)."""
+    off = b * lay.s_seq
+    return t[off // 2:] if dtype == kvq.KVQ_STORE_Q4 else t[off:]
+
+
 def append_rows(lay: kvq.Layout, cache: dict, b: int, start: int, k_rows: np.ndarray,
                 v_rows: np.ndarray, device="cuda") -> None:
     """kv_quant_append of host fp16 rows [n][n_kv][d] of sequence b at `start`."""
@@ -34,7 +40,7 @@ def append_rows(lay: kvq.Layout, cache: dict, b: int, start: int, k_rows: np.nda
     ks = cache["k_scales"]
     vs = cache["v_scales"]
     kvq.kv_quant_append(
-        lay, _store_view(cache["k"], b * lay.s_seq), _store_view(cache["v"], b * lay.s_seq),
+        lay, _seq_store(lay, cache["k"], lay.k_dtype, b), _seq_store(lay, cache["v"], lay.v_dtype, b),
         None if ks is None else _store_view(ks, b * lay.ss_seq),
         None if vs is None else _store_view(vs, b * lay.ss_seq),
         kn, vn, sp, 1, n)
@@ -46,7 +52,7 @@ def append_rows_device(lay: kvq.Layout, cache: dict, b: int, start: int, k_rows,
     ks = cache["k_scales"]
     vs = cache["v_scales"]
     kvq.kv_quant_append(
-        lay, _store_view(cache["k"], b * lay.s_seq), _store_view(cache["v"], b * lay.s_seq),
+        lay, _seq_store(lay, cache["k"], lay.k_dtype, b), _seq_store(lay, cache["v"], lay.v_dtype, b),
         None if ks is None else _store_view(ks, b * lay.ss_seq),
         None if vs is None else _store_view(vs, b * lay.ss_seq),
         k_rows.contiguous(), v_rows.contiguous(), sp, 1, k_rows.shape[0])

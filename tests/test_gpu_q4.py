@@ -4,7 +4,15 @@ PR": q4_0 and k8v4 with a Hadamard rotation over head_dim 256).
 kv_quant_append into a q4 store: the packed Q4_0 bytes and the fp16 block
 scales bit-exact with the oracle's rotation (fp32 butterflies) and quantizer,
 including rows built to give exact ties, zero blocks and extreme magnitudes;
-nothing written outside the target rows."""
+nothing written outside the target rows.
+
+Decode (kv_decode_attn_splitk + kv_decode_reduce) over q4_0 and k8v4 caches:
+max abs error <= 2e-3 against the fp64 oracle (which rotates the query for a
+q4 K store and rotates the output back for a q4 V store) over ragged lengths,
+split counts, windows, GQA groups, both layout orders and the full 128K
+context."""
+import math
+
 import numpy as np
 import pytest
 
@@ -141,3 +149,99 @@ def test_q4_append_slot_tail_and_batch():
             base = (b * lay.s_seq + h * lay.s_head + pos * lay.s_pos) // 2
             idx = torch.as_tensor(base[:, None] + np.arange(128, 256)[None, :]).cuda()
             assert (cache["v"][idx] == 0x5A).all()
+
+
+# ---- decode ---------------------------------------------------------------------------
+
+TOL = 2e-3
+
+
+def _oracle_seq(w, b, L, q_b, window, sm):
+    """fp64 oracle output [n_q][d] of sequence b over positions [0, L)."""
+    lo = max(0, L - window) if window else 0
+    cache = orc.Cache(1, L, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+    cache.append(wl.kv_rows(w, "k", b, lo, L - lo)[None], wl.kv_rows(w, "v", b, lo, L - lo)[None], [lo])
+    return orc.attend(q_b[None], cache, [L], window, sm)[0]
+
+
+def _run(w, lay, cache, q, lens, window, plan=None):
+    import int8_quantized_kv_quant_amd as kvq
+    qd = torch.from_numpy(q).cuda()
+    ld = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    out = kvq.decode(lay, cache, qd, ld, window, 1.0 / math.sqrt(w.head_dim), plan=plan, n_cu=_setup().n_cu())
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("name", ["long_q4", "long_k8v4"])
+@pytest.mark.parametrize("order", ["pos", "head"])
+def test_q4_decode_ragged_lengths_and_split_sweep(name, order):
+    """Lengths 0, 1, 33, 517, 1100 in one batch (tiles, a ragged tail, an
+    empty context); every split size gives the oracle's result."""
+    import int8_quantized_kv_quant_amd as kvq
+    w = wl.WORKLOADS[name].with_(batch=5, max_ctx=1100)
+    lens = np.array([0, 1, 33, 517, 1100], dtype=np.int32)
+    print(f"[q4 decode] {name} {order} lens {lens.tolist()}", flush=True)
+    lay, cache = _setup().fill_cache(w, lens, order=order)
+    q = wl.queries(w)
+    want = [(_oracle_seq(w, b, int(lens[b]), q[b], 0, 1 / 16) if lens[b] else np.zeros((16, 256)))
+            for b in range(w.batch)]
+    outs = []
+    for chunk in (32, 128, 512, 1120):
+        n = -(-1100 // chunk)
+        got = _run(w, lay, cache, q, lens, 0, plan=kvq.Plan(n, chunk, w.batch * 16 * n * 258 * 4))
+        outs.append(got)
+        for b in range(w.batch):
+            e = np.abs(got[b] - want[b]).max()
+            assert e <= TOL, (chunk, b, e)
+        assert not got[0].any()  # empty context -> zero row
+    assert np.abs(outs[0] - outs[-1]).max() <= 2 * TOL
+    got = _run(w, lay, cache, q, lens, 0)  # the planner's plan
+    for b in range(w.batch):
+        assert np.abs(got[b] - want[b]).max() <= TOL
+
+
+@pytest.mark.parametrize("name", ["long_q4", "long_k8v4"])
+@pytest.mark.parametrize("window", [1, 300])
+def test_q4_decode_sliding_window(name, window):
+    w = wl.WORKLOADS[name].with_(batch=2, max_ctx=2000, window=window)
+    lens = np.array([2000, 250], dtype=np.int32)
+    print(f"[q4 decode] {name} window {window}", flush=True)
+    lay, cache = _setup().fill_cache(w, lens)
+    q = wl.queries(w)
+    got = _run(w, lay, cache, q, lens, window)
+    for b in range(2):
+        want = _oracle_seq(w, b, int(lens[b]), q[b], window, 1 / 16)
+        assert np.abs(got[b] - want).max() <= TOL
+
+
+@pytest.mark.parametrize("name", ["long_q4", "long_k8v4"])
+@pytest.mark.parametrize("n_q,n_kv", [(1, 1), (32, 2), (20, 1)])
+def test_q4_decode_gqa_groups(name, n_q, n_kv):
+    """GQA groups of 1, 16 and 20 query heads per kv head (20: two head
+    blocks of 16 and 4)."""
+    w = wl.WORKLOADS[name].with_(max_ctx=700, n_q_heads=n_q, n_kv_heads=n_kv)
+    lens = np.array([700], dtype=np.int32)
+    print(f"[q4 decode] {name} n_q={n_q} n_kv={n_kv}", flush=True)
+    lay, cache = _setup().fill_cache(w, lens)
+    q = wl.queries(w)
+    got = _run(w, lay, cache, q, lens, 0)
+    want = _oracle_seq(w, 0, 700, q[0], 0, 1 / 16)
+    assert np.abs(got[0] - want).max() <= TOL
+
+
+@pytest.mark.parametrize("name", ["long_q4", "long_k8v4"])
+def test_q4_decode_long_context_128k(name):
+    """The full 131072-position context (K with 1 % outlier channels x20),
+    the planner's split plan, every query head against the oracle."""
+    w = wl.WORKLOADS[name]
+    L = w.contexts[-1]
+    print(f"[q4 decode] {name} 131072", flush=True)
+    lens = np.array([L], dtype=np.int32)
+    lay, cache = _setup().fill_cache(w, lens)
+    q = wl.queries(w)
+    got = _run(w, lay, cache, q, lens, 0)
+    want = _oracle_seq(w, 0, L, q[0], 0, 1 / 16)
+    e = np.abs(got[0] - want).max()
+    print(f"{name} 128K max abs err {e:.3g}", flush=True)
+    assert e <= TOL
