@@ -230,6 +230,87 @@ def chunk_workload(kvq, kvq_setup, wl, n_cu):
             "kernel": "kvq_chunk_kernel + kvq_reduce_kernel"}
 
 
+def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
+    """The decode step over the 4-bit stores at the long-context shape (Strata
+    PR 2698, "Not in this PR": q4_0 for K and V, k8v4 for V only, Hadamard-
+    rotated Q4_0 blocks at head_dim 256): kv_quant_append of the new token, then
+    kv_decode_attn_splitk + kv_decode_reduce, graph-replayed over COPIES caches
+    of 131072 positions. The caches are filled through kv_quant_append from rows
+    drawn on the device with a seeded torch.Generator (timing only: parity is
+    covered by the GPU tests). The partial kernel is also timed alone (its
+    roofline: algorithmic bytes / launch time)."""
+    import torch
+    dev = torch.device("cuda:0")
+    res = {}
+    for name in ("long_q4", "long_k8v4"):
+        w = wl.WORKLOADS[name]
+        L = w.contexts[-1]
+        lens = np.array([L], dtype=np.int32)
+        lay = kvq_setup.layout_for(w)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(w.seed)
+        c0 = kvq.alloc_cache(lay, 1, device=dev)
+        p = 0
+        while p < L - 1:
+            n = min(16384, L - 1 - p)
+            rows = torch.randn((2, n, w.n_kv_heads, w.head_dim), generator=gen, device=dev).half()
+            kvq_setup.append_rows_device(lay, c0, 0, p, rows[0], rows[1])
+            p += n
+        caches = [c0] + [{k: (None if t is None else t.clone()) for k, t in c0.items()} for _ in range(COPIES - 1)]
+        new = torch.randn((2, 1, 1, w.n_kv_heads, w.head_dim), generator=gen, device=dev).half()
+        qd = torch.from_numpy(wl.queries(w)).to(dev)
+        ld = torch.from_numpy(lens).to(dev)
+        sp = torch.tensor([L - 1], dtype=torch.int32, device=dev)
+        sm = 1.0 / math.sqrt(w.head_dim)
+        plan = kvq.kvq_plan(lay, 1, w.n_q_heads, w.max_ctx, w.window, n_cu)
+        ws = torch.zeros(plan.ws_bytes, dtype=torch.uint8, device=dev)
+        out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+
+        def append(c):
+            kvq.kv_quant_append(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], new[0], new[1], sp, 1, 1)
+
+        def partial(c):
+            kvq.kv_decode_attn_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], qd, 1, w.n_q_heads, ld,
+                                      w.window, sm, plan, ws, ws.numel())
+
+        def reduce():
+            kvq.kv_decode_reduce(lay, ws, ws.numel(), ld, 1, w.n_q_heads, w.window, plan, out)
+
+        def graph_us(fn):
+            for c in caches:
+                fn(c)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in caches:
+                    fn(c)
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(2, steps // len(caches))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (reps * len(caches))
+
+        us = graph_us(lambda c: (append(c), partial(c), reduce()))
+        part_us = graph_us(partial)
+        kvb = wl.kv_bytes_per_step(w, lens)
+        res[name + "_128k"] = {
+            "k_store": w.k_dtype, "v_store": w.v_dtype, "context": L, "cache_copies": COPIES,
+            "step": "kv_quant_append + kv_decode_attn_splitk + kv_decode_reduce",
+            "us_per_step": round(us, 2), "kv_bytes_per_step": int(kvb), "GB_s": round(kvb / us / 1e3, 1),
+            "pct_hbm_peak": round(100 * kvb / us / 1e3 / HBM_PEAK_GBS, 2),
+            "partial_us": round(part_us, 2), "partial_GB_s": round(kvb / part_us / 1e3, 1),
+            "partial_frac_hbm": round(kvb / part_us / 1e3 / HBM_PEAK_GBS, 4),
+            "n_splits": plan.n_splits, "chunk": plan.chunk}
+        del caches, c0
+        torch.cuda.empty_cache()
+    return res
+
+
 def blob_workload(kvq, lay, cache, L):
     """kv_cache_pack / kv_cache_unpack of all L positions of the 128K cache
     (codes with their scales: 138.4 MB of payload). Each direction reads and
@@ -443,6 +524,8 @@ def main() -> int:
         torch.cuda.empty_cache()
         others = secondary_workloads(kvq, kvq_setup, wl, n_cu, args.steps)
         others["cache_blob"] = blob
+        log("timing the decode step over the 4-bit stores (q4_0, k8v4) at 128K")
+        others.update(q4_workloads(kvq, kvq_setup, wl, n_cu, args.steps))
 
     kv_bytes = wl.kv_bytes_per_step(w, lens)
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
