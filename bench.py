@@ -233,9 +233,10 @@ def chunk_workload(kvq, kvq_setup, wl, n_cu):
 def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
     """The decode step over the 4-bit stores at the long-context shape (Strata
     PR 2698, "Not in this PR": q4_0 for K and V, k8v4 for V only, Hadamard-
-    rotated Q4_0 blocks at head_dim 256): kv_quant_append of the new token, then
-    kv_decode_attn_splitk + kv_decode_reduce, graph-replayed over COPIES caches
-    of 131072 positions. The caches are filled through kv_quant_append from rows
+    rotated Q4_0 blocks at head_dim 256): kv_append_decode_splitk (the new
+    token's rotation and quantization fused into the partials) +
+    kv_decode_reduce, graph-replayed over COPIES caches of 131072 positions;
+    the unfused three-call step beside it. The caches are filled through kv_quant_append from rows
     drawn on the device with a seeded torch.Generator (timing only: parity is
     covered by the GPU tests). The partial kernel is also timed alone (its
     roofline: algorithmic bytes / launch time)."""
@@ -269,6 +270,10 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
         def append(c):
             kvq.kv_quant_append(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], new[0], new[1], sp, 1, 1)
 
+        def fused(c):
+            kvq.kv_append_decode_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], new[0, 0], new[1, 0], qd,
+                                        1, w.n_q_heads, ld, w.window, sm, plan, ws, ws.numel())
+
         def partial(c):
             kvq.kv_decode_attn_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], qd, 1, w.n_q_heads, ld,
                                       w.window, sm, plan, ws, ws.numel())
@@ -295,14 +300,18 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) * 1e3 / (reps * len(caches))
 
-        us = graph_us(lambda c: (append(c), partial(c), reduce()))
+        us = graph_us(lambda c: (fused(c), reduce()))
+        unfused_us = graph_us(lambda c: (append(c), partial(c), reduce()))
         part_us = graph_us(partial)
+        fpart_us = graph_us(fused)
         kvb = wl.kv_bytes_per_step(w, lens)
         res[name + "_128k"] = {
             "k_store": w.k_dtype, "v_store": w.v_dtype, "context": L, "cache_copies": COPIES,
-            "step": "kv_quant_append + kv_decode_attn_splitk + kv_decode_reduce",
+            "step": "kv_append_decode_splitk + kv_decode_reduce (rotation and quantize-append fused)",
             "us_per_step": round(us, 2), "kv_bytes_per_step": int(kvb), "GB_s": round(kvb / us / 1e3, 1),
             "pct_hbm_peak": round(100 * kvb / us / 1e3 / HBM_PEAK_GBS, 2),
+            "unfused_step_us": round(unfused_us, 2),
+            "fused_partial_us": round(fpart_us, 2), "fused_partial_frac_hbm": round(kvb / fpart_us / 1e3 / HBM_PEAK_GBS, 4),
             "partial_us": round(part_us, 2), "partial_GB_s": round(kvb / part_us / 1e3, 1),
             "partial_frac_hbm": round(kvb / part_us / 1e3 / HBM_PEAK_GBS, 4),
             "n_splits": plan.n_splits, "chunk": plan.chunk}

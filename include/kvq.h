@@ -220,9 +220,10 @@ int kv_decode_attn_splitk(const kvq_layout* layout,
  *   written, so they are not const here. Combine with kv_decode_reduce.
  * Codes and scales are bit-identical to kv_quant_append's; the output of the
  * reduce differs from the unfused pair only in the order in which the new
- * position's term is summed. A layout with a q4 store is refused
- * (KVQ_ERR_UNSUPPORTED): such a step is kv_quant_append followed by
- * kv_decode_attn_splitk. */
+ * position's term is summed. Layouts with a q4 store: q4_0 and k8v4 as in
+ * kv_decode_attn_splitk (the new row rotated and quantized exactly as
+ * kv_quant_append does); the other combinations are refused
+ * (KVQ_ERR_UNSUPPORTED). */
 int kv_append_decode_splitk(const kvq_layout* layout, void* k_store, void* v_store,
                             uint16_t* k_scales, uint16_t* v_scales,
                             const uint16_t* k_new, const uint16_t* v_new,

@@ -45,6 +45,12 @@ struct Q4Args {
   const void* v_store;
   const uint16_t* k_scales;
   const uint16_t* v_scales;
+  // Fused append: the new token's K and V rows, fp16 [B][n_kv][D] (null: none);
+  // row L - 1 of the stores and scales is then written through the pointers
+  // above (the fused entry point receives them writable).
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int32_t group_lanes;  // lanes of one int8 scale group (4 values each), k8v4 keys
   const uint16_t* q;
   const int32_t* seq_lens;
   float* ws_o;   // [B][Hq][n_splits][D]
@@ -177,7 +183,8 @@ __device__ __forceinline__ void scores_q4(const KQ4Regs& t, int nvalid, float (&
       const uint32_t w0 = (t.k[ct][j].x >> sh) & 0x0F0F0F0Fu;
       const uint32_t w1 = (t.k[ct][j].y >> sh) & 0x0F0F0F0Fu;
       const uint32_t sw = t.ks[ct][j >> 1];
-      const f16x2 d2 = as_h2(__builtin_amdgcn_perm(sw, sw, (j & 1) ? 0x07060706u : 0x05040504u));  // (d_j, d_j)
+      const f16x2 sp = as_h2(sw);
+      const f16x2 d2 = (j & 1) ? sp.yy : sp.xx;  // (d_j, d_j): an operand select of the packed multiply
       u32x4 a4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -343,6 +350,15 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[16 * QROW];
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
+  // The new token's rows when the append is fused ([0] = K, [1] = V): the fp16
+  // input (landing place of its direct-to-LDS load), the dequantized values (in
+  // the stored, rotated basis for a q4 store), the bytes and scales for the
+  // cache, and the new position's scores.
+  __shared__ __attribute__((aligned(16))) uint16_t nw_in[2][D];
+  __shared__ __attribute__((aligned(16))) float nw_val[2][D];
+  __shared__ __attribute__((aligned(16))) uint32_t nw_code[2][D / 4];
+  __shared__ uint16_t nw_scale[2][D / kQ4Block];
+  __shared__ float nw_z[16];
 
   const int split = blockIdx.x;
   const int hk = blockIdx.y / a.head_blocks;
@@ -362,7 +378,11 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     return;
   }
   const int start = (int)start64;
-  const int end = (split == a.n_splits - 1) ? L : (int)min((int64_t)L, start64 + a.chunk);
+  int end = (split == a.n_splits - 1) ? L : (int)min((int64_t)L, start64 + a.chunk);
+  // Fused append: the workgroup whose range holds position L - 1 takes the new
+  // row from the quantizer instead of the cache, and its tiles stop before it.
+  const bool own_new = a.k_new != nullptr && L_in == L && L - 1 < end;
+  if (own_new) end = L - 1;
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -385,8 +405,14 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
 
   constexpr int STEP = NW * kTile;
   int p0 = start + wv * kTile;
-  // The query rows (4 per wavefront; rows past nh read as zeros), then this
+  // The new K (wavefront 0) or V (wavefront 1) row when the append is fused,
+  // the query rows (4 per wavefront; rows past nh read as zeros), then this
   // wavefront's first tile, all as counted direct-to-LDS loads.
+  if (own_new && wv < 2) {
+    const uint16_t* src = (wv == 0 ? a.k_new : a.v_new) + ((int64_t)b * a.n_kv + hk) * D;
+    if (lane < D / 8) dma<16>(rsrc_words(src, 2 * D), lds_addr_of(reinterpret_cast<const uint8_t*>(nw_in[wv])),
+                              16u * lane, 0u);
+  }
   {
     const u32x4 qrs = rsrc_words(a.q + ((int64_t)b * a.n_q + hq0) * D, (uint32_t)(nh * D * 2));
 #pragma unroll
@@ -403,6 +429,35 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   } else {
     wait_vm<0>();
   }
+  if (own_new && wv < 2) {
+    // The new row through the store's quantizer (as kv_quant_append): codes and
+    // scales for the cache, dequantized values for this workgroup's attention.
+    const uint32_t raw0 = reinterpret_cast<const uint32_t*>(nw_in[wv])[2 * lane];
+    const uint32_t raw1 = reinterpret_cast<const uint32_t*>(nw_in[wv])[2 * lane + 1];
+    const uint32_t hb[4] = {raw0 & 0xffffu, raw0 >> 16, raw1 & 0xffffu, raw1 >> 16};
+    float4 val;
+    if (wv == 1 || KQ4) {  // a q4 store: rotate, Q4_0
+      float y[4] = {h_bits_to_f32(hb[0]), h_bits_to_f32(hb[1]), h_bits_to_f32(hb[2]), h_bits_to_f32(hb[3])};
+      fwht256(y, lane);
+      uint16_t sb;
+      uint32_t own;
+      const uint32_t packed = q4_quantize(y, lane, &sb, &own);
+      const float d = h_bits_to_f32(sb);
+      val = make_float4((float)((int)(own & 0xff) - 8) * d, (float)((int)((own >> 8) & 0xff) - 8) * d,
+                        (float)((int)((own >> 16) & 0xff) - 8) * d, (float)((int)(own >> 24) - 8) * d);
+      if ((lane & 7) < 4) nw_code[wv][4 * (lane >> 3) + (lane & 7)] = packed;  // byte 16 (lane >> 3) + 4 (lane & 7)
+      if ((lane & 7) == 0) nw_scale[wv][lane >> 3] = sb;
+    } else {  // int8 keys (k8v4)
+      uint16_t sb;
+      const uint32_t code = quantize4(hb, a.group_lanes, &sb);
+      const float sc = h_bits_to_f32(sb);
+      val = make_float4((float)(int8_t)(code & 0xff) * sc, (float)(int8_t)((code >> 8) & 0xff) * sc,
+                        (float)(int8_t)((code >> 16) & 0xff) * sc, (float)(int8_t)(code >> 24) * sc);
+      nw_code[wv][lane] = code;
+      if (lane % a.group_lanes == 0) nw_scale[wv][lane / a.group_lanes] = sb;
+    }
+    *reinterpret_cast<float4*>(&nw_val[wv][4 * lane]) = val;
+  }
   if constexpr (KQ4) {
     // Rotate this wavefront's 4 query rows in place: lane l holds dims 4l .. 4l+3.
 #pragma unroll
@@ -416,8 +471,28 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
       *reinterpret_cast<u32x2*>(qr) = (u32x2){as_u32(h01), as_u32(h23)};
     }
   }
-  __syncthreads();  // every query row in LDS (rotated for a q4 K store)
+  __syncthreads();  // every query row in LDS (rotated for a q4 K store), the new rows quantized
   const uint8_t* const qrow = lds_q + c16 * QROW;
+  if (own_new && wv == 0) {
+    // Scores of the new position for the 16 heads (rows beyond nh are zero):
+    // lane 4h + r sums a quarter of the dims of head h.
+    const int h = lane >> 2, r = lane & 3;
+    const uint16_t* qr = reinterpret_cast<const uint16_t*>(lds_q + h * QROW);
+    float zs = 0.0f;
+#pragma unroll 4
+    for (int d = r * (D / 4); d < (r + 1) * (D / 4); d += 8) {
+      const f16x8 qv = *reinterpret_cast<const f16x8*>(qr + d);
+      const float4 k0 = *reinterpret_cast<const float4*>(&nw_val[0][d]);
+      const float4 k1 = *reinterpret_cast<const float4*>(&nw_val[0][d + 4]);
+      zs = fmaf((float)qv[0], k0.x, zs); zs = fmaf((float)qv[1], k0.y, zs);
+      zs = fmaf((float)qv[2], k0.z, zs); zs = fmaf((float)qv[3], k0.w, zs);
+      zs = fmaf((float)qv[4], k1.x, zs); zs = fmaf((float)qv[5], k1.y, zs);
+      zs = fmaf((float)qv[6], k1.z, zs); zs = fmaf((float)qv[7], k1.w, zs);
+    }
+    zs += __shfl_xor(zs, 1);
+    zs += __shfl_xor(zs, 2);
+    if (r == 0) nw_z[h] = zs * a.c2;  // read in the epilogue, after its barrier
+  }
 
   // ---- int8 keys: accumulator start values -1152 * (group sum of q) that
   // cancel the code bias (q4 keys are dequantized into the operand instead).
@@ -499,8 +574,8 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     if (more2) issue_half<KQ4, KG64, 0>(st, krw, ksrw, pn + STEP, end - pn - STEP, krow, srow, lane);
   }
 
-  // ---- merge the wavefronts: slots, one barrier, the weighted sum written back
-  // into slot 0, a barrier, then each head row rotated back and stored.
+  // ---- merge the wavefronts: slots, one barrier, then wavefront w combines head
+  // rows w, w + 4, ... (lane l: dims 4l .. 4l+3), rotates each back and stores it.
   if (q4 == 0) sm_m[wv][c16] = acc.m_ref;
   if (c16 == 0) {
 #pragma unroll
@@ -522,57 +597,68 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
-    const int h = idx / (D / 4);
-    const int f = slot_swz(idx % (D / 4));
-    float M = -INFINITY;
+  for (int h = wv; h < nh; h += NW) {  // uniform per wavefront: the rotation's shuffles see every lane
+    const int f = slot_swz(lane);
+    const float zn = own_new ? nw_z[h] : -INFINITY;  // the fused new position
+    float M = zn;
 #pragma unroll
     for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
-    float4 v = {0.f, 0.f, 0.f, 0.f};
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.0f;
+    if (own_new) {
+      const float wn = __builtin_amdgcn_exp2f(zn - M);
+      const float4 u = *reinterpret_cast<const float4*>(&nw_val[1][4 * lane]);
+      v[0] = wn * u.x;
+      v[1] = wn * u.y;
+      v[2] = wn * u.z;
+      v[3] = wn * u.w;
+      l = wn;
+    }
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
       const float mk = sm_m[k][h];
       const float wk = mk == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk - M);
       const float4 u = reinterpret_cast<const float4*>(lds_st + k * PITCH)[h * (D / 4) + f];
-      v.x = fmaf(wk, u.x, v.x);
-      v.y = fmaf(wk, u.y, v.y);
-      v.z = fmaf(wk, u.z, v.z);
-      v.w = fmaf(wk, u.w, v.w);
+      v[0] = fmaf(wk, u.x, v[0]);
+      v[1] = fmaf(wk, u.y, v[1]);
+      v[2] = fmaf(wk, u.z, v[2]);
+      v[3] = fmaf(wk, u.w, v[3]);
+      l = fmaf(wk, sm_l[k][h], l);
     }
-    reinterpret_cast<float4*>(lds_st)[h * (D / 4) + f] = v;  // same element, same thread: no race
-  }
-  if (threadIdx.x < nh) {
-    const int h = threadIdx.x;
-    float M = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
-    float l = 0.0f;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const float mk = sm_m[k][h];
-      if (mk != -INFINITY) l += sm_l[k][h] * __builtin_amdgcn_exp2f(mk - M);
-    }
-    ml_out[(int64_t)h * a.n_splits] = make_float2(M, l);
-  }
-  __syncthreads();
-  for (int h = wv; h < nh; h += NW) {
-    const float4 u = reinterpret_cast<const float4*>(lds_st)[h * (D / 4) + slot_swz(lane)];
-    float v[4] = {u.x, u.y, u.z, u.w};
     fwht256(v, lane);  // back to the original basis (H / 16 is its own inverse)
     reinterpret_cast<float4*>(a.ws_o + (row0 + (int64_t)h * a.n_splits) * D)[lane] = make_float4(v[0], v[1], v[2], v[3]);
+    if (lane == 0) ml_out[(int64_t)h * a.n_splits] = make_float2(M, l);
+  }
+  // ---- fused append: the new row into the cache (one head block writes it)
+  if (own_new && hblk == 0 && wv < 2) {
+    const int64_t r = (int64_t)b * a.s_seq + (int64_t)(L - 1) * a.s_pos + (int64_t)hk * a.s_head;  // elements
+    const int64_t sr = (int64_t)b * a.ss_seq + (int64_t)(L - 1) * a.ss_pos + (int64_t)hk * a.ss_head;
+    uint16_t* sc = const_cast<uint16_t*>(wv == 0 ? a.k_scales : a.v_scales);
+    if (wv == 1 || KQ4) {  // 128 bytes and 8 scales
+      uint8_t* store = static_cast<uint8_t*>(const_cast<void*>(wv == 0 ? a.k_store : a.v_store));
+      if (lane < D / 8) reinterpret_cast<uint32_t*>(store + r / 2)[lane] = nw_code[wv][lane];
+      if (lane < D / kQ4Block) sc[sr + lane] = nw_scale[wv][lane];
+    } else {
+      int8_t* store = static_cast<int8_t*>(const_cast<void*>(a.k_store));
+      reinterpret_cast<uint32_t*>(store + r)[lane] = nw_code[0][lane];
+      if (lane % a.group_lanes == 0) sc[sr + lane / a.group_lanes] = nw_scale[0][lane / a.group_lanes];
+    }
   }
 }
 
 int launch_partial_q4(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
-                      const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_q_heads,
-                      const int32_t* d_seq_lens, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
-                      void* stream) {
+                      const uint16_t* v_scales, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                      int32_t batch, int32_t n_q_heads, const int32_t* d_seq_lens, int32_t window, float sm_scale,
+                      const kvq_plan_t& plan, void* ws, void* stream) {
   if (L.head_dim != 256 || !q4_decode_supported(L)) return KVQ_ERR_UNSUPPORTED;
   Q4Args a{};
   a.k_store = k_store;
   a.v_store = v_store;
   a.k_scales = k_scales;
   a.v_scales = v_scales;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.group_lanes = L.scale_group == 64 ? 16 : L.head_dim / 4;
   a.q = q;
   a.seq_lens = d_seq_lens;
   const int64_t rows = (int64_t)batch * n_q_heads * plan.n_splits;

@@ -193,8 +193,8 @@ int kv_decode_attn_splitk(const kvq_layout* layout, const void* k_store, const v
   if (has_q4(L) && !q4_decode_supported(L)) return KVQ_ERR_UNSUPPORTED;
   if (batch == 0) return KVQ_OK;
   if (has_q4(L))
-    return launch_partial_q4(L, k_store, v_store, k_scales, v_scales, q, batch, n_q_heads, d_seq_lens, window,
-                             sm_scale, *plan, ws, stream);
+    return launch_partial_q4(L, k_store, v_store, k_scales, v_scales, nullptr, nullptr, q, batch, n_q_heads,
+                             d_seq_lens, window, sm_scale, *plan, ws, stream);
   return launch_partial(L, k_store, v_store, k_scales, v_scales, nullptr, nullptr, q, batch, n_q_heads,
                         d_seq_lens, window, sm_scale, *plan, ws, stream);
 }
@@ -207,7 +207,6 @@ int kv_append_decode_splitk(const kvq_layout* layout, void* k_store, void* v_sto
   int st = check_layout(layout);
   if (st) return st;
   const kvq_layout& L = *layout;
-  if (has_q4(L)) return KVQ_ERR_UNSUPPORTED;  // kv_quant_append + kv_decode_attn_splitk
   if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
   if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
   if ((st = check_heads(L, batch, n_q_heads))) return st;
@@ -220,7 +219,11 @@ int kv_append_decode_splitk(const kvq_layout* layout, void* k_store, void* v_sto
   if (!ws) return KVQ_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
   if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
+  if (has_q4(L) && !q4_decode_supported(L)) return KVQ_ERR_UNSUPPORTED;
   if (batch == 0) return KVQ_OK;
+  if (has_q4(L))
+    return launch_partial_q4(L, k_store, v_store, k_scales, v_scales, k_new, v_new, q, batch, n_q_heads,
+                             d_seq_lens, window, sm_scale, *plan, ws, stream);
   return launch_partial(L, k_store, v_store, k_scales, v_scales, k_new, v_new, q, batch, n_q_heads,
                         d_seq_lens, window, sm_scale, *plan, ws, stream);
 }

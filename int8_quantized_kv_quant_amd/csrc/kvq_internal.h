@@ -80,7 +80,7 @@ int check_store_ptrs(const kvq_layout& L, int dtype, const void* store, const vo
 // (four). Stores with fp32 rows keep their operands in registers: 256 VGPRs at
 // D = 256 (one), ~200 at D = 128 (two), ~125 at D = 64 (four).
 inline int resident_wgs_per_cu(const kvq_layout& L) {
-  if (has_q4(L)) return 2;  // the 4-bit kernel: ~72 KB of LDS per workgroup
+  if (has_q4(L)) return 2;  // the 4-bit kernel: ~78 KB of LDS per workgroup
   const bool staged = L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8;
   if (L.head_dim == 256) return staged ? 2 : 1;
   if (L.head_dim == 128) return staged ? 3 : 2;
@@ -132,10 +132,11 @@ int launch_blob(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k_s
                 int32_t seq, int32_t pos0, int32_t n_pos, void* blob, bool unpack, void* stream);
 
 // Partials of a layout with a q4 store (q4_decode_supported).
+// k_new / v_new non-null: the fused append of kv_append_decode_splitk.
 int launch_partial_q4(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
-                      const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_q_heads,
-                      const int32_t* d_seq_lens, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
-                      void* stream);
+                      const uint16_t* v_scales, const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q,
+                      int32_t batch, int32_t n_q_heads, const int32_t* d_seq_lens, int32_t window, float sm_scale,
+                      const kvq_plan_t& plan, void* ws, void* stream);
 
 int launch_reduce(const kvq_layout& L, const void* ws, int32_t batch, int32_t n_q_heads,
                   const kvq_plan_t& plan, uint16_t* out, void* stream);

@@ -28,11 +28,13 @@ __device__ __forceinline__ void fwht256(float (&v)[4], int lane) {
   v[3] = b - d;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {  // distance 4m between the paired elements
-    const bool lower = (lane & m) == 0;
+    // the lower element keeps a + b, the upper one a - b: p + (+-1) * v, the
+    // product exact, so the fused form rounds exactly as the sum or difference
+    const float sgn = (lane & m) ? -1.0f : 1.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float p = __shfl_xor(v[k], m);
-      v[k] = lower ? v[k] + p : p - v[k];
+      v[k] = fmaf(sgn, v[k], p);
     }
   }
 #pragma unroll
@@ -42,11 +44,13 @@ __device__ __forceinline__ void fwht256(float (&v)[4], int lane) {
 // Q4_0 quantization of a rotated row held as by fwht256: lanes 8k .. 8k+7 hold
 // block k (32 values). Returns, for lanes with (lane & 7) < 4, the dword of
 // the block's bytes 4 * (lane & 7) .. +3 (byte j = code j | code (j+16) << 4);
-// *scale_bits gets the block's fp16 scale (every lane of the block).
+// *scale_bits gets the block's fp16 scale (every lane of the block) and, if
+// given, *own the lane's 4 codes (byte k = code of y[k]).
 //   m: the value of largest magnitude, the first one on ties;
 //   d = m * -0.125 (= m / -8, exact), r = 1/d correctly rounded (0 if d = 0);
 //   q = min(15, trunc(fp32(fp32(y * r) + 8.5))), no fused multiply-add.
-__device__ __forceinline__ uint32_t q4_quantize(const float (&y)[4], int lane, uint16_t* scale_bits) {
+__device__ __forceinline__ uint32_t q4_quantize(const float (&y)[4], int lane, uint16_t* scale_bits,
+                                                uint32_t* own = nullptr) {
 #pragma clang fp contract(off)  // y * r and + 8.5 are two roundings, as in the published quantizer
   const int lb = lane & 7;
   float am = fabsf(y[0]), m = y[0];
@@ -77,6 +81,7 @@ __device__ __forceinline__ uint32_t q4_quantize(const float (&y)[4], int lane, u
     codes |= (uint32_t)min(15, (int)t) << (8 * k);
   }
   *scale_bits = __builtin_bit_cast(uint16_t, (f16)d);
+  if (own) *own = codes;
   const uint32_t hi = (uint32_t)__shfl_xor((int)codes, 4);  // codes of values 16 + 4 * (lane & 3) + k
   return codes | (hi << 4);
 }

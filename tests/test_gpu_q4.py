@@ -6,7 +6,8 @@ scales bit-exact with the oracle's rotation (fp32 butterflies) and quantizer,
 including rows built to give exact ties, zero blocks and extreme magnitudes;
 nothing written outside the target rows.
 
-Decode (kv_decode_attn_splitk + kv_decode_reduce) over q4_0 and k8v4 caches:
+Decode (kv_decode_attn_splitk + kv_decode_reduce, and the fused step
+kv_append_decode_splitk) over q4_0 and k8v4 caches:
 max abs error <= 2e-3 against the fp64 oracle (which rotates the query for a
 q4 K store and rotates the output back for a q4 V store) over ragged lengths,
 split counts, windows, GQA groups, both layout orders and the full 128K
@@ -245,3 +246,67 @@ def test_q4_decode_long_context_128k(name):
     e = np.abs(got[0] - want).max()
     print(f"{name} 128K max abs err {e:.3g}", flush=True)
     assert e <= TOL
+
+
+# ---- the fused step -------------------------------------------------------------------
+
+def _fused_pair(w, lens, plan=None):
+    """Positions [0, L_b - 1) filled, then the step at context L_b unfused
+    (kv_quant_append, partials, reduce) and fused (kv_append_decode_splitk):
+    (unfused out, fused out, unfused cache, fused cache)."""
+    import int8_quantized_kv_quant_amd as kvq
+    ks = _setup()
+    upto = np.maximum(lens - 1, 0)
+    lay, cache0 = ks.fill_cache(w, lens, upto=upto)
+    kn = np.stack([wl.kv_rows(w, "k", b, max(int(lens[b]) - 1, 0), 1)[0] for b in range(w.batch)])
+    vn = np.stack([wl.kv_rows(w, "v", b, max(int(lens[b]) - 1, 0), 1)[0] for b in range(w.batch)])
+    k_new, v_new = torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda()
+    q = torch.from_numpy(wl.queries(w)).cuda()
+    ld = torch.from_numpy(lens.astype(np.int32)).cuda()
+    sm = 1.0 / math.sqrt(w.head_dim)
+    ca = {k: (None if t is None else t.clone()) for k, t in cache0.items()}
+    start = torch.from_numpy((lens - 1).astype(np.int32)).cuda()
+    kvq.kv_quant_append(lay, ca["k"], ca["v"], ca["k_scales"], ca["v_scales"], k_new, v_new, start, w.batch, 1)
+    out_a = kvq.decode(lay, ca, q, ld, w.window, sm, plan=plan, n_cu=ks.n_cu())
+    cb = {k: (None if t is None else t.clone()) for k, t in cache0.items()}
+    out_b = kvq.decode(lay, cb, q, ld, w.window, sm, plan=plan, n_cu=ks.n_cu(), new_kv=(k_new, v_new))
+    torch.cuda.synchronize()
+    for name in ("k", "v", "k_scales", "v_scales"):
+        x, y = ca[name], cb[name]
+        if x.dtype == torch.float16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x, y), f"{name} differs between the fused and the unfused step"
+    return out_a.cpu().numpy().astype(np.float64), out_b.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("name", ["long_q4", "long_k8v4"])
+@pytest.mark.parametrize("window", [0, 700])
+def test_q4_fused_step_equals_append_then_decode(name, window):
+    """The fused step leaves the cache bit-identical to kv_quant_append's and
+    gives the oracle's output, on a batch of 3 with ragged contexts."""
+    w = wl.WORKLOADS[name].with_(batch=3, max_ctx=5000, window=window)
+    lens = np.array([5000, 2, 1337], dtype=np.int64)
+    print(f"[q4 fused] {name} window {window}", flush=True)
+    out_a, out_b = _fused_pair(w, lens)
+    q = wl.queries(w)
+    for b in range(w.batch):
+        want = _oracle_seq(w, b, int(lens[b]), q[b], window, 1 / 16)
+        assert np.abs(out_b[b] - want).max() <= TOL, b
+        assert np.abs(out_b[b] - out_a[b]).max() <= TOL, b
+
+
+@pytest.mark.parametrize("name", ["long_q4", "long_k8v4"])
+def test_q4_fused_new_row_alone_and_on_a_split_boundary(name):
+    """L = 1 (the new row is the whole context), L - 1 on a split start (that
+    split holds only the new row), L = 0 (nothing appended, zero output)."""
+    import int8_quantized_kv_quant_amd as kvq
+    w = wl.WORKLOADS[name].with_(batch=4, max_ctx=1024)
+    lens = np.array([1, 257, 0, 513], dtype=np.int64)
+    plan = kvq.Plan(4, 256, 4 * 16 * 4 * 258 * 4)  # splits start at 0, 256, 512, 768
+    print(f"[q4 fused] {name} edges", flush=True)
+    out_a, out_b = _fused_pair(w, lens, plan=plan)
+    q = wl.queries(w)
+    for b in (0, 1, 3):
+        want = _oracle_seq(w, b, int(lens[b]), q[b], 0, 1 / 16)
+        assert np.abs(out_b[b] - want).max() <= TOL, b
+    assert not out_b[2].any()

@@ -374,17 +374,19 @@ def test_q4_layout_rules():
 
 @needs_lib
 def test_q4_entry_point_refusals():
-    """Decode takes q4_0 and k8v4; every other combination with a q4 store is
-    refused before any device call, as are the fused step, chunk attention and
-    the blob calls."""
+    """Decode and the fused step take q4_0 and k8v4; every other combination
+    with a q4 store is refused before any device call, as are chunk attention
+    and the blob calls."""
     assert _partial(_q4_layout("q4", "int8")) == UNSUP
     assert _partial(_q4_layout("q4", "fp32")) == UNSUP
     assert _partial(_q4_layout("fp32", "q4")) == UNSUP
     assert _partial(_q4_layout(), batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
     assert _partial(_q4_layout("int8", "q4"), batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
     assert _partial(_q4_layout(), k_scales=None) == NULL_
-    assert _fused(_q4_layout()) == UNSUP
-    assert _fused(_q4_layout("int8", "q4")) == UNSUP
+    assert _fused(_q4_layout("q4", "int8")) == UNSUP
+    assert _fused(_q4_layout("fp32", "q4")) == UNSUP
+    assert _fused(_q4_layout(), batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
+    assert _fused(_q4_layout("int8", "q4"), k_new=None) == NULL_
     assert _chunk(_q4_layout()) == UNSUP
     out = ctypes.c_int64(0)
     assert kvq.load().kvq_blob_size(ctypes.byref(_q4_layout().c()), 4, ctypes.byref(out)) == UNSUP
