@@ -49,21 +49,26 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
+Q4_SOURCES = ("kvq_decode_q4.hip", "kvq_q4.h", "kvq_tile.h", "kvq_device.h")
+
+
+def kernel_source_digest(files=("kvq_decode.hip", "kvq_tile.h", "kvq_device.h")) -> str:
     h = hashlib.sha256()
-    for f in ("kvq_decode.hip", "kvq_tile.h", "kvq_device.h"):
+    for f in files:
         with open(os.path.join(ROOT, "int8_quantized_kv_quant_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(digest: str):
+def traffic_from_profiles(digest: str, name: str = "partial_long_128k_traffic.json", kernel: str | None = None):
     """HBM bytes per partial launch measured with rocprofv3 counters, if they
     were taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "partial_long_128k_traffic.json")
+    p = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
+    if kernel is not None:
+        d = d.get("kernels", {}).get(kernel, {})
     if d.get("kernel_src_sha") != digest:
         return None
     return d.get("hbm_bytes_per_launch")
@@ -314,6 +319,8 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
             "fused_partial_us": round(fpart_us, 2), "fused_partial_frac_hbm": round(kvb / fpart_us / 1e3 / HBM_PEAK_GBS, 4),
             "partial_us": round(part_us, 2), "partial_GB_s": round(kvb / part_us / 1e3, 1),
             "partial_frac_hbm": round(kvb / part_us / 1e3 / HBM_PEAK_GBS, 4),
+            "partial_traffic": traffic_from_profiles(kernel_source_digest(Q4_SOURCES),
+                                                     "partial_q4_long_128k_traffic.json", name),
             "n_splits": plan.n_splits, "chunk": plan.chunk}
         del caches, c0
         torch.cuda.empty_cache()
