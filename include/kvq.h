@@ -291,9 +291,10 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
  * region too], [G12 "Path F (#45) interop guard": int8 bytes saved without
  * their per-head scales read back as garbage]).
  * Payload (device memory): K values, V values, then the K scales and the V
- * scales of int8 stores; each region positions-major ([position][kv head]
- * [head_dim values] or [head_dim / scale_group scales]) and padded to a
- * multiple of 16 bytes. The header (host memory) holds the facts a reader must
+ * scales of int8 and q4 stores; each region positions-major ([position]
+ * [kv head][the row's bytes: head_dim codes, fp32 values, or head_dim / 2
+ * Q4_0 bytes] or [the row's scales: head_dim / scale_group, or head_dim / 32
+ * for q4]) and padded to a multiple of 16 bytes. The header (host memory) holds the facts a reader must
  * match; it is independent of the strides, so a blob can be placed into a
  * cache with another layout order. */
 #define KVQ_BLOB_MAGIC 0x3151564Bu /* "KVQ1" */
@@ -310,9 +311,7 @@ typedef struct {
   int64_t payload_bytes;
 } kvq_blob_header;
 
-/* kvq_blob_size -- host only: payload bytes of a blob of n_pos positions.
- * The blob format holds int8 and fp32 stores; the pack, unpack and size calls
- * refuse a layout with a q4 store (KVQ_ERR_UNSUPPORTED). */
+/* kvq_blob_size -- host only: payload bytes of a blob of n_pos positions. */
 int kvq_blob_size(const kvq_layout* layout, int32_t n_pos, int64_t* payload_bytes);
 
 /* kv_cache_pack -- copy positions [pos0, pos0 + n_pos) of sequence `seq` into

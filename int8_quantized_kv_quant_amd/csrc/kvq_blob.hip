@@ -1,7 +1,7 @@
 // kv_cache_pack / kv_cache_unpack: a contiguous blob of one sequence's cache
-// positions -- codes (or fp32 values) with the fp16 scales of every int8 store
-// -- and its placement back into a cache of the same store types, scale group,
-// head count and head_dim (any strides).
+// positions -- codes (or fp32 values, or Q4_0 bytes) with the fp16 scales of
+// every int8 or q4 store -- and its placement back into a cache of the same
+// store types, scale group, head count and head_dim (any strides).
 //
 // genie-ai-runtime release v0.1.0-alpha.11, "--int8-kv triage": a saved cache
 // must persist the scales region too; release v0.1.0-alpha.12, "Path F (#45)
@@ -9,7 +9,7 @@
 // garbage. The payload therefore always carries the scales next to the codes,
 // and the host refuses to place a blob whose layout facts differ.
 //
-// Payload: K values, V values, then K scales and V scales (int8 stores only),
+// Payload: K values, V values, then K scales and V scales (stores with scales),
 // each region positions-major ([position][kv head][...]) and padded to 16
 // bytes. One kernel copies either way: rows of the cache (strided, in a slot)
 // to or from the packed regions, 16 bytes per lane for values and one fp16
@@ -78,13 +78,12 @@ int launch_blob(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k_s
   const int64_t rows = (int64_t)n_pos * L.n_kv_heads;
   int64_t off = 0;
   for (int s = 0; s < 2; ++s) {
-    const int64_t eb = store_elem_bytes(dts[s]);
-    a.store[s] = static_cast<char*>(stores[s]) + (int64_t)seq * L.s_seq * eb;
-    a.s_pos_b[s] = L.s_pos * eb;
-    a.s_head_b[s] = L.s_head * eb;
-    a.row_bytes[s] = (int32_t)(L.head_dim * eb);
+    a.store[s] = static_cast<char*>(stores[s]) + store_bytes((int64_t)seq * L.s_seq, dts[s]);
+    a.s_pos_b[s] = store_bytes(L.s_pos, dts[s]);
+    a.s_head_b[s] = store_bytes(L.s_head, dts[s]);
+    a.row_bytes[s] = (int32_t)store_bytes(L.head_dim, dts[s]);
     a.code_off[s] = off;
-    off += blob_region_bytes(rows * L.head_dim * eb);
+    off += blob_region_bytes(store_bytes(rows * L.head_dim, dts[s]));
   }
   for (int s = 0; s < 2; ++s) {
     a.ng[s] = scales_per_row(L, dts[s]);

@@ -293,7 +293,6 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
 int kvq_blob_size(const kvq_layout* layout, int32_t n_pos, int64_t* payload_bytes) {
   int st = check_layout(layout);
   if (st) return st;
-  if (has_q4(*layout)) return KVQ_ERR_UNSUPPORTED;  // the blob format holds int8 and fp32 stores
   if (!payload_bytes) return KVQ_ERR_NULL;
   if (n_pos < 0) return KVQ_ERR_SHAPE;
   *payload_bytes = blob_payload_bytes(*layout, n_pos);
@@ -312,7 +311,6 @@ int kv_cache_pack(const kvq_layout* layout, const void* k_store, const void* v_s
   int st = check_layout(layout);
   if (st) return st;
   const kvq_layout& L = *layout;
-  if (has_q4(L)) return KVQ_ERR_UNSUPPORTED;
   if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
   if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
   if (!dst || !header) return KVQ_ERR_NULL;
@@ -333,7 +331,6 @@ int kv_cache_unpack(const kvq_layout* layout, void* k_store, void* v_store, uint
   int st = check_layout(layout);
   if (st) return st;
   const kvq_layout& L = *layout;
-  if (has_q4(L)) return KVQ_ERR_UNSUPPORTED;
   if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
   if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
   if (!src || !header) return KVQ_ERR_NULL;

@@ -91,13 +91,12 @@ inline int resident_wgs_per_cu(const kvq_layout& L) {
 inline int64_t blob_region_bytes(int64_t bytes) { return (bytes + 15) / 16 * 16; }
 
 // Payload bytes of a cache blob of n_pos positions: K values, V values, then
-// the fp16 scales of each int8 store, every region padded to 16 bytes.
+// the fp16 scales of each int8 or q4 store, every region padded to 16 bytes.
 inline int64_t blob_payload_bytes(const kvq_layout& L, int64_t n_pos) {
   const int64_t rows = n_pos * L.n_kv_heads;
   int64_t b = 0;
-  for (int dt : {L.k_dtype, L.v_dtype}) b += blob_region_bytes(rows * L.head_dim * store_elem_bytes(dt));
-  for (int dt : {L.k_dtype, L.v_dtype})
-    if (dt == KVQ_STORE_INT8) b += blob_region_bytes(rows * (L.head_dim / L.scale_group) * 2);
+  for (int dt : {L.k_dtype, L.v_dtype}) b += blob_region_bytes(store_bytes(rows * L.head_dim, dt));
+  for (int dt : {L.k_dtype, L.v_dtype}) b += blob_region_bytes(rows * scales_per_row(L, dt) * 2);
   return b;
 }
 

@@ -196,6 +196,14 @@ def pack_q4(codes) -> np.ndarray:
     return (cb[..., 0, :] | (cb[..., 1, :] << 4)).reshape(c.shape[:-1] + (n // 2,)).astype(np.uint8)
 
 
+def unpack_q4(packed) -> np.ndarray:
+    """Codes (uint8, 0..15) of Q4_0 bytes laid out as pack_q4 writes them."""
+    p = np.asarray(packed, dtype=np.uint8)
+    n = p.shape[-1] * 2
+    pb = p.reshape(p.shape[:-1] + (n // Q4_BLOCK, Q4_BLOCK // 2))
+    return np.concatenate([pb & 0x0F, pb >> 4], axis=-1).reshape(p.shape[:-1] + (n,)).astype(np.uint8)
+
+
 class Cache:
     """Logical KV cache of one layer: per store either int8 codes + fp16 scales
     or fp32 values, indexed [seq][position][kv head][element] (positions
@@ -443,9 +451,10 @@ BLOB_VERSION = 1
 
 def blob_payload(cache: Cache, b: int, pos0: int, n_pos: int) -> bytes:
     """Payload of the cache blob of positions [pos0, pos0 + n_pos) of
-    sequence b: K values, V values, then for each int8 store its fp16 scales,
-    every region positions-major ([position][kv head][...]) and padded to a
-    multiple of 16 bytes.
+    sequence b: K values, V values, then for each int8 or q4 store its fp16
+    scales, every region positions-major ([position][kv head][...]) and padded
+    to a multiple of 16 bytes. A q4 store's values are its Q4_0 bytes (two
+    codes per byte, pack_q4) and its scales the 8 block scales of each row.
 
     genie-ai-runtime release v0.1.0-alpha.11, "--int8-kv triage": a saved
     cache must carry the scales region too; release v0.1.0-alpha.12, "Path F
@@ -456,9 +465,12 @@ def blob_payload(cache: Cache, b: int, pos0: int, n_pos: int) -> bytes:
         return x + b"\0" * (-len(x) % 16)
     parts = []
     for s in ("k", "v"):
-        parts.append(pad(np.ascontiguousarray(cache.data[s][b, pos0:pos0 + n_pos]).tobytes()))
+        vals = cache.data[s][b, pos0:pos0 + n_pos]
+        if cache.dtypes[s] == "q4":
+            vals = pack_q4(vals)
+        parts.append(pad(np.ascontiguousarray(vals).tobytes()))
     for s in ("k", "v"):
-        if cache.dtypes[s] == "int8":
+        if cache.scales[s] is not None:
             parts.append(pad(np.ascontiguousarray(cache.scales[s][b, pos0:pos0 + n_pos]).tobytes()))
     return b"".join(parts)
 
@@ -467,9 +479,7 @@ def blob_header(cache: Cache, n_pos: int) -> dict:
     """The facts a reader must match before it may place the payload: format
     magic and version, kv heads, head_dim, both store types, scale group and
     the number of positions, plus the payload size."""
-    dt = {"int8": 1, "fp32": 2}
-    if any(cache.dtypes[s] not in dt for s in ("k", "v")):
-        raise ValueError("the blob format holds int8 and fp32 stores")
+    dt = {"int8": 1, "fp32": 2, "q4": 3}
     return {"magic": BLOB_MAGIC, "version": BLOB_VERSION, "n_kv_heads": cache.n_kv_heads,
             "head_dim": cache.head_dim, "k_dtype": dt[cache.dtypes["k"]], "v_dtype": dt[cache.dtypes["v"]],
             "scale_group": cache.group, "n_pos": n_pos}
@@ -486,11 +496,16 @@ def blob_restore(cache: Cache, header: dict, payload: bytes, b: int, pos0: int) 
     off = 0
     for s in ("k", "v"):
         arr = cache.data[s][b, pos0:pos0 + n]
-        nb = arr.nbytes
-        cache.data[s][b, pos0:pos0 + n] = np.frombuffer(payload[off:off + nb], dtype=arr.dtype).reshape(arr.shape)
+        if cache.dtypes[s] == "q4":
+            nb = arr.size // 2
+            packed = np.frombuffer(payload[off:off + nb], dtype=np.uint8).reshape(arr.shape[:-1] + (arr.shape[-1] // 2,))
+            cache.data[s][b, pos0:pos0 + n] = unpack_q4(packed)
+        else:
+            nb = arr.nbytes
+            cache.data[s][b, pos0:pos0 + n] = np.frombuffer(payload[off:off + nb], dtype=arr.dtype).reshape(arr.shape)
         off += nb + (-nb % 16)
     for s in ("k", "v"):
-        if cache.dtypes[s] == "int8":
+        if cache.scales[s] is not None:
             arr = cache.scales[s][b, pos0:pos0 + n]
             nb = arr.nbytes
             cache.scales[s][b, pos0:pos0 + n] = np.frombuffer(payload[off:off + nb], dtype=np.float16).reshape(arr.shape)

@@ -30,6 +30,8 @@ CASES = {
     "k8v32": (wl.WORKLOADS["mixed_k8v32"].with_(max_ctx=2048), 0, 37, 700),
     "k32v8": (wl.WORKLOADS["mixed_k32v8"].with_(max_ctx=2048), 0, 5, 64),
     "batched_d128": (wl.WORKLOADS["batched"].with_(batch=3, max_ctx=1024), 2, 100, 333),
+    "q4_0": (wl.WORKLOADS["long_q4"].with_(max_ctx=2048, batch=2), 1, 9, 1001),
+    "k8v4": (wl.WORKLOADS["long_k8v4"].with_(max_ctx=2048), 0, 0, 777),
 }
 
 
@@ -56,7 +58,7 @@ def test_pack_equals_the_oracle_blob(case):
                            oh["v_dtype"], oh["scale_group"], oh["n_pos"])
 
 
-@pytest.mark.parametrize("case", ["long_k8v8_g64", "k8v32", "batched_d128"])
+@pytest.mark.parametrize("case", ["long_k8v8_g64", "k8v32", "batched_d128", "q4_0", "k8v4"])
 def test_unpacked_into_another_layout_attends_identically(case):
     """Pack positions [0, L) of one sequence, place them into a heads-major
     cache, and decode both: the outputs are bit-identical, and the rows outside
@@ -80,8 +82,10 @@ def test_unpacked_into_another_layout_attends_identically(case):
     o2 = kvq.decode(lay2, cache2, q, ld, 0, sm, plan=plan)
     torch.cuda.synchronize()
     assert torch.equal(o1[b], o2[b])
-    for s in ("k", "v"):
+    for s, dt in (("k", w.k_dtype), ("v", w.v_dtype)):
         other = [x for x in range(w.batch) if x != b]
         if other:
-            rows = ks.rows_of(lay2, cache2[s], other[0], np.arange(0, L, 97), 0)
+            pos = np.arange(0, L, 97)
+            rows = (ks.q4_rows_of(lay2, cache2[s], other[0], pos, 0) if dt == "q4"
+                    else ks.rows_of(lay2, cache2[s], other[0], pos, 0))
             assert not rows.any()

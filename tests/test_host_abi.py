@@ -375,8 +375,9 @@ def test_q4_layout_rules():
 @needs_lib
 def test_q4_entry_point_refusals():
     """Decode and the fused step take q4_0 and k8v4; every other combination
-    with a q4 store is refused before any device call, as are chunk attention
-    and the blob calls."""
+    with a q4 store is refused before any device call, as is chunk attention.
+    The blob takes every combination (its size matches the oracle's payload)
+    and refuses a blob of other store types."""
     assert _partial(_q4_layout("q4", "int8")) == UNSUP
     assert _partial(_q4_layout("q4", "fp32")) == UNSUP
     assert _partial(_q4_layout("fp32", "q4")) == UNSUP
@@ -388,7 +389,14 @@ def test_q4_entry_point_refusals():
     assert _fused(_q4_layout(), batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
     assert _fused(_q4_layout("int8", "q4"), k_new=None) == NULL_
     assert _chunk(_q4_layout()) == UNSUP
-    out = ctypes.c_int64(0)
-    assert kvq.load().kvq_blob_size(ctypes.byref(_q4_layout().c()), 4, ctypes.byref(out)) == UNSUP
-    assert _blob(_q4_layout()) == UNSUP
-    assert _blob(_q4_layout("int8", "q4"), unpack=True) == UNSUP
+    from oracle import kvq_oracle as orc
+    for k, v in (("q4", "q4"), ("int8", "q4"), ("q4", "int8"), ("q4", "fp32")):
+        lay = _q4_layout(k, v)
+        c = orc.Cache(1, 40, 2, 256, 64, k, v)
+        for n in (0, 1, 7, 32):
+            assert kvq.kvq_blob_size(lay, n) == len(orc.blob_payload(c, 0, 0, n)), (k, v, n)
+        assert _blob(lay, n_pos=0) == 0                        # a valid call (nothing launched)
+    q4 = _q4_layout()
+    assert _blob(q4, unpack=True, header=_header(_q4_layout("int8", "q4"))) == MISMATCH
+    assert _blob(_base(), unpack=True, header=_header(q4)) == MISMATCH
+    assert _blob(q4, v_scales=None) == NULL_

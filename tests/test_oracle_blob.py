@@ -73,3 +73,45 @@ def test_int8_payload_is_refused_by_an_fp32_cache_and_a_short_payload_too():
     with pytest.raises(ValueError):
         orc.blob_restore(orc.Cache(1, 40, 2, 256, 64), orc.blob_header(src, 8), orc.blob_payload(src, 0, 0, 8)[:-16],
                          0, 0)
+
+
+# ---- 4-bit stores -----------------------------------------------------------------------
+
+def test_q4_nibbles_unpack_to_their_codes():
+    codes = np.random.default_rng(3).integers(0, 16, (5, 2, 256)).astype(np.uint8)
+    np.testing.assert_array_equal(orc.unpack_q4(orc.pack_q4(codes)), codes)
+    assert orc.unpack_q4(np.array([0xF0, 0xE1] + [0] * 14, dtype=np.uint8))[[0, 1, 16, 17]].tolist() == [0, 1, 15, 14]
+
+
+def test_q4_payload_size_is_the_cell_bytes():
+    """A q4 store's blob holds 128 code bytes and 8 fp16 scales per position
+    and kv head (4.5 bits per value)."""
+    for kdt, vdt in (("q4", "q4"), ("int8", "q4"), ("q4", "int8")):
+        c = _cache(kdt, vdt)
+        n = 32
+        assert len(orc.blob_payload(c, 0, 0, n)) == n * (orc.cell_bytes(2, 256, 64, kdt) + orc.cell_bytes(2, 256, 64, vdt))
+    assert orc.cell_bytes(2, 256, 64, "q4") == 2 * (128 + 16)
+
+
+@pytest.mark.parametrize("kdt,vdt", [("q4", "q4"), ("int8", "q4"), ("q4", "int8")])
+def test_q4_round_trip_and_attention_after_restore(kdt, vdt):
+    src = _cache(kdt, vdt)
+    pay = orc.blob_payload(src, 1, 3, 29)
+    dst = orc.Cache(2, 40, 2, 256, 64, kdt, vdt)
+    orc.blob_restore(dst, orc.blob_header(src, 29), pay, 0, 0)
+    for s in ("k", "v"):
+        np.testing.assert_array_equal(dst.data[s][0, :29], src.data[s][1, 3:32])
+        np.testing.assert_array_equal(dst.scales[s][0, :29].view(np.uint16), src.scales[s][1, 3:32].view(np.uint16))
+    q = wl.uniform_rows(91, (2, 16, 256))
+    want = orc.attend(q, src, [32, 32], 0, 1 / 16)[1]
+    # dst holds src's positions 3..31 of sequence 1 at 0..28; attend src over the same range via a window
+    got = orc.attend(q[1:], dst, [29], 0, 1 / 16)[0]
+    np.testing.assert_array_equal(got, orc.attend(q, src, [32, 32], 29, 1 / 16)[1])
+    assert np.abs(got - want).max() > 0  # the window really changed the range
+
+
+def test_q4_blob_is_refused_by_an_int8_cache():
+    src = _cache("q4", "q4")
+    hdr = orc.blob_header(src, 8)
+    with pytest.raises(ValueError):
+        orc.blob_restore(orc.Cache(1, 40, 2, 256, 64), hdr, orc.blob_payload(src, 0, 0, 8), 0, 0)
