@@ -160,6 +160,7 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
     del caches, c0
 
     res["prefill_chunk"] = chunk_workload(kvq, kvq_setup, wl, n_cu)
+    res["prefill_chunk_q4"] = chunk_workload(kvq, kvq_setup, wl, n_cu, "long_q4")
 
     w = wl.WORKLOADS["batched"]
     lens = wl.seq_lens(w)
@@ -182,17 +183,18 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
     return res
 
 
-def chunk_workload(kvq, kvq_setup, wl, n_cu):
+def chunk_workload(kvq, kvq_setup, wl, n_cu, name="long"):
     """kv_chunk_attn (partials + combine) on a 2048-token prompt chunk at
     position 30000 of the long-context layout (16 query / 2 kv heads, head_dim
-    256, group-64 scales; keys 0..32047 in the cache, causal inside the chunk).
-    Algorithmic work: 4 * head_dim flops per (token, query head, attended key)
-    (Q.K and P.V); bound by the matrix cores (fp16 MFMA peak 2.5 PFLOP/s).
-    Two sampled tokens are checked against the fp64 oracle."""
+    256, group-64 scales; keys 0..32047 in the cache, causal inside the chunk;
+    name="long_q4": the same over the q4_0 layout). Algorithmic work:
+    4 * head_dim flops per (token, query head, attended key) (Q.K and P.V);
+    bound by the matrix cores (fp16 MFMA peak 2.5 PFLOP/s). Two sampled tokens
+    are checked against the fp64 oracle."""
     import torch
     from oracle import kvq_oracle as orc
     dev = torch.device("cuda:0")
-    w = wl.WORKLOADS["long"].with_(max_ctx=32768)
+    w = wl.WORKLOADS[name].with_(max_ctx=32768)
     T, start = 2048, 30000
     end = start + T
     lay, cache = kvq_setup.fill_cache(w, np.array([end]))
@@ -232,7 +234,9 @@ def chunk_workload(kvq, kvq_setup, wl, n_cu):
             "tflops": round(flops / us / 1e6, 1), "bound": "mfma", "peak_tflops": 2500.0,
             "frac": round(flops / us / 1e6 / 2500.0, 4), "algorithmic_flops": int(flops),
             "n_splits": plan.n_splits, "chunk": plan.chunk, "max_abs_err_sampled": err,
-            "kernel": "kvq_chunk_kernel + kvq_reduce_kernel"}
+            "k_store": w.k_dtype, "v_store": w.v_dtype,
+            "kernel": ("kvq_chunk_q4_kernel" if w.k_dtype == "q4" or w.v_dtype == "q4" else "kvq_chunk_kernel")
+            + " + kvq_reduce_kernel"}
 
 
 def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):

@@ -274,8 +274,11 @@ int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32
  *   ws           device workspace of at least plan->ws_bytes bytes, 16-byte
  *                aligned (split partials of rows (b, t, hq); no initialization).
  *   out          fp16 [batch][n_tok][n_q_heads][head_dim], contiguous, 16-byte aligned.
- * Both stores must be int8 (KVQ_ERR_UNSUPPORTED otherwise). Two kernels are
- * enqueued on `stream`: the partials and the combine of kv_decode_reduce.
+ * Store types: int8 K and V, or the 4-bit layouts q4_0 and k8v4 (the query
+ * rotated for a q4 K store and the output rotated back, as in
+ * kv_decode_attn_splitk); other combinations are refused
+ * (KVQ_ERR_UNSUPPORTED). Two kernels are enqueued on `stream`: the partials
+ * and the combine of kv_decode_reduce.
  * Device precondition: 0 <= d_start_pos[b] and d_start_pos[b] + n_tok <= max_ctx;
  * a token that would sit at or beyond max_ctx sees no key and gets a zero row. */
 int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_store,

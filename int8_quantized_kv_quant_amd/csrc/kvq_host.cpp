@@ -263,7 +263,9 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
   int st = check_layout(layout);
   if (st) return st;
   const kvq_layout& L = *layout;
-  if (L.k_dtype != KVQ_STORE_INT8 || L.v_dtype != KVQ_STORE_INT8) return KVQ_ERR_UNSUPPORTED;
+  // int8 K and V, or the 4-bit layouts of the decode path (q4_0, k8v4)
+  if (!(L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8) && !q4_decode_supported(L))
+    return KVQ_ERR_UNSUPPORTED;
   if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
   if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
   if ((st = check_heads(L, batch, n_q_heads))) return st;
@@ -283,8 +285,10 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
   if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
   if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
   if (batch == 0 || n_tok == 0) return KVQ_OK;
-  st = launch_chunk(L, k_store, v_store, k_scales, v_scales, q, batch, n_tok, n_q_heads, d_start_pos, window,
-                    sm_scale, *plan, ws, stream);
+  st = has_q4(L) ? launch_chunk_q4(L, k_store, v_store, k_scales, v_scales, q, batch, n_tok, n_q_heads, d_start_pos,
+                                   window, sm_scale, *plan, ws, stream)
+                 : launch_chunk(L, k_store, v_store, k_scales, v_scales, q, batch, n_tok, n_q_heads, d_start_pos,
+                                window, sm_scale, *plan, ws, stream);
   if (st) return st;
   // The partial rows are (b, t, hq): the reduce treats batch * n_tok rows of n_q_heads.
   return launch_reduce(L, ws, (int32_t)rows, n_q_heads, *plan, out, stream);

@@ -15,6 +15,9 @@ constexpr int kPartialWaves = 4;     // wavefronts per partial-kernel workgroup
 constexpr int kMinSplitChunk = kPartialWaves * kTile;  // planner: one tile per wavefront at least
 constexpr int kChunkWaves = 4;       // wavefronts per chunk-attention workgroup
 
+// A layout with a 4-bit store.
+inline bool has_q4(const kvq_layout& L) { return L.k_dtype == KVQ_STORE_Q4 || L.v_dtype == KVQ_STORE_Q4; }
+
 // (token, head) query rows per chunk-attention workgroup: 16 per wavefront,
 // or 32 (two row blocks sharing each key and value operand) for head_dim <= 128
 // when the chunk has rows enough; at head_dim 256 two row blocks exceed the
@@ -37,6 +40,7 @@ inline int chunk_row_blocks(int64_t n_tok, int64_t G, int head_dim) {
 // (two), ~150 at D = 64 (three).
 inline int resident_chunk_wgs_per_cu(const kvq_layout& L, int rows_per_wg) {
   const bool two = rows_per_wg == 32 * kChunkWaves;
+  if (has_q4(L)) return 2;  // the 4-bit chunk kernel: ~210 VGPRs, 51-61 KB of LDS
   if (L.head_dim == 256) return two ? 1 : 2;
   if (L.head_dim == 128) return two ? 2 : 3;
   return two ? 3 : 4;
@@ -59,7 +63,6 @@ inline int scales_per_row(const kvq_layout& L, int dtype) {
   return dtype == KVQ_STORE_INT8 ? L.head_dim / L.scale_group : 0;
 }
 
-inline bool has_q4(const kvq_layout& L) { return L.k_dtype == KVQ_STORE_Q4 || L.v_dtype == KVQ_STORE_Q4; }
 
 // Store combinations with a q4 store that the decode kernels implement: q4 K
 // and V (q4_0), int8 K with q4 V (k8v4).
@@ -126,6 +129,12 @@ int launch_chunk(const kvq_layout& L, const void* k_store, const void* v_store, 
                  const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
                  const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
                  void* stream);
+
+// Chunk attention over a layout with a q4 store (q4_decode_supported).
+int launch_chunk_q4(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
+                    const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
+                    const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
+                    void* stream);
 
 int launch_blob(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k_scales, uint16_t* v_scales,
                 int32_t seq, int32_t pos0, int32_t n_pos, void* blob, bool unpack, void* stream);

@@ -1,0 +1,227 @@
+// Per-tile building blocks of the kernels that read 4-bit stores (the split-K
+// decode partials and chunk attention, head_dim 256): the LDS stage layout and
+// its direct-to-LDS loads, and the key operands and scores for q4 keys and for
+// the int8 keys of k8v4.
+//
+// Strata PR 2698, "Not in this PR": q4_0 (K and V) and k8v4 (V only) hold
+// Q4_0 blocks of rows rotated by the 256-point Hadamard transform.
+#pragma once
+
+#include <math.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "kvq_tile.h"
+
+namespace kvq {
+
+// Stage of one wavefront (bytes): K codes, V codes (128 bytes per q4 row),
+// K scale rows, V scale rows. Code rows hold their 16-byte chunk c at slot
+// c ^ swz(r); a scale region is 1 KiB for 16-byte rows (a 64-lane
+// direct-to-LDS load writes 16 bytes per lane, lanes past row 31 zeros).
+template <bool KQ4, bool KG64>
+struct Q4Stage {
+  static constexpr int D = 256;
+  static constexpr int KRB = KQ4 ? D / 2 : D;  // bytes per K row
+  static constexpr int VRB = D / 2;
+  static constexpr int KNG = KQ4 ? D / kQ4Block : (KG64 ? D / 64 : 1);  // K scales per row
+  static constexpr int KSB = 2 * KNG;
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 32 * KRB;
+  static constexpr int KS_OFF = V_OFF + 32 * VRB;
+  static constexpr int KS_SPITCH = KSB >= 4 ? KSB : 4;
+  static constexpr int KS_BYTES = KQ4 ? 1024 : 256;
+  static constexpr int VS_OFF = KS_OFF + KS_BYTES;
+  static constexpr int BYTES = VS_OFF + 1024;
+  static constexpr int NK = 32 * KRB / 1024 + 1;  // direct-to-LDS loads of a K half
+  static constexpr int NV = 32 * VRB / 1024 + 1;  // of a V half
+};
+
+// Rows per 256-byte LDS line = 16 / CH; consecutive such row groups get
+// distinct chunk slots, so 16 rows read at one chunk hit 16 distinct banks.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  constexpr int SH = CH == 16 ? 0 : (CH == 8 ? 1 : 2);
+  return (r >> SH) & (CH - 1);
+}
+
+// Direct-to-LDS loads of a 32-row code tile with ROWB bytes per row at byte
+// `lds` (rows >= nvalid read as zeros: out-of-range lane offset).
+template <int ROWB>
+__device__ __forceinline__ void issue_codes(uint32_t lds, const u32x4& rs, uint32_t soff, int nvalid, uint32_t row,
+                                            int lane) {
+  constexpr int CH = ROWB / 16;
+  constexpr int NI = 32 * ROWB / 1024;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int slot = 64 * i + lane;
+    const int r = slot / CH;
+    const int c = (slot % CH) ^ swz<CH>(r);
+    dma<16>(rs, lds + 1024 * i, (nvalid >= kTile || r < nvalid) ? (uint32_t)r * row + 16 * c : kOOB, soff);
+  }
+}
+
+// Direct-to-LDS load of the scale rows (SB bytes each) of a 32-row tile.
+template <int SB>
+__device__ __forceinline__ void issue_scales(uint32_t lds, const u32x4& rs, uint32_t soff, int nvalid, uint32_t srow,
+                                             int lane) {
+  const int nv = nvalid < kTile ? nvalid : kTile;
+  if constexpr (SB == 16) {  // lane l = row l, 16 bytes at 16 l
+    dma<16>(rs, lds, lane < nv ? (uint32_t)lane * srow : kOOB, soff);
+  } else if constexpr (SB == 8) {  // two lanes per row, 8 bytes at 8 r
+    const int r = lane >> 1;
+    dma<4>(rs, lds, r < nv ? (uint32_t)r * srow + 4 * (lane & 1) : kOOB, soff);
+  } else {  // one 2-byte scale per row, at 4 r
+    static_assert(SB == 2, "scale row size");
+    dma<2>(rs, lds, lane < nv ? (uint32_t)lane * srow : kOOB, soff);
+  }
+}
+
+// Fill the K half (HALF = 0) or the V half (HALF = 1) of a stage with the tile
+// at position p0. The half's previous contents were read by this wavefront:
+// those LDS reads complete before new data can land.
+template <bool KQ4, bool KG64, int HALF>
+__device__ __forceinline__ void issue_half(uint8_t* st, const u32x4& rs, const u32x4& srs, int p0, int nvalid,
+                                           uint32_t row, uint32_t srow, int lane) {
+  using T = Q4Stage<KQ4, KG64>;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const uint32_t base = lds_addr_of(st);
+  const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * row);
+  const uint32_t ssoff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * srow);
+  if constexpr (HALF == 0) {
+    issue_codes<T::KRB>(base + T::K_OFF, rs, soff, nvalid, row, lane);
+    issue_scales<T::KSB>(base + T::KS_OFF, srs, ssoff, nvalid, srow, lane);
+  } else {
+    issue_codes<T::VRB>(base + T::V_OFF, rs, soff, nvalid, row, lane);
+    issue_scales<16>(base + T::VS_OFF, srs, ssoff, nvalid, srow, lane);
+  }
+}
+
+// ---- keys ---------------------------------------------------------------------------
+// q4 K operands of one tile for lane (c16, q4): k[ct][j] = bytes 8 (q4 & 1) .. +7
+// of block j of row 16 ct + c16 (dims 32 j + 8 q4 .. +7 after the nibble
+// select); ks[ct] = the 8 block scales of that row's position.
+struct KQ4Regs {
+  u32x2 k[2][8];
+  u32x4 ks[2];
+};
+
+template <bool KG64>
+__device__ __forceinline__ void read_k_q4(KQ4Regs& t, const uint8_t* __restrict__ st, int c16, int q4) {
+  using T = Q4Stage<true, KG64>;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int r = 16 * ct + c16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      t.k[ct][j] = *reinterpret_cast<const u32x2*>(st + T::K_OFF + r * T::KRB + 16 * (j ^ swz<8>(r)) + 8 * (q4 & 1));
+    t.ks[ct] = *reinterpret_cast<const u32x4*>(st + T::KS_OFF + r * 16);
+  }
+}
+
+constexpr uint32_t kQ4NegBias = 0xE408E408u;  // fp16 pair (-1032, -1032)
+
+// Scores of a q4 K tile: z[ct][i] for positions x = 16 ct + 4 q4 + i of query
+// row c16 (log2 domain); positions outside [vlo, vhi) get -inf (the bounds may
+// differ per lane: per query row). qv[j] = the rotated query's dims
+// 32 j + 8 q4 .. +7 (fp16).
+__device__ __forceinline__ void scores_q4(const KQ4Regs& t, int vlo, int vhi, float (&z)[2][4], const f16x8 (&qv)[8],
+                                          float c2, int q4) {
+  const uint32_t sh = 4u * (uint32_t)(q4 >> 1);  // q4 = 2, 3: the high nibbles (dims 16..31 of the block)
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    f32x4 zz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w0 = (t.k[ct][j].x >> sh) & 0x0F0F0F0Fu;
+      const uint32_t w1 = (t.k[ct][j].y >> sh) & 0x0F0F0F0Fu;
+      const uint32_t sw = t.ks[ct][j >> 1];
+      const f16x2 sp = as_h2(sw);
+      const f16x2 d2 = (j & 1) ? sp.yy : sp.xx;  // (d_j, d_j): an operand select of the packed multiply
+      u32x4 a4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = e < 2 ? w0 : w1;
+        const uint32_t biased = (e & 1) ? biased_h2_hi(w) : biased_h2_lo(w);  // 1024 + code
+        a4[e] = as_u32((as_h2(biased) + as_h2(kQ4NegBias)) * d2);           // fp16((code - 8) * d)
+      }
+      zz = mfma16(__builtin_bit_cast(f16x8, a4), qv[j], zz);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int x = 16 * ct + 4 * q4 + i;
+      z[ct][i] = (x >= vlo && x < vhi) ? zz[i] * c2 : -INFINITY;
+    }
+  }
+}
+
+// int8 K operands (k8v4) from this stage layout, as stage_read_k reads them.
+template <bool KG64>
+__device__ __forceinline__ void read_k_i8(KRegs<Shape<256, true, true, KG64>>& t, const uint8_t* __restrict__ st,
+                                          int c16, int q4) {
+  using S = Shape<256, true, true, KG64>;
+  using T = Q4Stage<false, KG64>;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int r = 16 * ct + c16;
+#pragma unroll
+    for (int j = 0; j < S::NJ; ++j)
+      t.k[ct][j][0] = *reinterpret_cast<const u32x4*>(st + T::K_OFF + r * 256 + 16 * ((4 * j + q4) ^ swz<16>(r)));
+    const uint8_t* ksp = st + T::KS_OFF + (16 * ct + 4 * q4) * T::KS_SPITCH;
+    if constexpr (KG64) {  // 8-byte rows
+      const u32x4 a = *reinterpret_cast<const u32x4*>(ksp);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(ksp + 16);
+      t.ks[ct][0][0] = a.x; t.ks[ct][0][1] = a.y;
+      t.ks[ct][1][0] = a.z; t.ks[ct][1][1] = a.w;
+      t.ks[ct][2][0] = b.x; t.ks[ct][2][1] = b.y;
+      t.ks[ct][3][0] = b.z; t.ks[ct][3][1] = b.w;
+    } else {  // one 2-byte scale per row, rows 4 bytes apart
+      const u32x4 a = *reinterpret_cast<const u32x4*>(ksp);
+      t.ks[ct][0][0] = a.x & 0xffffu;
+      t.ks[ct][1][0] = a.y & 0xffffu;
+      t.ks[ct][2][0] = a.z & 0xffffu;
+      t.ks[ct][3][0] = a.w & 0xffffu;
+    }
+  }
+}
+
+// Scores of an int8 K tile (k8v4): as the int8 kernel's, with the bias
+// correction added after each MFMA instead of preloaded into its accumulator
+// (one register per group instead of four).
+template <bool KG64>
+__device__ __forceinline__ void scores_i8(const KRegs<Shape<256, true, true, KG64>>& t, int vlo, int vhi,
+                                          float (&z)[2][4], const f16x8 (&qv)[4][2], const float (&corr)[KG64 ? 4 : 1],
+                                          float c2, int q4) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    f32x4 zz = zero;
+    if constexpr (KG64) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 c = t.k[ct][j][0];
+        f32x4 a = mfma16(codes8_biased(c.x, c.y), qv[j][0], zero);
+        a = mfma16(codes8_biased(c.z, c.w), qv[j][1], a);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zz[i] = fmaf(a[i] + corr[j], scale_of(t.ks[ct][i], j), zz[i]);
+      }
+    } else {
+      f32x4 a = zero;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 c = t.k[ct][j][0];
+        a = mfma16(codes8_biased(c.x, c.y), qv[j][0], a);
+        a = mfma16(codes8_biased(c.z, c.w), qv[j][1], a);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zz[i] = (a[i] + corr[0]) * scale_of(t.ks[ct][i], 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int x = 16 * ct + 4 * q4 + i;
+      z[ct][i] = (x >= vlo && x < vhi) ? zz[i] * c2 : -INFINITY;
+    }
+  }
+}
+
+}  // namespace kvq

@@ -5,7 +5,8 @@ on prompt chunks and verify windows, windows, every GQA grouping and the
 ragged row blocks of a chunk.
 
 Strata PR 2698, "What it does": the prompt chunk and the verify windows read
-the same int8 cache as decode, dequantized on the fly.
+the same int8 cache as decode, dequantized on the fly; the 4-bit layouts of
+"Not in this PR" (q4_0, k8v4) are covered the same way.
 """
 import math
 
@@ -78,6 +79,13 @@ CASES = {
     # head_dim <= 128 with >= 1024 rows per kv head: two row blocks per wavefront
     "batched_two_row_blocks": (wl.WORKLOADS["batched"].with_(batch=2, max_ctx=2048), [500, 1400], 300, 0),
     "g16_d64_two_row_blocks": (wl.Workload("g16b", 1, 32, 2, 64, 64, 64, 1024, 0, 172), [600], 80, 100),
+    # the 4-bit layouts (Strata PR 2698 "Not in this PR": q4_0, k8v4): rotated
+    # query, Q4_0 keys and values, output rotated back
+    "q4_prompt_ragged_blocks": (wl.WORKLOADS["long_q4"].with_(max_ctx=4096), [3000], 130, 0),
+    "q4_verify_window": (wl.WORKLOADS["long_q4"].with_(max_ctx=8192), [6000], 4, 0),
+    "q4_batch_g16": (wl.WORKLOADS["long_q4"].with_(batch=2, n_q_heads=32, max_ctx=1024), [100, 600], 33, 0),
+    "k8v4_window_smaller_than_chunk": (wl.WORKLOADS["long_k8v4"].with_(max_ctx=2048), [1000], 100, 64),
+    "k8v4_mha_g1": (wl.WORKLOADS["long_k8v4"].with_(n_q_heads=2, max_ctx=1024), [300], 70, 0),
 }
 
 
@@ -90,11 +98,12 @@ def test_chunk_matches_oracle(case):
     _check(got, want, label=case)
 
 
-def test_forced_splits_equal_one_split():
+@pytest.mark.parametrize("name", ["long", "long_q4", "long_k8v4"])
+def test_forced_splits_equal_one_split(name):
     """The same chunk with the keys split 1, 3 and 17 ways: every result within
     the tolerance of the oracle (the combine of kv_decode_reduce per row)."""
     import int8_quantized_kv_quant_amd as kvq
-    w = wl.WORKLOADS["long"].with_(max_ctx=2048)
+    w = wl.WORKLOADS[name].with_(max_ctx=2048)
     T = 24
     for ns, chunk in ((1, 2048), (3, 704), (17, 128)):
         plan = kvq.Plan(ns, chunk, w.batch * T * w.n_q_heads * ns * (w.head_dim + 2) * 4)
@@ -102,11 +111,12 @@ def test_forced_splits_equal_one_split():
         _check(got, want, label=f"splits {ns}")
 
 
-def test_single_token_chunk_equals_decode():
+@pytest.mark.parametrize("name", ["long", "long_q4", "long_k8v4"])
+def test_single_token_chunk_equals_decode(name):
     """n_tok = 1 at start L - 1 is decode attention at context L."""
     import int8_quantized_kv_quant_amd as kvq
     import kvq_setup as ks
-    w = wl.WORKLOADS["long"].with_(max_ctx=4096)
+    w = wl.WORKLOADS[name].with_(max_ctx=4096)
     L = 3333
     lay, cache = ks.fill_cache(w, np.array([L]))
     q1 = wl.chunk_queries(w, 1)
@@ -129,11 +139,12 @@ def test_tokens_past_the_cache_end_get_zero_rows():
     assert not got[:, 24:].any()
 
 
-def test_full_size_prompt_chunk_sampled():
+@pytest.mark.parametrize("name", ["long", "long_q4"])
+def test_full_size_prompt_chunk_sampled(name):
     """The bench's prefill shape: 2048 tokens at position 30000 over the 128K
     layout of the long workload (16 query / 2 kv heads, head_dim 256, group-64
-    scales); sampled tokens against the oracle."""
-    w = wl.WORKLOADS["long"].with_(max_ctx=32768)
+    scales; or its q4_0 form); sampled tokens against the oracle."""
+    w = wl.WORKLOADS[name].with_(max_ctx=32768)
     T, start = 2048, 30000
     toks = [(0, 0), (0, 1), (0, 777), (0, 1500), (0, 2046), (0, 2047)]
     got, want, plan = _run(w, [start], T, 0, tokens=toks)

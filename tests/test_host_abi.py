@@ -374,8 +374,8 @@ def test_q4_layout_rules():
 
 @needs_lib
 def test_q4_entry_point_refusals():
-    """Decode and the fused step take q4_0 and k8v4; every other combination
-    with a q4 store is refused before any device call, as is chunk attention.
+    """Decode, the fused step and chunk attention take q4_0 and k8v4; every
+    other combination with a q4 store is refused before any device call.
     The blob takes every combination (its size matches the oracle's payload)
     and refuses a blob of other store types."""
     assert _partial(_q4_layout("q4", "int8")) == UNSUP
@@ -388,7 +388,9 @@ def test_q4_entry_point_refusals():
     assert _fused(_q4_layout("fp32", "q4")) == UNSUP
     assert _fused(_q4_layout(), batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
     assert _fused(_q4_layout("int8", "q4"), k_new=None) == NULL_
-    assert _chunk(_q4_layout()) == UNSUP
+    assert _chunk(_q4_layout("q4", "int8")) == UNSUP
+    assert _chunk(_q4_layout("fp32", "q4")) == UNSUP
+    assert _chunk(_q4_layout(), batch=0) == 0
     from oracle import kvq_oracle as orc
     for k, v in (("q4", "q4"), ("int8", "q4"), ("q4", "int8"), ("q4", "fp32")):
         lay = _q4_layout(k, v)
