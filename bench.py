@@ -49,7 +49,7 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-Q4_SOURCES = ("kvq_decode_q4.hip", "kvq_q4.h", "kvq_tile.h", "kvq_device.h")
+Q4_SOURCES = ("kvq_decode_q4.hip", "kvq_q4_tile.h", "kvq_q4.h", "kvq_tile.h", "kvq_device.h")
 
 
 def kernel_source_digest(files=("kvq_decode.hip", "kvq_tile.h", "kvq_device.h")) -> str:
