@@ -117,13 +117,15 @@ def test_new_row_alone_and_on_a_split_boundary():
     assert not out_b[2].any()
 
 
-def test_fused_step_in_a_graph_matches_eager():
+@pytest.mark.parametrize("name", ["long", "long_q4", "long_k8v4"])
+def test_fused_step_in_a_graph_matches_eager(name):
     """Captured once, replayed at growing contexts with the token rows and the
     lengths changed on the device between replays: every replay equals the
-    same fused step run eagerly, bit for bit, and leaves the same cache."""
+    same fused step run eagerly, bit for bit, and leaves the same cache (int8
+    and the 4-bit layouts)."""
     import int8_quantized_kv_quant_amd as kvq
     import kvq_setup as ks
-    w = wl.WORKLOADS["long"].with_(max_ctx=4096)
+    w = wl.WORKLOADS[name].with_(max_ctx=4096)
     L0 = 3000
     lay, cache = ks.fill_cache(w, np.array([L0]), upto=np.array([L0 - 1]))
     plan = kvq.kvq_plan(lay, 1, w.n_q_heads, w.max_ctx, 0, ks.n_cu())
