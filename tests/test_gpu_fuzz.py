@@ -1,0 +1,119 @@
+"""Seeded random configurations of the whole surface on the GPU against the
+fp64 oracle: head_dim, store types (int8, fp32, q4 -- k8v32, k32v8, q4_0,
+k8v4), scale group, kv heads and GQA group size (one or two 16-head blocks),
+batch with ragged lengths (empty contexts included), sliding windows, slot
+width and layout order. Each configuration runs decode (planner plan and a
+forced split count), the fused decode step (its cache bit-identical to
+kv_quant_append's) and, where the stores allow it, chunk attention; outputs
+within 2e-3 of the oracle.
+
+genie-ai-runtime v1.3.0 "split-K decode attention" and "Details" (windows,
+slot width); Strata PR 2698, "What it does" (group-64 scales, k8v32 / k32v8)
+and "Not in this PR" (q4_0, k8v4)."""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import kvq_oracle as orc
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+N_CONFIGS = 40
+
+
+def _config(i):
+    rng = np.random.default_rng([2024, i])
+    d = int(rng.choice([64, 128, 256, 256]))
+    # the int8 pair and the 4-bit pairs weigh more than the fp32 mixes
+    pairs = [("int8", "int8")] * 3 + [("int8", "fp32"), ("fp32", "int8"), ("fp32", "fp32")]
+    if d == 256:
+        pairs += [("q4", "q4"), ("q4", "q4"), ("int8", "q4"), ("int8", "q4")]
+    kdt, vdt = pairs[int(rng.integers(len(pairs)))]
+    g = int(rng.choice([64, d]))
+    n_kv = int(rng.integers(1, 4))
+    G = int(rng.choice([1, 2, 5, 8, 16, 17]))
+    batch = int(rng.integers(1, 5))
+    max_ctx = int(rng.integers(40, 700))
+    window = int(rng.integers(1, max_ctx + 1)) if rng.random() < 0.4 else 0
+    slot = d + 64 * int(rng.integers(0, 3))
+    order = str(rng.choice(["pos", "head"]))
+    lens = rng.integers(0, max_ctx + 1, batch)
+    lens[0] = max_ctx                      # a full context
+    if batch > 1:
+        lens[1] = int(rng.choice([0, 1, 31, 33]))  # an empty or tiny one
+    w = wl.Workload(f"fuzz{i}", batch, n_kv * G, n_kv, d, slot, g, max_ctx, window, 300 + i,
+                    k_dtype=kdt, v_dtype=vdt, contexts=(max_ctx,))
+    return w, lens.astype(np.int64), order
+
+
+def _oracle(w, lens, q, sm):
+    cache = orc.Cache(w.batch, w.max_ctx, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+    for b in range(w.batch):
+        L = int(lens[b])
+        if L:
+            one = orc.Cache(1, w.max_ctx, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+            one.append(wl.kv_rows(w, "k", b, 0, L)[None], wl.kv_rows(w, "v", b, 0, L)[None], [0])
+            for s in ("k", "v"):
+                cache.data[s][b] = one.data[s][0]
+                if cache.scales[s] is not None:
+                    cache.scales[s][b] = one.scales[s][0]
+    return cache, orc.attend(q, cache, lens, w.window, sm)
+
+
+@pytest.mark.parametrize("i", range(N_CONFIGS))
+def test_random_configuration(i):
+    import int8_quantized_kv_quant_amd as kvq
+    import kvq_setup as ks
+    w, lens, order = _config(i)
+    print(f"[fuzz {i}] d={w.head_dim} {w.k_dtype}/{w.v_dtype} g={w.scale_group} kv={w.n_kv_heads} "
+          f"G={w.gqa} B={w.batch} lens={lens.tolist()} max_ctx={w.max_ctx} W={w.window} "
+          f"slot={w.slot_dim} order={order}", flush=True)
+    sm = 1.0 / math.sqrt(w.head_dim)
+    q = wl.queries(w)
+    oc, want = _oracle(w, lens, q, sm)
+    lay, cache = ks.fill_cache(w, lens, order=order)
+    qd = torch.from_numpy(q).cuda()
+    ld = torch.from_numpy(lens.astype(np.int32)).cuda()
+
+    # decode: the planner's plan and a forced split of 96 positions
+    got = kvq.decode(lay, cache, qd, ld, w.window, sm, n_cu=ks.n_cu()).cpu().numpy().astype(np.float64)
+    assert np.abs(got - want).max() <= TOL
+    l_eff = min(w.max_ctx, w.window) if w.window else w.max_ctx
+    ns = -(-l_eff // 96)
+    plan = kvq.Plan(ns, 96, w.batch * w.n_q_heads * ns * (w.head_dim + 2) * 4)
+    got = kvq.decode(lay, cache, qd, ld, w.window, sm, plan=plan).cpu().numpy().astype(np.float64)
+    assert np.abs(got - want).max() <= TOL
+
+    # the fused step at the same contexts: position L_b - 1 rewritten from its rows
+    k_new = torch.from_numpy(np.stack([wl.kv_rows(w, "k", b, max(int(lens[b]) - 1, 0), 1)[0]
+                                       for b in range(w.batch)])).cuda()
+    v_new = torch.from_numpy(np.stack([wl.kv_rows(w, "v", b, max(int(lens[b]) - 1, 0), 1)[0]
+                                       for b in range(w.batch)])).cuda()
+    fused = {k: (None if t is None else t.clone()) for k, t in cache.items()}
+    got = kvq.decode(lay, fused, qd, ld, w.window, sm, n_cu=ks.n_cu(), new_kv=(k_new, v_new))
+    torch.cuda.synchronize()
+    assert np.abs(got.cpu().numpy().astype(np.float64) - want).max() <= TOL
+    for name in ("k", "v", "k_scales", "v_scales"):
+        if cache[name] is not None:
+            assert torch.equal(cache[name].view(torch.uint8), fused[name].view(torch.uint8)), name
+
+    # chunk attention (int8 or 4-bit stores): the last n_tok tokens of each context
+    if (w.k_dtype, w.v_dtype) in (("int8", "int8"), ("q4", "q4"), ("int8", "q4")):
+        rng = np.random.default_rng([77, i])
+        n_tok = int(rng.integers(1, 41))
+        starts = np.maximum(lens - n_tok, 0)
+        qc = wl.chunk_queries(w, n_tok)
+        got = kvq.chunk_attn(lay, cache, torch.from_numpy(qc).cuda(),
+                             torch.from_numpy(starts.astype(np.int32)).cuda(), w.window, sm,
+                             max_seq_len=w.max_ctx).cpu().numpy().astype(np.float64)
+        want_c = orc.attend_chunk(qc, oc, starts, w.window, sm)
+        # tokens past a sequence's filled context attend to unfilled (zero) rows
+        # on both sides; compare the tokens inside the context
+        for b in range(w.batch):
+            n_in = int(min(n_tok, lens[b] - starts[b]))
+            if n_in > 0:
+                assert np.abs(got[b, :n_in] - want_c[b, :n_in]).max() <= TOL, b
