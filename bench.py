@@ -76,25 +76,60 @@ def traffic_from_profiles(digest: str, name: str = "partial_long_128k_traffic.js
 
 def cpu_baseline(w, lens, q, sm):
     """The oracle as it stands, timed on the host: decode attention of the full
-    step (both kv heads, 131072 positions) over the dequantized cache in fp64."""
+    step (both kv heads, 131072 positions) over the dequantized cache in fp64,
+    repeated for about 10 s with the BLAS threads it has by default, then for
+    about 10 s on one thread. Returns (output, seconds per step, threads,
+    repetitions, seconds per step on one thread, its repetitions)."""
     from oracle import kvq_oracle as orc
     import workloads as wl
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         cores = os.cpu_count() or 1
     L = int(lens[0])
     cache = orc.Cache(1, L, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
     cache.append(wl.kv_rows(w, "k", 0, 0, L)[None], wl.kv_rows(w, "v", 0, 0, L)[None], [0])
-    reps, t0 = 0, time.perf_counter()
-    while True:  # repeat the step until about 10 s of host work have been timed
-        want = orc.attend(q, cache, lens, 0, sm)
-        reps += 1
-        if time.perf_counter() - t0 >= 10.0:
-            break
-    dt = (time.perf_counter() - t0) / reps
-    return want, dt, cores, reps
+
+    def timed():
+        reps, t0 = 0, time.perf_counter()
+        while True:  # repeat the step until about 10 s of host work have been timed
+            out = orc.attend(q, cache, lens, 0, sm)
+            reps += 1
+            if time.perf_counter() - t0 >= 10.0:
+                return out, (time.perf_counter() - t0) / reps, reps
+
+    want, dt, reps = timed()
+    dt1, reps1 = None, None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            _, dt1, reps1 = timed()
+    return want, dt, cores, reps, dt1, reps1
+
+
+def stream_reference(kvq, n_cu):
+    """Bytes per second of kvq_stream_read (a read-only kernel of contiguous
+    per-workgroup slices, non-temporal 128-bit loads) over 4 GiB: median and
+    best of 20 timed launches after 3 warm-ups, in GB/s."""
+    import torch
+    n = 1 << 32
+    buf = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    for _ in range(3):
+        kvq.kvq_stream_read(buf, n, sink, n_cu)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvq.kvq_stream_read(buf, n, sink, n_cu)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del buf
+    torch.cuda.empty_cache()
+    return n / float(np.median(ts)) / 1e9, n / float(np.min(ts)) / 1e9, n
 
 
 def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
@@ -474,14 +509,16 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the full step")
-        want, cpu_s, cores, cpu_reps = cpu_baseline(w, lens, q, sm)
+        want, cpu_s, cores, cpu_reps, cpu_s1, cpu_reps1 = cpu_baseline(w, lens, q, sm)
         max_err = float(np.abs(got - want).max())
         kv_bytes = wl.kv_bytes_per_step(w, lens)
         cpu = {"value": round(kv_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(cores),
                "kind": "oracle", "seconds": round(cpu_s, 3),
-               "sample": f"full step repeated {cpu_reps}x (~10 s): numpy fp64 decode attention of 16 "
-                         "query heads over the dequantized 131072-position cache (both kv heads); "
-                         "cache set-up not timed"}
+               "value_1core": None if cpu_s1 is None else round(kv_bytes / cpu_s1 / 1e9, 4),
+               "seconds_1core": None if cpu_s1 is None else round(cpu_s1, 3),
+               "sample": f"full step repeated {cpu_reps}x (~10 s) on {int(cores)} BLAS threads, then "
+                         f"{cpu_reps1}x (~10 s) on one: numpy fp64 decode attention of 16 query heads over "
+                         "the dequantized 131072-position cache (both kv heads); cache set-up not timed"}
     else:
         max_err = None
 
@@ -523,6 +560,23 @@ def main() -> int:
     g_step = capture(lambda c: (fused_partial(c, plan_g), reduce(plan_g)))
     log(f"timing {reps * COPIES} graph-replayed steps")
     ms_per_step = replay_ms(g_step, reps)
+    # The spread: each replay (one step per cache copy) timed on its own.
+    per_replay = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g_step.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_replay.append(e0.elapsed_time(e1) * 1e3 / COPIES)
+    # Hot cache: the same step repeated on one copy (132 MiB stays in the
+    # 256 MB Infinity Cache) -- labelled as such, not the headline.
+    g_hot = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_hot):
+        for _ in range(COPIES):
+            fused_partial(caches[0], plan_g)
+            reduce(plan_g)
+    hot_ms = replay_ms(g_hot, reps)
     graph_out = out.clone()
     step(caches[COPIES - 1])  # eager step on the copy the graph ended with
     torch.cuda.synchronize()
@@ -547,6 +601,9 @@ def main() -> int:
         log("timing the decode step over the 4-bit stores (q4_0, k8v4) at 128K")
         others.update(q4_workloads(kvq, kvq_setup, wl, n_cu, args.steps))
 
+    log("timing the read-only streaming reference (4 GiB)")
+    stream_gbs, stream_best, stream_bytes = stream_reference(kvq, n_cu)
+
     kv_bytes = wl.kv_bytes_per_step(w, lens)
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (fpart_ms * 1e-3) / 1e9
@@ -563,6 +620,16 @@ def main() -> int:
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "stream_reference": {"kernel": "kvq_stream_read (non-temporal 128-bit loads, read only)",
+                             "bytes": stream_bytes, "GB_s": round(stream_gbs, 1), "GB_s_best": round(stream_best, 1),
+                             "pct_hbm_peak": round(100 * stream_gbs / HBM_PEAK_GBS, 2),
+                             "step_pct_of_stream": round(100 * value / stream_gbs, 2),
+                             "partial_pct_of_stream": round(100 * achieved / stream_gbs, 2)},
+        "step_us_percentiles": {"p10": round(float(np.percentile(per_replay, 10)), 2),
+                                "median": round(float(np.median(per_replay)), 2),
+                                "p90": round(float(np.percentile(per_replay, 90)), 2),
+                                "replays": len(per_replay), "steps_per_replay": COPIES},
+        "hot_cache_us_per_step": round(hot_ms * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

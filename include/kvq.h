@@ -17,6 +17,7 @@
  *                          contiguous blob (codes with their scales) and back
  *   kvq_plan               host-only choice of the split count and workspace
  *   kvq_plan_chunk         the same for kv_chunk_attn
+ *   kvq_stream_read        a read-only streaming reference for measurements
  *
  * Sources of the method (web pages; cited by title and section):
  *   [G12]  genie-ai-runtime release v0.1.0-alpha.12, "Path I: INT8 KV cache",
@@ -334,6 +335,16 @@ int kv_cache_pack(const kvq_layout* layout, const void* k_store, const void* v_s
 int kv_cache_unpack(const kvq_layout* layout, void* k_store, void* v_store, uint16_t* k_scales,
                     uint16_t* v_scales, int32_t seq, int32_t pos0, const kvq_blob_header* header,
                     const void* src, int64_t src_bytes, void* stream);
+
+/* kvq_stream_read -- measurement reference, not part of the method: reads
+ * `bytes` of device memory at `buf` (16-byte aligned, bytes a multiple of 16)
+ * once with 128-bit loads and discards them, on `n_cu` compute units' worth of
+ * workgroups. Its bytes per second are what a kernel that only streams can
+ * take of this GPU's HBM, the reference beside the 8 TB/s peak for the decode
+ * kernels' KV bytes per second. `sink` (device, 4 bytes) is written only in
+ * the practically impossible case that the XOR of a lane's loads equals a
+ * fixed constant. Enqueued on `stream`. */
+int kvq_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t n_cu, void* stream);
 
 /* Text for a kvq_status value (static storage). */
 const char* kvq_status_string(int status);

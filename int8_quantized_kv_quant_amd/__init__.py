@@ -19,7 +19,8 @@ __all__ = [
     "KVQ_STORE_INT8", "KVQ_STORE_FP32", "KVQ_STORE_Q4", "KvqError", "KvqLibraryMissing", "Layout", "Plan",
     "lib_path", "load", "kvq_version", "kvq_status_string", "kvq_plan", "kv_quant_append",
     "kv_decode_attn_splitk", "kv_append_decode_splitk", "kv_decode_reduce", "kvq_plan_chunk",
-    "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack", "kv_cache_unpack", "BlobHeader", "make_layout",
+    "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack", "kv_cache_unpack", "kvq_stream_read", "BlobHeader",
+    "make_layout",
     "alloc_cache", "decode", "chunk_attn",
     "EXPORTED_SYMBOLS",
 ]
@@ -32,7 +33,7 @@ Q4_BLOCK = 32  # values per Q4_0 block (one fp16 scale each)
 
 EXPORTED_SYMBOLS = ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
                     "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack",
-                    "kv_cache_unpack", "kvq_status_string", "kvq_version")
+                    "kv_cache_unpack", "kvq_stream_read", "kvq_status_string", "kvq_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -132,12 +133,13 @@ def load():
     lib.kv_cache_pack.argtypes = [LP, vp, vp, vp, vp, i32, i32, i32, vp, i64, HP, vp]
     lib.kv_cache_unpack.argtypes = [LP, vp, vp, vp, vp, i32, i32, HP, vp, i64, vp]
     lib.kv_chunk_attn.argtypes = [LP, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, f32, PP, vp, i64, vp, vp]
+    lib.kvq_stream_read.argtypes = [vp, i64, vp, i32, vp]
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_version.argtypes = []
     for fn in ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
                "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack",
-               "kv_cache_unpack", "kvq_version"):
+               "kv_cache_unpack", "kvq_stream_read", "kvq_version"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -238,6 +240,11 @@ class BlobHeader(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("k_dtype", ctypes.c_int32), ("v_dtype", ctypes.c_int32),
                 ("scale_group", ctypes.c_int32), ("n_pos", ctypes.c_int32), ("payload_bytes", ctypes.c_int64)]
+
+
+def kvq_stream_read(buf, n_bytes: int, sink, n_cu: int, stream=None) -> None:
+    """The read-only streaming reference (measurement only)."""
+    _check("kvq_stream_read", load().kvq_stream_read(_ptr(buf), n_bytes, _ptr(sink), n_cu, _stream(stream)))
 
 
 def kvq_blob_size(layout: Layout, n_pos: int) -> int:

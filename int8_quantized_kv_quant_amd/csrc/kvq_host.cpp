@@ -351,6 +351,14 @@ int kv_cache_unpack(const kvq_layout* layout, void* k_store, void* v_store, uint
                      stream);
 }
 
+int kvq_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int32_t n_cu, void* stream) {
+  if (!buf || !sink) return KVQ_ERR_NULL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return KVQ_ERR_ALIGN;
+  if (bytes < 0 || bytes % 16 || n_cu < 1) return KVQ_ERR_SHAPE;
+  if (bytes == 0) return KVQ_OK;
+  return launch_stream(buf, bytes, sink, n_cu, stream);
+}
+
 int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,
                      const int32_t* d_seq_lens, int32_t batch, int32_t n_q_heads, int32_t window,
                      const kvq_plan_t* plan, uint16_t* out, void* stream) {

@@ -146,6 +146,9 @@ int launch_partial_q4(const kvq_layout& L, const void* k_store, const void* v_st
                       int32_t batch, int32_t n_q_heads, const int32_t* d_seq_lens, int32_t window, float sm_scale,
                       const kvq_plan_t& plan, void* ws, void* stream);
 
+// The read-only streaming reference of kvq_stream_read.
+int launch_stream(const void* buf, int64_t bytes, uint32_t* sink, int n_cu, void* stream);
+
 int launch_reduce(const kvq_layout& L, const void* ws, int32_t batch, int32_t n_q_heads,
                   const kvq_plan_t& plan, uint16_t* out, void* stream);
 

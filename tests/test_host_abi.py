@@ -402,3 +402,14 @@ def test_q4_entry_point_refusals():
     assert _blob(q4, unpack=True, header=_header(_q4_layout("int8", "q4"))) == MISMATCH
     assert _blob(_base(), unpack=True, header=_header(q4)) == MISMATCH
     assert _blob(q4, v_scales=None) == NULL_
+
+
+@needs_lib
+def test_stream_reference_refusals():
+    lib = kvq.load()
+    assert lib.kvq_stream_read(None, 1024, FAKE, 256, None) == NULL_
+    assert lib.kvq_stream_read(FAKE, 1024, None, 256, None) == NULL_
+    assert lib.kvq_stream_read(FAKE + 8, 1024, FAKE, 256, None) == ALIGN
+    assert lib.kvq_stream_read(FAKE, 1000, FAKE, 256, None) == SHAPE   # not a multiple of 16 bytes
+    assert lib.kvq_stream_read(FAKE, 1024, FAKE, 0, None) == SHAPE
+    assert lib.kvq_stream_read(FAKE, 0, FAKE, 256, None) == 0           # nothing to read, nothing launched
