@@ -46,8 +46,9 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 // Direct-to-LDS loads of a 32-row code tile with ROWB bytes per row at byte
-// `lds` (rows >= nvalid read as zeros: out-of-range lane offset).
-template <int ROWB>
+// `lds` (rows >= nvalid read as zeros: out-of-range lane offset), with the
+// non-temporal cache policy when NT.
+template <int ROWB, bool NT = false>
 __device__ __forceinline__ void issue_codes(uint32_t lds, const u32x4& rs, uint32_t soff, int nvalid, uint32_t row,
                                             int lane) {
   constexpr int CH = ROWB / 16;
@@ -57,23 +58,23 @@ __device__ __forceinline__ void issue_codes(uint32_t lds, const u32x4& rs, uint3
     const int slot = 64 * i + lane;
     const int r = slot / CH;
     const int c = (slot % CH) ^ swz<CH>(r);
-    dma<16>(rs, lds + 1024 * i, (nvalid >= kTile || r < nvalid) ? (uint32_t)r * row + 16 * c : kOOB, soff);
+    dma<16, NT>(rs, lds + 1024 * i, (nvalid >= kTile || r < nvalid) ? (uint32_t)r * row + 16 * c : kOOB, soff);
   }
 }
 
 // Direct-to-LDS load of the scale rows (SB bytes each) of a 32-row tile.
-template <int SB>
+template <int SB, bool NT = false>
 __device__ __forceinline__ void issue_scales(uint32_t lds, const u32x4& rs, uint32_t soff, int nvalid, uint32_t srow,
                                              int lane) {
   const int nv = nvalid < kTile ? nvalid : kTile;
   if constexpr (SB == 16) {  // lane l = row l, 16 bytes at 16 l
-    dma<16>(rs, lds, lane < nv ? (uint32_t)lane * srow : kOOB, soff);
+    dma<16, NT>(rs, lds, lane < nv ? (uint32_t)lane * srow : kOOB, soff);
   } else if constexpr (SB == 8) {  // two lanes per row, 8 bytes at 8 r
     const int r = lane >> 1;
-    dma<4>(rs, lds, r < nv ? (uint32_t)r * srow + 4 * (lane & 1) : kOOB, soff);
+    dma<4, NT>(rs, lds, r < nv ? (uint32_t)r * srow + 4 * (lane & 1) : kOOB, soff);
   } else {  // one 2-byte scale per row, at 4 r
     static_assert(SB == 2, "scale row size");
-    dma<2>(rs, lds, lane < nv ? (uint32_t)lane * srow : kOOB, soff);
+    dma<2, NT>(rs, lds, lane < nv ? (uint32_t)lane * srow : kOOB, soff);
   }
 }
 
@@ -89,11 +90,11 @@ __device__ __forceinline__ void issue_half(uint8_t* st, const u32x4& rs, const u
   const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * row);
   const uint32_t ssoff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * srow);
   if constexpr (HALF == 0) {
-    issue_codes<T::KRB>(base + T::K_OFF, rs, soff, nvalid, row, lane);
-    issue_scales<T::KSB>(base + T::KS_OFF, srs, ssoff, nvalid, srow, lane);
+    issue_codes<T::KRB, kNtCodes>(base + T::K_OFF, rs, soff, nvalid, row, lane);
+    issue_scales<T::KSB, kNtScales>(base + T::KS_OFF, srs, ssoff, nvalid, srow, lane);
   } else {
-    issue_codes<T::VRB>(base + T::V_OFF, rs, soff, nvalid, row, lane);
-    issue_scales<16>(base + T::VS_OFF, srs, ssoff, nvalid, srow, lane);
+    issue_codes<T::VRB, kNtCodes>(base + T::V_OFF, rs, soff, nvalid, row, lane);
+    issue_scales<16, kNtScales>(base + T::VS_OFF, srs, ssoff, nvalid, srow, lane);
   }
 }
 
