@@ -139,7 +139,9 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
       gemma_4k  -- 8 query / 1 kv head, head_dim 256 in a 512-wide slot, one scale
                    per (position, kv head), context 4096 with a 512-key window;
       batched   -- 64 sequences of lengths U[1024, 32768], 32 query / 8 kv heads,
-                   head_dim 128, group-64 scales (2.2 GB of KV per step).
+                   head_dim 128, group-64 scales (2.2 GB of KV per step);
+      mixed     -- k8v32 and k32v8 stores (16 query / 2 kv heads, head_dim 256):
+                   the 2048-token append at 30000, then the step at 32048.
     Gemma rows come from workloads.py; the batched cache (1.1 G values) is filled
     through kv_quant_append from rows drawn on the device with a seeded
     torch.Generator (timing only: its parity is covered by the GPU tests)."""
@@ -196,6 +198,53 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
 
     res["prefill_chunk"] = chunk_workload(kvq, kvq_setup, wl, n_cu)
     res["prefill_chunk_q4"] = chunk_workload(kvq, kvq_setup, wl, n_cu, "long_q4")
+
+    # Mixed stores: positions [0, 30000) prefilled, the 2048-token chunk
+    # quantize-appended at 30000 (timed on its own: it rewrites the same rows,
+    # so the cache is unchanged, which is checked), then the decode step at
+    # context 32048 over 8 cache copies.
+    for name in ("mixed_k8v32", "mixed_k32v8"):
+        w = wl.WORKLOADS[name]
+        L = w.prefill + w.append
+        lens = np.array([L], dtype=np.int32)
+        lay, c0 = kvq_setup.fill_cache(w, lens)
+        kr = torch.from_numpy(wl.kv_rows(w, "k", 0, w.prefill, w.append)).to(dev)
+        vr = torch.from_numpy(wl.kv_rows(w, "v", 0, w.prefill, w.append)).to(dev)
+        sp = torch.tensor([w.prefill], dtype=torch.int32, device=dev)
+        before = {k: (None if t is None else t.clone()) for k, t in c0.items()}
+
+        def append():
+            kvq.kv_quant_append(lay, c0["k"], c0["v"], c0["k_scales"], c0["v_scales"], kr, vr, sp, 1, w.append)
+
+        append()
+        torch.cuda.synchronize()
+        same = all(t is None or torch.equal(t.view(torch.uint8), c0[k].view(torch.uint8)) for k, t in before.items())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            append()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        app_us = e0.elapsed_time(e1) * 1e3 / reps
+        # fp16 rows in; int8 codes + fp16 scales of one store, fp32 values of the other out
+        n_rows = w.append * w.n_kv_heads
+        app_bytes = n_rows * (2 * 2 * w.head_dim + w.head_dim + 2 * w.n_groups + 4 * w.head_dim)
+        del g, before
+        caches = [c0] + [{k: (None if t is None else t.clone()) for k, t in c0.items()} for _ in range(COPIES - 1)]
+        k_new = torch.from_numpy(wl.kv_rows(w, "k", 0, L - 1, 1)).to(dev)
+        v_new = torch.from_numpy(wl.kv_rows(w, "v", 0, L - 1, 1)).to(dev)
+        res[name] = {"k_store": w.k_dtype, "v_store": w.v_dtype, "context": L, "cache_copies": COPIES,
+                     "append_tokens": w.append, "append_at": w.prefill, "append_us": round(app_us, 2),
+                     "append_bytes": int(app_bytes), "append_GB_s": round(app_bytes / app_us / 1e3, 1),
+                     "append_rewrite_bitexact": bool(same), **timed(w, lens, lay, caches, k_new, v_new)}
+        del caches, c0
+        torch.cuda.empty_cache()
 
     w = wl.WORKLOADS["batched"]
     lens = wl.seq_lens(w)
