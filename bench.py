@@ -60,16 +60,17 @@ def kernel_source_digest(files=("kvq_decode.hip", "kvq_tile.h", "kvq_device.h"))
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(digest: str, name: str = "partial_long_128k_traffic.json", kernel: str | None = None):
+def traffic_from_profiles(digest: str, plan, name: str = "partial_long_128k_traffic.json", kernel: str | None = None):
     """HBM bytes per partial launch measured with rocprofv3 counters, if they
-    were taken on the current kernel source; else None."""
+    were taken on the current kernel source and with the same split plan
+    (n_splits, chunk); else None."""
     p = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
     if kernel is not None:
         d = d.get("kernels", {}).get(kernel, {})
-    if d.get("kernel_src_sha") != digest:
+    if d.get("kernel_src_sha") != digest or d.get("plan") != [plan.n_splits, plan.chunk]:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -407,7 +408,7 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
             "fused_partial_us": round(fpart_us, 2), "fused_partial_frac_hbm": round(kvb / fpart_us / 1e3 / HBM_PEAK_GBS, 4),
             "partial_us": round(part_us, 2), "partial_GB_s": round(kvb / part_us / 1e3, 1),
             "partial_frac_hbm": round(kvb / part_us / 1e3 / HBM_PEAK_GBS, 4),
-            "partial_traffic": traffic_from_profiles(kernel_source_digest(Q4_SOURCES),
+            "partial_traffic": traffic_from_profiles(kernel_source_digest(Q4_SOURCES), plan,
                                                      "partial_q4_long_128k_traffic.json", name),
             "n_splits": plan.n_splits, "chunk": plan.chunk}
         del caches, c0
@@ -657,10 +658,12 @@ def main() -> int:
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = kv_bytes / (fpart_ms * 1e-3) / 1e9
     digest = kernel_source_digest()
-    traffic = traffic_from_profiles(digest)
+    traffic = traffic_from_profiles(digest, plan0)
 
     res = {
-        "metric": "int8-KV decode-attention HBM GB/s (% of peak) and us/step at 128K ctx",
+        # value, ms_per_step, us_per_step: the 128K step; the 4K step's figure is
+        # us_per_step_4k (other_workloads.gemma_4k)
+        "metric": "int8-KV decode-attention HBM GB/s (% of peak) and \u00b5s/step at 4K and 128K ctx",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -668,6 +671,7 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_4k": (others or {}).get("gemma_4k", {}).get("us_per_step"),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "stream_reference": {"kernel": "kvq_stream_read (non-temporal 128-bit loads, read only)",
                              "bytes": stream_bytes, "GB_s": round(stream_gbs, 1), "GB_s_best": round(stream_best, 1),

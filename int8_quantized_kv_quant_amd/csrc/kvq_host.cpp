@@ -134,9 +134,13 @@ int kvq_plan(const kvq_layout* layout, int32_t batch, int32_t n_q_heads, int32_t
     // Long splits keep the partial traffic near 1 % of the KV bytes ...
     chunk = ceil_div(part * 100, kv_pos);
     if (chunk < 512) chunk = 512;
-    // ... unless that leaves the chip less than one full wave of resident
-    // workgroups; then the chip is filled first.
-    const int64_t want_wg = (int64_t)resident_wgs_per_cu(L) * n_cu;
+    // ... unless that leaves fewer workgroups than compute units; then the
+    // chip gets one workgroup per CU. (Measured on single sequences of 32K to
+    // 128K positions at head_dim 64 to 256: one workgroup per CU, each with
+    // longer splits, beats filling every CU's resident slots, since each
+    // workgroup pays its pipeline start and merge once and the reduce reads
+    // half as many partials.)
+    const int64_t want_wg = n_cu;
     if (units * ceil_div(l_eff, chunk) < want_wg) chunk = ceil_div(units * l_eff, want_wg);
     // A split gets at least one tile per wavefront of its workgroup.
     chunk = round_up(chunk < kMinSplitChunk ? kMinSplitChunk : chunk, kTile);

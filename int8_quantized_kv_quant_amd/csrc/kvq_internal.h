@@ -76,20 +76,6 @@ int check_layout(const kvq_layout* L);
 // Checks pointer alignment of a store and its scale array for `L`.
 int check_store_ptrs(const kvq_layout& L, int dtype, const void* store, const void* scales);
 
-// Workgroups (of four wavefronts) of the partial kernel that fit on one
-// compute unit at once, from the kernels' register and LDS footprints on
-// gfx950. LDS-staged int8 K and V: ~250 VGPRs and ~77 KB at D = 256 (two
-// workgroups), ~160 VGPRs and ~42 KB at D = 128 (three), ~115 VGPRs at D = 64
-// (four). Stores with fp32 rows keep their operands in registers: 256 VGPRs at
-// D = 256 (one), ~200 at D = 128 (two), ~125 at D = 64 (four).
-inline int resident_wgs_per_cu(const kvq_layout& L) {
-  if (has_q4(L)) return 2;  // the 4-bit kernel: ~78 KB of LDS per workgroup
-  const bool staged = L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8;
-  if (L.head_dim == 256) return staged ? 2 : 1;
-  if (L.head_dim == 128) return staged ? 3 : 2;
-  return 4;
-}
-
 // Bytes of one region of a cache blob: padded to 16.
 inline int64_t blob_region_bytes(int64_t bytes) { return (bytes + 15) / 16 * 16; }
 
