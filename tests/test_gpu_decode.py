@@ -94,6 +94,26 @@ def test_long_context_128k():
     assert e <= TOL
 
 
+@pytest.mark.parametrize("name", ["long", "long_q4"])
+@pytest.mark.parametrize("L", [32768, 65536])
+def test_long_layout_at_its_planner_plan(name, L):
+    """One sequence of L positions in a layout of max_ctx L, so the planner's
+    own plan for that context runs (one workgroup per CU: 128 splits of L/128),
+    K with 1 % outlier channels x20; within 2e-3 of the oracle."""
+    kvq = _kvq()
+    w = wl.WORKLOADS[name].with_(max_ctx=L, contexts=(L,))
+    lens = np.array([L], dtype=np.int32)
+    lay, cache = _ks().fill_cache(w, lens)
+    plan = kvq.kvq_plan(lay, 1, w.n_q_heads, L, 0, _ks().n_cu())
+    print(f"[decode] {name} L={L} plan {plan.n_splits} x {plan.chunk}", flush=True)
+    q = wl.queries(w)
+    got = _run(w, lay, cache, q, lens, 0)
+    want = _oracle_seq(w, 0, L, q[0], 0, 1 / 16)
+    e, at = _err(got[0], want)
+    print(f"{name} L={L} max abs err {e:.3g}")
+    assert e <= TOL
+
+
 def test_batched_ragged_sampled_sequences():
     w = wl.WORKLOADS["batched"]
     lens = wl.seq_lens(w)
