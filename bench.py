@@ -475,7 +475,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: this decode path has no multi-GPU mode "
-              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+              "(one GPU's share of a sharded step is this same kernel at its shape); use --gpus 1", file=sys.stderr)
         return 2
 
     import torch
