@@ -69,7 +69,7 @@ typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_NULL = -1,        /* a required pointer is NULL (scales of an int8 store included, [G11]) */
   KVQ_ERR_SHAPE = -2,       /* inconsistent sizes or strides */
-  KVQ_ERR_UNSUPPORTED = -3, /* a valid request this build does not implement (e.g. head_dim 96) */
+  KVQ_ERR_UNSUPPORTED = -3, /* a valid request this library does not implement (e.g. head_dim 96) */
   KVQ_ERR_ALIGN = -4,       /* a pointer or stride breaks the alignment the loads need */
   KVQ_ERR_WORKSPACE = -5,   /* workspace missing or smaller than kvq_plan_t.ws_bytes */
   KVQ_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
