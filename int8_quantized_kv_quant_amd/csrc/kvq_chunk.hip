@@ -125,8 +125,10 @@ __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a
   // would sit at or beyond max_ctx see nothing).
   const int hi_all = min(s0 + t_last + 1, a.max_ctx);
   const int lo_all = a.window > 0 ? max(0, s0 + t_first + 1 - a.window) : 0;
-  const int start = lo_all + split * a.chunk;
-  const int end = (split == a.n_splits - 1) ? hi_all : min(hi_all, start + a.chunk);
+  // split * chunk in 64 bits: the split's first key may lie far past hi_all
+  const int64_t start64 = (int64_t)lo_all + (int64_t)split * a.chunk;
+  const int start = (int)min(start64, (int64_t)hi_all);
+  const int end = (split == a.n_splits - 1) ? hi_all : (int)min((int64_t)hi_all, start64 + a.chunk);
 
   // Row block rb of this wavefront: flat rows fr0 + 16 * (RB * wv + rb) + c16.
   // The lane's row is the S^T column c16 and the O^T column c16.

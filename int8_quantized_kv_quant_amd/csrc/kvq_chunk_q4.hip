@@ -117,11 +117,6 @@ __device__ __forceinline__ void rotate_output_row(RowAcc<256>& acc, int lane) {
     for (int i = 0; i < 4; ++i) acc.o[mt][i] = x[4 * mt + i] * 0.0625f;
 }
 
-// Two codes (bytes 0, 1 or 2, 3 of a dword of code bytes) as the fp16
-// subnormals code * 2^-24 (exact).
-__device__ __forceinline__ uint32_t sub_h2_lo(uint32_t w) { return __builtin_amdgcn_perm(0u, w, 0x0c010c00u); }
-__device__ __forceinline__ uint32_t sub_h2_hi(uint32_t w) { return __builtin_amdgcn_perm(0u, w, 0x0c030c02u); }
-
 // fp16 element j of 8 packed values, widened.
 __device__ __forceinline__ float half8(const u32x4& w, int j) {
   const uint32_t d = w[j >> 1];
@@ -238,8 +233,10 @@ __global__ __launch_bounds__(kChunkWaves * 64, 2) void kvq_chunk_q4_kernel(Chunk
   s0 = s0 < 0 ? 0 : (s0 > a.max_ctx ? a.max_ctx : s0);
   const int hi_all = min(s0 + t_last + 1, a.max_ctx);
   const int lo_all = a.window > 0 ? max(0, s0 + t_first + 1 - a.window) : 0;
-  const int start = lo_all + split * a.chunk;
-  const int end = (split == a.n_splits - 1) ? hi_all : min(hi_all, start + a.chunk);
+  // split * chunk in 64 bits: the split's first key may lie far past hi_all
+  const int64_t start64 = (int64_t)lo_all + (int64_t)split * a.chunk;
+  const int start = (int)min(start64, (int64_t)hi_all);
+  const int end = (split == a.n_splits - 1) ? hi_all : (int)min((int64_t)hi_all, start64 + a.chunk);
 
   const int fr = fr0 + 16 * wv + c16;  // the lane's flat row t * G + h
   const int tok = fr / G;

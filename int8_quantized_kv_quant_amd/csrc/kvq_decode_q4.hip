@@ -12,14 +12,17 @@
 // with direct-to-LDS loads, one half refilling while the other is computed.
 //
 // Query. A q4 K store holds rotated keys, so the query rows are rotated the
-// same way in LDS (fwht256 in fp32, rounded to fp16) before any score; with
-// H / 16 orthonormal, q_rot . k_rot = q . k.
-// Keys (q4). One MFMA v_mfma_f32_16x16x32_f16 contracts one Q4_0 block (32
-// dims) of 16 positions. The A operand is the dequantized key K_hat =
-// fp16((code - 8) * d) of the lane's own position (its row of S^T), built from
-// the exact fp16 value 1024 + code (0x64 above the nibble, by byte permutes)
-// minus 1032 (exact) times the block scale (one rounding, as the values are),
-// so the eight blocks of a row accumulate in one MFMA chain.
+// same way in LDS (fwht256 in fp32) before any score; with H / 16 orthonormal,
+// q_rot . k_rot = q . k. The rotated rows are kept as hi + lo fp16 terms (22
+// significant bits), with their fp32 sums per Q4_0 block.
+// Keys (q4), exact scores. One pair of MFMAs v_mfma_f32_16x16x32_f16 contracts
+// one Q4_0 block (32 dims) of 16 positions with the hi and the lo query terms;
+// the codes enter as the fp16 subnormals code * 2^-24 (a byte permute, no
+// arithmetic), so every product is exact. Each block's fp32 result, less 8
+// times the query's block sum, is scaled by the position's fp16 block scale in
+// fp32: the key (code - 8) * d is never rounded. (Rounding the rotated query
+// and fp16((code - 8) * d) instead measured up to 2.0e-3 on short, peaked
+// contexts with 16 query heads per kv head.)
 // Keys (int8, k8v4): the int8 kernel's operands and scores, unrotated.
 // Values (q4). Lane (column c16) holds dims 16 c16 .. +15, i.e. the low
 // (c16 even) or high (c16 odd) nibbles of 16 bytes of block c16 / 2; after a
@@ -140,6 +143,10 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   constexpr int QROW = QOperand<SA>::ROW;
   __shared__ __attribute__((aligned(16))) uint8_t lds_st[NW * PITCH];
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[16 * QROW];
+  // q4 keys: the lo fp16 terms of the rotated query rows (lds_q holds the hi
+  // terms) and each row's fp32 sums over the 8 Q4_0 blocks.
+  __shared__ __attribute__((aligned(16))) uint8_t lds_ql[KQ4 ? 16 * QROW : 16];
+  __shared__ __attribute__((aligned(16))) float lds_qsum[16][8];
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
   // The new token's rows when the append is fused ([0] = K, [1] = V): the fp16
@@ -251,16 +258,31 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     *reinterpret_cast<float4*>(&nw_val[wv][4 * lane]) = val;
   }
   if constexpr (KQ4) {
-    // Rotate this wavefront's 4 query rows in place: lane l holds dims 4l .. 4l+3.
+    // Rotate this wavefront's 4 query rows: lane l holds dims 4l .. 4l+3. The
+    // hi terms replace the row in lds_q, the lo terms go to lds_ql, and lanes
+    // 8j hold the sum over block j (dims 32j .. 32j+31, lanes 8j .. 8j+7).
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint8_t* qr = lds_q + (wv * 4 + i) * QROW + 8 * lane;
+      const int r = wv * 4 + i;
+      uint8_t* qr = lds_q + r * QROW + 8 * lane;
       const u32x2 raw = *reinterpret_cast<const u32x2*>(qr);
       float v[4] = {h_bits_to_f32(raw.x & 0xffffu), h_bits_to_f32(raw.x >> 16), h_bits_to_f32(raw.y & 0xffffu),
                     h_bits_to_f32(raw.y >> 16)};
       fwht256(v, lane);
-      const f16x2 h01 = {(f16)v[0], (f16)v[1]}, h23 = {(f16)v[2], (f16)v[3]};
+      f16 hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = (f16)v[e];
+        lo[e] = (f16)(v[e] - (float)hi[e]);
+      }
+      const f16x2 h01 = {hi[0], hi[1]}, h23 = {hi[2], hi[3]}, l01 = {lo[0], lo[1]}, l23 = {lo[2], lo[3]};
       *reinterpret_cast<u32x2*>(qr) = (u32x2){as_u32(h01), as_u32(h23)};
+      *reinterpret_cast<u32x2*>(lds_ql + r * QROW + 8 * lane) = (u32x2){as_u32(l01), as_u32(l23)};
+      float bs = (v[0] + v[1]) + (v[2] + v[3]);
+      bs += __shfl_xor(bs, 1);
+      bs += __shfl_xor(bs, 2);
+      bs += __shfl_xor(bs, 4);
+      if ((lane & 7) == 0) lds_qsum[r][lane >> 3] = bs;
     }
   }
   __syncthreads();  // every query row in LDS (rotated for a q4 K store), the new rows quantized
@@ -268,26 +290,40 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   if (own_new && wv == 0) {
     // Scores of the new position for the 16 heads (rows beyond nh are zero):
     // lane 4h + r sums a quarter of the dims of head h.
+    // For q4 keys the query is the rotated row, hi + lo.
     const int h = lane >> 2, r = lane & 3;
     const uint16_t* qr = reinterpret_cast<const uint16_t*>(lds_q + h * QROW);
+    const uint16_t* qrl = reinterpret_cast<const uint16_t*>(lds_ql + (KQ4 ? h * QROW : 0));
     float zs = 0.0f;
 #pragma unroll 4
     for (int d = r * (D / 4); d < (r + 1) * (D / 4); d += 8) {
       const f16x8 qv = *reinterpret_cast<const f16x8*>(qr + d);
+      f16x8 ql = {};
+      if constexpr (KQ4) ql = *reinterpret_cast<const f16x8*>(qrl + d);
       const float4 k0 = *reinterpret_cast<const float4*>(&nw_val[0][d]);
       const float4 k1 = *reinterpret_cast<const float4*>(&nw_val[0][d + 4]);
-      zs = fmaf((float)qv[0], k0.x, zs); zs = fmaf((float)qv[1], k0.y, zs);
-      zs = fmaf((float)qv[2], k0.z, zs); zs = fmaf((float)qv[3], k0.w, zs);
-      zs = fmaf((float)qv[4], k1.x, zs); zs = fmaf((float)qv[5], k1.y, zs);
-      zs = fmaf((float)qv[6], k1.z, zs); zs = fmaf((float)qv[7], k1.w, zs);
+      const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zs = fmaf((float)qv[e] + (float)ql[e], kk[e], zs);
     }
     zs += __shfl_xor(zs, 1);
     zs += __shfl_xor(zs, 2);
     if (r == 0) nw_z[h] = zs * a.c2;  // read in the epilogue, after its barrier
   }
 
+  // ---- q4 keys: the -8 offset of the codes per block, in the units of the
+  // MFMA results (codes * 2^-24): qb[j] = -8 * 2^-24 * (block sum of row c16).
+  float qb[8];
+  if constexpr (KQ4) {
+    const float4 s0 = *reinterpret_cast<const float4*>(&lds_qsum[c16][0]);
+    const float4 s1 = *reinterpret_cast<const float4*>(&lds_qsum[c16][4]);
+    const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qb[j] = ss[j] * (-8.0f / 16777216.0f);
+  }
+  const float c2s = a.c2 * 16777216.0f;
   // ---- int8 keys: accumulator start values -1152 * (group sum of q) that
-  // cancel the code bias (q4 keys are dequantized into the operand instead).
+  // cancel the code bias.
   constexpr int NC = KQ4 ? 1 : SK::NG;
   float corr[NC];
   if constexpr (!KQ4) {
@@ -332,22 +368,23 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     if constexpr (KQ4) read_k_q4<KG64>(t, st, c16, q4);
     else read_k_i8<KG64>(t, st, c16, q4);
   };
+  // Tile n of this wavefront keeps its q4 K scale rows in half n & 1 of the K
+  // scale region until its scores are taken (the K half of tile n + 2 is
+  // issued after them).
+  int kpar = 0;
   if (p0 < end) {
     wait_vm<T::NV>();  // K half of the first tile landed (its V half may still be loading)
     read_k(tk);
-    if (p0 + STEP < end) issue_half<KQ4, KG64, 0>(st, krw, ksrw, p0 + STEP, end - p0 - STEP, krow, srow, lane);
+    if (p0 + STEP < end) issue_half<KQ4, KG64, 0>(st, krw, ksrw, p0 + STEP, end - p0 - STEP, krow, srow, lane, 1);
   }
-  for (; p0 < end; p0 += STEP) {
+  for (; p0 < end; p0 += STEP, kpar ^= 1) {
     const int pn = p0 + STEP;
     const bool more = pn < end;
     const bool more2 = pn + STEP < end;
     float z[2][4];
     if constexpr (KQ4) {
-      f16x8 qv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qv[j] = *reinterpret_cast<const f16x8*>(qrow + 64 * j + 16 * q4);
-      __builtin_amdgcn_sched_barrier(0);
-      scores_q4(tk, 0, end - p0, z, qv, a.c2, q4);
+      scores_q4(tk, 0, end - p0, z, st + T::KS_OFF + 512 * kpar, qrow + 16 * q4, lds_ql + c16 * QROW + 16 * q4, qb,
+                c2s, q4);
     } else {
       const uint8_t* qb = qrow + 32 * q4;
       f16x8 qv[4][2];
@@ -371,7 +408,7 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
       read_k(tk);
     }
     pv_q4<2>(tv, pa, acc);
-    if (more2) issue_half<KQ4, KG64, 0>(st, krw, ksrw, pn + STEP, end - pn - STEP, krow, srow, lane);
+    if (more2) issue_half<KQ4, KG64, 0>(st, krw, ksrw, pn + STEP, end - pn - STEP, krow, srow, lane, kpar);
   }
 
   // ---- merge the wavefronts: slots, one barrier, then wavefront w combines head

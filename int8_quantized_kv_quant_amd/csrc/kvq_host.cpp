@@ -277,6 +277,8 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
   if (!plan) return KVQ_ERR_NULL;
   if (plan->n_splits < 1 || plan->n_splits > kMaxSplits) return KVQ_ERR_SHAPE;
   if (plan->chunk < kTile || plan->chunk % kTile) return KVQ_ERR_SHAPE;
+  // Key positions of a split are 32-bit in the chunk kernels.
+  if ((int64_t)plan->n_splits * plan->chunk > (int64_t)INT_MAX) return KVQ_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)batch * n_tok;
   if (rows * n_q_heads > INT_MAX / 8 || (int64_t)L.n_kv_heads * chunk_row_blocks(n_tok, n_q_heads / L.n_kv_heads, L.head_dim) > 65535)
     return KVQ_ERR_UNSUPPORTED;  // grid limits

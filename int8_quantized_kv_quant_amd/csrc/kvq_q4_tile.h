@@ -18,7 +18,9 @@ namespace kvq {
 // Stage of one wavefront (bytes): K codes, V codes (128 bytes per q4 row),
 // K scale rows, V scale rows. Code rows hold their 16-byte chunk c at slot
 // c ^ swz(r); a scale region is 1 KiB for 16-byte rows (a 64-lane
-// direct-to-LDS load writes 16 bytes per lane, lanes past row 31 zeros).
+// direct-to-LDS load writes 16 bytes per lane, lanes past row 31 zeros). The
+// decode kernel splits the q4 K scale region into two 512-byte halves filled
+// by 32 lanes each, for tiles of even and odd index.
 template <bool KQ4, bool KG64>
 struct Q4Stage {
   static constexpr int D = 256;
@@ -63,11 +65,15 @@ __device__ __forceinline__ void issue_codes(uint32_t lds, const u32x4& rs, uint3
 }
 
 // Direct-to-LDS load of the scale rows (SB bytes each) of a 32-row tile.
-template <int SB, bool NT = false>
+// HALF32 (16-byte rows only): lanes 32..63 write nothing, so the load fills
+// exactly 512 bytes.
+template <int SB, bool NT = false, bool HALF32 = false>
 __device__ __forceinline__ void issue_scales(uint32_t lds, const u32x4& rs, uint32_t soff, int nvalid, uint32_t srow,
                                              int lane) {
   const int nv = nvalid < kTile ? nvalid : kTile;
-  if constexpr (SB == 16) {  // lane l = row l, 16 bytes at 16 l
+  if constexpr (SB == 16 && HALF32) {
+    if (lane < 32) dma<16, NT>(rs, lds, lane < nv ? (uint32_t)lane * srow : kOOB, soff);
+  } else if constexpr (SB == 16) {  // lane l = row l, 16 bytes at 16 l
     dma<16, NT>(rs, lds, lane < nv ? (uint32_t)lane * srow : kOOB, soff);
   } else if constexpr (SB == 8) {  // two lanes per row, 8 bytes at 8 r
     const int r = lane >> 1;
@@ -80,10 +86,11 @@ __device__ __forceinline__ void issue_scales(uint32_t lds, const u32x4& rs, uint
 
 // Fill the K half (HALF = 0) or the V half (HALF = 1) of a stage with the tile
 // at position p0. The half's previous contents were read by this wavefront:
-// those LDS reads complete before new data can land.
+// those LDS reads complete before new data can land. For q4 keys the scale
+// rows go to the 512-byte half `kpar` of the K scale region.
 template <bool KQ4, bool KG64, int HALF>
 __device__ __forceinline__ void issue_half(uint8_t* st, const u32x4& rs, const u32x4& srs, int p0, int nvalid,
-                                           uint32_t row, uint32_t srow, int lane) {
+                                           uint32_t row, uint32_t srow, int lane, int kpar = 0) {
   using T = Q4Stage<KQ4, KG64>;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   const uint32_t base = lds_addr_of(st);
@@ -91,7 +98,10 @@ __device__ __forceinline__ void issue_half(uint8_t* st, const u32x4& rs, const u
   const uint32_t ssoff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * srow);
   if constexpr (HALF == 0) {
     issue_codes<T::KRB, kNtCodes>(base + T::K_OFF, rs, soff, nvalid, row, lane);
-    issue_scales<T::KSB, kNtScales>(base + T::KS_OFF, srs, ssoff, nvalid, srow, lane);
+    if constexpr (KQ4)
+      issue_scales<T::KSB, kNtScales, true>(base + T::KS_OFF + 512 * kpar, srs, ssoff, nvalid, srow, lane);
+    else
+      issue_scales<T::KSB, kNtScales>(base + T::KS_OFF, srs, ssoff, nvalid, srow, lane);
   } else {
     issue_codes<T::VRB, kNtCodes>(base + T::V_OFF, rs, soff, nvalid, row, lane);
     issue_scales<16, kNtScales>(base + T::VS_OFF, srs, ssoff, nvalid, srow, lane);
@@ -99,12 +109,16 @@ __device__ __forceinline__ void issue_half(uint8_t* st, const u32x4& rs, const u
 }
 
 // ---- keys ---------------------------------------------------------------------------
-// q4 K operands of one tile for lane (c16, q4): k[ct][j] = bytes 8 (q4 & 1) .. +7
+// Two codes (bytes 0, 1 or 2, 3 of a dword of code bytes) as the fp16
+// subnormals code * 2^-24 (exact: the matrix cores take subnormal inputs).
+__device__ __forceinline__ uint32_t sub_h2_lo(uint32_t w) { return __builtin_amdgcn_perm(0u, w, 0x0c010c00u); }
+__device__ __forceinline__ uint32_t sub_h2_hi(uint32_t w) { return __builtin_amdgcn_perm(0u, w, 0x0c030c02u); }
+
+// q4 K codes of one tile for lane (c16, q4): k[ct][j] = bytes 8 (q4 & 1) .. +7
 // of block j of row 16 ct + c16 (dims 32 j + 8 q4 .. +7 after the nibble
-// select); ks[ct] = the 8 block scales of that row's position.
+// select). The tile's scale rows stay in LDS until its scores are taken.
 struct KQ4Regs {
   u32x2 k[2][8];
-  u32x4 ks[2];
 };
 
 template <bool KG64>
@@ -116,44 +130,67 @@ __device__ __forceinline__ void read_k_q4(KQ4Regs& t, const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       t.k[ct][j] = *reinterpret_cast<const u32x2*>(st + T::K_OFF + r * T::KRB + 16 * (j ^ swz<8>(r)) + 8 * (q4 & 1));
-    t.ks[ct] = *reinterpret_cast<const u32x4*>(st + T::KS_OFF + r * 16);
   }
 }
 
 constexpr uint32_t kQ4NegBias = 0xE408E408u;  // fp16 pair (-1032, -1032)
 
-// Scores of a q4 K tile: z[ct][i] for positions x = 16 ct + 4 q4 + i of query
-// row c16 (log2 domain); positions outside [vlo, vhi) get -inf (the bounds may
-// differ per lane: per query row). qv[j] = the rotated query's dims
-// 32 j + 8 q4 .. +7 (fp16).
-__device__ __forceinline__ void scores_q4(const KQ4Regs& t, int vlo, int vhi, float (&z)[2][4], const f16x8 (&qv)[8],
-                                          float c2, int q4) {
+// Exact scores of a q4 K tile: z[ct][i] for positions x = 16 ct + 4 q4 + i of
+// query row c16 (log2 domain); positions outside [vlo, vhi) get -inf.
+// ks = the tile's 32 scale rows (16 bytes: the 8 block scales, fp16) in LDS;
+// qh + 64 j and ql + 64 j (LDS, 16 bytes each) hold the rotated query's dims
+// 32 j + 8 q4 .. +7 as hi and lo fp16 terms; qb[j] = -8 * 2^-24 * (sum of the
+// rotated query over block j) of row c16; c2s = sm_scale * log2(e) * 2^24.
+// With the codes entering the MFMA as code * 2^-24, block j gives
+// a_j = 2^-24 * sum_d code_d q_d (exact products, fp32 sums), and
+//   z = c2s * sum_j d_j * (a_j + qb[j])  =  c2 * sum_j d_j sum_d (code_d - 8) q_d,
+// the dequantized key (code - 8) * d taken without rounding. The query terms
+// are read block pair by block pair, so only two blocks' operands are live.
+__device__ __forceinline__ void scores_q4(const KQ4Regs& t, int vlo, int vhi, float (&z)[2][4],
+                                          const uint8_t* __restrict__ ks, const uint8_t* __restrict__ qh,
+                                          const uint8_t* __restrict__ ql, const float (&qb)[8], float c2s, int q4) {
   const uint32_t sh = 4u * (uint32_t)(q4 >> 1);  // q4 = 2, 3: the high nibbles (dims 16..31 of the block)
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  u32x4 ps[2][4];  // the 8 block scales of row 16 ct + 4 q4 + i: the position of score z[ct][i]
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    f32x4 zz = {0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w0 = (t.k[ct][j].x >> sh) & 0x0F0F0F0Fu;
-      const uint32_t w1 = (t.k[ct][j].y >> sh) & 0x0F0F0F0Fu;
-      const uint32_t sw = t.ks[ct][j >> 1];
-      const f16x2 sp = as_h2(sw);
-      const f16x2 d2 = (j & 1) ? sp.yy : sp.xx;  // (d_j, d_j): an operand select of the packed multiply
-      u32x4 a4;
+    for (int i = 0; i < 4; ++i) ps[ct][i] = *reinterpret_cast<const u32x4*>(ks + (16 * ct + 4 * q4 + i) * 16);
+  f32x4 zz[2] = {zero, zero};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = e < 2 ? w0 : w1;
-        const uint32_t biased = (e & 1) ? biased_h2_hi(w) : biased_h2_lo(w);  // 1024 + code
-        a4[e] = as_u32((as_h2(biased) + as_h2(kQ4NegBias)) * d2);           // fp16((code - 8) * d)
-      }
-      zz = mfma16(__builtin_bit_cast(f16x8, a4), qv[j], zz);
+  for (int jp = 0; jp < 4; ++jp) {
+    f16x8 h[2], l[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      h[u] = *reinterpret_cast<const f16x8*>(qh + 64 * (2 * jp + u));
+      l[u] = *reinterpret_cast<const f16x8*>(ql + 64 * (2 * jp + u));
     }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = 2 * jp + u;
+        const uint32_t w0 = (t.k[ct][j].x >> sh) & 0x0F0F0F0Fu;
+        const uint32_t w1 = (t.k[ct][j].y >> sh) & 0x0F0F0F0Fu;
+        const u32x4 a4 = {sub_h2_lo(w0), sub_h2_hi(w0), sub_h2_lo(w1), sub_h2_hi(w1)};  // code * 2^-24
+        f32x4 a = mfma16(__builtin_bit_cast(f16x8, a4), h[u], zero);
+        a = mfma16(__builtin_bit_cast(f16x8, a4), l[u], a);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t sw = ps[ct][i][j >> 1];
+          const f16 d = __builtin_bit_cast(f16x2, sw)[j & 1];
+          zz[ct][i] = fmaf(a[i] + qb[j], (float)d, zz[ct][i]);
+        }
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int x = 16 * ct + 4 * q4 + i;
-      z[ct][i] = (x >= vlo && x < vhi) ? zz[i] * c2 : -INFINITY;
+      z[ct][i] = (x >= vlo && x < vhi) ? zz[ct][i] * c2s : -INFINITY;
     }
-  }
 }
 
 // int8 K operands (k8v4) from this stage layout, as stage_read_k reads them.

@@ -1,5 +1,6 @@
 """A decode step (quantize-append + split-K partials + reduce) captured in a HIP
-graph gives, on every replay, exactly the output of the same step run eagerly.
+graph gives, on every replay, the oracle's output at the replay's context
+(within 2e-3) and exactly the output of the same step run eagerly.
 
 genie-ai-runtime releases, v1.3.0 "Details": the graph-captured decode bakes the
 split count at capture and reads positions from device memory; here the context
@@ -11,9 +12,21 @@ import numpy as np
 import pytest
 
 import workloads as wl
+from oracle import kvq_oracle as orc
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
+
+
+TOL = 2e-3
+
+
+def _oracle(w, L, q_b, sm):
+    """fp64 oracle output [n_q][d] of sequence 0 at context L (window of w)."""
+    lo = max(0, L - w.window) if w.window else 0
+    cache = orc.Cache(1, L, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+    cache.append(wl.kv_rows(w, "k", 0, lo, L - lo)[None], wl.kv_rows(w, "v", 0, lo, L - lo)[None], [lo])
+    return orc.attend(q_b[None], cache, [L], w.window, sm)[0]
 
 
 def test_graph_replays_match_eager_steps():
@@ -59,6 +72,8 @@ def test_graph_replays_match_eager_steps():
         g.replay()
         torch.cuda.synchronize()
         got = out.clone()
+        e = float(np.abs(got[0].cpu().numpy().astype(np.float64) - _oracle(w, L, wl.queries(w)[0], sm)).max())
+        assert e <= TOL, f"graph replay at L={L}: max abs err {e:.3g} against the oracle"
         out.zero_()
         step()  # the same step eagerly (re-appends the same token: idempotent)
         torch.cuda.synchronize()

@@ -310,3 +310,82 @@ def test_q4_fused_new_row_alone_and_on_a_split_boundary(name):
         want = _oracle_seq(w, b, int(lens[b]), q[b], 0, 1 / 16)
         assert np.abs(out_b[b] - want).max() <= TOL, b
     assert not out_b[2].any()
+
+
+# ---- short, peaked contexts at 16 query heads per kv head -------------------------------
+# The chunk case q4_batch_g16 (two sequences of the long-context 4-bit layouts
+# with x20 outlier K channels, 32 query / 2 kv heads, chunks of 33 tokens at
+# positions 100 and 600) run token by token as decode queries: token t of
+# sequence b is the query of a context of start_b + t + 1 positions, so the
+# contexts are 101..133 and 601..633. Few keys and peaked softmax rows are
+# where the rounding of scores is least averaged out.
+
+_G16_STARTS = (100, 600)
+_G16_TOKENS = 33
+
+
+def _g16_workload(name):
+    return wl.WORKLOADS[name].with_(batch=2, n_q_heads=32, max_ctx=1024)
+
+
+def _g16_oracle(w, qs):
+    """fp64 oracle outputs [t][b][32][256] at contexts start_b + t + 1."""
+    out = np.zeros((_G16_TOKENS, 2, 32, 256))
+    for b, s in enumerate(_G16_STARTS):
+        for t in range(_G16_TOKENS):
+            out[t, b] = _oracle_seq(w, b, s + t + 1, qs[b, t], 0, 1 / 16)
+    return out
+
+
+@pytest.mark.parametrize("name", ["long_q4", "long_k8v4"])
+def test_q4_decode_short_peaked_contexts_g16(name):
+    """kv_decode_attn_splitk + kv_decode_reduce at every context 101..133 and
+    601..633, with the planner's plan and with 32-position splits, element by
+    element within 2e-3 of the oracle."""
+    import int8_quantized_kv_quant_amd as kvq
+    w = _g16_workload(name)
+    ends = np.array([s + _G16_TOKENS for s in _G16_STARTS])
+    print(f"[q4 decode g16] {name} contexts 101..133, 601..633", flush=True)
+    lay, cache = _setup().fill_cache(w, ends)
+    qs = wl.chunk_queries(w, _G16_TOKENS)
+    want = _g16_oracle(w, qs)
+    worst = 0.0
+    for plan in (None, kvq.Plan(20, 32, 2 * 32 * 20 * 258 * 4)):
+        for t in range(_G16_TOKENS):
+            lens = [s + t + 1 for s in _G16_STARTS]
+            got = _run(w, lay, cache, np.ascontiguousarray(qs[:, t]), lens, 0, plan=plan)
+            e = float(np.abs(got - want[t]).max())
+            worst = max(worst, e)
+            assert e <= TOL, (name, "planner" if plan is None else "32-position splits", lens, e)
+    print(f"[q4 decode g16] {name} max abs err {worst:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["long_q4", "long_k8v4"])
+def test_q4_fused_short_peaked_contexts_g16(name):
+    """The fused step (kv_append_decode_splitk) token after token: each step
+    appends the row at start_b + t and attends at context start_b + t + 1;
+    every output within 2e-3 of the oracle, and the rows it appended equal the
+    oracle's quantization."""
+    import int8_quantized_kv_quant_amd as kvq
+    ks = _setup()
+    w = _g16_workload(name)
+    print(f"[q4 fused g16] {name} contexts 101..133, 601..633", flush=True)
+    lay, cache = ks.fill_cache(w, np.array(_G16_STARTS))
+    qs = wl.chunk_queries(w, _G16_TOKENS)
+    want = _g16_oracle(w, qs)
+    worst = 0.0
+    for t in range(_G16_TOKENS):
+        lens = np.array([s + t + 1 for s in _G16_STARTS], dtype=np.int32)
+        kn = np.stack([wl.kv_rows(w, "k", b, s + t, 1)[0] for b, s in enumerate(_G16_STARTS)])
+        vn = np.stack([wl.kv_rows(w, "v", b, s + t, 1)[0] for b, s in enumerate(_G16_STARTS)])
+        out = kvq.decode(lay, cache, torch.from_numpy(np.ascontiguousarray(qs[:, t])).cuda(),
+                         torch.from_numpy(lens).cuda(), 0, 1 / 16, n_cu=ks.n_cu(),
+                         new_kv=(torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda()))
+        torch.cuda.synchronize()
+        e = float(np.abs(out.cpu().numpy().astype(np.float64) - want[t]).max())
+        worst = max(worst, e)
+        assert e <= TOL, (name, lens.tolist(), e)
+    print(f"[q4 fused g16] {name} max abs err {worst:.3g}", flush=True)
+    for b, s in enumerate(_G16_STARTS):
+        pos = np.arange(s, s + _G16_TOKENS)
+        _check(lay, cache, w, b, pos, wl.kv_rows(w, "k", b, s, _G16_TOKENS), wl.kv_rows(w, "v", b, s, _G16_TOKENS))

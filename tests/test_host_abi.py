@@ -197,6 +197,9 @@ def test_chunk_attention_refusals():
     assert _chunk(lay, n_tok=-1) == SHAPE
     assert _chunk(lay, window=-1) == SHAPE
     assert _chunk(lay, plan=kvq.Plan(2, 100, 10 ** 9)) == SHAPE
+    # split starts past 2^31 key positions (n_splits * chunk) are refused, not wrapped
+    assert _chunk(lay, plan=kvq.Plan(4, 1 << 30, 10 ** 12)) == UNSUP
+    assert _chunk(lay, plan=kvq.Plan(2, (1 << 30) + 32, 10 ** 12)) == UNSUP
     assert _chunk(lay, plan=kvq.Plan(2, 256, 1000)) == WS           # smaller than the partials
     assert _chunk(lay, ws_bytes=16) == WS
     assert _chunk(lay, ws=None) == WS
