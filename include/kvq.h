@@ -10,6 +10,9 @@
  *   kv_append_decode_splitk  the decode step's one-token quantize-append fused
  *                          into kv_decode_attn_splitk
  *   kv_decode_reduce       combine the split partials into the fp16 output
+ *   kv_decode_attn_static  partials + combine in one call, with the partials
+ *                          in the library's static device scratch (no
+ *                          workspace, no allocation)
  *   kv_chunk_attn          attention of a chunk of consecutive query tokens per
  *                          sequence (prompt chunk, verify window): causal
  *                          inside the chunk, partials + combine in one call
@@ -73,7 +76,8 @@ typedef enum {
   KVQ_ERR_ALIGN = -4,       /* a pointer or stride breaks the alignment the loads need */
   KVQ_ERR_WORKSPACE = -5,   /* workspace missing or smaller than kvq_plan_t.ws_bytes */
   KVQ_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
-  KVQ_ERR_MISMATCH = -7     /* a cache blob whose layout facts differ from the target cache's */
+  KVQ_ERR_MISMATCH = -7,    /* a cache blob whose layout facts differ from the target cache's */
+  KVQ_ERR_SCRATCH = -8      /* the partials exceed the static scratch of kv_decode_attn_static */
 } kvq_status;
 
 /* Store element types ([S2698]: fp32 = the unquantized store; q4 = the 4-bit
@@ -247,6 +251,30 @@ int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,
                      const int32_t* d_seq_lens, int32_t batch, int32_t n_q_heads,
                      int32_t window, const kvq_plan_t* plan, uint16_t* out,
                      void* stream);
+
+/* kv_decode_attn_static -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): kv_decode_attn_splitk followed by kv_decode_reduce, with the
+ * split partials kept in a device array of the library instead of a caller
+ * workspace. Nothing is allocated by the call: the array is a fixed part of
+ * the library on each device (KVQ_STATIC_SCRATCH_BYTES, held until the
+ * process ends); the first call on a device looks up its address there.
+ *   Arguments as for kv_decode_attn_splitk (no ws, ws_bytes) and
+ *   out  fp16 [batch][n_q_heads][head_dim], contiguous, 16-byte aligned.
+ * The output is that of kv_decode_attn_splitk + kv_decode_reduce with the same
+ * plan. Returns KVQ_ERR_SCRATCH, with nothing enqueued, when the plan's
+ * partials (plan->ws_bytes) exceed KVQ_STATIC_SCRATCH_BYTES; the other errors
+ * as kv_decode_attn_splitk. No part of the scratch needs to start at zero.
+ * All calls on one device share the array: calls that overlap on a device
+ * (two streams, or two host threads, without ordering between them) race and
+ * give undefined output. */
+#define KVQ_STATIC_SCRATCH_BYTES (16ll << 20) /* 16 MiB per device */
+int kv_decode_attn_static(const kvq_layout* layout,
+                          const void* k_store, const void* v_store,
+                          const uint16_t* k_scales, const uint16_t* v_scales,
+                          const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                          const int32_t* d_seq_lens, int32_t window, float sm_scale,
+                          const kvq_plan_t* plan, uint16_t* out, void* stream);
 
 /* kvq_plan_chunk -- host only, no device call. Split plan of kv_chunk_attn
  * for `batch` sequences of `n_tok` query tokens whose last token sits below

@@ -20,6 +20,7 @@ __all__ = [
     "lib_path", "load", "kvq_version", "kvq_status_string", "kvq_plan", "kv_quant_append",
     "kv_decode_attn_splitk", "kv_append_decode_splitk", "kv_decode_reduce", "kvq_plan_chunk",
     "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack", "kv_cache_unpack", "kvq_stream_read", "BlobHeader",
+    "kv_decode_attn_static", "STATIC_SCRATCH_BYTES",
     "make_layout",
     "alloc_cache", "decode", "chunk_attn",
     "EXPORTED_SYMBOLS",
@@ -33,7 +34,11 @@ Q4_BLOCK = 32  # values per Q4_0 block (one fp16 scale each)
 
 EXPORTED_SYMBOLS = ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
                     "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack",
-                    "kv_cache_unpack", "kvq_stream_read", "kvq_status_string", "kvq_version")
+                    "kv_cache_unpack", "kvq_stream_read", "kvq_status_string", "kvq_version",
+                    "kv_decode_attn_static")
+
+# Bytes of the library's static device scratch (KVQ_STATIC_SCRATCH_BYTES).
+STATIC_SCRATCH_BYTES = 16 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -127,6 +132,7 @@ def load():
     lib.kv_append_decode_splitk.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, f32, PP, vp,
                                             i64, vp]
     lib.kv_decode_reduce.argtypes = [LP, vp, i64, vp, i32, i32, i32, PP, vp, vp]
+    lib.kv_decode_attn_static.argtypes = [LP, vp, vp, vp, vp, vp, i32, i32, vp, i32, f32, PP, vp, vp]
     lib.kvq_plan_chunk.argtypes = [LP, i32, i32, i32, i32, i32, i32, PP]
     HP = ctypes.POINTER(BlobHeader)
     lib.kvq_blob_size.argtypes = [LP, i32, ctypes.POINTER(i64)]
@@ -139,7 +145,7 @@ def load():
     lib.kvq_version.argtypes = []
     for fn in ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
                "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack",
-               "kv_cache_unpack", "kvq_stream_read", "kvq_version"):
+               "kv_cache_unpack", "kvq_stream_read", "kvq_version", "kv_decode_attn_static"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -216,6 +222,15 @@ def kv_decode_reduce(layout: Layout, ws, ws_bytes: int, seq_lens, batch: int, n_
     _check("kv_decode_reduce", load().kv_decode_reduce(
         ctypes.byref(layout.c()), _ptr(ws), ws_bytes, _ptr(seq_lens), batch, n_q_heads, window,
         ctypes.byref(plan.c()), _ptr(out), _stream(stream)))
+
+
+def kv_decode_attn_static(layout: Layout, k_store, v_store, k_scales, v_scales, q, batch: int, n_q_heads: int,
+                          seq_lens, window: int, sm_scale: float, plan: Plan, out, stream=None) -> None:
+    """Partials + combine with the partials in the library's static scratch
+    (no workspace argument; nothing allocated)."""
+    _check("kv_decode_attn_static", load().kv_decode_attn_static(
+        ctypes.byref(layout.c()), _ptr(k_store), _ptr(v_store), _ptr(k_scales), _ptr(v_scales), _ptr(q), batch,
+        n_q_heads, _ptr(seq_lens), window, sm_scale, ctypes.byref(plan.c()), _ptr(out), _stream(stream)))
 
 
 def kvq_plan_chunk(layout: Layout, batch: int, n_tok: int, n_q_heads: int, max_seq_len: int, window: int,

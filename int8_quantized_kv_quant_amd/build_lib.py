@@ -26,7 +26,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 
 SOURCES = ["kvq_host.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_q4.hip", "kvq_reduce.hip", "kvq_chunk.hip",
-           "kvq_chunk_q4.hip", "kvq_blob.hip", "kvq_stream.hip"]
+           "kvq_chunk_q4.hip", "kvq_blob.hip", "kvq_stream.hip", "kvq_static.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
           "-I" + os.path.join(ROOT, "include")]

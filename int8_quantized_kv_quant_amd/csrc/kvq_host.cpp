@@ -103,6 +103,7 @@ const char* kvq_status_string(int s) {
     case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
     case KVQ_ERR_HIP: return "HIP runtime error at launch";
     case KVQ_ERR_MISMATCH: return "cache blob does not match the cache layout (store types, scale group, heads)";
+    case KVQ_ERR_SCRATCH: return "split partials exceed the library's static scratch (16 MiB)";
     default: return "unknown status";
   }
 }
@@ -201,6 +202,36 @@ int kv_decode_attn_splitk(const kvq_layout* layout, const void* k_store, const v
                              d_seq_lens, window, sm_scale, *plan, ws, stream);
   return launch_partial(L, k_store, v_store, k_scales, v_scales, nullptr, nullptr, q, batch, n_q_heads,
                         d_seq_lens, window, sm_scale, *plan, ws, stream);
+}
+
+int kv_decode_attn_static(const kvq_layout* layout, const void* k_store, const void* v_store,
+                          const uint16_t* k_scales, const uint16_t* v_scales, const uint16_t* q, int32_t batch,
+                          int32_t n_q_heads, const int32_t* d_seq_lens, int32_t window, float sm_scale,
+                          const kvq_plan_t* plan, uint16_t* out, void* stream) {
+  int st = check_layout(layout);
+  if (st) return st;
+  const kvq_layout& L = *layout;
+  if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
+  if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
+  if ((st = check_heads(L, batch, n_q_heads))) return st;
+  if (!plan) return KVQ_ERR_NULL;
+  if (plan->n_splits < 1 || plan->n_splits > kMaxSplits) return KVQ_ERR_SHAPE;
+  if (plan->chunk < kTile || plan->chunk % kTile) return KVQ_ERR_SHAPE;
+  if (workspace_bytes(batch, n_q_heads, plan->n_splits, L.head_dim) > kStaticScratchBytes) return KVQ_ERR_SCRATCH;
+  if (!q || !d_seq_lens || !out) return KVQ_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(d_seq_lens, 4) || !aligned(out, 16)) return KVQ_ERR_ALIGN;
+  if (window < 0) return KVQ_ERR_SHAPE;
+  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return KVQ_ERR_SHAPE;
+  if (has_q4(L) && !q4_decode_supported(L)) return KVQ_ERR_UNSUPPORTED;
+  if (batch == 0) return KVQ_OK;
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws))) return st;
+  st = has_q4(L) ? launch_partial_q4(L, k_store, v_store, k_scales, v_scales, nullptr, nullptr, q, batch, n_q_heads,
+                                     d_seq_lens, window, sm_scale, *plan, ws, stream)
+                 : launch_partial(L, k_store, v_store, k_scales, v_scales, nullptr, nullptr, q, batch, n_q_heads,
+                                  d_seq_lens, window, sm_scale, *plan, ws, stream);
+  if (st) return st;
+  return launch_reduce(L, ws, batch, n_q_heads, *plan, out, stream);
 }
 
 int kv_append_decode_splitk(const kvq_layout* layout, void* k_store, void* v_store, uint16_t* k_scales,

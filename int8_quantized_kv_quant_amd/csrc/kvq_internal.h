@@ -99,6 +99,13 @@ inline int64_t workspace_bytes(int64_t batch, int64_t n_q, int64_t n_splits, int
   return batch * n_q * n_splits * (head_dim + 2) * 4;
 }
 
+// Bytes of the library's static device scratch (kv_decode_attn_static).
+constexpr int64_t kStaticScratchBytes = KVQ_STATIC_SCRATCH_BYTES;
+
+// The device address of the static scratch on the current device (looked up
+// once per device, kvq_static.hip). Returns KVQ_OK or KVQ_ERR_HIP.
+int static_scratch(void** out);
+
 // Kernel launchers (defined in the .hip files). They assume validated input.
 int launch_append(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k_scales,
                   uint16_t* v_scales, const uint16_t* k_new, const uint16_t* v_new,

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_status_strings_and_version():
     assert kvq.kvq_status_string(0) == "ok"
-    for st in range(-7, 0):
+    for st in range(-8, 0):
         assert kvq.kvq_status_string(st) != "unknown status"
     assert kvq.kvq_status_string(-99) == "unknown status"
     assert kvq.kvq_version() > 0
@@ -114,6 +114,17 @@ def _partial(lay, plan=None, **kw):
         ctypes.byref(plan.c()), args["ws"], args["ws_bytes"], None)
 
 
+def _static(lay, plan=None, **kw):
+    plan = plan or kvq.Plan(4, 256, 1 * 16 * 4 * 258 * 4)
+    args = dict(k_store=FAKE, v_store=FAKE, k_scales=FAKE, v_scales=FAKE, q=FAKE, batch=1, n_q=16,
+                seq_lens=FAKE, window=0, sm=0.0625, out=FAKE)
+    args.update(kw)
+    return kvq.load().kv_decode_attn_static(
+        ctypes.byref(lay.c()), args["k_store"], args["v_store"], args["k_scales"], args["v_scales"],
+        args["q"], args["batch"], args["n_q"], args["seq_lens"], args["window"], args["sm"],
+        ctypes.byref(plan.c()), args["out"], None)
+
+
 def _fused(lay, plan=None, **kw):
     plan = plan or kvq.Plan(4, 256, 1 * 16 * 4 * 258 * 4)
     args = dict(k_store=FAKE, v_store=FAKE, k_scales=FAKE, v_scales=FAKE, k_new=FAKE, v_new=FAKE, q=FAKE,
@@ -167,6 +178,27 @@ def test_null_scale_pointer_is_refused_not_read_as_one():
     assert _partial(mixed, v_scales=None, k_scales=None) == NULL_
     assert _fused(lay, k_scales=None) == NULL_
     assert _fused(lay, v_scales=None) == NULL_
+
+
+@needs_lib
+def test_static_entry_refuses_before_any_device_call():
+    """kv_decode_attn_static validates like kv_decode_attn_splitk and refuses
+    plans whose partials exceed the static scratch (KVQ_ERR_SCRATCH = -8)."""
+    lay = _base()
+    assert _static(lay, k_scales=None) == NULL_
+    assert _static(lay, q=None) == NULL_
+    assert _static(lay, out=None) == NULL_
+    assert _static(lay, seq_lens=None) == NULL_
+    assert _static(lay, out=FAKE + 2) == ALIGN
+    assert _static(lay, n_q=15) == SHAPE
+    assert _static(lay, window=-1) == SHAPE
+    assert _static(lay, plan=kvq.Plan(2, 100, 0)) == SHAPE
+    # 16 heads x 1017 splits x 258 floats x 4 B > 16 MiB; 1016 splits fit
+    assert 16 * 1016 * 258 * 4 <= kvq.STATIC_SCRATCH_BYTES < 16 * 1017 * 258 * 4
+    assert _static(lay, plan=kvq.Plan(1017, 128, 0)) == -8
+    assert _static(lay, plan=kvq.Plan(1016, 128, 0), q=None) == NULL_
+    assert _static(lay, batch=0) == 0
+    assert kvq.kvq_status_string(-8) != "unknown status"
 
 
 @needs_lib
