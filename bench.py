@@ -211,39 +211,12 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
         lay, c0 = kvq_setup.fill_cache(w, lens)
         kr = torch.from_numpy(wl.kv_rows(w, "k", 0, w.prefill, w.append)).to(dev)
         vr = torch.from_numpy(wl.kv_rows(w, "v", 0, w.prefill, w.append)).to(dev)
-        sp = torch.tensor([w.prefill], dtype=torch.int32, device=dev)
-        before = {k: (None if t is None else t.clone()) for k, t in c0.items()}
-
-        def append():
-            kvq.kv_quant_append(lay, c0["k"], c0["v"], c0["k_scales"], c0["v_scales"], kr, vr, sp, 1, w.append)
-
-        append()
-        torch.cuda.synchronize()
-        same = all(t is None or torch.equal(t.view(torch.uint8), c0[k].view(torch.uint8)) for k, t in before.items())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            append()
-        g.replay()
-        torch.cuda.synchronize()
-        reps = 20
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        app_us = e0.elapsed_time(e1) * 1e3 / reps
-        # fp16 rows in; int8 codes + fp16 scales of one store, fp32 values of the other out
-        n_rows = w.append * w.n_kv_heads
-        app_bytes = n_rows * (2 * 2 * w.head_dim + w.head_dim + 2 * w.n_groups + 4 * w.head_dim)
-        del g, before
+        app = append_chunk_timing(kvq, wl, w, lay, c0)
         caches = [c0] + [{k: (None if t is None else t.clone()) for k, t in c0.items()} for _ in range(COPIES - 1)]
         k_new = torch.from_numpy(wl.kv_rows(w, "k", 0, L - 1, 1)).to(dev)
         v_new = torch.from_numpy(wl.kv_rows(w, "v", 0, L - 1, 1)).to(dev)
         res[name] = {"k_store": w.k_dtype, "v_store": w.v_dtype, "context": L, "cache_copies": COPIES,
-                     "append_tokens": w.append, "append_at": w.prefill, "append_us": round(app_us, 2),
-                     "append_bytes": int(app_bytes), "append_GB_s": round(app_bytes / app_us / 1e3, 1),
-                     "append_rewrite_bitexact": bool(same), **timed(w, lens, lay, caches, k_new, v_new)}
+                     **app, **timed(w, lens, lay, caches, k_new, v_new)}
         del caches, c0
         torch.cuda.empty_cache()
 
@@ -266,6 +239,51 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
     del cache
     torch.cuda.empty_cache()
     return res
+
+
+def append_chunk_timing(kvq, wl, w, lay, c0, reps=25):
+    """kv_quant_append of the mixed workload's chunk (w.append tokens at
+    position w.prefill, both kv heads) into the cache c0, which already holds
+    those rows: the rewrite must leave it bit-identical (checked). Timed as
+    graphs of COPIES back-to-back appends (one graph launch per COPIES kernels,
+    so the host's launch rate does not bound the figure)."""
+    import torch
+    dev = c0["k"].device
+    kr = torch.from_numpy(wl.kv_rows(w, "k", 0, w.prefill, w.append)).to(dev)
+    vr = torch.from_numpy(wl.kv_rows(w, "v", 0, w.prefill, w.append)).to(dev)
+    sp = torch.tensor([w.prefill], dtype=torch.int32, device=dev)
+    before = {k: (None if t is None else t.clone()) for k, t in c0.items()}
+
+    def append():
+        kvq.kv_quant_append(lay, c0["k"], c0["v"], c0["k_scales"], c0["v_scales"], kr, vr, sp, 1, w.append)
+
+    append()
+    torch.cuda.synchronize()
+    same = all(t is None or torch.equal(t.view(torch.uint8), c0[k].view(torch.uint8)) for k, t in before.items())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(COPIES):
+            append()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    app_us = e0.elapsed_time(e1) * 1e3 / (reps * COPIES)
+    same = same and all(t is None or torch.equal(t.view(torch.uint8), c0[k].view(torch.uint8))
+                        for k, t in before.items())
+    # fp16 rows in; per store int8 codes + fp16 scales, or fp32 values, out
+    n_rows = w.append * w.n_kv_heads
+    out_b = sum(w.head_dim + 2 * w.n_groups if dt == "int8" else 4 * w.head_dim for dt in (w.k_dtype, w.v_dtype))
+    app_bytes = n_rows * (2 * 2 * w.head_dim + out_b)
+    del g, before
+    return {"append_tokens": w.append, "append_at": w.prefill, "append_us": round(app_us, 2),
+            "append_bytes": int(app_bytes), "append_GB_s": round(app_bytes / app_us / 1e3, 1),
+            "append_frac_hbm": round(app_bytes / app_us / 1e3 / HBM_PEAK_GBS, 4),
+            "append_launches_per_graph": COPIES, "append_rewrite_bitexact": bool(same)}
 
 
 def chunk_workload(kvq, kvq_setup, wl, n_cu, name="long"):
@@ -458,6 +476,9 @@ def main() -> int:
                     help="cache layout: positions major (default) or heads major")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the Gemma 4K and batched-serving timings (profiling runs of the 128K step)")
+    ap.add_argument("--only", choices=("append2048",),
+                    help="run one sub-benchmark alone (profiling runs): append2048 = the 2048-token "
+                         "quantize-append of the mixed-store workloads (k8v32, k32v8)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (the reference for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters of a rocprofv3 --pmc run to bytes)")
@@ -488,6 +509,17 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     n_cu = kvq_setup.n_cu()
+    if args.only == "append2048":
+        res = {}
+        for name in ("mixed_k8v32", "mixed_k32v8"):
+            w = wl.WORKLOADS[name]
+            log(f"{name}: filling {w.prefill + w.append} positions")
+            lay, c0 = kvq_setup.fill_cache(w, np.array([w.prefill + w.append]))
+            res[name] = append_chunk_timing(kvq, wl, w, lay, c0)
+            del c0
+            torch.cuda.empty_cache()
+        print(json.dumps({"only": "append2048", **res}), flush=True)
+        return 0 if all(r["append_rewrite_bitexact"] for r in res.values()) else 1
     w = wl.WORKLOADS["long"]
     L = w.contexts[-1]
     lens = np.array([L], dtype=np.int32)

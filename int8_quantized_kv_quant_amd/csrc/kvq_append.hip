@@ -90,9 +90,145 @@ __global__ __launch_bounds__(256) void kvq_append_kernel(AppendArgs a) {
   }
 }
 
+// ---- int8 and fp32 stores: 8 values per lane ---------------------------------------
+// Lane l of a wavefront owns values 8 (l % LPR) .. +7 of row l / LPR, LPR = D / 8
+// lanes per row (32, 16, 8): one 16-byte load per lane, RW = 64 / LPR rows per
+// wavefront. A workgroup (4 wavefronts) covers 4 RW consecutive tokens of one
+// kv head and one sequence, so the token and head of a row come from the grid
+// (no division per lane).
+
+// Maximum of x over aligned groups of GL lanes (GL = 8, 16, 32 or 64), every
+// lane of a group receiving it: DPP quad permutes (lanes ^ 1, ^ 2), the
+// half-row and row mirrors (lanes 7 - i within 8, 15 - i within 16), then
+// v_permlane16_swap / v_permlane32_swap for lanes ^ 16 and ^ 32.
+template <int GL>
+__device__ __forceinline__ uint32_t group_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  if constexpr (GL >= 16) x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));
+  if constexpr (GL >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max((uint32_t)r[0], (uint32_t)r[1]);
+  }
+  if constexpr (GL >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    x = max((uint32_t)r[0], (uint32_t)r[1]);
+  }
+  return x;
+}
+
+// Code of x (fp16 value, widened) for the fp16 scale s > 0 with rs = rcp(s)
+// (within 1 ulp): clamp(round-half-even(x / s), -127, 127), exactly as a
+// correctly rounded division followed by rint. For fp16 x and s the exact
+// quotient q is either a half-integer or at least 2^-13 away from every
+// half-integer, while t = x * rs is within 3e-7 |q| (< 6e-5 for |q| <= 190,
+// the largest quotient a subnormal scale allows) of q: so rint(t) is the
+// correctly rounded code except at exact ties, where it may land on the odd
+// neighbour. The residual r = x - c s (exact: c s has at most 19 significant
+// bits and |r| <= 1.5 s) is then +-s/2, and the tie goes to the even code.
+__device__ __forceinline__ int code_of(float x, float s, float rs) {
+  float c = __builtin_rintf(x * rs);
+  const float r = fmaf(-c, s, x);
+  if (fabsf(r) == 0.5f * s && ((int)c & 1)) c += r > 0.0f ? 1.0f : -1.0f;
+  return (int)fminf(fmaxf(c, -127.0f), 127.0f);
+}
+
+struct Append8Args {
+  AppendStore st[2];  // [0] = K, [1] = V
+  const int32_t* start_pos;
+  int64_t s_seq, s_pos, s_head;
+  int64_t ss_seq, ss_pos, ss_head;
+  int64_t max_ctx;
+  int32_t n_kv, n_tok;
+};
+
+template <int D, bool G64>
+__global__ __launch_bounds__(256) void kvq_append8_kernel(Append8Args a) {
+  constexpr int LPR = D / 8;               // lanes per row
+  constexpr int RW = 64 / LPR;             // rows per wavefront
+  constexpr int GL = G64 ? 8 : LPR;        // lanes per scale group
+  const AppendStore S = a.st[blockIdx.y];
+  const int b = blockIdx.z;
+  const int h = blockIdx.x % a.n_kv;       // uniform: scalar arithmetic
+  const int tb = blockIdx.x / a.n_kv;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int t = (tb * 4 + wv) * RW + lane / LPR;
+  const int lr = lane % LPR;
+  const bool live = t < a.n_tok;
+  u32x4 raw = {0u, 0u, 0u, 0u};
+  if (live) raw = *reinterpret_cast<const u32x4*>(S.src + (((int64_t)b * a.n_tok + t) * a.n_kv + h) * D + 8 * lr);
+  const int64_t pos = (int64_t)a.start_pos[b] + t;
+  const bool store = live && pos >= 0 && pos < a.max_ctx;  // rows outside the cache are dropped
+  const int64_t row_off = b * a.s_seq + pos * a.s_pos + h * a.s_head;
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = h_bits_to_f32((raw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+
+  if (S.dtype == KVQ_STORE_FP32) {  // the fp16 values widened exactly
+    if (store) {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(S.store) + row_off + 8 * lr);
+      dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+      dst[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+    return;
+  }
+  // absmax on the fp16 bit patterns (exact), over the group's lanes
+  uint32_t amax = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) amax = max(amax, max(raw[k] & 0x7fffu, (raw[k] >> 16) & 0x7fffu));
+  amax = group_max<GL>(amax);
+  const f16 scale_h = (f16)(h_bits_to_f32(amax) / 127.0f);  // fp32 IEEE division, then fp16 RNE
+  const float s = (float)scale_h;
+  const float rs = __builtin_amdgcn_rcpf(s);
+  uint32_t w[2] = {0u, 0u};
+  if (s > 0.0f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e >> 2] |= ((uint32_t)code_of(x[e], s, rs) & 0xffu) << (8 * (e & 3));
+  }
+  if (store) {
+    *reinterpret_cast<u32x2*>(static_cast<int8_t*>(S.store) + row_off + 8 * lr) = (u32x2){w[0], w[1]};
+    if (lr % GL == 0) S.scales[b * a.ss_seq + pos * a.ss_pos + h * a.ss_head + lr / GL] = __builtin_bit_cast(uint16_t, scale_h);
+  }
+}
+
+template <int D>
+static void launch_append8_t(const Append8Args& a, bool g64, dim3 grid, hipStream_t s) {
+  if (g64) hipLaunchKernelGGL((kvq_append8_kernel<D, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((kvq_append8_kernel<D, false>), grid, dim3(256), 0, s, a);
+}
+
 int launch_append(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k_scales,
                   uint16_t* v_scales, const uint16_t* k_new, const uint16_t* v_new,
                   const int32_t* d_start_pos, int32_t batch, int32_t n_tok, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!has_q4(L)) {
+    Append8Args a{};
+    a.st[0] = {k_store, k_scales, k_new, L.k_dtype, 0};
+    a.st[1] = {v_store, v_scales, v_new, L.v_dtype, 0};
+    a.start_pos = d_start_pos;
+    a.s_seq = L.s_seq;
+    a.s_pos = L.s_pos;
+    a.s_head = L.s_head;
+    a.ss_seq = L.ss_seq;
+    a.ss_pos = L.ss_pos;
+    a.ss_head = L.ss_head;
+    a.max_ctx = L.max_ctx;
+    a.n_kv = L.n_kv_heads;
+    a.n_tok = n_tok;
+    const int tok_per_wg = 4 * (64 / (L.head_dim / 8));
+    const dim3 grid(L.n_kv_heads * ((n_tok + tok_per_wg - 1) / tok_per_wg), 2, batch);
+    const bool g64 = L.scale_group == 64 && L.head_dim != 64;
+    switch (L.head_dim) {
+      case 64: launch_append8_t<64>(a, g64, grid, s); break;
+      case 128: launch_append8_t<128>(a, g64, grid, s); break;
+      case 256: launch_append8_t<256>(a, g64, grid, s); break;
+      default: return KVQ_ERR_UNSUPPORTED;
+    }
+    return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+  }
+  // Layouts with a q4 store: one row per wavefront (the rotation spans it).
   AppendArgs a{};
   a.st[0] = {k_store, k_scales, k_new, L.k_dtype, 0};
   a.st[1] = {v_store, v_scales, v_new, L.v_dtype, 0};
@@ -111,7 +247,6 @@ int launch_append(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k
   a.group_lanes = (L.scale_group == 64) ? 16 : tpr;
   const int rpb = 256 / tpr;
   dim3 grid((a.rows + rpb - 1) / rpb, 2);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   switch (L.head_dim) {
     case 64: hipLaunchKernelGGL(kvq_append_kernel<64>, grid, dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL(kvq_append_kernel<128>, grid, dim3(256), 0, s, a); break;
