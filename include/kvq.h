@@ -131,11 +131,15 @@ typedef struct {
 } kvq_layout;
 
 /* Split plan of one decode step ([G130]: split count fixed on the host).
- * Split s of a sequence with context L covers positions
- *   [lo + s*chunk, lo + (s+1)*chunk)  clipped to L, where lo = max(0, L - window)
- * if window > 0 else 0; the last split (s = n_splits-1) runs to L, so a context
- * longer than the planned one is still covered. ws_bytes is the workspace that
- * kv_decode_attn_splitk writes and kv_decode_reduce reads. */
+ * The attended range [lo, L) of a sequence with context L (lo = max(0, L -
+ * window) if window > 0, else 0) is cut into blocks of 128 positions from lo;
+ * decode split s covers blocks s, s + n_splits, s + 2*n_splits, ... (block-
+ * cyclic), so every context length is covered whatever the planned one.
+ * chunk is the split length the planner aimed at (about n_splits * chunk
+ * positions are covered without a split taking a second round of blocks);
+ * kv_chunk_attn's splits are contiguous: [lo + s*chunk, lo + (s+1)*chunk),
+ * the last one running to the chunk's end. ws_bytes is the workspace that
+ * kv_decode_attn_splitk (or kv_chunk_attn) writes and kv_decode_reduce reads. */
 typedef struct {
   int32_t n_splits;
   int32_t chunk;       /* positions per split, a multiple of 32 */
@@ -214,7 +218,7 @@ int kv_decode_attn_splitk(const kvq_layout* layout,
  * K and V rows of every kv head are quantized exactly as kv_quant_append does
  * (d_start_pos[b] = L_b - 1, n_tok = 1) and written to row L_b - 1 of the
  * stores and scales; the partials are those of kv_decode_attn_splitk over
- * [lo, L_b) with that row in place. The workgroup whose range holds position
+ * [lo, L_b) with that row in place. The workgroup whose blocks hold position
  * L_b - 1 takes the new row from its own quantizer, so within the call nothing
  * reads that row from memory. A sequence with L_b = 0 or L_b > max_ctx gets
  * no append (as kv_quant_append drops such rows) and the partials of
