@@ -75,6 +75,83 @@ def traffic_from_profiles(digest: str, plan, name: str = "partial_long_128k_traf
     return d.get("hbm_bytes_per_launch")
 
 
+def oracle_seq(w, b, L, q_b):
+    """fp64 oracle output [n_q][d] of sequence b of workload w at context L
+    (w's window and store types), from the workload's own rows."""
+    from oracle import kvq_oracle as orc
+    import workloads as wl
+    lo = max(0, L - w.window) if w.window else 0
+    c = orc.Cache(1, L, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+    c.append(wl.kv_rows(w, "k", b, lo, L - lo)[None], wl.kv_rows(w, "v", b, lo, L - lo)[None], [lo])
+    return orc.attend(np.asarray(q_b)[None], c, [L], w.window, 1.0 / math.sqrt(w.head_dim))[0]
+
+
+def codes_match(kvq_setup, lay, cache, w, b, positions):
+    """True if the cache rows (b, positions) of every kv head hold exactly the
+    oracle's quantization of the workload's rows: int8 codes and fp16 scales,
+    Q4_0 bytes and block scales, or the fp16 values widened for an fp32 store."""
+    from oracle import kvq_oracle as orc
+    import workloads as wl
+    positions = np.asarray(positions)
+    ok = True
+    for s, dt in (("k", w.k_dtype), ("v", w.v_dtype)):
+        rows = np.concatenate([wl.kv_rows(w, s, b, int(p), 1) for p in positions])
+        for h in range(w.n_kv_heads):
+            if dt == "int8":
+                want_c, want_s = orc.quantize_rows(rows[:, h], w.scale_group)
+                got_c = kvq_setup.rows_of(lay, cache[s], b, positions, h)
+                got_s = kvq_setup.scales_of(lay, cache[s + "_scales"], b, positions, h)
+                ok &= bool(np.array_equal(got_c, want_c) and np.array_equal(got_s.view(np.uint16), want_s.view(np.uint16)))
+            elif dt == "q4":
+                codes, want_s = orc.quantize_q4_0(orc.rotate_f32(rows[:, h]))
+                got = kvq_setup.q4_rows_of(lay, cache[s], b, positions, h)
+                got_s = kvq_setup.scales_of(lay, cache[s + "_scales"], b, positions, h, n=w.head_dim // 32)
+                ok &= bool(np.array_equal(got, orc.pack_q4(codes)) and
+                           np.array_equal(got_s.view(np.uint16), want_s.view(np.uint16)))
+            else:
+                got = kvq_setup.rows_of(lay, cache[s], b, positions, h)
+                ok &= bool(np.array_equal(got.view(np.uint32), rows[:, h].astype(np.float32).view(np.uint32)))
+    return ok
+
+
+def cpu_info():
+    """Host cores and CPU model (for the CPU-baseline record)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "cpu_model": model,
+            "sched_affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def cpu_quantize_baseline(seconds=3.0):
+    """The oracle's quantize leg timed on the host: orc.quantize_rows of the
+    mixed workload's 2048-token chunk (both kv heads, K and V as int8 group-64
+    rows of head_dim 256), repeated for about `seconds`, with the BLAS threads
+    it has by default. Returns values quantized per second and the repeats."""
+    from oracle import kvq_oracle as orc
+    import workloads as wl
+    w = wl.WORKLOADS["mixed_k8v32"]
+    rows = [wl.kv_rows(w, s, 0, w.prefill, w.append) for s in ("k", "v")]
+    n_vals = sum(r.size for r in rows)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for r in rows:
+            orc.quantize_rows(r, w.scale_group)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    return {"values_per_s": round(n_vals / dt, 1), "seconds_per_chunk": round(dt, 4), "repeats": reps,
+            "sample": f"quantize_rows of the {w.append}-token chunk of the mixed workload: K and V, "
+                      f"{w.n_kv_heads} kv heads x {w.head_dim} values per row ({n_vals} values), group-64 scales"}
+
+
 def cpu_baseline(w, lens, q, sm):
     """The oracle as it stands, timed on the host: decode attention of the full
     step (both kv heads, 131072 positions) over the dequantized cache in fp64,
@@ -150,7 +227,10 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
     dev = torch.device("cuda:0")
     res = {}
 
-    def timed(w, lens, lay, caches, k_new, v_new):
+    def timed(w, lens, lay, caches, k_new, v_new, parity=None):
+        """Graph-replayed decode steps over the cache copies; parity(out, q)
+        -> dict of checks on the output of the last step (every copy holds the
+        same rows, so every step's output is the same)."""
         B = w.batch
         qd = torch.from_numpy(wl.queries(w)).to(dev)
         ld = torch.from_numpy(lens.astype(np.int32)).to(dev)
@@ -167,35 +247,56 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
         for c in caches:
             step(c)
         torch.cuda.synchronize()
+        # COPIES steps per graph (cycling over the cache copies), so that one
+        # graph launch covers several steps
+        rounds = max(1, COPIES // len(caches))
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for c in caches:
-                step(c)
+            for _ in range(rounds):
+                for c in caches:
+                    step(c)
         g.replay()
         torch.cuda.synchronize()
-        reps = max(2, steps // len(caches))
+        per_graph = rounds * len(caches)
+        reps = max(2, steps // per_graph)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
             g.replay()
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * len(caches))
+        us = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
         kvb = wl.kv_bytes_per_step(w, lens)
-        return {"us_per_step": round(us, 2), "kv_bytes_per_step": int(kvb), "GB_s": round(kvb / us / 1e3, 1),
-                "pct_hbm_peak": round(100 * kvb / us / 1e3 / HBM_PEAK_GBS, 2), "n_splits": plan.n_splits,
-                "chunk": plan.chunk, "steps": reps * len(caches)}
+        res = {"us_per_step": round(us, 2), "kv_bytes_per_step": int(kvb), "GB_s": round(kvb / us / 1e3, 1),
+               "pct_hbm_peak": round(100 * kvb / us / 1e3 / HBM_PEAK_GBS, 2), "n_splits": plan.n_splits,
+               "chunk": plan.chunk, "steps": reps * per_graph, "steps_per_graph": per_graph}
+        if parity is not None:
+            res.update(parity(out.float().cpu().numpy().astype(np.float64), wl.queries(w)))
+        return res
 
-    w = wl.WORKLOADS["gemma"]
-    L = 4096
-    lens = np.array([L], dtype=np.int32)
-    lay, c0 = kvq_setup.fill_cache(w, lens, upto=np.array([L - 1]))
-    caches = [c0] + [{k: (None if t is None else t.clone()) for k, t in c0.items()} for _ in range(COPIES - 1)]
-    k_new = torch.from_numpy(wl.kv_rows(w, "k", 0, L - 1, 1)).to(dev)
-    v_new = torch.from_numpy(wl.kv_rows(w, "v", 0, L - 1, 1)).to(dev)
-    res["gemma_4k"] = {"context": L, "window": w.window, "cache_copies": COPIES,
-                       **timed(w, lens, lay, caches, k_new, v_new)}
-    del caches, c0
+    def single_parity(w, L, lay, cache, extra_positions=()):
+        """max abs error of sequence 0 against the oracle at context L, and the
+        codes of the appended row and of sampled rows bit-exact."""
+        def check(got, q):
+            err = float(np.abs(got[0] - oracle_seq(w, 0, L, q[0])).max())
+            rng = np.random.default_rng(5)
+            pos = np.unique(np.concatenate([rng.integers(0, L, 64), [L - 1], np.asarray(extra_positions, dtype=np.int64)]))
+            return {"max_abs_err": err, "codes_bitexact": codes_match(kvq_setup, lay, cache, w, 0, pos),
+                    "tol": TOL}
+        return check
+
+    for key, name in (("tiny", "tiny"), ("gemma_4k", "gemma")):
+        w = wl.WORKLOADS[name]
+        L = w.contexts[-1]
+        lens = np.array([L], dtype=np.int32)
+        lay, c0 = kvq_setup.fill_cache(w, lens, upto=np.array([L - 1]))
+        caches = [c0] + [{k: (None if t is None else t.clone()) for k, t in c0.items()} for _ in range(COPIES - 1)]
+        k_new = torch.from_numpy(wl.kv_rows(w, "k", 0, L - 1, 1)).to(dev)
+        v_new = torch.from_numpy(wl.kv_rows(w, "v", 0, L - 1, 1)).to(dev)
+        res[key] = {"context": L, "window": w.window, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                    "head_dim": w.head_dim, "cache_copies": COPIES,
+                    **timed(w, lens, lay, caches, k_new, v_new, single_parity(w, L, lay, caches[-1]))}
+        del caches, c0
 
     res["prefill_chunk"] = chunk_workload(kvq, kvq_setup, wl, n_cu)
     res["prefill_chunk_q4"] = chunk_workload(kvq, kvq_setup, wl, n_cu, "long_q4")
@@ -215,8 +316,10 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
         caches = [c0] + [{k: (None if t is None else t.clone()) for k, t in c0.items()} for _ in range(COPIES - 1)]
         k_new = torch.from_numpy(wl.kv_rows(w, "k", 0, L - 1, 1)).to(dev)
         v_new = torch.from_numpy(wl.kv_rows(w, "v", 0, L - 1, 1)).to(dev)
+        chunk_rows = np.arange(w.prefill, w.prefill + w.append, 97)
         res[name] = {"k_store": w.k_dtype, "v_store": w.v_dtype, "context": L, "cache_copies": COPIES,
-                     **app, **timed(w, lens, lay, caches, k_new, v_new)}
+                     **app, **timed(w, lens, lay, caches, k_new, v_new,
+                                    single_parity(w, L, lay, caches[-1], extra_positions=chunk_rows))}
         del caches, c0
         torch.cuda.empty_cache()
 
@@ -226,16 +329,38 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
     cache = kvq.alloc_cache(lay, w.batch, device=dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed)
+    # Four sampled sequences (the shortest, the longest and two others) hold
+    # the workload's own rows and are checked against the oracle; the other 60
+    # are filled from rows drawn on the device (1.1 G host-drawn values would
+    # dominate the run).
+    sampled = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 7, 40})
     for b in range(w.batch):
         p, n_fill = 0, int(lens[b]) - 1
         while p < n_fill:
             n = min(16384, n_fill - p)
-            rows = torch.randn((2, n, w.n_kv_heads, w.head_dim), generator=gen, device=dev).half()
-            kvq_setup.append_rows_device(lay, cache, b, p, rows[0], rows[1])
+            if b in sampled:
+                kvq_setup.append_rows(lay, cache, b, p, wl.kv_rows(w, "k", b, p, n), wl.kv_rows(w, "v", b, p, n))
+            else:
+                rows = torch.randn((2, n, w.n_kv_heads, w.head_dim), generator=gen, device=dev).half()
+                kvq_setup.append_rows_device(lay, cache, b, p, rows[0], rows[1])
             p += n
     new = torch.randn((2, w.batch, w.n_kv_heads, w.head_dim), generator=gen, device=dev).half()
+    for b in sampled:
+        Lb = int(lens[b])
+        new[0, b] = torch.from_numpy(wl.kv_rows(w, "k", b, Lb - 1, 1)[0]).to(dev)
+        new[1, b] = torch.from_numpy(wl.kv_rows(w, "v", b, Lb - 1, 1)[0]).to(dev)
+
+    def batched_parity(got, q):
+        err = max(float(np.abs(got[b] - oracle_seq(w, b, int(lens[b]), q[b])).max()) for b in sampled)
+        rng = np.random.default_rng(6)
+        ok = all(codes_match(kvq_setup, lay, cache, w, b,
+                             np.unique(np.concatenate([rng.integers(0, int(lens[b]), 32), [int(lens[b]) - 1]])))
+                 for b in sampled)
+        return {"max_abs_err": err, "codes_bitexact": ok, "tol": TOL,
+                "parity_sequences": [int(b) for b in sampled]}
+
     res["batched"] = {"batch": w.batch, "contexts": "U[1024, 32768]", "total_positions": int(lens.sum()),
-                      **timed(w, lens, lay, [cache], new[0].contiguous(), new[1].contiguous())}
+                      **timed(w, lens, lay, [cache], new[0].contiguous(), new[1].contiguous(), batched_parity)}
     del cache
     torch.cuda.empty_cache()
     return res
@@ -348,10 +473,10 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
     rotated Q4_0 blocks at head_dim 256): kv_append_decode_splitk (the new
     token's rotation and quantization fused into the partials) +
     kv_decode_reduce, graph-replayed over COPIES caches of 131072 positions;
-    the unfused three-call step beside it. The caches are filled through kv_quant_append from rows
-    drawn on the device with a seeded torch.Generator (timing only: parity is
-    covered by the GPU tests). The partial kernel is also timed alone (its
-    roofline: algorithmic bytes / launch time)."""
+    the unfused three-call step beside it. The caches hold the workload's own
+    rows (kv_quant_append); the step's output is checked against the oracle and
+    sampled rows' Q4_0 bytes against the oracle's quantizer. The partial kernel
+    is also timed alone (its roofline: algorithmic bytes / launch time)."""
     import torch
     dev = torch.device("cuda:0")
     res = {}
@@ -359,18 +484,9 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
         w = wl.WORKLOADS[name]
         L = w.contexts[-1]
         lens = np.array([L], dtype=np.int32)
-        lay = kvq_setup.layout_for(w)
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(w.seed)
-        c0 = kvq.alloc_cache(lay, 1, device=dev)
-        p = 0
-        while p < L - 1:
-            n = min(16384, L - 1 - p)
-            rows = torch.randn((2, n, w.n_kv_heads, w.head_dim), generator=gen, device=dev).half()
-            kvq_setup.append_rows_device(lay, c0, 0, p, rows[0], rows[1])
-            p += n
+        lay, c0 = kvq_setup.fill_cache(w, lens, upto=np.array([L - 1]))
         caches = [c0] + [{k: (None if t is None else t.clone()) for k, t in c0.items()} for _ in range(COPIES - 1)]
-        new = torch.randn((2, 1, 1, w.n_kv_heads, w.head_dim), generator=gen, device=dev).half()
+        new = torch.stack([torch.from_numpy(wl.kv_rows(w, s, 0, L - 1, 1)) for s in ("k", "v")])[:, None].to(dev)
         qd = torch.from_numpy(wl.queries(w)).to(dev)
         ld = torch.from_numpy(lens).to(dev)
         sp = torch.tensor([L - 1], dtype=torch.int32, device=dev)
@@ -413,6 +529,12 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
             return e0.elapsed_time(e1) * 1e3 / (reps * len(caches))
 
         us = graph_us(lambda c: (fused(c), reduce()))
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        err = float(np.abs(got[0] - oracle_seq(w, 0, L, wl.queries(w)[0])).max())
+        rng = np.random.default_rng(7)
+        codes_ok = codes_match(kvq_setup, lay, caches[-1], w, 0,
+                               np.unique(np.concatenate([rng.integers(0, L, 64), [L - 1]])))
         unfused_us = graph_us(lambda c: (append(c), partial(c), reduce()))
         part_us = graph_us(partial)
         fpart_us = graph_us(fused)
@@ -428,7 +550,8 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
             "partial_frac_hbm": round(kvb / part_us / 1e3 / HBM_PEAK_GBS, 4),
             "partial_traffic": traffic_from_profiles(kernel_source_digest(Q4_SOURCES), plan,
                                                      "partial_q4_long_128k_traffic.json", name),
-            "n_splits": plan.n_splits, "chunk": plan.chunk}
+            "n_splits": plan.n_splits, "chunk": plan.chunk,
+            "max_abs_err": err, "codes_bitexact": codes_ok, "tol": TOL}
         del caches, c0
         torch.cuda.empty_cache()
     return res
@@ -600,7 +723,8 @@ def main() -> int:
                "seconds_1core": None if cpu_s1 is None else round(cpu_s1, 3),
                "sample": f"full step repeated {cpu_reps}x (~10 s) on {int(cores)} BLAS threads, then "
                          f"{cpu_reps1}x (~10 s) on one: numpy fp64 decode attention of 16 query heads over "
-                         "the dequantized 131072-position cache (both kv heads); cache set-up not timed"}
+                         "the dequantized 131072-position cache (both kv heads); cache set-up not timed",
+               "quantize": cpu_quantize_baseline(), **cpu_info()}
     else:
         max_err = None
 
@@ -644,7 +768,7 @@ def main() -> int:
     ms_per_step = replay_ms(g_step, reps)
     # The spread: each replay (one step per cache copy) timed on its own.
     per_replay = []
-    for _ in range(reps):
+    for _ in range(50):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         g_step.replay()
@@ -670,6 +794,33 @@ def main() -> int:
     unfused_ms = replay_ms(capture(lambda c: (append(c), partial(c, plan_g), reduce(plan_g))), reps)
     app_ms = replay_ms(capture(append), reps)
     part_ms = replay_ms(capture(lambda c: partial(c, plan_g)), reps)
+
+    # The same step at 32K and 64K context on the same caches (rows [0, L - 1)
+    # are the workload's; the fused append rewrites row L - 1 with the same
+    # values), each with its own plan.
+    sweep = []
+    for Lc in (32768, 65536):
+        ldc = torch.tensor([Lc], dtype=torch.int32, device=dev)
+        plan_c = kvq.kvq_plan(lay, 1, w.n_q_heads, Lc, 0, n_cu)
+        ws_c = torch.zeros(plan_c.ws_bytes, dtype=torch.uint8, device=dev)
+        kn = torch.from_numpy(wl.kv_rows(w, "k", 0, Lc - 1, 1)).to(dev)
+        vn = torch.from_numpy(wl.kv_rows(w, "v", 0, Lc - 1, 1)).to(dev)
+
+        def step_c(c):
+            kvq.kv_append_decode_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], kn, vn, qd, 1,
+                                        w.n_q_heads, ldc, 0, sm, plan_c, ws_c, ws_c.numel())
+            kvq.kv_decode_reduce(lay, ws_c, ws_c.numel(), ldc, 1, w.n_q_heads, 0, plan_c, out)
+
+        ms_c = replay_ms(capture(step_c), reps)
+        got_c = out.float().cpu().numpy().astype(np.float64)
+        kvb_c = wl.kv_bytes_per_step(w, np.array([Lc]))
+        err_c = float(np.abs(got_c[0] - oracle_seq(w, 0, Lc, q[0])).max())
+        sweep.append({"context": Lc, "us_per_step": round(ms_c * 1e3, 2), "kv_bytes_per_step": int(kvb_c),
+                      "GB_s": round(kvb_c / ms_c / 1e6, 1), "pct_hbm_peak": round(100 * kvb_c / ms_c / 1e6 / HBM_PEAK_GBS, 2),
+                      "n_splits": plan_c.n_splits, "chunk": plan_c.chunk, "max_abs_err": err_c, "tol": TOL,
+                      "codes_bitexact": codes_match(kvq_setup, lay, caches[-1], w, 0, [Lc - 1, Lc - 2, 7])})
+        del ws_c
+    log("context sweep: " + ", ".join(f"{d['context']}: {d['us_per_step']} us" for d in sweep))
 
     others = None
     if not args.no_other_workloads:
@@ -713,8 +864,10 @@ def main() -> int:
         "step_us_percentiles": {"p10": round(float(np.percentile(per_replay, 10)), 2),
                                 "median": round(float(np.median(per_replay)), 2),
                                 "p90": round(float(np.percentile(per_replay, 90)), 2),
-                                "replays": len(per_replay), "steps_per_replay": COPIES},
+                                "replays": len(per_replay), "steps_per_replay": COPIES,
+                                "note": "50 graph replays timed one by one, beside the --steps timed ones"},
         "hot_cache_us_per_step": round(hot_ms * 1e3, 2),
+        "context_sweep": sweep,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -133,12 +133,12 @@ typedef struct {
 /* Split plan of one decode step ([G130]: split count fixed on the host).
  * The attended range [lo, L) of a sequence with context L (lo = max(0, L -
  * window) if window > 0, else 0) is cut into blocks of 128 positions from lo;
- * decode split s covers blocks s, s + n_splits, s + 2*n_splits, ... (block-
- * cyclic), so every context length is covered whatever the planned one.
- * chunk is the split length the planner aimed at (about n_splits * chunk
- * positions are covered without a split taking a second round of blocks);
- * kv_chunk_attn's splits are contiguous: [lo + s*chunk, lo + (s+1)*chunk),
- * the last one running to the chunk's end. ws_bytes is the workspace that
+ * with S = min(n_splits, ceil((L - lo) / chunk)) (the splits that contiguous
+ * ranges of chunk positions would use), decode split s < S covers blocks
+ * s, s + S, s + 2*S, ... (block-cyclic) and splits s >= S are empty, so every
+ * context length is covered whatever the planned one. kv_chunk_attn's splits
+ * are contiguous: [lo + s*chunk, lo + (s+1)*chunk), the last one running to
+ * the chunk's end. ws_bytes is the workspace that
  * kv_decode_attn_splitk (or kv_chunk_attn) writes and kv_decode_reduce reads. */
 typedef struct {
   int32_t n_splits;

@@ -8,11 +8,12 @@
 // PR 2698 "What it does": one FP16 scale per 64 values; k8v32 / k32v8.
 //
 // Mapping. One workgroup = (sequence b, kv head, block of up to 16 query heads
-// sharing it, split s). Split s owns the 128-position blocks s, s + n_splits,
-// s + 2 n_splits, ... of the attended range (block-cyclic: with one workgroup
-// per compute unit this spread each XCD's reads over the whole context and
-// shortened the 128K step by ~1.5 us against contiguous ranges); wavefront w
-// takes tile w of each block. Per tile a wavefront computes, with
+// sharing it, split s). Split s owns the 128-position blocks s, s + S,
+// s + 2 S, ... of the attended range, S = min(n_splits, ceil((L - lo) /
+// chunk)) (block-cyclic: as many splits as contiguous ranges would use, but
+// with one workgroup per compute unit this spreads each XCD's reads over the
+// whole context, which shortened the 128K step by ~1.5 us against contiguous
+// ranges); wavefront w takes tile w of each block. Per tile a wavefront computes, with
 // v_mfma_f32_16x16x32_f16:
 //   S^T (32 positions x 16 heads) = K (codes) . Q^T      (D/16 MFMAs)
 //   O   (16 heads x D)           += P (fp16) . V_hat     (D/16 MFMAs)
@@ -183,12 +184,14 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   const int L_in = a.seq_lens[b];
   const int L = L_in < 0 ? 0 : (L_in > a.max_ctx ? a.max_ctx : L_in);
   const int lo = a.window > 0 ? max(0, L - a.window) : 0;
-  // Split s takes the blocks s, s + n_splits, s + 2 n_splits, ... of BLK
-  // positions of [lo, L) (block-cyclic), so every split's reads spread over the
-  // whole context; wavefront w takes tile w of each of its blocks.
+  // Split s takes the blocks s, s + S, s + 2 S, ... of BLK positions of
+  // [lo, L) (block-cyclic), S = min(n_splits, ceil((L - lo) / chunk)): as many
+  // splits as contiguous ranges of `chunk` positions would use, each reading
+  // across the whole context; wavefront w takes tile w of each of its blocks.
   constexpr int BLK = NW * kTile;
+  const int n_used = (int)min((int64_t)a.n_splits, ((int64_t)L - lo + a.chunk - 1) / a.chunk);
   const int64_t start64 = (int64_t)lo + (int64_t)split * BLK;
-  if (start64 >= L) {  // empty split: recorded as (m, l) = (-inf, 0), O not written
+  if (split >= n_used || start64 >= L) {  // empty split: recorded as (m, l) = (-inf, 0), O not written
     if (threadIdx.x < nh) ml_out[(int64_t)threadIdx.x * a.n_splits] = make_float2(-INFINITY, 0.0f);
     return;
   }
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   int end = L;
   // Fused append: the workgroup whose blocks hold position L - 1 takes the new
   // row from the quantizer instead of the cache, and its tiles stop before it.
-  const bool own_new = a.k_new != nullptr && L_in == L && ((L - 1 - lo) / BLK) % a.n_splits == split;
+  const bool own_new = a.k_new != nullptr && L_in == L && ((L - 1 - lo) / BLK) % n_used == split;
   if (own_new) end = L - 1;
 
   const int lane = threadIdx.x & 63;
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   const auto ksrs = make_rsrc(KI8 ? static_cast<const void*>(a.k_scales + sc_off) : nullptr, KI8 ? sc_bytes : 0u);
   const auto vsrs = make_rsrc(VI8 ? static_cast<const void*>(a.v_scales + sc_off) : nullptr, VI8 ? sc_bytes : 0u);
 
-  const int STEP = BLK * a.n_splits;  // from a tile to the same tile of the split's next block
+  const int STEP = BLK * n_used;  // from a tile to the same tile of the split's next block
   int p0 = start + wv * kTile;
   // Loads into LDS before the first tile's, counted like them (compiler-visible
   // loads here would make the compiler wait for every load in flight before

@@ -171,11 +171,13 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   const int L_in = a.seq_lens[b];
   const int L = L_in < 0 ? 0 : (L_in > a.max_ctx ? a.max_ctx : L_in);
   const int lo = a.window > 0 ? max(0, L - a.window) : 0;
-  // Split s takes the blocks s, s + n_splits, ... of BLK positions of [lo, L)
-  // (block-cyclic, as in the int8 kernel).
+  // Split s takes the blocks s, s + S, ... of BLK positions of [lo, L),
+  // S = min(n_splits, ceil((L - lo) / chunk)) (block-cyclic, as in the int8
+  // kernel).
   constexpr int BLK = NW * kTile;
+  const int n_used = (int)min((int64_t)a.n_splits, ((int64_t)L - lo + a.chunk - 1) / a.chunk);
   const int64_t start64 = (int64_t)lo + (int64_t)split * BLK;
-  if (start64 >= L) {  // empty split: (m, l) = (-inf, 0), O not written
+  if (split >= n_used || start64 >= L) {  // empty split: (m, l) = (-inf, 0), O not written
     if (threadIdx.x < nh) ml_out[(int64_t)threadIdx.x * a.n_splits] = make_float2(-INFINITY, 0.0f);
     return;
   }
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   int end = L;
   // Fused append: the workgroup whose blocks hold position L - 1 takes the new
   // row from the quantizer instead of the cache, and its tiles stop before it.
-  const bool own_new = a.k_new != nullptr && L_in == L && ((L - 1 - lo) / BLK) % a.n_splits == split;
+  const bool own_new = a.k_new != nullptr && L_in == L && ((L - 1 - lo) / BLK) % n_used == split;
   if (own_new) end = L - 1;
 
   const int lane = threadIdx.x & 63;
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   const u32x4 ksrw = rsrc_words(a.k_scales + sc_off, (uint32_t)(((int64_t)(L - 1) * a.ss_pos + T::KNG) * 2));
   const u32x4 vsrw = rsrc_words(a.v_scales + sc_off, (uint32_t)(((int64_t)(L - 1) * a.ss_pos + D / kQ4Block) * 2));
 
-  const int STEP = BLK * a.n_splits;  // from a tile to the same tile of the split's next block
+  const int STEP = BLK * n_used;  // from a tile to the same tile of the split's next block
   int p0 = start + wv * kTile;
   // The new K (wavefront 0) or V (wavefront 1) row when the append is fused,
   // the query rows (4 per wavefront; rows past nh read as zeros), then this
