@@ -25,10 +25,11 @@
 // contexts with 16 query heads per kv head.)
 // Keys (int8, k8v4): the int8 kernel's operands and scores, unrotated.
 // Values (q4). Lane (column c16) holds dims 16 c16 .. +15, i.e. the low
-// (c16 even) or high (c16 odd) nibbles of 16 bytes of block c16 / 2; after a
-// shift and mask they are bytes holding the codes, transposed per position
-// pair by byte permutes into the fp16 operand (code - 8) * d_b, one rounding,
-// exactly as the int8 kernel builds code * scale.
+// (c16 even) or high (c16 odd) nibbles of 16 bytes of block c16 / 2, masked in
+// place (bytes q or 16 q), transposed per position pair by byte permutes into
+// the fp16 operand (code - 8) * d_b, one rounding, exactly as the int8 kernel
+// builds code * scale: 1024 + byte (exact) minus 1032 or 1152 gives q - 8 or
+// 16 (q - 8), and the high lanes multiply by d_b / 16 (exact).
 // Output. O of each split stays in the rotated basis through the softmax; the
 // merged partial rows are rotated back (fwht256, fp32) before they are
 // written, so the reduce (linear in O) combines unrotated rows.
@@ -69,7 +70,8 @@ struct Q4Args {
 
 // ---- values ---------------------------------------------------------------------------
 // v[e][w]: bytes holding the codes of dims 16 c16 + 4 w .. +3 at position
-// kpos(e, q4); vs[e]: that position's scale of block c16 / 2.
+// kpos(e, q4) (q for even c16, 16 q for odd c16); vs[e]: that position's scale
+// of block c16 / 2.
 struct VQ4Regs {
   uint32_t v[8][4];
   uint32_t vs[8];
@@ -78,14 +80,14 @@ struct VQ4Regs {
 template <bool KQ4, bool KG64>
 __device__ __forceinline__ void read_v_q4(VQ4Regs& t, const uint8_t* __restrict__ st, int c16, int q4) {
   using T = Q4Stage<KQ4, KG64>;
-  const uint32_t sh = 4u * (uint32_t)(c16 & 1);
+  const uint32_t mask = (c16 & 1) ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
   const int blk = c16 >> 1;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int r = kpos(e, q4);
     const u32x4 raw = *reinterpret_cast<const u32x4*>(st + T::V_OFF + r * T::VRB + 16 * (blk ^ swz<8>(r)));
 #pragma unroll
-    for (int w = 0; w < 4; ++w) t.v[e][w] = (raw[w] >> sh) & 0x0F0F0F0Fu;
+    for (int w = 0; w < 4; ++w) t.v[e][w] = raw[w] & mask;
     t.vs[e] = *reinterpret_cast<const uint16_t*>(st + T::VS_OFF + r * 16 + 2 * blk);
   }
 }
@@ -93,12 +95,16 @@ __device__ __forceinline__ void read_v_q4(VQ4Regs& t, const uint8_t* __restrict_
 // O += P . V_hat with V_hat = fp16((code - 8) * d) and l += P . 1; PART 1 and 2
 // split the output columns in halves (l with PART 2) so that a wait can sit
 // between them.
+// vbias: fp16 pair (-1032, -1032) for even c16 lanes, (-1152, -1152) for odd
+// ones; vsc: (1, 1) or (1/16, 1/16).
 template <int PART>
-__device__ __forceinline__ void pv_q4(const VQ4Regs& t, f16x8 pa, WaveAcc<Shape<256, true, true, true>>& acc) {
+__device__ __forceinline__ void pv_q4(const VQ4Regs& t, f16x8 pa, WaveAcc<Shape<256, true, true, true>>& acc,
+                                      uint32_t vbias, f16x2 vsc) {
   constexpr int W0 = PART == 2 ? 2 : 0, W1 = PART == 1 ? 2 : 4;
   f16x2 sv[4];
 #pragma unroll
-  for (int pi = 0; pi < 4; ++pi) sv[pi] = as_h2(__builtin_amdgcn_perm(t.vs[2 * pi + 1], t.vs[2 * pi], 0x05040100u));
+  for (int pi = 0; pi < 4; ++pi)
+    sv[pi] = as_h2(__builtin_amdgcn_perm(t.vs[2 * pi + 1], t.vs[2 * pi], 0x05040100u)) * vsc;
 #pragma unroll
   for (int w = W0; w < W1; ++w) {
     uint32_t z01[4], z23[4];
@@ -113,8 +119,8 @@ __device__ __forceinline__ void pv_q4(const VQ4Regs& t, f16x8 pa, WaveAcc<Shape<
 #pragma unroll
       for (int pi = 0; pi < 4; ++pi) {
         const uint32_t src = bb < 2 ? z01[pi] : z23[pi];
-        const uint32_t biased = (bb & 1) ? biased_h2_hi(src) : biased_h2_lo(src);  // 1024 + code
-        const f16x2 c = as_h2(biased) + as_h2(kQ4NegBias);                         // code - 8, exact
+        const uint32_t biased = (bb & 1) ? biased_h2_hi(src) : biased_h2_lo(src);  // 1024 + byte
+        const f16x2 c = as_h2(biased) + as_h2(vbias);                              // q - 8 or 16 (q - 8), exact
         r[pi] = as_u32(c * sv[pi]);                                                 // fp16((code - 8) * d)
       }
       acc.o[4 * w + bb] = mfma16(pa, __builtin_bit_cast(f16x8, r), acc.o[4 * w + bb]);
@@ -146,7 +152,8 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   // q4 keys: the lo fp16 terms of the rotated query rows (lds_q holds the hi
   // terms) and each row's fp32 sums over the 8 Q4_0 blocks.
   __shared__ __attribute__((aligned(16))) uint8_t lds_ql[KQ4 ? 16 * QROW : 16];
-  __shared__ __attribute__((aligned(16))) float lds_qsum[16][8];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_qsh[16][8];  // block sums, hi fp16 terms
+  __shared__ __attribute__((aligned(16))) uint16_t lds_qsl[16][8];  // and lo terms
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
   // The new token's rows when the append is fused ([0] = K, [1] = V): the fp16
@@ -264,8 +271,10 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   }
   if constexpr (KQ4) {
     // Rotate this wavefront's 4 query rows: lane l holds dims 4l .. 4l+3. The
-    // hi terms replace the row in lds_q, the lo terms go to lds_ql, and lanes
-    // 8j hold the sum over block j (dims 32j .. 32j+31, lanes 8j .. 8j+7).
+    // hi terms replace the row in lds_q, the lo terms go to lds_ql, dims 16..31
+    // of each block (lanes with l & 7 >= 4) divided by 16 (exact; see
+    // scores_q4), and lanes 8j hold the sum over block j (dims 32j .. 32j+31,
+    // lanes 8j .. 8j+7), split hi + lo into lds_qsh / lds_qsl.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wv * 4 + i;
@@ -275,10 +284,11 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
                     h_bits_to_f32(raw.y >> 16)};
       fwht256(v, lane);
       f16 hi[4], lo[4];
+      const float f = (lane & 7) >= 4 ? 0.0625f : 1.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        hi[e] = (f16)v[e];
-        lo[e] = (f16)(v[e] - (float)hi[e]);
+        hi[e] = (f16)(v[e] * f);
+        lo[e] = (f16)(v[e] * f - (float)hi[e]);
       }
       const f16x2 h01 = {hi[0], hi[1]}, h23 = {hi[2], hi[3]}, l01 = {lo[0], lo[1]}, l23 = {lo[2], lo[3]};
       *reinterpret_cast<u32x2*>(qr) = (u32x2){as_u32(h01), as_u32(h23)};
@@ -287,7 +297,11 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
       bs += __shfl_xor(bs, 1);
       bs += __shfl_xor(bs, 2);
       bs += __shfl_xor(bs, 4);
-      if ((lane & 7) == 0) lds_qsum[r][lane >> 3] = bs;
+      if ((lane & 7) == 0) {
+        const f16 bh = (f16)bs;
+        lds_qsh[r][lane >> 3] = __builtin_bit_cast(uint16_t, bh);
+        lds_qsl[r][lane >> 3] = __builtin_bit_cast(uint16_t, (f16)(bs - (float)bh));
+      }
     }
   }
   __syncthreads();  // every query row in LDS (rotated for a q4 K store), the new rows quantized
@@ -295,7 +309,8 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   if (own_new && wv == 0) {
     // Scores of the new position for the 16 heads (rows beyond nh are zero):
     // lane 4h + r sums a quarter of the dims of head h.
-    // For q4 keys the query is the rotated row, hi + lo.
+    // For q4 keys the query is the rotated row, hi + lo (dims 16..31 of each
+    // block stored divided by 16).
     const int h = lane >> 2, r = lane & 3;
     const uint16_t* qr = reinterpret_cast<const uint16_t*>(lds_q + h * QROW);
     const uint16_t* qrl = reinterpret_cast<const uint16_t*>(lds_ql + (KQ4 ? h * QROW : 0));
@@ -308,25 +323,19 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
       const float4 k0 = *reinterpret_cast<const float4*>(&nw_val[0][d]);
       const float4 k1 = *reinterpret_cast<const float4*>(&nw_val[0][d + 4]);
       const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      const float f = (KQ4 && (d & 31) >= 16) ? 16.0f : 1.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) zs = fmaf((float)qv[e] + (float)ql[e], kk[e], zs);
+      for (int e = 0; e < 8; ++e) zs = fmaf(((float)qv[e] + (float)ql[e]) * f, kk[e], zs);
     }
     zs += __shfl_xor(zs, 1);
     zs += __shfl_xor(zs, 2);
     if (r == 0) nw_z[h] = zs * a.c2;  // read in the epilogue, after its barrier
   }
 
-  // ---- q4 keys: the -8 offset of the codes per block, in the units of the
-  // MFMA results (codes * 2^-24): qb[j] = -8 * 2^-24 * (block sum of row c16).
-  float qb[8];
-  if constexpr (KQ4) {
-    const float4 s0 = *reinterpret_cast<const float4*>(&lds_qsum[c16][0]);
-    const float4 s1 = *reinterpret_cast<const float4*>(&lds_qsum[c16][4]);
-    const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) qb[j] = ss[j] * (-8.0f / 16777216.0f);
-  }
   const float c2s = a.c2 * 16777216.0f;
+  // q4 values: the bias and scale factor of the lane's nibbles (see pv_q4)
+  const uint32_t vbias = (c16 & 1) ? 0xE480E480u : kQ4NegBias;
+  const f16x2 vsc = (c16 & 1) ? (f16x2){(f16)0.0625f, (f16)0.0625f} : (f16x2){(f16)1.0f, (f16)1.0f};
   // ---- int8 keys: accumulator start values -1152 * (group sum of q) that
   // cancel the code bias.
   constexpr int NC = KQ4 ? 1 : SK::NG;
@@ -388,8 +397,9 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     const bool more2 = pn + STEP < end;
     float z[2][4];
     if constexpr (KQ4) {
-      scores_q4(tk, 0, end - p0, z, st + T::KS_OFF + 512 * kpar, qrow + 16 * q4, lds_ql + c16 * QROW + 16 * q4, qb,
-                c2s, q4);
+      scores_q4(tk, 0, end - p0, z, st + T::KS_OFF + 512 * kpar, qrow + 16 * q4, lds_ql + c16 * QROW + 16 * q4,
+                reinterpret_cast<const uint8_t*>(lds_qsh[c16]), reinterpret_cast<const uint8_t*>(lds_qsl[c16]), c2s,
+                c16, q4);
     } else {
       const uint8_t* qb = qrow + 32 * q4;
       f16x8 qv[4][2];
@@ -407,12 +417,12 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     read_v_q4<KQ4, KG64>(tv, st, c16, q4);
     const f16x8 pa = tile_softmax<SA>(z, acc, q4);
     if (more) issue_half<KQ4, KG64, 1>(st, vrw, vsrw, pn, end - pn, vrow, srow, lane);
-    pv_q4<1>(tv, pa, acc);
+    pv_q4<1>(tv, pa, acc, vbias, vsc);
     if (more) {
       wait_vm<T::NV>();  // K half of the next tile landed; its V half is in flight
       read_k(tk);
     }
-    pv_q4<2>(tv, pa, acc);
+    pv_q4<2>(tv, pa, acc, vbias, vsc);
     if (more2) issue_half<KQ4, KG64, 0>(st, krw, ksrw, pn + STEP, end - pn - STEP, krow, srow, lane, kpar);
   }
 

@@ -137,26 +137,44 @@ constexpr uint32_t kQ4NegBias = 0xE408E408u;  // fp16 pair (-1032, -1032)
 
 // Exact scores of a q4 K tile: z[ct][i] for positions x = 16 ct + 4 q4 + i of
 // query row c16 (log2 domain); positions outside [vlo, vhi) get -inf.
-// ks = the tile's 32 scale rows (16 bytes: the 8 block scales, fp16) in LDS;
-// qh + 64 j and ql + 64 j (LDS, 16 bytes each) hold the rotated query's dims
-// 32 j + 8 q4 .. +7 as hi and lo fp16 terms; qb[j] = -8 * 2^-24 * (sum of the
-// rotated query over block j) of row c16; c2s = sm_scale * log2(e) * 2^24.
-// With the codes entering the MFMA as code * 2^-24, block j gives
-// a_j = 2^-24 * sum_d code_d q_d (exact products, fp32 sums), and
-//   z = c2s * sum_j d_j * (a_j + qb[j])  =  c2 * sum_j d_j sum_d (code_d - 8) q_d,
+//   ks       the tile's 32 scale rows (16 bytes: the 8 block scales, fp16) in LDS;
+//   qh, ql   (LDS, + 64 j for block j) the rotated query's dims 32 j + 8 q4 .. +7
+//            as hi and lo fp16 terms, the dims 16..31 of each block (the lanes
+//            q4 = 2, 3) divided by 16;
+//   sh, sl   (LDS, 16 bytes) the row's 8 block sums of the rotated query as hi
+//            and lo fp16 terms (read by the lanes q4 = 0 only);
+//   c2s      sm_scale * log2(e) * 2^24.
+// The lanes q4 = 0, 1 take the low nibbles (code q) of their bytes and the
+// lanes q4 = 2, 3 the high ones in place (16 q), both as the fp16 subnormals
+// of the masked byte times 2^-24, so that with the /16 of their query dims
+// every product is exactly code * q_d * 2^-24. Block j gives
+// a_j = 2^-24 * sum_d code_d q_d (fp32 sums); one MFMA pair per C-tile gives
+// c = sum_j d_j Q_j over the row scales (k slots 0..7 of the lanes q4 = 0) and
+// the block sums, and
+//   z = c2s * (sum_j d_j a_j - 8 * 2^-24 * c)  =  c2 * sum_j d_j sum_d (code_d - 8) q_d,
 // the dequantized key (code - 8) * d taken without rounding. The query terms
 // are read block pair by block pair, so only two blocks' operands are live.
 __device__ __forceinline__ void scores_q4(const KQ4Regs& t, int vlo, int vhi, float (&z)[2][4],
                                           const uint8_t* __restrict__ ks, const uint8_t* __restrict__ qh,
-                                          const uint8_t* __restrict__ ql, const float (&qb)[8], float c2s, int q4) {
-  const uint32_t sh = 4u * (uint32_t)(q4 >> 1);  // q4 = 2, 3: the high nibbles (dims 16..31 of the block)
+                                          const uint8_t* __restrict__ ql, const uint8_t* __restrict__ sh,
+                                          const uint8_t* __restrict__ sl, float c2s, int c16, int q4) {
+  const uint32_t mask = q4 >= 2 ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const f16x8 fz = {};
+  const f16x8 bsh = q4 == 0 ? *reinterpret_cast<const f16x8*>(sh) : fz;
+  const f16x8 bsl = q4 == 0 ? *reinterpret_cast<const f16x8*>(sl) : fz;
+  f32x4 zz[2];
   u32x4 ps[2][4];  // the 8 block scales of row 16 ct + 4 q4 + i: the position of score z[ct][i]
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct)
+  for (int ct = 0; ct < 2; ++ct) {
+    const f16x8 own = *reinterpret_cast<const f16x8*>(ks + (16 * ct + c16) * 16);  // A: row c16's scales
+    f32x4 c = mfma16(own, bsh, zero);
+    c = mfma16(own, bsl, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zz[ct][i] = c[i] * (-8.0f / 16777216.0f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) ps[ct][i] = *reinterpret_cast<const u32x4*>(ks + (16 * ct + 4 * q4 + i) * 16);
-  f32x4 zz[2] = {zero, zero};
+  }
 #pragma unroll
   for (int jp = 0; jp < 4; ++jp) {
     f16x8 h[2], l[2];
@@ -170,16 +188,16 @@ __device__ __forceinline__ void scores_q4(const KQ4Regs& t, int vlo, int vhi, fl
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int j = 2 * jp + u;
-        const uint32_t w0 = (t.k[ct][j].x >> sh) & 0x0F0F0F0Fu;
-        const uint32_t w1 = (t.k[ct][j].y >> sh) & 0x0F0F0F0Fu;
-        const u32x4 a4 = {sub_h2_lo(w0), sub_h2_hi(w0), sub_h2_lo(w1), sub_h2_hi(w1)};  // code * 2^-24
+        const uint32_t w0 = t.k[ct][j].x & mask;
+        const uint32_t w1 = t.k[ct][j].y & mask;
+        const u32x4 a4 = {sub_h2_lo(w0), sub_h2_hi(w0), sub_h2_lo(w1), sub_h2_hi(w1)};  // (masked byte) * 2^-24
         f32x4 a = mfma16(__builtin_bit_cast(f16x8, a4), h[u], zero);
         a = mfma16(__builtin_bit_cast(f16x8, a4), l[u], a);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t sw = ps[ct][i][j >> 1];
           const f16 d = __builtin_bit_cast(f16x2, sw)[j & 1];
-          zz[ct][i] = fmaf(a[i] + qb[j], (float)d, zz[ct][i]);
+          zz[ct][i] = fmaf(a[i], (float)d, zz[ct][i]);
         }
       }
     __builtin_amdgcn_sched_barrier(0);
