@@ -210,6 +210,40 @@ def stream_reference(kvq, n_cu):
     return n / float(np.median(ts)) / 1e9, n / float(np.min(ts)) / 1e9, n
 
 
+def stream_at(kvq, n_cu, nbytes, copies=COPIES):
+    """What one launch of the read-only streaming kernel takes for exactly
+    `nbytes`: kvq_stream_read over `copies` rotating buffers of that size
+    (each last read `copies - 1` launches earlier, so not served by the
+    Infinity Cache), graphs of back-to-back launches as the decode steps are
+    timed; median over 5 timings of 2 graph replays. Returns us and GB/s."""
+    import torch
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda:0") for _ in range(copies)]
+    for b in bufs:
+        kvq.kvq_stream_read(b, nbytes, sink, n_cu)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for b in bufs:
+            kvq.kvq_stream_read(b, nbytes, sink, n_cu)
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / (2 * copies))
+    del bufs, g
+    torch.cuda.empty_cache()
+    us = float(np.median(ts))
+    return {"us": round(us, 2), "GB_s": round(nbytes / us / 1e3, 1),
+            "pct_hbm_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBS, 2)}
+
+
 def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
     """The decode step (kv_append_decode_splitk + kv_decode_reduce, graph-replayed)
     on the other two shapes the metric is quoted on, and the chunk attention of
@@ -834,8 +868,12 @@ def main() -> int:
         log("timing the decode step over the 4-bit stores (q4_0, k8v4) at 128K")
         others.update(q4_workloads(kvq, kvq_setup, wl, n_cu, args.steps))
 
-    log("timing the read-only streaming reference (4 GiB)")
+    log("timing the read-only streaming reference (4 GiB, and at each context's KV bytes)")
     stream_gbs, stream_best, stream_bytes = stream_reference(kvq, n_cu)
+    for d in sweep:
+        d["stream_at_size"] = stream_at(kvq, n_cu, d["kv_bytes_per_step"])
+        d["step_pct_of_stream_at_size"] = round(100 * d["stream_at_size"]["us"] / d["us_per_step"], 2)
+    stream_128k = stream_at(kvq, n_cu, wl.kv_bytes_per_step(w, lens))
 
     kv_bytes = wl.kv_bytes_per_step(w, lens)
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -860,7 +898,12 @@ def main() -> int:
                              "bytes": stream_bytes, "GB_s": round(stream_gbs, 1), "GB_s_best": round(stream_best, 1),
                              "pct_hbm_peak": round(100 * stream_gbs / HBM_PEAK_GBS, 2),
                              "step_pct_of_stream": round(100 * value / stream_gbs, 2),
-                             "partial_pct_of_stream": round(100 * achieved / stream_gbs, 2)},
+                             "partial_pct_of_stream": round(100 * achieved / stream_gbs, 2),
+                             "at_step_size": stream_128k,
+                             "step_pct_of_stream_at_size": round(100 * stream_128k["us"] / (ms_per_step * 1e3), 2),
+                             "partial_pct_of_stream_at_size": round(100 * stream_128k["us"] / (fpart_ms * 1e3), 2),
+                             "note": "at_step_size: one launch of the read-only kernel over exactly the step's "
+                                     "KV bytes, back to back in a graph as the steps are"},
         "step_us_percentiles": {"p10": round(float(np.percentile(per_replay, 10)), 2),
                                 "median": round(float(np.median(per_replay)), 2),
                                 "p90": round(float(np.percentile(per_replay, 90)), 2),

@@ -32,7 +32,7 @@
  *          row instead of one per kv head.
  *   [G130] genie-ai-runtime releases, v1.3.0 "split-K decode attention" and its
  *          "Details": the KV range of each head is split over blocks, each block
- *          forms an online-softmax partial, a reduce kernel combines them; the
+ *          forms an online-softmax partial and a second kernel merges them; the
  *          split count is fixed on the host while positions come from the
  *          device; sliding-window mask and slot width are honoured.
  *   [G121] genie-ai-runtime releases, v1.2.1 "Bugs fixed": head_dim 256 stored
@@ -242,7 +242,8 @@ int kv_append_decode_splitk(const kvq_layout* layout, void* k_store, void* v_sto
                             void* stream);
 
 /* kv_decode_reduce -- combine the partials of kv_decode_attn_splitk.
- * [G130: "a reduce kernel combines them"]. For each (b, hq): with split maxima
+ * [G130 "split-K decode attention": a separate kernel merges the split
+ * partials]. For each (b, hq): with split maxima
  * m_s, sums l_s and unnormalized outputs O_s, M = max m_s, w_s = exp(m_s - M),
  * out = sum_s w_s O_s / sum_s w_s l_s, rounded to fp16 (nearest even).
  * Splits recorded as empty add nothing; a sequence with no attended position
