@@ -185,3 +185,102 @@ def test_append_out_of_range_positions_are_not_written():
             np.testing.assert_array_equal(ks.rows_of(lay, cache["k"], b, ok, h), want)
             others = [p for p in range(16) if p not in ok]
             assert (ks.rows_of(lay, cache["k"], b, others, h) == 0x55).all()
+
+
+# Scales with at most three significant bits: absmax = 127 * s is an fp16
+# value whose quotient by 127 is s exactly, and every (k + 1/2) * s with
+# |k + 1/2| <= 126.5 is an fp16 value, so x / s lands exactly half-way between
+# two codes. 6 * 2^-24 is a subnormal scale.
+TIE_SCALES = (2.0 ** -6, 3 * 2.0 ** -8, 5 * 2.0 ** -9, 7 * 2.0 ** -9, 6 * 2.0 ** -24, 2.0 ** 4, 96.0)
+
+
+def _tie_rows(d, group, n_kv, seed):
+    """Rows [n][n_kv][d] whose groups each hold one +-127*s element and, for
+    the rest, exact ties (k + 1/2) * s; together they take every tie value
+    -126.5 .. 126.5 of every scale in TIE_SCALES."""
+    rng = np.random.default_rng(seed)
+    groups = []
+    for s in TIE_SCALES:
+        ties = (np.arange(-127, 127) + 0.5) * s
+        rng.shuffle(ties)
+        for i in range(0, len(ties), group - 1):
+            part = ties[i:i + group - 1]
+            g = np.concatenate([[127 * s * rng.choice([-1.0, 1.0])], part,
+                                rng.choice(ties, group - 1 - len(part))])
+            rng.shuffle(g)
+            groups.append(g)
+    per_row = n_kv * d // group
+    while len(groups) % per_row:
+        groups.append(groups[len(groups) % len(TIE_SCALES)])
+    x = np.concatenate(groups).reshape(-1, n_kv, d)
+    x16 = x.astype(np.float16)
+    assert np.array_equal(x16.astype(np.float64), x), "tie values must be exact in fp16"
+    return x16
+
+
+def _assert_ties(x, group):
+    """The oracle on the tie rows: every scale is one of TIE_SCALES, every
+    non-max element sits exactly half-way, and its code is the even neighbour."""
+    c, s = orc.quantize_rows(x, group)
+    s64 = np.repeat(s.astype(np.float64), group, axis=-1)
+    assert set(np.unique(s.astype(np.float64))) <= set(TIE_SCALES)
+    q = x.astype(np.float64) / s64
+    tie = np.abs(q) < 127
+    assert np.all(q[tie] - np.floor(q[tie]) == 0.5)
+    assert np.all(c[tie] % 2 == 0) and np.all(np.abs(c[tie] - q[tie]) == 0.5)
+    return c, s
+
+
+@pytest.mark.parametrize("group,d,v_dtype", [(64, 256, "int8"), (128, 128, "int8"), (256, 256, "int8"),
+                                             (64, 64, "int8"), (256, 256, "q4")])
+def test_append_every_exact_tie(group, d, v_dtype):
+    """Every exact half-way quotient of several scales rounds to the even code,
+    as in the oracle, through the append kernel (int8 stores, and the int8 K of
+    a layout whose V is a 4-bit store)."""
+    import int8_quantized_kv_quant_amd as kvq
+    ks = _setup()
+    x = _tie_rows(d, group, 2, seed=group + d)
+    n = x.shape[0]
+    lay = kvq.make_layout(2, d, n, 1, v_dtype=v_dtype, scale_group=group)
+    cache = kvq.alloc_cache(lay, 1)
+    v = np.ascontiguousarray(x[::-1])
+    ks.append_rows(lay, cache, 0, 0, x, v)
+    for s, rows in (("k", x), ("v", v)) if v_dtype == "int8" else (("k", x),):
+        for h in range(2):
+            want_c, want_s = _assert_ties(rows[:, h], group)
+            np.testing.assert_array_equal(ks.rows_of(lay, cache[s], 0, np.arange(n), h), want_c,
+                                          err_msg=f"{s} codes h={h}")
+            got_s = ks.scales_of(lay, cache[s + "_scales"], 0, np.arange(n), h)
+            np.testing.assert_array_equal(got_s.view(np.uint16), want_s.view(np.uint16))
+
+
+@pytest.mark.parametrize("group,d", [(64, 128), (256, 256)])
+def test_fused_step_every_exact_tie(group, d):
+    """The fused decode step appends tie rows at L_b - 1 with the same codes."""
+    import int8_quantized_kv_quant_amd as kvq
+    ks = _setup()
+    n_kv, n_q = 2, 8
+    x = _tie_rows(d, group, n_kv, seed=7 * group + d)
+    lens = np.array([1, 129, 700, 2049] * ((x.shape[0] + 3) // 4))[:x.shape[0]]
+    batch = len(lens)
+    lay = kvq.make_layout(n_kv, d, int(lens.max()), batch, scale_group=group)
+    cache = kvq.alloc_cache(lay, batch)
+    for b, L in enumerate(lens):
+        if L > 1:
+            rows = wl.uniform_rows(100 + b, (int(L) - 1, n_kv, d))
+            ks.append_rows_device(lay, cache, b, 0, torch.from_numpy(rows).cuda(),
+                                  torch.from_numpy(rows).cuda())
+    k_new = torch.from_numpy(x).cuda()
+    v_new = torch.from_numpy(np.ascontiguousarray(-x)).cuda()
+    q = torch.from_numpy(wl.uniform_rows(3, (batch, n_q, d))).cuda()
+    ld = torch.from_numpy(lens.astype(np.int32)).cuda()
+    kvq.decode(lay, cache, q, ld, 0, new_kv=(k_new, v_new), n_cu=ks.n_cu())
+    torch.cuda.synchronize()
+    for s, rows in (("k", x), ("v", -x)):
+        for h in range(n_kv):
+            want_c, want_s = _assert_ties(rows[:, h], group)
+            for b, L in enumerate(lens):
+                got = ks.rows_of(lay, cache[s], b, [int(L) - 1], h)[0]
+                np.testing.assert_array_equal(got, want_c[b], err_msg=f"{s} b={b} h={h}")
+                got_s = ks.scales_of(lay, cache[s + "_scales"], b, [int(L) - 1], h)[0]
+                np.testing.assert_array_equal(got_s.view(np.uint16), want_s[b].view(np.uint16))
