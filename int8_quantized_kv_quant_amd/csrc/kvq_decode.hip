@@ -41,9 +41,12 @@
 // copied the half's current tile into registers, so every half is loading the
 // next tile for about one tile of compute. Rows land as 16-byte chunks
 // XOR-swizzled by row, so the MFMA-layout reads are free of bank conflicts. A
-// store with fp32 rows (k8v32, k32v8, k32v32) is four times wider per
-// position; those variants read their operands straight from HBM into
-// registers instead.
+// store with fp32 rows is four times wider per position, so with one int8 and
+// one fp32 store (k8v32, k32v8) only the fp32 tile is staged (32 * 4D bytes per
+// wavefront) and the int8 operands load straight into a second register set;
+// all of tile t + 1's loads are in flight while tile t is computed (measured
+// 1.6 us shorter at context 32048 than loading each tile just before its
+// use). k32v32 reads both operands straight into registers.
 //
 // Bounds. Every K/V/scale load goes through a buffer resource whose size ends
 // at the last row of the context, and positions outside the split get an
@@ -79,12 +82,12 @@ struct PartialArgs {
   float c2;  // sm_scale * log2(e)
 };
 
-// ---- operand loads straight from HBM (any store dtype) --------------------------
+// ---- operand loads straight from HBM into registers (any store dtype) ----------
+// K operands (codes or fp32 rows, and an int8 store's scale rows) of the tile
+// at p0; positions at or beyond `end` read as zeros.
 template <class S>
-__device__ __forceinline__ void load_tile_global(KRegs<S>& t, VRegs<S>& tv, __amdgpu_buffer_rsrc_t krs,
-                                                 __amdgpu_buffer_rsrc_t vrs, __amdgpu_buffer_rsrc_t ksrs,
-                                                 __amdgpu_buffer_rsrc_t vsrs, int p0, int end, uint32_t krow,
-                                                 uint32_t vrow, uint32_t srow, int c16, int q4) {
+__device__ __forceinline__ void load_k_global(KRegs<S>& t, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t ksrs,
+                                              int p0, int end, uint32_t krow, uint32_t srow, int c16, int q4) {
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int pk = p0 + 16 * ct + c16;
@@ -112,6 +115,12 @@ __device__ __forceinline__ void load_tile_global(KRegs<S>& t, VRegs<S>& tv, __am
         }
       }
   }
+}
+
+// V operands (codes or fp32 rows, and an int8 store's scales) of the tile at p0.
+template <class S>
+__device__ __forceinline__ void load_v_global(VRegs<S>& tv, __amdgpu_buffer_rsrc_t vrs, __amdgpu_buffer_rsrc_t vsrs,
+                                              int p0, int end, uint32_t vrow, uint32_t srow, int c16, int q4) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int pv = p0 + kpos(e, q4);
@@ -140,6 +149,12 @@ __device__ __forceinline__ void load_tile_global(KRegs<S>& t, VRegs<S>& tv, __am
   }
 }
 
+// s_waitcnt vmcnt(0) as the compiler's own wait instruction (expcnt and
+// lgkmcnt fields at their maxima): unlike a wait in inline asm, the compiler
+// sees it, so it knows every register load issued before it has landed and adds
+// no waits of its own for them.
+__device__ __forceinline__ void wait_vm0_visible() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Float4 position of float4 f of a merge-slot row. The 16 lanes that write one
 // row at a time hold f = 4c + n for c = 0..15: XOR-ing bits 0-1 with bits 4-5
 // spreads them over the 16 distinct 16-byte bank groups.
@@ -150,13 +165,17 @@ template <int D, bool KI8, bool VI8, bool G64, int NW>
 __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   using S = Shape<D, KI8, VI8, G64>;
   constexpr bool kStaged = KI8 && VI8;
-  constexpr int STAGE_BYTES = kStaged ? Stage<S>::BYTES : 16;
+  // One store int8, the other fp32: the fp32 tile is staged in LDS, the int8
+  // operands go straight to registers.
+  constexpr bool kMix = KI8 != VI8;
+  using FS = F32Stage<S, !KI8>;
+  constexpr int STAGE_BYTES = kStaged ? Stage<S>::BYTES : (kMix ? FS::BYTES : 16);
   // One stage per wavefront. After its last tile a wavefront reuses its own
   // stage as its slot of the output merge (16 head rows of D floats, which fit
   // in a stage), so no wavefront waits for another before writing its slot.
   constexpr int SLOT_BYTES = 16 * D * 4;
-  constexpr int SLOT_PITCH = kStaged ? STAGE_BYTES : SLOT_BYTES;
-  static_assert(!kStaged || SLOT_BYTES <= STAGE_BYTES, "merge slot must fit in a stage");
+  constexpr int SLOT_PITCH = (kStaged || kMix) ? STAGE_BYTES : SLOT_BYTES;
+  static_assert(!(kStaged || kMix) || SLOT_BYTES <= STAGE_BYTES, "merge slot must fit in a stage");
   constexpr int ST_BYTES = NW * SLOT_PITCH;
   __shared__ __attribute__((aligned(16))) uint8_t lds_st[ST_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[16 * QOperand<S>::ROW];
@@ -230,6 +249,14 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   // as zeros). A query row lands as D consecutive fp16 values at the start of
   // its padded LDS row.
   constexpr int QROWS = 16 / NW;
+  KRegs<S> tk;  // int8 operands of the mixed stores' first tile, loaded first
+  VRegs<S> tv;
+  if constexpr (kMix) {
+    if (p0 < end) {
+      if constexpr (KI8) load_k_global<S>(tk, krs, ksrs, p0, end, krow, srow, c16, q4);
+      else load_v_global<S>(tv, vrs, vsrs, p0, end, vrow, srow, c16, q4);
+    }
+  }
   if (own_new && wv < 2) {
     const uint16_t* src = (wv == 0 ? a.k_new : a.v_new) + ((int64_t)b * a.n_kv + hk) * D;
     if (lane < D / 8) dma<16>(rsrc_words(src, 2 * D), lds_addr_of(reinterpret_cast<const uint8_t*>(nw_in[wv])),
@@ -255,10 +282,17 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       stage_issue<S, 1>(lds_st + wv * STAGE_BYTES, vrw, vsrw, p0, end - p0, krow, srow, lane);
     }
   }
+  u32x4 frw = {0, 0, 0, 0};  // the fp32 store of the mixed stores
+  if constexpr (kMix) {
+    frw = KI8 ? rsrc_words(static_cast<const char*>(a.v_store) + st_off * 4, (uint32_t)(((int64_t)(L - 1) * a.s_pos + D) * 4))
+              : rsrc_words(static_cast<const char*>(a.k_store) + st_off * 4, (uint32_t)(((int64_t)(L - 1) * a.s_pos + D) * 4));
+    if (p0 < end) f32stage_issue<S, !KI8>(lds_st + wv * STAGE_BYTES, frw, p0, end - p0, KI8 ? vrow : krow, lane);
+  }
 
   // ---- this wavefront's LDS loads have landed (the first tile's two halves may
   // still be loading); after the barrier every query row is in LDS.
   if (kStaged && p0 < end) wait_vm<2 * kHalfLoads<S>>();
+  else if (kMix && p0 < end) wait_vm<FS::LOADS>();
   else wait_vm<0>();
   if (own_new && wv < 2) {
     const bool i8 = wv == 0 ? KI8 : VI8;
@@ -352,7 +386,6 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     // of each half overlap the arithmetic that precedes their use.
     constexpr int NH = kHalfLoads<S>;
     uint8_t* const st = lds_st + wv * STAGE_BYTES;
-    KRegs<S> tk;
     if (p0 < end) {
       wait_vm<NH>();  // K half of the first tile landed (its V half may still be loading)
       stage_read_k<S>(tk, st, c16, q4);
@@ -378,11 +411,38 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       tile_pv<S, 2>(tv, pa, acc);
       if (more2) stage_issue<S, 0>(st, krw, ksrw, pn + STEP, end - pn - STEP, krow, srow, lane);
     }
+  } else if constexpr (kMix) {
+    // Pipeline over this wavefront's tiles: at the start of tile t all of its
+    // loads have landed; its fp32 operands are copied from the stage into
+    // registers, then tile t + 1's int8 operands (to a second register set)
+    // and fp32 tile (to the stage) start loading, in flight while t is
+    // computed.
+    uint8_t* const st = lds_st + wv * STAGE_BYTES;
+    const uint32_t frow = KI8 ? vrow : krow;
+    for (; p0 < end; p0 += STEP) {
+      const int pn = p0 + STEP;
+      const bool more = pn < end;
+      wait_vm0_visible();
+      if constexpr (KI8) f32stage_read_v<S>(tv, st, c16, q4);
+      else f32stage_read_k<S>(tk, st, c16, q4);
+      KRegs<S> tkn;
+      VRegs<S> tvn;
+      if (more) {
+        if constexpr (KI8) load_k_global<S>(tkn, krs, ksrs, pn, end, krow, srow, c16, q4);
+        else load_v_global<S>(tvn, vrs, vsrs, pn, end, vrow, srow, c16, q4);
+        f32stage_issue<S, !KI8>(st, frw, pn, end - pn, frow, lane);
+      }
+      float z[2][4];
+      tile_scores<S>(tk, end - p0, z, qb, corr, a.c2, q4);
+      const f16x8 pa = tile_softmax<S>(z, acc, q4);
+      tile_pv<S>(tv, pa, acc);
+      if constexpr (KI8) tk = tkn;
+      else tv = tvn;
+    }
   } else {
     for (; p0 < end; p0 += STEP) {
-      KRegs<S> tk;
-      VRegs<S> tv;
-      load_tile_global<S>(tk, tv, krs, vrs, ksrs, vsrs, p0, end, krow, vrow, srow, c16, q4);
+      load_k_global<S>(tk, krs, ksrs, p0, end, krow, srow, c16, q4);
+      load_v_global<S>(tv, vrs, vsrs, p0, end, vrow, srow, c16, q4);
       float z[2][4];
       tile_scores<S>(tk, end - p0, z, qb, corr, a.c2, q4);
       const f16x8 pa = tile_softmax<S>(z, acc, q4);

@@ -445,4 +445,77 @@ __device__ __forceinline__ void stage_read_v(VRegs<S>& t, const uint8_t* __restr
   }
 }
 
+
+// ---- LDS staging for an fp32 store (the fp32 side of k8v32 / k32v8) ----------------
+// One 32-position tile of fp32 rows: row r's 16-byte chunk c (dims 4c..4c+3)
+// sits at byte r * 4D + 16 * F32Stage::slot(r, c). The permutation of a row's
+// chunks is chosen for the MFMA-layout reads, which fetch 16 bytes per lane:
+//   K (S^T's A operand): 16 lanes read chunk c of rows r .. r + 15, so the low
+//     four chunk bits are XOR-ed with the row's;
+//   V (P.V's B operand): 16 lanes read one row at chunks NC*c16 + m, NC = the
+//     chunks per lane (D / 64), so the low log2(NC) bits are XOR-ed with bits
+//     4-5 (chunks 16 apart hit the same banks).
+// Both maps only change bits below the ones they depend on, so each is its own
+// inverse: the direct-to-LDS loads fetch chunk slot(r, c) into slot c.
+template <class S, bool IS_K>
+struct F32Stage {
+  static constexpr int CH = S::D / 4;  // 16-byte chunks per fp32 row
+  static constexpr int NC = S::D / 64;  // chunks of V per lane per position
+  static constexpr int BYTES = 32 * S::D * 4;
+  static constexpr int LOADS = BYTES / 1024;  // 1 KiB direct-to-LDS loads per tile
+  static __device__ __forceinline__ int slot(int r, int c) {
+    if constexpr (IS_K) return c ^ (r & 15);
+    else return c ^ ((c >> 4) & (NC - 1));
+  }
+};
+
+// Load the fp32 tile at p0 (positions >= nvalid read as zeros) into a stage.
+template <class S, bool IS_K>
+__device__ __forceinline__ void f32stage_issue(uint8_t* st, const u32x4& rs, int p0, int nvalid, uint32_t row,
+                                               int lane) {
+  using T = F32Stage<S, IS_K>;
+  // this wavefront's LDS reads of the stage's previous tile have completed
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const uint32_t base = lds_addr_of(st);
+  const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)p0 * row);
+#pragma unroll
+  for (int i = 0; i < T::LOADS; ++i) {
+    const int sl = i * 64 + lane;
+    const int r = sl / T::CH;
+    const uint32_t off = r < nvalid ? (uint32_t)r * row + 16 * T::slot(r, sl % T::CH) : kOOB;
+    dma<16, kNtCodes>(rs, base + 1024 * i, off, soff);
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void f32stage_read_k(KRegs<S>& t, const uint8_t* __restrict__ st, int c16, int q4) {
+  using T = F32Stage<S, true>;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int r = 16 * ct + c16;
+#pragma unroll
+    for (int j = 0; j < S::NJ; ++j)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        t.k[ct][j][m] = *reinterpret_cast<const u32x4*>(st + r * 4 * S::D + 16 * T::slot(r, 16 * j + 4 * q4 + m));
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void f32stage_read_v(VRegs<S>& t, const uint8_t* __restrict__ st, int c16, int q4) {
+  using T = F32Stage<S, false>;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int r = kpos(e, q4);
+#pragma unroll
+    for (int m = 0; m < T::NC; ++m) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * 4 * S::D + 16 * T::slot(r, T::NC * c16 + m));
+      t.v[e][4 * m + 0] = v.x;
+      t.v[e][4 * m + 1] = v.y;
+      t.v[e][4 * m + 2] = v.z;
+      t.v[e][4 * m + 3] = v.w;
+    }
+  }
+}
+
 }  // namespace kvq
