@@ -12,9 +12,11 @@
 // with direct-to-LDS loads, one half refilling while the other is computed.
 //
 // Query. A q4 K store holds rotated keys, so the query rows are rotated the
-// same way in LDS (fwht256 in fp32) before any score; with H / 16 orthonormal,
-// q_rot . k_rot = q . k. The rotated rows are kept as hi + lo fp16 terms (22
-// significant bits), with their fp32 sums per Q4_0 block.
+// same way in LDS (fwht256 in fp32, lane exchanges in registers) before any
+// score; with H / 16 orthonormal, q_rot . k_rot = q . k. The rotated rows are
+// kept as hi + lo fp16 terms (22 significant bits), with their fp32 sums per
+// Q4_0 block; each lane holds its operands of them in registers for the whole
+// split.
 // Keys (q4), exact scores. One pair of MFMAs v_mfma_f32_16x16x32_f16 contracts
 // one Q4_0 block (32 dims) of 16 positions with the hi and the lo query terms;
 // the codes enter as the fp16 subnormals code * 2^-24 (a byte permute, no
@@ -294,9 +296,9 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
       *reinterpret_cast<u32x2*>(qr) = (u32x2){as_u32(h01), as_u32(h23)};
       *reinterpret_cast<u32x2*>(lds_ql + r * QROW + 8 * lane) = (u32x2){as_u32(l01), as_u32(l23)};
       float bs = (v[0] + v[1]) + (v[2] + v[3]);
-      bs += __shfl_xor(bs, 1);
-      bs += __shfl_xor(bs, 2);
-      bs += __shfl_xor(bs, 4);
+      bs += lane_xor<1>(bs);
+      bs += lane_xor<2>(bs);
+      bs += lane_xor<4>(bs);
       if ((lane & 7) == 0) {
         const f16 bh = (f16)bs;
         lds_qsh[r][lane >> 3] = __builtin_bit_cast(uint16_t, bh);
@@ -385,6 +387,10 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   // Tile n of this wavefront keeps its q4 K scale rows in half n & 1 of the K
   // scale region until its scores are taken (the K half of tile n + 2 is
   // issued after them).
+  Q4Query qy;  // the rotated query's operands, in registers for the whole split
+  if constexpr (KQ4)
+    load_q4_query(qy, qrow + 16 * q4, lds_ql + c16 * QROW + 16 * q4, reinterpret_cast<const uint8_t*>(lds_qsh[c16]),
+                  reinterpret_cast<const uint8_t*>(lds_qsl[c16]), q4);
   int kpar = 0;
   if (p0 < end) {
     wait_vm<T::NV>();  // K half of the first tile landed (its V half may still be loading)
@@ -397,9 +403,7 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     const bool more2 = pn + STEP < end;
     float z[2][4];
     if constexpr (KQ4) {
-      scores_q4(tk, 0, end - p0, z, st + T::KS_OFF + 512 * kpar, qrow + 16 * q4, lds_ql + c16 * QROW + 16 * q4,
-                reinterpret_cast<const uint8_t*>(lds_qsh[c16]), reinterpret_cast<const uint8_t*>(lds_qsl[c16]), c2s,
-                c16, q4);
+      scores_q4(tk, 0, end - p0, z, st + T::KS_OFF + 512 * kpar, qy, c2s, c16, q4);
     } else {
       const uint8_t* qb = qrow + 32 * q4;
       f16x8 qv[4][2];

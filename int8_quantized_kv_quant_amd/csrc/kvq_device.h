@@ -84,6 +84,53 @@ __device__ __forceinline__ f16x8 f32x8_to_f16x8(u32x4 a, u32x4 b) {
   return __builtin_bit_cast(f16x8, r);
 }
 
+// ---- cross-lane exchanges in registers (no LDS round trip) -----------------------
+// The value of lane l ^ M (M = 1, 2, 4, 8) by DPP moves, each a gather from
+// one lane: quad permutations give l ^ 1, l ^ 2 and l ^ 3, the half-row mirror
+// l ^ 7 (within 8 lanes) and the row mirror l ^ 15 (within 16); l ^ 4 is
+// (l ^ 7) ^ 3 and l ^ 8 is (l ^ 15) ^ 7.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "DPP lane exchange");
+  if constexpr (M == 1) return dpp_u32<0xB1>(x);        // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_u32<0x4E>(x);   // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) return dpp_u32<0x1B>(dpp_u32<0x141>(x));  // half-row mirror, quad_perm [3,2,1,0]
+  else return dpp_u32<0x141>(dpp_u32<0x140>(x));        // row mirror, half-row mirror
+}
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+  return __builtin_bit_cast(float, lane_xor_u32<M>(__builtin_bit_cast(uint32_t, x)));
+}
+template <int M>
+__device__ __forceinline__ int lane_xor(int x) {
+  return (int)lane_xor_u32<M>((uint32_t)x);
+}
+// The values of both lanes of the pair (l, l ^ M), M = 16 or 32, the lower
+// lane's (bit M clear) in .x: v_permlane16_swap / v_permlane32_swap with x in
+// both operands exchange the odd 16-lane rows (upper 32 lanes) of the first
+// with the even rows (lower 32 lanes) of the second, so the first result holds
+// the lower lane's value and the second the upper lane's, in both lanes.
+template <int M>
+__device__ __forceinline__ float2 lane_pair(float x) {
+  static_assert(M == 16 || M == 32, "permlane swap distance");
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  uint32_t lo, hi;
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = r[0];
+    hi = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = r[0];
+    hi = r[1];
+  }
+  return make_float2(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }

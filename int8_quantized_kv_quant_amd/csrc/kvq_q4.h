@@ -13,12 +13,31 @@
 
 namespace kvq {
 
+// One butterfly stage of fwht256 between lanes l and l ^ M (elements 4M
+// apart): the lower element keeps a + b, the upper one a - b, each as
+// fma(+-1, b, a) or fma(+-1, own, partner) with an exact product, so it rounds
+// exactly as the sum or the difference.
+template <int M>
+__device__ __forceinline__ void fwht_stage(float (&v)[4], int lane) {
+  const float sgn = (lane & M) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (M < 16) {
+      v[k] = fmaf(sgn, v[k], lane_xor<M>(v[k]));
+    } else {
+      const float2 ab = lane_pair<M>(v[k]);  // (a, b): the lower and the upper lane's value
+      v[k] = fmaf(sgn, ab.y, ab.x);
+    }
+  }
+}
+
 // y = H x / 16 for the 256 values of one row, lane l holding elements
 // 4l .. 4l+3 in v[0..3] (all 64 lanes of the wavefront take part). fp32
 // butterflies (a, b) -> (a + b, a - b) over index pairs at distance 1, 2, 4,
 // ..., 128, in that order, then * 1/16 (exact): every step is one correctly
 // rounded fp32 addition or subtraction, so the result does not depend on how
-// the pairs are assigned to lanes.
+// the pairs are assigned to lanes. The lane exchanges are DPP moves and
+// permlane swaps (registers only).
 __device__ __forceinline__ void fwht256(float (&v)[4], int lane) {
 #pragma clang fp contract(off)
   float a = v[0] + v[1], b = v[0] - v[1], c = v[2] + v[3], d = v[2] - v[3];
@@ -26,17 +45,12 @@ __device__ __forceinline__ void fwht256(float (&v)[4], int lane) {
   v[2] = a - c;
   v[1] = b + d;
   v[3] = b - d;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {  // distance 4m between the paired elements
-    // the lower element keeps a + b, the upper one a - b: p + (+-1) * v, the
-    // product exact, so the fused form rounds exactly as the sum or difference
-    const float sgn = (lane & m) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float p = __shfl_xor(v[k], m);
-      v[k] = fmaf(sgn, v[k], p);
-    }
-  }
+  fwht_stage<1>(v, lane);
+  fwht_stage<2>(v, lane);
+  fwht_stage<4>(v, lane);
+  fwht_stage<8>(v, lane);
+  fwht_stage<16>(v, lane);
+  fwht_stage<32>(v, lane);
 #pragma unroll
   for (int k = 0; k < 4; ++k) v[k] *= 0.0625f;
 }
@@ -62,16 +76,16 @@ __device__ __forceinline__ uint32_t q4_quantize(const float (&y)[4], int lane, u
       m = y[k];
       idx = 4 * lb + k;
     }
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) {
-    const float pam = __shfl_xor(am, o), pm = __shfl_xor(m, o);
-    const int pidx = __shfl_xor(idx, o);
+  auto take = [&](float pam, float pm, int pidx) {
     if (pam > am || (pam == am && pidx < idx)) {
       am = pam;
       m = pm;
       idx = pidx;
     }
-  }
+  };
+  take(lane_xor<1>(am), lane_xor<1>(m), lane_xor<1>(idx));
+  take(lane_xor<2>(am), lane_xor<2>(m), lane_xor<2>(idx));
+  take(lane_xor<4>(am), lane_xor<4>(m), lane_xor<4>(idx));
   const float d = m * -0.125f;
   const float r = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
   uint32_t codes = 0;
@@ -82,7 +96,7 @@ __device__ __forceinline__ uint32_t q4_quantize(const float (&y)[4], int lane, u
   }
   *scale_bits = __builtin_bit_cast(uint16_t, (f16)d);
   if (own) *own = codes;
-  const uint32_t hi = (uint32_t)__shfl_xor((int)codes, 4);  // codes of values 16 + 4 * (lane & 3) + k
+  const uint32_t hi = lane_xor_u32<4>(codes);  // codes of values 16 + 4 * (lane & 3) + k
   return codes | (hi << 4);
 }
 

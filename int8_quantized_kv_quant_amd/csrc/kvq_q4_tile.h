@@ -135,14 +135,34 @@ __device__ __forceinline__ void read_k_q4(KQ4Regs& t, const uint8_t* __restrict_
 
 constexpr uint32_t kQ4NegBias = 0xE408E408u;  // fp16 pair (-1032, -1032)
 
+// Query operands of scores_q4 for lane (c16, q4), loaded once per split: for
+// block j the rotated query's dims 32 j + 8 q4 .. +7 of row c16 as hi and lo
+// fp16 terms (the dims 16..31 of each block, lanes q4 = 2, 3, divided by 16),
+// and, in the lanes q4 = 0, the row's 8 block sums as hi and lo terms (zero in
+// the other lanes).
+struct Q4Query {
+  f16x8 h[8], l[8];
+  f16x8 sh, sl;
+};
+
+// qh, ql: LDS rows of the hi and lo terms (+ 64 j for block j, lane's q4
+// offset included); sh, sl: LDS block sums of row c16.
+__device__ __forceinline__ void load_q4_query(Q4Query& q, const uint8_t* qh, const uint8_t* ql, const uint8_t* sh,
+                                              const uint8_t* sl, int q4) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    q.h[j] = *reinterpret_cast<const f16x8*>(qh + 64 * j);
+    q.l[j] = *reinterpret_cast<const f16x8*>(ql + 64 * j);
+  }
+  const f16x8 fz = {};
+  q.sh = q4 == 0 ? *reinterpret_cast<const f16x8*>(sh) : fz;
+  q.sl = q4 == 0 ? *reinterpret_cast<const f16x8*>(sl) : fz;
+}
+
 // Exact scores of a q4 K tile: z[ct][i] for positions x = 16 ct + 4 q4 + i of
 // query row c16 (log2 domain); positions outside [vlo, vhi) get -inf.
 //   ks       the tile's 32 scale rows (16 bytes: the 8 block scales, fp16) in LDS;
-//   qh, ql   (LDS, + 64 j for block j) the rotated query's dims 32 j + 8 q4 .. +7
-//            as hi and lo fp16 terms, the dims 16..31 of each block (the lanes
-//            q4 = 2, 3) divided by 16;
-//   sh, sl   (LDS, 16 bytes) the row's 8 block sums of the rotated query as hi
-//            and lo fp16 terms (read by the lanes q4 = 0 only);
+//   qy       the query operands (Q4Query);
 //   c2s      sm_scale * log2(e) * 2^24.
 // The lanes q4 = 0, 1 take the low nibbles (code q) of their bytes and the
 // lanes q4 = 2, 3 the high ones in place (16 q), both as the fp16 subnormals
@@ -152,56 +172,40 @@ constexpr uint32_t kQ4NegBias = 0xE408E408u;  // fp16 pair (-1032, -1032)
 // c = sum_j d_j Q_j over the row scales (k slots 0..7 of the lanes q4 = 0) and
 // the block sums, and
 //   z = c2s * (sum_j d_j a_j - 8 * 2^-24 * c)  =  c2 * sum_j d_j sum_d (code_d - 8) q_d,
-// the dequantized key (code - 8) * d taken without rounding. The query terms
-// are read block pair by block pair, so only two blocks' operands are live.
+// the dequantized key (code - 8) * d taken without rounding.
 __device__ __forceinline__ void scores_q4(const KQ4Regs& t, int vlo, int vhi, float (&z)[2][4],
-                                          const uint8_t* __restrict__ ks, const uint8_t* __restrict__ qh,
-                                          const uint8_t* __restrict__ ql, const uint8_t* __restrict__ sh,
-                                          const uint8_t* __restrict__ sl, float c2s, int c16, int q4) {
+                                          const uint8_t* __restrict__ ks, const Q4Query& qy, float c2s, int c16,
+                                          int q4) {
   const uint32_t mask = q4 >= 2 ? 0xF0F0F0F0u : 0x0F0F0F0Fu;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  const f16x8 fz = {};
-  const f16x8 bsh = q4 == 0 ? *reinterpret_cast<const f16x8*>(sh) : fz;
-  const f16x8 bsl = q4 == 0 ? *reinterpret_cast<const f16x8*>(sl) : fz;
   f32x4 zz[2];
   u32x4 ps[2][4];  // the 8 block scales of row 16 ct + 4 q4 + i: the position of score z[ct][i]
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const f16x8 own = *reinterpret_cast<const f16x8*>(ks + (16 * ct + c16) * 16);  // A: row c16's scales
-    f32x4 c = mfma16(own, bsh, zero);
-    c = mfma16(own, bsl, c);
+    f32x4 c = mfma16(own, qy.sh, zero);
+    c = mfma16(own, qy.sl, c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) zz[ct][i] = c[i] * (-8.0f / 16777216.0f);
 #pragma unroll
     for (int i = 0; i < 4; ++i) ps[ct][i] = *reinterpret_cast<const u32x4*>(ks + (16 * ct + 4 * q4 + i) * 16);
   }
 #pragma unroll
-  for (int jp = 0; jp < 4; ++jp) {
-    f16x8 h[2], l[2];
+  for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      h[u] = *reinterpret_cast<const f16x8*>(qh + 64 * (2 * jp + u));
-      l[u] = *reinterpret_cast<const f16x8*>(ql + 64 * (2 * jp + u));
-    }
+    for (int ct = 0; ct < 2; ++ct) {
+      const uint32_t w0 = t.k[ct][j].x & mask;
+      const uint32_t w1 = t.k[ct][j].y & mask;
+      const u32x4 a4 = {sub_h2_lo(w0), sub_h2_hi(w0), sub_h2_lo(w1), sub_h2_hi(w1)};  // (masked byte) * 2^-24
+      f32x4 a = mfma16(__builtin_bit_cast(f16x8, a4), qy.h[j], zero);
+      a = mfma16(__builtin_bit_cast(f16x8, a4), qy.l[j], a);
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int j = 2 * jp + u;
-        const uint32_t w0 = t.k[ct][j].x & mask;
-        const uint32_t w1 = t.k[ct][j].y & mask;
-        const u32x4 a4 = {sub_h2_lo(w0), sub_h2_hi(w0), sub_h2_lo(w1), sub_h2_hi(w1)};  // (masked byte) * 2^-24
-        f32x4 a = mfma16(__builtin_bit_cast(f16x8, a4), h[u], zero);
-        a = mfma16(__builtin_bit_cast(f16x8, a4), l[u], a);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t sw = ps[ct][i][j >> 1];
-          const f16 d = __builtin_bit_cast(f16x2, sw)[j & 1];
-          zz[ct][i] = fmaf(a[i], (float)d, zz[ct][i]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t sw = ps[ct][i][j >> 1];
+        const f16 d = __builtin_bit_cast(f16x2, sw)[j & 1];
+        zz[ct][i] = fmaf(a[i], (float)d, zz[ct][i]);
       }
-    __builtin_amdgcn_sched_barrier(0);
-  }
+    }
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
