@@ -157,7 +157,8 @@ def _small(name="inv", H=2, G=4, d=128, g=64, max_ctx=300, kdt="int8", vdt="int8
 
 @pytest.mark.parametrize("kdt,vdt,g,d", [("int8", "int8", 64, 256), ("int8", "int8", 128, 128),
                                          ("int8", "fp32", 64, 128), ("fp32", "int8", 64, 64),
-                                         ("fp32", "fp32", 256, 256)])
+                                         ("int8", "fp32", 64, 256), ("fp32", "int8", 64, 256),
+                                         ("fp32", "int8", 128, 128), ("fp32", "fp32", 256, 256)])
 def test_ragged_lengths_and_split_sweep(kdt, vdt, g, d):
     """Lengths 0, 1, 31, 33, 64, 95, 300 in one batch; every split count from 1
     to the maximum gives the oracle's result within tolerance."""
