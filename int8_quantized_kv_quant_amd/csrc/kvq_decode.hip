@@ -419,14 +419,14 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     // computed.
     uint8_t* const st = lds_st + wv * STAGE_BYTES;
     const uint32_t frow = KI8 ? vrow : krow;
+    KRegs<S> tkn = {};  // the int8 operands of tile t + 1 (after the last tile: the last ones again)
+    VRegs<S> tvn = {};
     for (; p0 < end; p0 += STEP) {
       const int pn = p0 + STEP;
       const bool more = pn < end;
       wait_vm0_visible();
       if constexpr (KI8) f32stage_read_v<S>(tv, st, c16, q4);
       else f32stage_read_k<S>(tk, st, c16, q4);
-      KRegs<S> tkn;
-      VRegs<S> tvn;
       if (more) {
         if constexpr (KI8) load_k_global<S>(tkn, krs, ksrs, pn, end, krow, srow, c16, q4);
         else load_v_global<S>(tvn, vrs, vsrs, pn, end, vrow, srow, c16, q4);
