@@ -157,7 +157,8 @@ def cpu_baseline(w, lens, q, sm):
     step (both kv heads, 131072 positions) over the dequantized cache in fp64,
     repeated for about 10 s with the BLAS threads it has by default, then for
     about 10 s on one thread. Returns (output, seconds per step, threads,
-    repetitions, seconds per step on one thread, its repetitions)."""
+    repetitions, seconds per step on one thread, its repetitions, the oracle's
+    cache)."""
     from oracle import kvq_oracle as orc
     import workloads as wl
     try:
@@ -183,7 +184,7 @@ def cpu_baseline(w, lens, q, sm):
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
             _, dt1, reps1 = timed()
-    return want, dt, cores, reps, dt1, reps1
+    return want, dt, cores, reps, dt1, reps1, cache
 
 
 def stream_reference(kvq, n_cu):
@@ -501,6 +502,50 @@ def chunk_workload(kvq, kvq_setup, wl, n_cu, name="long"):
             + " + kvq_reduce_kernel"}
 
 
+def verify_windows(kvq, wl, w, lay, caches, L, n_cu, capture, replay_ms, reps, oc=None, sizes=(2, 4, 8)):
+    """kv_chunk_attn (partials + combine) of a verify window of T tokens at
+    positions L - T .. L - 1 over the 128K caches of the headline step (all
+    copies, graph-replayed as the steps are; causal inside the window). The
+    keys are read once per 16-row block: T * 8 (token, head) rows per kv head
+    up to 32 go through the decode partial kernel (chunk rows), more through
+    the chunk kernel. The first and last token of each window are checked
+    against the fp64 oracle (its cache oc of positions [0, L), built here if
+    not given)."""
+    import torch
+    from oracle import kvq_oracle as orc
+    dev = torch.device("cuda:0")
+    sm = 1.0 / math.sqrt(w.head_dim)
+    if oc is None:
+        oc = orc.Cache(1, L, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+        oc.append(wl.kv_rows(w, "k", 0, 0, L)[None], wl.kv_rows(w, "v", 0, 0, L)[None], [0])
+    kvb = wl.kv_bytes_per_step(w, np.array([L]))
+    res = []
+    for T in sizes:
+        start = L - T
+        qh = wl.chunk_queries(w, T)
+        q = torch.from_numpy(qh).to(dev)
+        sp = torch.tensor([start], dtype=torch.int32, device=dev)
+        plan = kvq.kvq_plan_chunk(lay, 1, T, w.n_q_heads, L, 0, n_cu)
+        ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device=dev)
+        o = torch.empty((1, T, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+
+        def call(c):
+            kvq.kv_chunk_attn(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], q, 1, T, w.n_q_heads, sp, 0, sm,
+                              plan, ws, ws.numel(), o)
+
+        ms = replay_ms(capture(call), reps)
+        got = o.float().cpu().numpy().astype(np.float64)
+        toks = [(0, 0), (0, T - 1)]
+        want = orc.attend_chunk(qh, oc, np.array([start]), 0, sm, tokens=toks)
+        err = max(float(np.abs(got[b, t] - want[b, t]).max()) for b, t in toks)
+        rows = T * (w.n_q_heads // w.n_kv_heads)
+        res.append({"tokens": T, "start": start, "rows_per_kv_head": rows, "us": round(ms * 1e3, 2),
+                    "kv_bytes_once": int(kvb), "GB_s_once": round(kvb / ms / 1e6, 1),
+                    "n_splits": plan.n_splits, "chunk": plan.chunk, "max_abs_err_sampled": err, "tol": TOL})
+        del ws
+    return res
+
+
 def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
     """The decode step over the 4-bit stores at the long-context shape (Strata
     PR 2698, "Not in this PR": q4_0 for K and V, k8v4 for V only, Hadamard-
@@ -746,9 +791,10 @@ def main() -> int:
     got = out.cpu().numpy().astype(np.float64)
 
     cpu = None
+    oracle_cache = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the full step")
-        want, cpu_s, cores, cpu_reps, cpu_s1, cpu_reps1 = cpu_baseline(w, lens, q, sm)
+        want, cpu_s, cores, cpu_reps, cpu_s1, cpu_reps1, oracle_cache = cpu_baseline(w, lens, q, sm)
         max_err = float(np.abs(got - want).max())
         kv_bytes = wl.kv_bytes_per_step(w, lens)
         cpu = {"value": round(kv_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": int(cores),
@@ -855,6 +901,10 @@ def main() -> int:
                       "codes_bitexact": codes_match(kvq_setup, lay, caches[-1], w, 0, [Lc - 1, Lc - 2, 7])})
         del ws_c
     log("context sweep: " + ", ".join(f"{d['context']}: {d['us_per_step']} us" for d in sweep))
+    log("timing verify windows of 2, 4 and 8 tokens at the end of the 128K context")
+    verify = verify_windows(kvq, wl, w, lay, caches, L, n_cu, capture, replay_ms, reps, oracle_cache)
+    del oracle_cache
+    log("verify windows: " + ", ".join(f"T={d['tokens']}: {d['us']} us" for d in verify))
 
     others = None
     if not args.no_other_workloads:
@@ -911,6 +961,7 @@ def main() -> int:
                                 "note": "50 graph replays timed one by one, beside the --steps timed ones"},
         "hot_cache_us_per_step": round(hot_ms * 1e3, 2),
         "context_sweep": sweep,
+        "verify_windows": verify,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -939,6 +990,7 @@ def main() -> int:
     }
     print(json.dumps(res), flush=True)
     ok = codes_ok and graph_matches_eager and (max_err is None or max_err <= TOL)
+    ok = ok and all(d["max_abs_err_sampled"] <= TOL for d in verify)
     return 0 if ok else 1
 
 

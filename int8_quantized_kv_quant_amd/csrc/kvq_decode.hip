@@ -80,6 +80,12 @@ struct PartialArgs {
   int32_t n_kv, G, n_q, head_blocks;
   int32_t n_splits, chunk, window;
   float c2;  // sm_scale * log2(e)
+  // Chunk attention through this kernel (the CHUNK instances): T tokens per
+  // sequence at positions start_pos[b] + t; the query rows of a kv head are
+  // its (token, head) pairs t * G + h, in blocks of 16 (head_blocks of them),
+  // q is fp16 [B][T][n_q][D], and the partial rows are (b, t, hq).
+  const int32_t* start_pos;
+  int32_t T;
 };
 
 // ---- operand loads straight from HBM into registers (any store dtype) ----------
@@ -161,10 +167,11 @@ __device__ __forceinline__ void wait_vm0_visible() { __builtin_amdgcn_s_waitcnt(
 __device__ __forceinline__ int merge_swz(int f) { return f ^ ((f >> 4) & 3); }
 
 // ---- kernel ----------------------------------------------------------------------
-template <int D, bool KI8, bool VI8, bool G64, int NW>
+template <int D, bool KI8, bool VI8, bool G64, int NW, bool CHUNK = false>
 __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   using S = Shape<D, KI8, VI8, G64>;
   constexpr bool kStaged = KI8 && VI8;
+  static_assert(!CHUNK || kStaged, "chunk rows through the int8 kernel only");
   // One store int8, the other fp32: the fp32 tile is staged in LDS, the int8
   // operands go straight to registers.
   constexpr bool kMix = KI8 != VI8;
@@ -195,14 +202,37 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   const int hblk = blockIdx.y % a.head_blocks;
   const int b = blockIdx.z;
 
-  const int nh = min(16, a.G - hblk * 16);
-  const int hq0 = hk * a.G + hblk * 16;
+  // Query rows of the workgroup (up to 16) and the keys [lo, L) they attend.
+  // Decode: heads hblk * 16 .. of kv head hk, at context seq_lens[b]. Chunk:
+  // flat rows fr0 + r = t * G + h of kv head hk; token t sits at s0 + t and
+  // attends [max(0, s0 + t + 1 - window) (window > 0), s0 + t + 1).
+  const int fr0 = hblk * 16;
+  const int nh = CHUNK ? min(16, a.T * a.G - fr0) : min(16, a.G - fr0);
+  const int hq0 = hk * a.G + fr0;
   const int64_t row0 = ((int64_t)b * a.n_q + hq0) * a.n_splits + split;
-  float2* const ml_out = reinterpret_cast<float2*>(a.ws_ml) + row0;
-
-  const int L_in = a.seq_lens[b];
-  const int L = L_in < 0 ? 0 : (L_in > a.max_ctx ? a.max_ctx : L_in);
-  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+  float2* const ml = reinterpret_cast<float2*>(a.ws_ml);
+  // Partial row (within ws) of the workgroup's row r < nh.
+  auto rowid = [&](int r) -> int64_t {
+    if constexpr (CHUNK) {
+      const int fr = fr0 + r;
+      return (((int64_t)b * a.T + fr / a.G) * a.n_q + hk * a.G + fr % a.G) * a.n_splits + split;
+    } else {
+      return row0 + (int64_t)r * a.n_splits;
+    }
+  };
+  int L_in, L, lo, s0 = 0;
+  if constexpr (CHUNK) {
+    s0 = a.start_pos[b];
+    s0 = s0 < 0 ? 0 : (s0 > a.max_ctx ? a.max_ctx : s0);
+    const int t_first = fr0 / a.G, t_last = min(a.T - 1, (fr0 + nh - 1) / a.G);
+    L = (int)min((int64_t)s0 + t_last + 1, (int64_t)a.max_ctx);
+    lo = a.window > 0 ? max(0, s0 + t_first + 1 - a.window) : 0;
+    L_in = -1;  // no fused append
+  } else {
+    L_in = a.seq_lens[b];
+    L = L_in < 0 ? 0 : (L_in > a.max_ctx ? a.max_ctx : L_in);
+    lo = a.window > 0 ? max(0, L - a.window) : 0;
+  }
   // Split s takes the blocks s, s + S, s + 2 S, ... of BLK positions of
   // [lo, L) (block-cyclic), S = min(n_splits, ceil((L - lo) / chunk)): as many
   // splits as contiguous ranges of `chunk` positions would use, each reading
@@ -211,14 +241,14 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   const int n_used = (int)min((int64_t)a.n_splits, ((int64_t)L - lo + a.chunk - 1) / a.chunk);
   const int64_t start64 = (int64_t)lo + (int64_t)split * BLK;
   if (split >= n_used || start64 >= L) {  // empty split: recorded as (m, l) = (-inf, 0), O not written
-    if (threadIdx.x < nh) ml_out[(int64_t)threadIdx.x * a.n_splits] = make_float2(-INFINITY, 0.0f);
+    if ((int)threadIdx.x < nh) ml[rowid(threadIdx.x)] = make_float2(-INFINITY, 0.0f);
     return;
   }
   const int start = (int)start64;
   int end = L;
   // Fused append: the workgroup whose blocks hold position L - 1 takes the new
   // row from the quantizer instead of the cache, and its tiles stop before it.
-  const bool own_new = a.k_new != nullptr && L_in == L && ((L - 1 - lo) / BLK) % n_used == split;
+  const bool own_new = !CHUNK && a.k_new != nullptr && L_in == L && ((L - 1 - lo) / BLK) % n_used == split;
   if (own_new) end = L - 1;
 
   const int lane = threadIdx.x & 63;
@@ -262,7 +292,17 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     if (lane < D / 8) dma<16>(rsrc_words(src, 2 * D), lds_addr_of(reinterpret_cast<const uint8_t*>(nw_in[wv])),
                               16u * lane, 0u);
   }
-  {
+  if constexpr (CHUNK) {  // the rows of this block: q [b][t][hk * G + h]
+    const u32x4 qrs = rsrc_words(a.q + (int64_t)b * a.T * a.n_q * D, (uint32_t)((int64_t)a.T * a.n_q * D * 2));
+#pragma unroll
+    for (int i = 0; i < QROWS; ++i) {
+      const int r = wv * QROWS + i;
+      const int fr = fr0 + r;
+      const uint32_t off = (uint32_t)((((int64_t)(fr / a.G) * a.n_q + hk * a.G + fr % a.G) * D) * 2);
+      if (lane < D / 8)
+        dma<16>(qrs, lds_addr_of(lds_q + r * QOperand<S>::ROW), r < nh ? off + 16 * lane : kOOB, 0u);
+    }
+  } else {
     const u32x4 qrs = rsrc_words(a.q + ((int64_t)b * a.n_q + hq0) * D, (uint32_t)(nh * D * 2));
 #pragma unroll
     for (int i = 0; i < QROWS; ++i) {
@@ -386,6 +426,14 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     // of each half overlap the arithmetic that precedes their use.
     constexpr int NH = kHalfLoads<S>;
     uint8_t* const st = lds_st + wv * STAGE_BYTES;
+    // Chunk: keys [rlo, rhi) of the lane's query row c16 (none for rows past nh).
+    int rlo = 0, rhi = 0;
+    if constexpr (CHUNK) {
+      const int fr = fr0 + c16;
+      const int P = s0 + fr / a.G;
+      rhi = (c16 < nh && P < a.max_ctx) ? P + 1 : 0;
+      rlo = a.window > 0 ? max(0, P + 1 - a.window) : 0;
+    }
     if (p0 < end) {
       wait_vm<NH>();  // K half of the first tile landed (its V half may still be loading)
       stage_read_k<S>(tk, st, c16, q4);
@@ -396,7 +444,8 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       const bool more = pn < end;
       const bool more2 = pn + STEP < end;
       float z[2][4];
-      tile_scores<S>(tk, end - p0, z, qb, corr, a.c2, q4);
+      if constexpr (CHUNK) tile_scores<S>(tk, rlo - p0, min(rhi, end) - p0, z, qb, corr, a.c2, q4);
+      else tile_scores<S>(tk, end - p0, z, qb, corr, a.c2, q4);
       if (more) wait_vm<NH>();  // V half of this tile landed; the next K half is in flight
       else wait_vm<0>();
       VRegs<S> tv;
@@ -499,7 +548,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       v.z = fmaf(wk, u.z, v.z);
       v.w = fmaf(wk, u.w, v.w);
     }
-    reinterpret_cast<float4*>(a.ws_o + (row0 + (int64_t)h * a.n_splits) * D)[d / 4] = v;
+    reinterpret_cast<float4*>(a.ws_o + rowid(h) * D)[d / 4] = v;
   }
   if (threadIdx.x < nh) {
     const int h = threadIdx.x;
@@ -513,7 +562,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       const float mk = sm_m[k][h];
       if (mk != -INFINITY) l += sm_l[k][h] * __builtin_amdgcn_exp2f(mk - M);
     }
-    ml_out[(int64_t)h * a.n_splits] = make_float2(M, l);
+    ml[rowid(h)] = make_float2(M, l);
   }
   // ---- fused append: the new row into the cache (one head block writes it) --
   if (own_new && hblk == 0 && wv < 2 && lane < D / 4) {
@@ -606,6 +655,57 @@ int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store
     default: return KVQ_ERR_UNSUPPORTED;
   }
   if (st) return st;
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int launch_chunk_rows(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
+                      const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
+                      const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
+                      void* stream) {
+  if (L.k_dtype != KVQ_STORE_INT8 || L.v_dtype != KVQ_STORE_INT8) return KVQ_ERR_UNSUPPORTED;
+  PartialArgs a{};
+  a.k_store = k_store;
+  a.v_store = v_store;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.group_lanes = L.scale_group == 64 ? 16 : L.head_dim / 4;
+  a.q = q;
+  a.start_pos = d_start_pos;
+  a.T = n_tok;
+  const int64_t rows = (int64_t)batch * n_tok * n_q_heads * plan.n_splits;
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_ml = static_cast<float*>(ws) + rows * L.head_dim;
+  a.s_seq = L.s_seq;
+  a.s_pos = L.s_pos;
+  a.s_head = L.s_head;
+  a.ss_seq = L.ss_seq;
+  a.ss_pos = L.ss_pos;
+  a.ss_head = L.ss_head;
+  a.max_ctx = L.max_ctx > 0x7fffffff ? 0x7fffffff : (int32_t)L.max_ctx;
+  a.n_kv = L.n_kv_heads;
+  a.G = n_q_heads / L.n_kv_heads;
+  a.n_q = n_q_heads;
+  a.head_blocks = (int32_t)(((int64_t)n_tok * a.G + kHeadsPerBlock - 1) / kHeadsPerBlock);
+  a.n_splits = plan.n_splits;
+  a.chunk = plan.chunk;
+  a.window = window;
+  a.c2 = sm_scale * kLog2e;
+  dim3 grid(plan.n_splits, L.n_kv_heads * a.head_blocks, batch);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  constexpr int NW = kPartialWaves;
+  const bool g64 = L.scale_group == 64 && L.head_dim != 64;
+  switch (L.head_dim) {
+    case 64: hipLaunchKernelGGL((kvq_partial_kernel<64, true, true, false, NW, true>), grid, dim3(NW * 64), 0, s, a); break;
+    case 128:
+      if (g64) hipLaunchKernelGGL((kvq_partial_kernel<128, true, true, true, NW, true>), grid, dim3(NW * 64), 0, s, a);
+      else hipLaunchKernelGGL((kvq_partial_kernel<128, true, true, false, NW, true>), grid, dim3(NW * 64), 0, s, a);
+      break;
+    case 256:
+      if (g64) hipLaunchKernelGGL((kvq_partial_kernel<256, true, true, true, NW, true>), grid, dim3(NW * 64), 0, s, a);
+      else hipLaunchKernelGGL((kvq_partial_kernel<256, true, true, false, NW, true>), grid, dim3(NW * 64), 0, s, a);
+      break;
+    default: return KVQ_ERR_UNSUPPORTED;
+  }
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

@@ -108,30 +108,19 @@ const char* kvq_status_string(int s) {
   }
 }
 
-int kvq_plan(const kvq_layout* layout, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
-             int32_t window, int32_t n_cu, kvq_plan_t* out) {
-  int st = check_layout(layout);
-  if (st) return st;
-  if (!out) return KVQ_ERR_NULL;
-  const kvq_layout& L = *layout;
-  if ((st = check_heads(L, batch, n_q_heads))) return st;
-  if (max_seq_len < 0 || window < 0 || n_cu < 1) return KVQ_ERR_SHAPE;
-
-  const int64_t l_eff = effective_len(max_seq_len, window);
-  const int64_t G = n_q_heads / L.n_kv_heads;
-  const int64_t head_blocks = ceil_div(G, kHeadsPerBlock);
-  const int64_t units = (int64_t)(batch > 0 ? batch : 1) * L.n_kv_heads * head_blocks;
+// Key positions per split of the decode partial kernel for l_eff keys, with
+// `units` workgroups per split index (sequences x kv heads x 16-row blocks)
+// and `rows` (<= 16) query rows per workgroup.
+static int64_t decode_split_chunk(const kvq_layout& L, int64_t l_eff, int64_t units, int64_t rows, int32_t n_cu) {
   int64_t chunk;
   if (l_eff < 64) {
     // genie v1.3.0: a single block below 64 positions.
     chunk = round_up(l_eff > 0 ? l_eff : 1, kTile);
   } else {
     // Bytes one position of one kv head costs to read (algorithmic).
-    int64_t kv_pos = 0;
-    for (int dt : {L.k_dtype, L.v_dtype})
-      kv_pos += store_bytes(L.head_dim, dt) + 2 * scales_per_row(L, dt);
-    // Partial (m, l, O) bytes one split writes for its query heads.
-    const int64_t part = (G < kHeadsPerBlock ? G : kHeadsPerBlock) * (L.head_dim + 2) * 4;
+    const int64_t kv_pos = kv_bytes_per_pos(L);
+    // Partial (m, l, O) bytes one split writes for its query rows.
+    const int64_t part = rows * (L.head_dim + 2) * 4;
     // Long splits keep the partial traffic near 1 % of the KV bytes ...
     chunk = ceil_div(part * 100, kv_pos);
     if (chunk < 512) chunk = 512;
@@ -151,6 +140,23 @@ int kvq_plan(const kvq_layout* layout, int32_t batch, int32_t n_q_heads, int32_t
     const int64_t min_chunk = round_up(ceil_div(l_eff, kMaxSplits), kTile);
     if (chunk < min_chunk) chunk = min_chunk;
   }
+  return chunk;
+}
+
+int kvq_plan(const kvq_layout* layout, int32_t batch, int32_t n_q_heads, int32_t max_seq_len,
+             int32_t window, int32_t n_cu, kvq_plan_t* out) {
+  int st = check_layout(layout);
+  if (st) return st;
+  if (!out) return KVQ_ERR_NULL;
+  const kvq_layout& L = *layout;
+  if ((st = check_heads(L, batch, n_q_heads))) return st;
+  if (max_seq_len < 0 || window < 0 || n_cu < 1) return KVQ_ERR_SHAPE;
+
+  const int64_t l_eff = effective_len(max_seq_len, window);
+  const int64_t G = n_q_heads / L.n_kv_heads;
+  const int64_t head_blocks = ceil_div(G, kHeadsPerBlock);
+  const int64_t units = (int64_t)(batch > 0 ? batch : 1) * L.n_kv_heads * head_blocks;
+  const int64_t chunk = decode_split_chunk(L, l_eff, units, G < kHeadsPerBlock ? G : kHeadsPerBlock, n_cu);
   if (chunk > INT_MAX) return KVQ_ERR_UNSUPPORTED;
   int64_t n_splits = l_eff > 0 ? ceil_div(l_eff, chunk) : 1;
   out->chunk = (int32_t)chunk;
@@ -274,6 +280,18 @@ int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32
   const int64_t G = n_q_heads / L.n_kv_heads;
   // Keys one workgroup may walk: the whole prefix, or the window plus the chunk.
   const int64_t l_eff = window > 0 ? std::min<int64_t>(max_seq_len, (int64_t)window + n_tok) : max_seq_len;
+  if (chunk_as_rows(L, batch, n_tok, G)) {  // the decode partial kernel and its split rule
+    const int64_t rows = std::max<int64_t>(1, (int64_t)n_tok * G);
+    const int64_t blocks = ceil_div(rows, kHeadsPerBlock);
+    const int64_t units = (int64_t)(batch > 0 ? batch : 1) * L.n_kv_heads * blocks;
+    const int64_t chunk = decode_split_chunk(L, l_eff, units, std::min<int64_t>(rows, kHeadsPerBlock), n_cu);
+    const int64_t n_splits = l_eff > 0 ? ceil_div(l_eff, chunk) : 1;
+    if (n_splits > kMaxSplits || chunk > INT_MAX) return KVQ_ERR_UNSUPPORTED;
+    out->n_splits = (int32_t)n_splits;
+    out->chunk = (int32_t)chunk;
+    out->ws_bytes = workspace_bytes((int64_t)batch * n_tok, n_q_heads, n_splits, L.head_dim);
+    return KVQ_OK;
+  }
   const int64_t units = (int64_t)(batch > 0 ? batch : 1) * L.n_kv_heads * chunk_row_blocks(n_tok > 0 ? n_tok : 1, G, L.head_dim);
   const int64_t want = (int64_t)resident_chunk_wgs_per_cu(L, chunk_rows_per_wg(n_tok > 0 ? n_tok : 1, G, L.head_dim)) * n_cu;
   int64_t n_splits = 1, chunk = round_up(l_eff > 0 ? l_eff : 1, kTile);
@@ -322,10 +340,15 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
   if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
   if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
   if (batch == 0 || n_tok == 0) return KVQ_OK;
-  st = has_q4(L) ? launch_chunk_q4(L, k_store, v_store, k_scales, v_scales, q, batch, n_tok, n_q_heads, d_start_pos,
-                                   window, sm_scale, *plan, ws, stream)
-                 : launch_chunk(L, k_store, v_store, k_scales, v_scales, q, batch, n_tok, n_q_heads, d_start_pos,
-                                window, sm_scale, *plan, ws, stream);
+  if (has_q4(L))
+    st = launch_chunk_q4(L, k_store, v_store, k_scales, v_scales, q, batch, n_tok, n_q_heads, d_start_pos, window,
+                         sm_scale, *plan, ws, stream);
+  else if (chunk_as_rows(L, batch, n_tok, n_q_heads / L.n_kv_heads))
+    st = launch_chunk_rows(L, k_store, v_store, k_scales, v_scales, q, batch, n_tok, n_q_heads, d_start_pos, window,
+                           sm_scale, *plan, ws, stream);
+  else
+    st = launch_chunk(L, k_store, v_store, k_scales, v_scales, q, batch, n_tok, n_q_heads, d_start_pos, window,
+                      sm_scale, *plan, ws, stream);
   if (st) return st;
   // The partial rows are (b, t, hq): the reduce treats batch * n_tok rows of n_q_heads.
   return launch_reduce(L, ws, (int32_t)rows, n_q_heads, *plan, out, stream);

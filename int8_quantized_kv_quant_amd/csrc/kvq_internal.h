@@ -94,6 +94,36 @@ inline int64_t effective_len(int64_t max_len, int32_t window) {
   return window > 0 && window < max_len ? window : max_len;
 }
 
+// Bytes of K and V (codes and scales, without slot padding) of one position
+// of one kv head.
+inline int64_t kv_bytes_per_pos(const kvq_layout& L) {
+  int64_t b = 0;
+  for (int dt : {L.k_dtype, L.v_dtype}) b += store_bytes(L.head_dim, dt) + 2 * scales_per_row(L, dt);
+  return b;
+}
+
+// An int8 chunk whose (token, head) rows per kv head fit in one 16-row block
+// goes through the decode partial kernel (launch_chunk_rows): the rows share
+// every key tile, the waves and splits divide the keys, where the chunk
+// kernel would give a short verify window few workgroups with long key
+// ranges. Two blocks (up to 32 rows) when the batch's whole cache fits in the
+// 256 MB last-level cache, so that the second block's read of the same keys
+// is served from there. Measured, 128K keys with 8 heads per kv head: 1 and
+// 2 tokens 32 us against 50 us with the chunk kernel, 4 tokens (two blocks)
+// 40 us against 49 us; 64 sequences of 32K keys with 4 heads per kv head
+// (4.4 GB): 1 to 4 tokens 0.75-0.80 ms against 1.40 ms, 8 tokens (two
+// blocks) 1.53 ms against 1.46 ms.
+constexpr int64_t kRowsTwoBlockCacheBytes = 256ll << 20;
+inline bool chunk_as_rows(const kvq_layout& L, int64_t batch, int64_t n_tok, int64_t G) {
+  if (L.k_dtype != KVQ_STORE_INT8 || L.v_dtype != KVQ_STORE_INT8) return false;
+  const int64_t rows = n_tok * G;
+  if (rows <= kHeadsPerBlock) return true;
+  // (in double: the product of the extents may pass 2^63)
+  return rows <= 2 * kHeadsPerBlock &&
+         (double)batch * (double)L.max_ctx * (double)L.n_kv_heads * (double)kv_bytes_per_pos(L) <=
+             (double)kRowsTwoBlockCacheBytes;
+}
+
 // Workspace bytes for a plan.
 inline int64_t workspace_bytes(int64_t batch, int64_t n_q, int64_t n_splits, int64_t head_dim) {
   return batch * n_q * n_splits * (head_dim + 2) * 4;
@@ -122,6 +152,14 @@ int launch_chunk(const kvq_layout& L, const void* k_store, const void* v_store, 
                  const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
                  const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
                  void* stream);
+
+// Chunk attention through the decode partial kernel (int8 K and V): the
+// (token, head) rows of a kv head in blocks of 16, every key read once per
+// block. For chunks with few rows per kv head (a verify window).
+int launch_chunk_rows(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
+                      const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
+                      const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
+                      void* stream);
 
 // Chunk attention over a layout with a q4 store (q4_decode_supported).
 int launch_chunk_q4(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,

@@ -132,10 +132,11 @@ __device__ __forceinline__ void tile_scores_q(const KRegs<S>& t, int vlo, int vh
 }
 
 // tile_scores_q with the query operands read from LDS (`qb`, see QOperand)
-// and positions [0, nvalid) of the tile kept. All query operand reads are
-// issued before the first MFMA so that their LDS latency is paid once per tile.
+// and positions [vlo, vhi) of the tile kept (per query row). All query
+// operand reads are issued before the first MFMA so that their LDS latency is
+// paid once per tile.
 template <class S>
-__device__ __forceinline__ void tile_scores(const KRegs<S>& t, int nvalid, float (&z)[2][4],
+__device__ __forceinline__ void tile_scores(const KRegs<S>& t, int vlo, int vhi, float (&z)[2][4],
                                             const uint8_t* __restrict__ qb, const float (&corr)[S::NG],
                                             float c2, int q4) {
   f16x8 qv[S::NJ][2];
@@ -145,7 +146,14 @@ __device__ __forceinline__ void tile_scores(const KRegs<S>& t, int nvalid, float
     qv[j][1] = q_get(qb, j, 1);
   }
   __builtin_amdgcn_sched_barrier(0);
-  tile_scores_q<S>(t, 0, nvalid, z, qv, corr, c2, q4);
+  tile_scores_q<S>(t, vlo, vhi, z, qv, corr, c2, q4);
+}
+// The same with positions [0, nvalid) kept for every query row.
+template <class S>
+__device__ __forceinline__ void tile_scores(const KRegs<S>& t, int nvalid, float (&z)[2][4],
+                                            const uint8_t* __restrict__ qb, const float (&corr)[S::NG],
+                                            float c2, int q4) {
+  tile_scores<S>(t, 0, nvalid, z, qb, corr, c2, q4);
 }
 
 // Maximum over lanes l, l ^ 16 and l ^ 32 without going through LDS:

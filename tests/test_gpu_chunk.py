@@ -86,6 +86,21 @@ CASES = {
     "q4_batch_g16": (wl.WORKLOADS["long_q4"].with_(batch=2, n_q_heads=32, max_ctx=1024), [100, 600], 33, 0),
     "k8v4_window_smaller_than_chunk": (wl.WORKLOADS["long_k8v4"].with_(max_ctx=2048), [1000], 100, 64),
     "k8v4_mha_g1": (wl.WORKLOADS["long_k8v4"].with_(n_q_heads=2, max_ctx=1024), [300], 70, 0),
+    # int8 chunks with at most 32 (token, head) rows per kv head run through
+    # the decode partial kernel (16-row blocks, per-row causal limits): 16, 12
+    # and 32 rows, a second block of one row, one row per token (G = 1) with a
+    # window narrower than the chunk, a first token at position 0, group-64
+    # and row scales (verify_window_long and tiny_prompt above: 32 and 20 rows)
+    "rows_verify_long_t2": (wl.WORKLOADS["long"].with_(max_ctx=8192), [6000], 2, 0),
+    "rows_gemma_window_t2": (wl.WORKLOADS["gemma"].with_(max_ctx=1024), [700], 2, 512),
+    "rows_gemma_window_t4": (wl.WORKLOADS["gemma"].with_(max_ctx=1024), [900], 4, 512),
+    "rows_batched_ragged_t3": (wl.WORKLOADS["batched"].with_(batch=3, max_ctx=2304), [100, 2000, 0], 3, 0),
+    "rows_tiny_d64_t4": (wl.WORKLOADS["tiny"].with_(batch=2, max_ctx=512), [0, 37], 4, 0),
+    "rows_mha_t16_window5": (wl.Workload("mha16", 1, 4, 4, 128, 128, 128, 1024, 0, 173), [300], 16, 5),
+    "rows_mha_d64_t16": (wl.Workload("mha64", 2, 2, 2, 64, 64, 64, 1024, 0, 174), [0, 900], 16, 0),
+    "rows_mha_t17_two_blocks": (wl.Workload("mha17", 1, 4, 4, 128, 128, 128, 1024, 0, 175), [300], 17, 0),
+    # one row past two 16-row blocks: the chunk kernel
+    "chunk_mha_t33": (wl.Workload("mha33", 1, 4, 4, 128, 128, 128, 1024, 0, 176), [300], 33, 7),
 }
 
 
@@ -109,6 +124,39 @@ def test_forced_splits_equal_one_split(name):
         plan = kvq.Plan(ns, chunk, w.batch * T * w.n_q_heads * ns * (w.head_dim + 2) * 4)
         got, want, _ = _run(w, [1500], T, 0, plan=plan)
         _check(got, want, label=f"splits {ns}")
+
+
+def test_rows_path_forced_splits():
+    """Verify windows of 16 and 24 rows (2 and 3 tokens x 8 heads) through the
+    decode partial kernel with the keys split 1, 3 and 17 ways, and a window:
+    every result within the tolerance of the oracle."""
+    import int8_quantized_kv_quant_amd as kvq
+    w = wl.WORKLOADS["long"].with_(max_ctx=4096)
+    for T, ns, chunk, window in ((2, 1, 4096, 0), (2, 3, 1376, 0), (2, 17, 128, 0), (2, 5, 224, 1000),
+                                 (3, 17, 128, 0), (3, 5, 224, 1000)):
+        plan = kvq.Plan(ns, chunk, w.batch * T * w.n_q_heads * ns * (w.head_dim + 2) * 4)
+        got, want, _ = _run(w, [3100], T, window, plan=plan)
+        _check(got, want, label=f"rows T={T} splits {ns} window {window}")
+
+
+@pytest.mark.parametrize("n_tok", [2, 4])
+def test_rows_path_full_size_verify_window(n_tok):
+    """Verify tokens at the end of the 128K context of the long workload (16
+    query / 2 kv heads, head_dim 256, group-64 scales; one and two 16-row
+    blocks) with the planner's split, every output against the oracle."""
+    w = wl.WORKLOADS["long"]
+    got, want, plan = _run(w, [131072 - n_tok], n_tok, 0)
+    print(f"[chunk] 128K verify T={n_tok} plan {plan.n_splits} x {plan.chunk}", flush=True)
+    _check(got, want, label=f"128K verify window T={n_tok}")
+
+
+def test_rows_path_token_past_the_cache_end():
+    """The rows path with its second token at max_ctx: the first token sees
+    every key, the second gets a zero row."""
+    w = wl.WORKLOADS["long"].with_(max_ctx=1024)
+    got, want, _ = _run(w, [1023], 2, 0)
+    _check(got[:, :1], want[:, :1], label="inside")
+    assert not got[:, 1:].any()
 
 
 @pytest.mark.parametrize("name", ["long", "long_q4", "long_k8v4"])

@@ -255,6 +255,28 @@ def test_chunk_plan_covers_every_key_range(n_tok, start, window):
         assert p.n_splits > 16
 
 
+@needs_lib
+@pytest.mark.parametrize("n_tok,L,window", [(1, 131072, 0), (2, 131072, 0), (1, 3333, 0), (2, 4096, 512),
+                                            (4, 131072, 0)])
+def test_short_int8_chunk_plan_follows_the_decode_rule(n_tok, L, window):
+    """An int8 chunk with at most 32 (token, head) rows per kv head goes through
+    the decode partial kernel and takes the decode planner's split: at one
+    token (the decode shape) the very same plan, at two the same key chunk
+    (the chip-filling rule decides at these lengths), at four (two 16-row
+    blocks per kv head) twice the chunk."""
+    w = wl.WORKLOADS["long"]
+    lay = _layout(w)
+    pc = kvq.kvq_plan_chunk(lay, 1, n_tok, 16, L, window, 256)
+    pd = kvq.kvq_plan(lay, 1, 16, L, window, 256)
+    l_eff = min(L, window + n_tok) if window else L
+    assert pc.n_splits * pc.chunk >= l_eff and pc.chunk % 32 == 0
+    assert pc.ws_bytes == n_tok * 16 * pc.n_splits * (256 + 2) * 4
+    if n_tok == 1 and not window:
+        assert (pc.n_splits, pc.chunk) == (pd.n_splits, pd.chunk)
+    if L == 131072:
+        assert pd.chunk == 1024 and pc.chunk == 1024 * (1 if n_tok <= 2 else 2)
+
+
 def _blob(lay, unpack=False, **kw):
     hdr = kw.pop("header", None)
     args = dict(k_store=FAKE, v_store=FAKE, k_scales=FAKE, v_scales=FAKE, seq=0, pos0=0, n_pos=8, buf=FAKE,
