@@ -136,9 +136,12 @@ typedef struct {
  * with S = min(n_splits, ceil((L - lo) / chunk)) (the splits that contiguous
  * ranges of chunk positions would use), decode split s < S covers blocks
  * s, s + S, s + 2*S, ... (block-cyclic) and splits s >= S are empty, so every
- * context length is covered whatever the planned one. kv_chunk_attn's splits
- * are contiguous: [lo + s*chunk, lo + (s+1)*chunk), the last one running to
- * the chunk's end. ws_bytes is the workspace that
+ * context length is covered whatever the planned one. kv_chunk_attn splits
+ * the keys of a group of query rows the same way (from the lo of its first
+ * token to the position of its last) when it runs an int8 chunk of at most 32
+ * (token, head) rows per kv head, otherwise contiguously: [lo + s*chunk,
+ * lo + (s+1)*chunk), the last split running to the chunk's end. Either way
+ * every key is covered whatever the plan. ws_bytes is the workspace that
  * kv_decode_attn_splitk (or kv_chunk_attn) writes and kv_decode_reduce reads. */
 typedef struct {
   int32_t n_splits;
@@ -286,7 +289,10 @@ int kv_decode_attn_static(const kvq_layout* layout,
  * position max_seq_len (the largest start + n_tok). Chunks with many query
  * rows run one split per (sequence, kv head, 64-row block); a few tokens over
  * a long prefix (a verify window) get their keys split so that the grid covers
- * the chip. ws_bytes = batch * n_tok * n_q_heads * n_splits * (head_dim + 2) * 4.
+ * the chip. int8 chunks with at most 16 (token, head) rows per kv head, or 32
+ * when batch * max_ctx * n_kv_heads positions of K and V fit in 256 MiB, run
+ * through the decode partial kernel and get kvq_plan's split rule.
+ * ws_bytes = batch * n_tok * n_q_heads * n_splits * (head_dim + 2) * 4.
  * Writes *out; returns KVQ_OK or an error for invalid layout/sizes. */
 int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32_t n_q_heads,
                    int32_t max_seq_len, int32_t window, int32_t n_cu, kvq_plan_t* out);
@@ -312,7 +318,12 @@ int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32
  * rotated for a q4 K store and the output rotated back, as in
  * kv_decode_attn_splitk); other combinations are refused
  * (KVQ_ERR_UNSUPPORTED). Two kernels are enqueued on `stream`: the partials
- * and the combine of kv_decode_reduce.
+ * and the combine of kv_decode_reduce. The partials of an int8 chunk with at
+ * most 16 (token, head) rows per kv head (32 if batch * max_ctx * n_kv_heads
+ * positions of K and V take at most 256 MiB) come from the decode partial
+ * kernel, whose 16 query rows are then (token, head) pairs with their own
+ * causal limits (a verify window reads every key once per 16 rows); larger
+ * chunks and the 4-bit layouts from the chunk kernels.
  * Device precondition: 0 <= d_start_pos[b] and d_start_pos[b] + n_tok <= max_ctx;
  * a token that would sit at or beyond max_ctx sees no key and gets a zero row. */
 int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_store,

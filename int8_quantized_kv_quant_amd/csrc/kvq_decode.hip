@@ -51,6 +51,16 @@
 // Bounds. Every K/V/scale load goes through a buffer resource whose size ends
 // at the last row of the context, and positions outside the split get an
 // out-of-range offset, so they read as zero and are masked out of the softmax.
+//
+// Chunk rows (int8 K and V, the CHUNK instances; Strata PR 2698 "What it
+// does": verify windows read the same cache as decode). The 16 rows of a
+// workgroup are (token, head) pairs t * G + h of a chunk of T tokens at
+// positions start + t, each row masking keys outside its own causal (and
+// window) range, and the partials go to rows (b, t, hq) for the same reduce.
+// A verify window of a few tokens then reads every key once per 16 rows with
+// the decode kernel's split over the whole chip, where the chunk kernel (64
+// rows per workgroup sharing each tile) would leave most of its wavefronts
+// without rows.
 #include <math.h>
 
 #include "kvq_device.h"
