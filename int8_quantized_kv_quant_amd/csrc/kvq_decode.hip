@@ -53,14 +53,15 @@
 // out-of-range offset, so they read as zero and are masked out of the softmax.
 //
 // Chunk rows (int8 K and V, the CHUNK instances; Strata PR 2698 "What it
-// does": verify windows read the same cache as decode). The 16 rows of a
+// does": verify windows read the same cache as decode). The rows of a
 // workgroup are (token, head) pairs t * G + h of a chunk of T tokens at
-// positions start + t, each row masking keys outside its own causal (and
-// window) range, and the partials go to rows (b, t, hq) for the same reduce.
-// A verify window of a few tokens then reads every key once per 16 rows with
-// the decode kernel's split over the whole chip, where the chunk kernel (64
-// rows per workgroup sharing each tile) would leave most of its wavefronts
-// without rows.
+// positions start + t, in RB blocks of 16 that share every key and value
+// operand (each block its own MFMAs, softmax state and accumulators), each
+// row masking keys outside its own causal (and window) range; the partials go
+// to rows (b, t, hq) for the same reduce. A verify window of up to 32 rows
+// per kv head then reads every key once, with the decode kernel's split over
+// the whole chip, where the chunk kernel (64 rows per workgroup sharing each
+// tile) would leave most of its wavefronts without rows.
 #include <math.h>
 
 #include "kvq_device.h"
@@ -177,11 +178,14 @@ __device__ __forceinline__ void wait_vm0_visible() { __builtin_amdgcn_s_waitcnt(
 __device__ __forceinline__ int merge_swz(int f) { return f ^ ((f >> 4) & 3); }
 
 // ---- kernel ----------------------------------------------------------------------
-template <int D, bool KI8, bool VI8, bool G64, int NW, bool CHUNK = false>
+template <int D, bool KI8, bool VI8, bool G64, int NW, bool CHUNK = false, int RB = 1>
 __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   using S = Shape<D, KI8, VI8, G64>;
   constexpr bool kStaged = KI8 && VI8;
   static_assert(!CHUNK || kStaged, "chunk rows through the int8 kernel only");
+  // RB blocks of 16 query rows per workgroup, sharing every key and value
+  // operand (chunk rows only).
+  static_assert(RB == 1 || (CHUNK && RB == 2), "two row blocks for chunk rows only");
   // One store int8, the other fp32: the fp32 tile is staged in LDS, the int8
   // operands go straight to registers.
   constexpr bool kMix = KI8 != VI8;
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   static_assert(!(kStaged || kMix) || SLOT_BYTES <= STAGE_BYTES, "merge slot must fit in a stage");
   constexpr int ST_BYTES = NW * SLOT_PITCH;
   __shared__ __attribute__((aligned(16))) uint8_t lds_st[ST_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_q[16 * QOperand<S>::ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_q[16 * RB * QOperand<S>::ROW];
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
   // The new token's rows when the append is fused ([0] = K, [1] = V): the fp16
@@ -212,12 +216,12 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   const int hblk = blockIdx.y % a.head_blocks;
   const int b = blockIdx.z;
 
-  // Query rows of the workgroup (up to 16) and the keys [lo, L) they attend.
+  // Query rows of the workgroup (up to 16 * RB) and the keys [lo, L) they attend.
   // Decode: heads hblk * 16 .. of kv head hk, at context seq_lens[b]. Chunk:
   // flat rows fr0 + r = t * G + h of kv head hk; token t sits at s0 + t and
   // attends [max(0, s0 + t + 1 - window) (window > 0), s0 + t + 1).
-  const int fr0 = hblk * 16;
-  const int nh = CHUNK ? min(16, a.T * a.G - fr0) : min(16, a.G - fr0);
+  const int fr0 = hblk * 16 * RB;
+  const int nh = CHUNK ? min(16 * RB, a.T * a.G - fr0) : min(16, a.G - fr0);
   const int hq0 = hk * a.G + fr0;
   const int64_t row0 = ((int64_t)b * a.n_q + hq0) * a.n_splits + split;
   float2* const ml = reinterpret_cast<float2*>(a.ws_ml);
@@ -288,7 +292,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   // append is fused, then 16 / NW query rows per wavefront (rows past nh read
   // as zeros). A query row lands as D consecutive fp16 values at the start of
   // its padded LDS row.
-  constexpr int QROWS = 16 / NW;
+  constexpr int QROWS = 16 * RB / NW;
   KRegs<S> tk;  // int8 operands of the mixed stores' first tile, loaded first
   VRegs<S> tv;
   if constexpr (kMix) {
@@ -368,16 +372,19 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     if (lane < D / 4) *reinterpret_cast<float4*>(&nw_val[wv][4 * lane]) = val;
   }
   __syncthreads();  // query rows (and the new rows) in LDS
+  // The lane's query row c16 of row block rb: qb + rb * QB.
   const uint8_t* const qb = lds_q + c16 * QOperand<S>::ROW + 32 * q4;
+  constexpr int QB = 16 * QOperand<S>::ROW;
 
   // ---- per-group sums of q: the accumulator start values -1152 * sum(q) that
   // cancel the +1152 code bias (rows beyond nh are zero).
-  float corr[S::NG];
-  {
+  float corr[RB][S::NG];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
     float qsum[S::NJ];
 #pragma unroll
     for (int j = 0; j < S::NJ; ++j) {
-      const f16x8 h0 = q_get(qb, j, 0), h1 = q_get(qb, j, 1);
+      const f16x8 h0 = q_get(qb + rb * QB, j, 0), h1 = q_get(qb + rb * QB, j, 1);
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += (float)h0[e] + (float)h1[e];
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
 #pragma unroll
         for (int j = 0; j < S::NJ; ++j) t += qsum[j];
       }
-      corr[g] = KI8 ? -kCodeBias * t : 0.0f;
+      corr[rb][g] = KI8 ? -kCodeBias * t : 0.0f;
     }
   }
   if (own_new && wv == 0) {
@@ -419,11 +426,14 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     if (r == 0) nw_z[h] = zs * a.c2;  // read in the epilogue, after its barrier
   }
 
-  WaveAcc<S> acc;
+  WaveAcc<S> acc[RB];
 #pragma unroll
-  for (int n = 0; n < S::VB; ++n) acc.o[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  acc.l = (f32x4){0.f, 0.f, 0.f, 0.f};
-  acc.m_ref = -INFINITY;
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int n = 0; n < S::VB; ++n) acc[rb].o[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    acc[rb].l = (f32x4){0.f, 0.f, 0.f, 0.f};
+    acc[rb].m_ref = -INFINITY;
+  }
 
   if constexpr (kStaged) {
     // Pipeline over this wavefront's tiles p0, p0 + STEP, ... For tile t:
@@ -436,13 +446,19 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     // of each half overlap the arithmetic that precedes their use.
     constexpr int NH = kHalfLoads<S>;
     uint8_t* const st = lds_st + wv * STAGE_BYTES;
-    // Chunk: keys [rlo, rhi) of the lane's query row c16 (none for rows past nh).
-    int rlo = 0, rhi = 0;
-    if constexpr (CHUNK) {
-      const int fr = fr0 + c16;
-      const int P = s0 + fr / a.G;
-      rhi = (c16 < nh && P < a.max_ctx) ? P + 1 : 0;
-      rlo = a.window > 0 ? max(0, P + 1 - a.window) : 0;
+    // Chunk: keys [rlo, rhi) of the lane's query row c16 of block rb (none
+    // for rows past nh).
+    int rlo[RB], rhi[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      rlo[rb] = 0;
+      rhi[rb] = 0;
+      if constexpr (CHUNK) {
+        const int r = 16 * rb + c16;
+        const int P = s0 + (fr0 + r) / a.G;
+        rhi[rb] = (r < nh && P < a.max_ctx) ? P + 1 : 0;
+        rlo[rb] = a.window > 0 ? max(0, P + 1 - a.window) : 0;
+      }
     }
     if (p0 < end) {
       wait_vm<NH>();  // K half of the first tile landed (its V half may still be loading)
@@ -453,21 +469,31 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       const int pn = p0 + STEP;
       const bool more = pn < end;
       const bool more2 = pn + STEP < end;
-      float z[2][4];
-      if constexpr (CHUNK) tile_scores<S>(tk, rlo - p0, min(rhi, end) - p0, z, qb, corr, a.c2, q4);
-      else tile_scores<S>(tk, end - p0, z, qb, corr, a.c2, q4);
+      // (the blocks written out, not as a loop: a one-trip unrolled loop
+      // around the scores changed the register allocation of the decode
+      // instances, 248 -> 292 registers at head_dim 256)
+      float z[RB][2][4];
+      auto scores = [&](int rb) {
+        if constexpr (CHUNK)
+          tile_scores<S>(tk, rlo[rb] - p0, min(rhi[rb], end) - p0, z[rb], qb + rb * QB, corr[rb], a.c2, q4);
+        else tile_scores<S>(tk, end - p0, z[rb], qb, corr[rb], a.c2, q4);
+      };
+      scores(0);
+      if constexpr (RB == 2) scores(1);
       if (more) wait_vm<NH>();  // V half of this tile landed; the next K half is in flight
       else wait_vm<0>();
       VRegs<S> tv;
       stage_read_v<S>(tv, st, c16, q4);
-      const f16x8 pa = tile_softmax<S>(z, acc, q4);
+      f16x8 pa[RB];
+      pa[0] = tile_softmax<S>(z[0], acc[0], q4);
+      if constexpr (RB == 2) pa[1] = tile_softmax<S>(z[1], acc[1], q4);
       if (more) stage_issue<S, 1>(st, vrw, vsrw, pn, end - pn, krow, srow, lane);
-      tile_pv<S, 1>(tv, pa, acc);
+      tile_pv_rows<S, 1, RB>(tv, pa, acc);
       if (more) {
         wait_vm<NH>();  // K half of the next tile landed; its V half is in flight
         stage_read_k<S>(tk, st, c16, q4);
       }
-      tile_pv<S, 2>(tv, pa, acc);
+      tile_pv_rows<S, 2, RB>(tv, pa, acc);
       if (more2) stage_issue<S, 0>(st, krw, ksrw, pn + STEP, end - pn - STEP, krow, srow, lane);
     }
   } else if constexpr (kMix) {
@@ -492,9 +518,9 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
         f32stage_issue<S, !KI8>(st, frw, pn, end - pn, frow, lane);
       }
       float z[2][4];
-      tile_scores<S>(tk, end - p0, z, qb, corr, a.c2, q4);
-      const f16x8 pa = tile_softmax<S>(z, acc, q4);
-      tile_pv<S>(tv, pa, acc);
+      tile_scores<S>(tk, end - p0, z, qb, corr[0], a.c2, q4);
+      const f16x8 pa = tile_softmax<S>(z, acc[0], q4);
+      tile_pv<S>(tv, pa, acc[0]);
       if constexpr (KI8) tk = tkn;
       else tv = tvn;
     }
@@ -503,76 +529,88 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       load_k_global<S>(tk, krs, ksrs, p0, end, krow, srow, c16, q4);
       load_v_global<S>(tv, vrs, vsrs, p0, end, vrow, srow, c16, q4);
       float z[2][4];
-      tile_scores<S>(tk, end - p0, z, qb, corr, a.c2, q4);
-      const f16x8 pa = tile_softmax<S>(z, acc, q4);
-      tile_pv<S>(tv, pa, acc);
+      tile_scores<S>(tk, end - p0, z, qb, corr[0], a.c2, q4);
+      const f16x8 pa = tile_softmax<S>(z, acc[0], q4);
+      tile_pv<S>(tv, pa, acc[0]);
     }
   }
 
   // ---- merge the wavefronts of the workgroup -----------------------------------
   // Each wavefront stores its unscaled O rows (in its own stage), its max and
   // its sum; after one barrier every lane combines the wavefronts for one
-  // (head, 4 dims) with weights 2^(m_k - M).
-  if (q4 == 0) sm_m[wv][c16] = acc.m_ref;
-  if (c16 == 0) {
+  // (head, 4 dims) with weights 2^(m_k - M). Row block rb has nr rows.
+  auto merge = [&](const int rb, const int nr) {
+    if (q4 == 0) sm_m[wv][c16] = acc[rb].m_ref;
+    if (c16 == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm_l[wv][4 * q4 + i] = acc.l[i];
-  }
-  {
-    float* slot = reinterpret_cast<float*>(lds_st + wv * SLOT_PITCH);
+      for (int i = 0; i < 4; ++i) sm_l[wv][4 * q4 + i] = acc[rb].l[i];
+    }
+    {
+      float* slot = reinterpret_cast<float*>(lds_st + wv * SLOT_PITCH);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * q4 + i;
-      if (h < nh) {
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * q4 + i;
+        if (h < nr) {
 #pragma unroll
-        for (int n4 = 0; n4 < S::VB / 4; ++n4) {
-          const int f = (S::VB * c16 + 4 * n4) / 4;  // float4 index within the row
-          const float4 v = {acc.o[4 * n4 + 0][i], acc.o[4 * n4 + 1][i], acc.o[4 * n4 + 2][i], acc.o[4 * n4 + 3][i]};
-          reinterpret_cast<float4*>(slot + h * D)[merge_swz(f)] = v;
+          for (int n4 = 0; n4 < S::VB / 4; ++n4) {
+            const int f = (S::VB * c16 + 4 * n4) / 4;  // float4 index within the row
+            const float4 v = {acc[rb].o[4 * n4 + 0][i], acc[rb].o[4 * n4 + 1][i], acc[rb].o[4 * n4 + 2][i],
+                              acc[rb].o[4 * n4 + 3][i]};
+            reinterpret_cast<float4*>(slot + h * D)[merge_swz(f)] = v;
+          }
         }
       }
     }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < nh * (D / 4); idx += NW * 64) {
-    const int h = idx / (D / 4);
-    const int d = 4 * (idx % (D / 4));
-    const float zn = own_new ? nw_z[h] : -INFINITY;  // the fused new position
-    float M = zn;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nr * (D / 4); idx += NW * 64) {
+      const int h = idx / (D / 4);
+      const int d = 4 * (idx % (D / 4));
+      const float zn = own_new ? nw_z[h] : -INFINITY;  // the fused new position
+      float M = zn;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
-    const int f = merge_swz(d / 4);
-    float4 v = {0.f, 0.f, 0.f, 0.f};
-    if (own_new) {
-      const float wn = __builtin_amdgcn_exp2f(zn - M);
-      const float4 u = *reinterpret_cast<const float4*>(&nw_val[1][d]);
-      v = make_float4(wn * u.x, wn * u.y, wn * u.z, wn * u.w);
+      for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
+      const int f = merge_swz(d / 4);
+      float4 v = {0.f, 0.f, 0.f, 0.f};
+      if (own_new) {
+        const float wn = __builtin_amdgcn_exp2f(zn - M);
+        const float4 u = *reinterpret_cast<const float4*>(&nw_val[1][d]);
+        v = make_float4(wn * u.x, wn * u.y, wn * u.z, wn * u.w);
+      }
+#pragma unroll
+      for (int k = 0; k < NW; ++k) {
+        const float mk = sm_m[k][h];
+        const float wk = mk == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk - M);
+        const float4 u = reinterpret_cast<const float4*>(lds_st + k * SLOT_PITCH)[h * (D / 4) + f];
+        v.x = fmaf(wk, u.x, v.x);
+        v.y = fmaf(wk, u.y, v.y);
+        v.z = fmaf(wk, u.z, v.z);
+        v.w = fmaf(wk, u.w, v.w);
+      }
+      reinterpret_cast<float4*>(a.ws_o + rowid(16 * rb + h) * D)[d / 4] = v;
     }
+    if (threadIdx.x < nr) {
+      const int h = threadIdx.x;
+      const float zn = own_new ? nw_z[h] : -INFINITY;
+      float M = zn;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const float mk = sm_m[k][h];
-      const float wk = mk == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mk - M);
-      const float4 u = reinterpret_cast<const float4*>(lds_st + k * SLOT_PITCH)[h * (D / 4) + f];
-      v.x = fmaf(wk, u.x, v.x);
-      v.y = fmaf(wk, u.y, v.y);
-      v.z = fmaf(wk, u.z, v.z);
-      v.w = fmaf(wk, u.w, v.w);
+      for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
+      float l = own_new ? __builtin_amdgcn_exp2f(zn - M) : 0.0f;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) {
+        const float mk = sm_m[k][h];
+        if (mk != -INFINITY) l += sm_l[k][h] * __builtin_amdgcn_exp2f(mk - M);
+      }
+      ml[rowid(16 * rb + h)] = make_float2(M, l);
     }
-    reinterpret_cast<float4*>(a.ws_o + rowid(h) * D)[d / 4] = v;
-  }
-  if (threadIdx.x < nh) {
-    const int h = threadIdx.x;
-    const float zn = own_new ? nw_z[h] : -INFINITY;
-    float M = zn;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
-    float l = own_new ? __builtin_amdgcn_exp2f(zn - M) : 0.0f;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const float mk = sm_m[k][h];
-      if (mk != -INFINITY) l += sm_l[k][h] * __builtin_amdgcn_exp2f(mk - M);
+  };
+  if constexpr (RB == 1) {
+    merge(0, nh);
+  } else {
+    merge(0, min(16, nh));
+    if (nh > 16) {
+      __syncthreads();  // the first block's slots and maxima have been read
+      merge(1, nh - 16);
     }
-    ml[rowid(h)] = make_float2(M, l);
   }
   // ---- fused append: the new row into the cache (one head block writes it) --
   if (own_new && hblk == 0 && wv < 2 && lane < D / 4) {
@@ -668,6 +706,12 @@ int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
+template <int D, bool G64, int RB>
+static void launch_rows_t(const PartialArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int NW = kPartialWaves;
+  hipLaunchKernelGGL((kvq_partial_kernel<D, true, true, G64, NW, true, RB>), grid, dim3(NW * 64), 0, s, a);
+}
+
 int launch_chunk_rows(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
                       const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
                       const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
@@ -682,9 +726,9 @@ int launch_chunk_rows(const kvq_layout& L, const void* k_store, const void* v_st
   a.q = q;
   a.start_pos = d_start_pos;
   a.T = n_tok;
-  const int64_t rows = (int64_t)batch * n_tok * n_q_heads * plan.n_splits;
+  const int64_t ws_rows = (int64_t)batch * n_tok * n_q_heads * plan.n_splits;
   a.ws_o = static_cast<float*>(ws);
-  a.ws_ml = static_cast<float*>(ws) + rows * L.head_dim;
+  a.ws_ml = static_cast<float*>(ws) + ws_rows * L.head_dim;
   a.s_seq = L.s_seq;
   a.s_pos = L.s_pos;
   a.s_head = L.s_head;
@@ -695,24 +739,30 @@ int launch_chunk_rows(const kvq_layout& L, const void* k_store, const void* v_st
   a.n_kv = L.n_kv_heads;
   a.G = n_q_heads / L.n_kv_heads;
   a.n_q = n_q_heads;
-  a.head_blocks = (int32_t)(((int64_t)n_tok * a.G + kHeadsPerBlock - 1) / kHeadsPerBlock);
+  // One or two row blocks of 16 per workgroup (all rows sharing every key and
+  // value operand).
+  const int per_wg = chunk_rows_per_block(n_tok, a.G);
+  const int rb = per_wg / kHeadsPerBlock;
+  a.head_blocks = (int32_t)(((int64_t)n_tok * a.G + per_wg - 1) / per_wg);
   a.n_splits = plan.n_splits;
   a.chunk = plan.chunk;
   a.window = window;
   a.c2 = sm_scale * kLog2e;
   dim3 grid(plan.n_splits, L.n_kv_heads * a.head_blocks, batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  constexpr int NW = kPartialWaves;
   const bool g64 = L.scale_group == 64 && L.head_dim != 64;
   switch (L.head_dim) {
-    case 64: hipLaunchKernelGGL((kvq_partial_kernel<64, true, true, false, NW, true>), grid, dim3(NW * 64), 0, s, a); break;
+    case 64:
+      if (rb == 2) launch_rows_t<64, false, 2>(a, grid, s);
+      else launch_rows_t<64, false, 1>(a, grid, s);
+      break;
     case 128:
-      if (g64) hipLaunchKernelGGL((kvq_partial_kernel<128, true, true, true, NW, true>), grid, dim3(NW * 64), 0, s, a);
-      else hipLaunchKernelGGL((kvq_partial_kernel<128, true, true, false, NW, true>), grid, dim3(NW * 64), 0, s, a);
+      if (rb == 2) g64 ? launch_rows_t<128, true, 2>(a, grid, s) : launch_rows_t<128, false, 2>(a, grid, s);
+      else g64 ? launch_rows_t<128, true, 1>(a, grid, s) : launch_rows_t<128, false, 1>(a, grid, s);
       break;
     case 256:
-      if (g64) hipLaunchKernelGGL((kvq_partial_kernel<256, true, true, true, NW, true>), grid, dim3(NW * 64), 0, s, a);
-      else hipLaunchKernelGGL((kvq_partial_kernel<256, true, true, false, NW, true>), grid, dim3(NW * 64), 0, s, a);
+      if (rb == 2) g64 ? launch_rows_t<256, true, 2>(a, grid, s) : launch_rows_t<256, false, 2>(a, grid, s);
+      else g64 ? launch_rows_t<256, true, 1>(a, grid, s) : launch_rows_t<256, false, 1>(a, grid, s);
       break;
     default: return KVQ_ERR_UNSUPPORTED;
   }

@@ -102,26 +102,23 @@ inline int64_t kv_bytes_per_pos(const kvq_layout& L) {
   return b;
 }
 
-// An int8 chunk whose (token, head) rows per kv head fit in one 16-row block
-// goes through the decode partial kernel (launch_chunk_rows): the rows share
-// every key tile, the waves and splits divide the keys, where the chunk
-// kernel would give a short verify window few workgroups with long key
-// ranges. Two blocks (up to 32 rows) when the batch's whole cache fits in the
-// 256 MB last-level cache, so that the second block's read of the same keys
-// is served from there. Measured, 128K keys with 8 heads per kv head: 1 and
-// 2 tokens 32 us against 50 us with the chunk kernel, 4 tokens (two blocks)
-// 40 us against 49 us; 64 sequences of 32K keys with 4 heads per kv head
-// (4.4 GB): 1 to 4 tokens 0.75-0.80 ms against 1.40 ms, 8 tokens (two
-// blocks) 1.53 ms against 1.46 ms.
-constexpr int64_t kRowsTwoBlockCacheBytes = 256ll << 20;
-inline bool chunk_as_rows(const kvq_layout& L, int64_t batch, int64_t n_tok, int64_t G) {
-  if (L.k_dtype != KVQ_STORE_INT8 || L.v_dtype != KVQ_STORE_INT8) return false;
-  const int64_t rows = n_tok * G;
-  if (rows <= kHeadsPerBlock) return true;
-  // (in double: the product of the extents may pass 2^63)
-  return rows <= 2 * kHeadsPerBlock &&
-         (double)batch * (double)L.max_ctx * (double)L.n_kv_heads * (double)kv_bytes_per_pos(L) <=
-             (double)kRowsTwoBlockCacheBytes;
+// Query rows per workgroup of the chunk-rows path (launch_chunk_rows): one
+// block of 16 (token, head) rows, or two sharing every key and value operand
+// when a kv head has more than 16.
+inline int chunk_rows_per_block(int64_t n_tok, int64_t G) { return n_tok * G > kHeadsPerBlock ? 32 : 16; }
+
+// An int8 chunk with at most 32 (token, head) rows per kv head goes through
+// the decode partial kernel (launch_chunk_rows), one workgroup per (sequence,
+// kv head, split) holding all of them: its rows share every key tile, the
+// waves and splits divide the keys, where the chunk kernel would give a short
+// verify window few workgroups with long key ranges. Measured (kv_chunk_attn
+// alone): 128K keys, 8 heads per kv head, 1 / 2 / 4 tokens 32 / 32 / 42 us
+// against 50 / 50 / 49 us with the chunk kernel; 64 sequences of 32K keys, 4
+// heads per kv head, 1 to 8 tokens 0.75-0.86 ms against 1.40-1.46 ms. With
+// 64 rows (two such workgroups, each reading the keys) the chunk kernel is
+// faster (128K, 8 tokens: 57 against 60 us).
+inline bool chunk_as_rows(const kvq_layout& L, int64_t n_tok, int64_t G) {
+  return L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8 && n_tok * G <= 2 * kHeadsPerBlock;
 }
 
 // Workspace bytes for a plan.

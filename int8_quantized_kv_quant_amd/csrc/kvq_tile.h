@@ -210,8 +210,10 @@ __device__ __forceinline__ f16x8 tile_softmax(const float (&z)[2][4], WaveAcc<S>
 // V half of a tile: O += P . V_hat ;  l += P . 1. PART 1 and 2 split the work
 // in two halves of the output columns (l goes with PART 2), so that a wait can
 // sit between them; PART 0 does all of it.
-template <class S, int PART = 0>
-__device__ __forceinline__ void tile_pv(const VRegs<S>& t, f16x8 pa, WaveAcc<S>& acc) {
+// RB row blocks (acc[0 .. RB)) share every value operand: each dequantized
+// operand feeds one MFMA per block.
+template <class S, int PART = 0, int RB = 1>
+__device__ __forceinline__ void tile_pv_rows(const VRegs<S>& t, const f16x8 (&pa)[RB], WaveAcc<S>* acc) {
   constexpr int W0 = PART == 2 ? S::VW / 2 : 0, W1 = PART == 1 ? S::VW / 2 : S::VW;
   constexpr int N0 = PART == 2 ? S::VB / 2 : 0, N1 = PART == 1 ? S::VB / 2 : S::VB;
   if constexpr (S::VI8) {
@@ -237,7 +239,9 @@ __device__ __forceinline__ void tile_pv(const VRegs<S>& t, f16x8 pa, WaveAcc<S>&
           const f16x2 c = as_h2(biased) + as_h2(kNegBias);  // exact code
           r[pi] = as_u32(c * sv[pi]);                        // fp16(code * scale)
         }
-        acc.o[4 * w + bb] = mfma16(pa, __builtin_bit_cast(f16x8, r), acc.o[4 * w + bb]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc[rb].o[4 * w + bb] = mfma16(pa[rb], __builtin_bit_cast(f16x8, r), acc[rb].o[4 * w + bb]);
       }
     }
   } else {
@@ -249,13 +253,21 @@ __device__ __forceinline__ void tile_pv(const VRegs<S>& t, f16x8 pa, WaveAcc<S>&
         r[pi] = as_u32(__builtin_bit_cast(
             f16x2, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, t.v[2 * pi][n]),
                                               __builtin_bit_cast(float, t.v[2 * pi + 1][n]))));
-      acc.o[n] = mfma16(pa, __builtin_bit_cast(f16x8, r), acc.o[n]);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb].o[n] = mfma16(pa[rb], __builtin_bit_cast(f16x8, r), acc[rb].o[n]);
     }
   }
   if constexpr (PART != 1) {
     const f16x8 ones = {(f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1, (f16)1};
-    acc.l = mfma16(pa, ones, acc.l);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb].l = mfma16(pa[rb], ones, acc[rb].l);
   }
+}
+// One row block.
+template <class S, int PART = 0>
+__device__ __forceinline__ void tile_pv(const VRegs<S>& t, f16x8 pa, WaveAcc<S>& acc) {
+  const f16x8 p1[1] = {pa};
+  tile_pv_rows<S, PART, 1>(t, p1, &acc);
 }
 
 // ---- LDS staging for int8 K and V --------------------------------------------------

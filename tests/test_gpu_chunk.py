@@ -87,10 +87,11 @@ CASES = {
     "k8v4_window_smaller_than_chunk": (wl.WORKLOADS["long_k8v4"].with_(max_ctx=2048), [1000], 100, 64),
     "k8v4_mha_g1": (wl.WORKLOADS["long_k8v4"].with_(n_q_heads=2, max_ctx=1024), [300], 70, 0),
     # int8 chunks with at most 32 (token, head) rows per kv head run through
-    # the decode partial kernel (16-row blocks, per-row causal limits): 16, 12
-    # and 32 rows, a second block of one row, one row per token (G = 1) with a
-    # window narrower than the chunk, a first token at position 0, group-64
-    # and row scales (verify_window_long and tiny_prompt above: 32 and 20 rows)
+    # the decode partial kernel (one or two 16-row blocks per workgroup,
+    # per-row causal limits): 16, 12 and 32 rows, a second block of one row,
+    # one row per token (G = 1) with a window narrower than the chunk, a first
+    # token at position 0, group-64 and row scales (verify_window_long and
+    # tiny_prompt above: 32 and 20 rows)
     "rows_verify_long_t2": (wl.WORKLOADS["long"].with_(max_ctx=8192), [6000], 2, 0),
     "rows_gemma_window_t2": (wl.WORKLOADS["gemma"].with_(max_ctx=1024), [700], 2, 512),
     "rows_gemma_window_t4": (wl.WORKLOADS["gemma"].with_(max_ctx=1024), [900], 4, 512),
@@ -99,8 +100,11 @@ CASES = {
     "rows_mha_t16_window5": (wl.Workload("mha16", 1, 4, 4, 128, 128, 128, 1024, 0, 173), [300], 16, 5),
     "rows_mha_d64_t16": (wl.Workload("mha64", 2, 2, 2, 64, 64, 64, 1024, 0, 174), [0, 900], 16, 0),
     "rows_mha_t17_two_blocks": (wl.Workload("mha17", 1, 4, 4, 128, 128, 128, 1024, 0, 175), [300], 17, 0),
-    # one row past two 16-row blocks: the chunk kernel
+    "rows_gemma_t4_batch2": (wl.WORKLOADS["gemma"].with_(batch=2, max_ctx=1024), [0, 1000], 4, 512),
+    "rows_batched_t8_d128": (wl.WORKLOADS["batched"].with_(batch=2, max_ctx=2048), [1500, 17], 8, 0),
+    # just past 32 rows: the chunk kernel
     "chunk_mha_t33": (wl.Workload("mha33", 1, 4, 4, 128, 128, 128, 1024, 0, 176), [300], 33, 7),
+    "chunk_gemma_t8_batch2": (wl.WORKLOADS["gemma"].with_(batch=2, max_ctx=1024), [0, 1000], 8, 512),
 }
 
 
@@ -139,11 +143,12 @@ def test_rows_path_forced_splits():
         _check(got, want, label=f"rows T={T} splits {ns} window {window}")
 
 
-@pytest.mark.parametrize("n_tok", [2, 4])
+@pytest.mark.parametrize("n_tok", [2, 4, 8])
 def test_rows_path_full_size_verify_window(n_tok):
     """Verify tokens at the end of the 128K context of the long workload (16
-    query / 2 kv heads, head_dim 256, group-64 scales; one and two 16-row
-    blocks) with the planner's split, every output against the oracle."""
+    query / 2 kv heads, head_dim 256, group-64 scales; one 16-row block, two
+    blocks in one workgroup, and 64 rows through the chunk kernel) with the
+    planner's split, every output against the oracle."""
     w = wl.WORKLOADS["long"]
     got, want, plan = _run(w, [131072 - n_tok], n_tok, 0)
     print(f"[chunk] 128K verify T={n_tok} plan {plan.n_splits} x {plan.chunk}", flush=True)

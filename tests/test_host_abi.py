@@ -259,11 +259,11 @@ def test_chunk_plan_covers_every_key_range(n_tok, start, window):
 @pytest.mark.parametrize("n_tok,L,window", [(1, 131072, 0), (2, 131072, 0), (1, 3333, 0), (2, 4096, 512),
                                             (4, 131072, 0)])
 def test_short_int8_chunk_plan_follows_the_decode_rule(n_tok, L, window):
-    """An int8 chunk with at most 32 (token, head) rows per kv head goes through
-    the decode partial kernel and takes the decode planner's split: at one
-    token (the decode shape) the very same plan, at two the same key chunk
-    (the chip-filling rule decides at these lengths), at four (two 16-row
-    blocks per kv head) twice the chunk."""
+    """An int8 chunk with at most 32 (token, head) rows per kv head goes
+    through the decode partial kernel (one workgroup of 16 or 32 rows per kv
+    head and split) and takes the decode planner's split: at one token (the
+    decode shape) the very same plan, at two and four the same key chunk (the
+    chip-filling rule decides at these lengths)."""
     w = wl.WORKLOADS["long"]
     lay = _layout(w)
     pc = kvq.kvq_plan_chunk(lay, 1, n_tok, 16, L, window, 256)
@@ -274,7 +274,7 @@ def test_short_int8_chunk_plan_follows_the_decode_rule(n_tok, L, window):
     if n_tok == 1 and not window:
         assert (pc.n_splits, pc.chunk) == (pd.n_splits, pd.chunk)
     if L == 131072:
-        assert pd.chunk == 1024 and pc.chunk == 1024 * (1 if n_tok <= 2 else 2)
+        assert pd.chunk == pc.chunk == 1024
 
 
 def _blob(lay, unpack=False, **kw):
