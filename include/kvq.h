@@ -138,7 +138,7 @@ typedef struct {
  * s, s + S, s + 2*S, ... (block-cyclic) and splits s >= S are empty, so every
  * context length is covered whatever the planned one. kv_chunk_attn splits
  * the keys of a kv head's query rows the same way (from the lo of its first
- * token to the position of its last) when it runs an int8 chunk of at most 32
+ * token to the position of its last) when it runs a chunk of at most 32
  * (token, head) rows per kv head, otherwise contiguously: [lo + s*chunk,
  * lo + (s+1)*chunk), the last split running to the chunk's end. Either way
  * every key is covered whatever the plan. ws_bytes is the workspace that
@@ -289,8 +289,8 @@ int kv_decode_attn_static(const kvq_layout* layout,
  * position max_seq_len (the largest start + n_tok). Chunks with many query
  * rows run one split per (sequence, kv head, 64-row block); a few tokens over
  * a long prefix (a verify window) get their keys split so that the grid covers
- * the chip. int8 chunks with at most 32 (token, head) rows per kv head run
- * through the decode partial kernel and get kvq_plan's split rule.
+ * the chip. Chunks with at most 32 (token, head) rows per kv head run
+ * through the decode partial kernels and get kvq_plan's split rule.
  * ws_bytes = batch * n_tok * n_q_heads * n_splits * (head_dim + 2) * 4.
  * Writes *out; returns KVQ_OK or an error for invalid layout/sizes. */
 int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32_t n_q_heads,
@@ -317,11 +317,11 @@ int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32
  * rotated for a q4 K store and the output rotated back, as in
  * kv_decode_attn_splitk); other combinations are refused
  * (KVQ_ERR_UNSUPPORTED). Two kernels are enqueued on `stream`: the partials
- * and the combine of kv_decode_reduce. The partials of an int8 chunk with at
- * most 32 (token, head) rows per kv head come from the decode partial kernel,
+ * and the combine of kv_decode_reduce. The partials of a chunk with at most
+ * 32 (token, head) rows per kv head come from the decode partial kernels,
  * whose query rows are then (token, head) pairs with their own causal limits
- * (a verify window reads every key once); larger chunks and the 4-bit layouts
- * from the chunk kernels.
+ * (a verify window reads every key once, or once per 16 rows over a 4-bit
+ * layout); larger chunks from the chunk kernels.
  * Device precondition: 0 <= d_start_pos[b] and d_start_pos[b] + n_tok <= max_ctx;
  * a token that would sit at or beyond max_ctx sees no key and gets a zero row. */
 int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_store,

@@ -35,6 +35,11 @@
 // Output. O of each split stays in the rotated basis through the softmax; the
 // merged partial rows are rotated back (fwht256, fp32) before they are
 // written, so the reduce (linear in O) combines unrotated rows.
+// Chunk rows (the CHUNK instances; Strata PR 2698 "What it does": verify
+// windows read the same cache as decode). The 16 rows of a workgroup are
+// (token, head) pairs t * G + h of a chunk of T tokens at positions start + t,
+// each rotated like a decode query and masking keys outside its own causal
+// (and window) range; the partials go to rows (b, t, hq) for the same reduce.
 #include <math.h>
 
 #include <type_traits>
@@ -68,6 +73,12 @@ struct Q4Args {
   int32_t n_kv, G, n_q, head_blocks;
   int32_t n_splits, chunk, window;
   float c2;  // sm_scale * log2(e)
+  // Chunk attention through this kernel (the CHUNK instances): T tokens per
+  // sequence at positions start_pos[b] + t; the query rows of a kv head are
+  // its (token, head) pairs t * G + h in blocks of 16 (head_blocks of them), q
+  // is fp16 [B][T][n_q][D], and the partial rows are (b, t, hq).
+  const int32_t* start_pos;
+  int32_t T;
 };
 
 // ---- values ---------------------------------------------------------------------------
@@ -140,7 +151,7 @@ __device__ __forceinline__ void pv_q4(const VQ4Regs& t, f16x8 pa, WaveAcc<Shape<
 __device__ __forceinline__ int slot_swz(int f) { return f ^ ((f >> 4) & 3); }
 
 // ---- kernel ------------------------------------------------------------------------
-template <bool KQ4, bool KG64>
+template <bool KQ4, bool KG64, bool CHUNK = false>
 __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   constexpr int D = 256, NW = 4;
   using T = Q4Stage<KQ4, KG64>;
@@ -172,14 +183,37 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   const int hk = blockIdx.y / a.head_blocks;
   const int hblk = blockIdx.y % a.head_blocks;
   const int b = blockIdx.z;
-  const int nh = min(16, a.G - hblk * 16);
-  const int hq0 = hk * a.G + hblk * 16;
+  // Query rows of the workgroup (up to 16) and the keys [lo, L) they attend.
+  // Decode: heads hblk * 16 .. of kv head hk at context seq_lens[b]. Chunk:
+  // flat rows fr0 + r = t * G + h of kv head hk; token t sits at s0 + t and
+  // attends [max(0, s0 + t + 1 - window) (window > 0), s0 + t + 1).
+  const int fr0 = hblk * 16;
+  const int nh = CHUNK ? min(16, a.T * a.G - fr0) : min(16, a.G - fr0);
+  const int hq0 = hk * a.G + fr0;
   const int64_t row0 = ((int64_t)b * a.n_q + hq0) * a.n_splits + split;
-  float2* const ml_out = reinterpret_cast<float2*>(a.ws_ml) + row0;
-
-  const int L_in = a.seq_lens[b];
-  const int L = L_in < 0 ? 0 : (L_in > a.max_ctx ? a.max_ctx : L_in);
-  const int lo = a.window > 0 ? max(0, L - a.window) : 0;
+  float2* const ml = reinterpret_cast<float2*>(a.ws_ml);
+  // Partial row (within ws) of the workgroup's row r < nh.
+  auto rowid = [&](int r) -> int64_t {
+    if constexpr (CHUNK) {
+      const int fr = fr0 + r;
+      return (((int64_t)b * a.T + fr / a.G) * a.n_q + hk * a.G + fr % a.G) * a.n_splits + split;
+    } else {
+      return row0 + (int64_t)r * a.n_splits;
+    }
+  };
+  int L_in, L, lo, s0 = 0;
+  if constexpr (CHUNK) {
+    s0 = a.start_pos[b];
+    s0 = s0 < 0 ? 0 : (s0 > a.max_ctx ? a.max_ctx : s0);
+    const int t_first = fr0 / a.G, t_last = min(a.T - 1, (fr0 + nh - 1) / a.G);
+    L = (int)min((int64_t)s0 + t_last + 1, (int64_t)a.max_ctx);
+    lo = a.window > 0 ? max(0, s0 + t_first + 1 - a.window) : 0;
+    L_in = -1;  // no fused append
+  } else {
+    L_in = a.seq_lens[b];
+    L = L_in < 0 ? 0 : (L_in > a.max_ctx ? a.max_ctx : L_in);
+    lo = a.window > 0 ? max(0, L - a.window) : 0;
+  }
   // Split s takes the blocks s, s + S, ... of BLK positions of [lo, L),
   // S = min(n_splits, ceil((L - lo) / chunk)) (block-cyclic, as in the int8
   // kernel).
@@ -187,14 +221,14 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   const int n_used = (int)min((int64_t)a.n_splits, ((int64_t)L - lo + a.chunk - 1) / a.chunk);
   const int64_t start64 = (int64_t)lo + (int64_t)split * BLK;
   if (split >= n_used || start64 >= L) {  // empty split: (m, l) = (-inf, 0), O not written
-    if (threadIdx.x < nh) ml_out[(int64_t)threadIdx.x * a.n_splits] = make_float2(-INFINITY, 0.0f);
+    if (threadIdx.x < nh) ml[rowid(threadIdx.x)] = make_float2(-INFINITY, 0.0f);
     return;
   }
   const int start = (int)start64;
   int end = L;
   // Fused append: the workgroup whose blocks hold position L - 1 takes the new
   // row from the quantizer instead of the cache, and its tiles stop before it.
-  const bool own_new = a.k_new != nullptr && L_in == L && ((L - 1 - lo) / BLK) % n_used == split;
+  const bool own_new = !CHUNK && a.k_new != nullptr && L_in == L && ((L - 1 - lo) / BLK) % n_used == split;
   if (own_new) end = L - 1;
 
   const int lane = threadIdx.x & 63;
@@ -226,7 +260,16 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     if (lane < D / 8) dma<16>(rsrc_words(src, 2 * D), lds_addr_of(reinterpret_cast<const uint8_t*>(nw_in[wv])),
                               16u * lane, 0u);
   }
-  {
+  if constexpr (CHUNK) {  // the rows of this block: q [b][t][hk * G + h]
+    const u32x4 qrs = rsrc_words(a.q + (int64_t)b * a.T * a.n_q * D, (uint32_t)((int64_t)a.T * a.n_q * D * 2));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wv * 4 + i;
+      const int fr = fr0 + r;
+      const uint32_t off = (uint32_t)((((int64_t)(fr / a.G) * a.n_q + hk * a.G + fr % a.G) * D) * 2);
+      if (lane < D / 8) dma<16>(qrs, lds_addr_of(lds_q + r * QROW), r < nh ? off + 16 * lane : kOOB, 0u);
+    }
+  } else {
     const u32x4 qrs = rsrc_words(a.q + ((int64_t)b * a.n_q + hq0) * D, (uint32_t)(nh * D * 2));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -392,6 +435,13 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     load_q4_query(qy, qrow + 16 * q4, lds_ql + c16 * QROW + 16 * q4, reinterpret_cast<const uint8_t*>(lds_qsh[c16]),
                   reinterpret_cast<const uint8_t*>(lds_qsl[c16]), q4);
   int kpar = 0;
+  // Chunk: keys [rlo, rhi) of the lane's query row c16 (none for rows past nh).
+  int rlo = 0, rhi = 0;
+  if constexpr (CHUNK) {
+    const int P = s0 + (fr0 + c16) / a.G;
+    rhi = (c16 < nh && P < a.max_ctx) ? P + 1 : 0;
+    rlo = a.window > 0 ? max(0, P + 1 - a.window) : 0;
+  }
   if (p0 < end) {
     wait_vm<T::NV>();  // K half of the first tile landed (its V half may still be loading)
     read_k(tk);
@@ -402,8 +452,9 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     const bool more = pn < end;
     const bool more2 = pn + STEP < end;
     float z[2][4];
+    const int vlo = CHUNK ? rlo - p0 : 0, vhi = CHUNK ? min(rhi, end) - p0 : end - p0;
     if constexpr (KQ4) {
-      scores_q4(tk, 0, end - p0, z, st + T::KS_OFF + 512 * kpar, qy, c2s, c16, q4);
+      scores_q4(tk, vlo, vhi, z, st + T::KS_OFF + 512 * kpar, qy, c2s, c16, q4);
     } else {
       const uint8_t* qb = qrow + 32 * q4;
       f16x8 qv[4][2];
@@ -413,7 +464,7 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
         qv[j][1] = q_get(qb, j, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
-      scores_i8<KG64>(tk, 0, end - p0, z, qv, corr, a.c2, q4);
+      scores_i8<KG64>(tk, vlo, vhi, z, qv, corr, a.c2, q4);
     }
     if (more) wait_vm<T::NK>();  // V half of this tile landed; the next K half is in flight
     else wait_vm<0>();
@@ -482,8 +533,8 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
       l = fmaf(wk, sm_l[k][h], l);
     }
     fwht256(v, lane);  // back to the original basis (H / 16 is its own inverse)
-    reinterpret_cast<float4*>(a.ws_o + (row0 + (int64_t)h * a.n_splits) * D)[lane] = make_float4(v[0], v[1], v[2], v[3]);
-    if (lane == 0) ml_out[(int64_t)h * a.n_splits] = make_float2(M, l);
+    reinterpret_cast<float4*>(a.ws_o + rowid(h) * D)[lane] = make_float4(v[0], v[1], v[2], v[3]);
+    if (lane == 0) ml[rowid(h)] = make_float2(M, l);
   }
   // ---- fused append: the new row into the cache (one head block writes it)
   if (own_new && hblk == 0 && wv < 2) {
@@ -543,6 +594,49 @@ int launch_partial_q4(const kvq_layout& L, const void* k_store, const void* v_st
     hipLaunchKernelGGL((kvq_partial_q4_kernel<false, true>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((kvq_partial_q4_kernel<false, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int launch_chunk_rows_q4(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
+                         const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
+                         const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
+                         void* stream) {
+  if (L.head_dim != 256 || !q4_decode_supported(L)) return KVQ_ERR_UNSUPPORTED;
+  Q4Args a{};
+  a.k_store = k_store;
+  a.v_store = v_store;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.group_lanes = L.scale_group == 64 ? 16 : L.head_dim / 4;
+  a.q = q;
+  a.start_pos = d_start_pos;
+  a.T = n_tok;
+  const int64_t ws_rows = (int64_t)batch * n_tok * n_q_heads * plan.n_splits;
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_ml = static_cast<float*>(ws) + ws_rows * L.head_dim;
+  a.s_seq = L.s_seq;
+  a.s_pos = L.s_pos;
+  a.s_head = L.s_head;
+  a.ss_seq = L.ss_seq;
+  a.ss_pos = L.ss_pos;
+  a.ss_head = L.ss_head;
+  a.max_ctx = L.max_ctx > 0x7fffffff ? 0x7fffffff : (int32_t)L.max_ctx;
+  a.n_kv = L.n_kv_heads;
+  a.G = n_q_heads / L.n_kv_heads;
+  a.n_q = n_q_heads;
+  a.head_blocks = (int32_t)(((int64_t)n_tok * a.G + kHeadsPerBlock - 1) / kHeadsPerBlock);
+  a.n_splits = plan.n_splits;
+  a.chunk = plan.chunk;
+  a.window = window;
+  a.c2 = sm_scale * kLog2e;
+  const dim3 grid(plan.n_splits, L.n_kv_heads * a.head_blocks, batch);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L.k_dtype == KVQ_STORE_Q4)
+    hipLaunchKernelGGL((kvq_partial_q4_kernel<true, false, true>), grid, dim3(256), 0, s, a);
+  else if (L.scale_group == 64)
+    hipLaunchKernelGGL((kvq_partial_q4_kernel<false, true, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((kvq_partial_q4_kernel<false, false, true>), grid, dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

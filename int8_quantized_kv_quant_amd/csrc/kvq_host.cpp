@@ -282,8 +282,9 @@ int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32
   const int64_t l_eff = window > 0 ? std::min<int64_t>(max_seq_len, (int64_t)window + n_tok) : max_seq_len;
   if (chunk_as_rows(L, n_tok, G)) {  // the decode partial kernel and its split rule
     const int64_t rows = std::max<int64_t>(1, (int64_t)n_tok * G);
-    const int64_t units = (int64_t)(batch > 0 ? batch : 1) * L.n_kv_heads;
-    const int64_t chunk = decode_split_chunk(L, l_eff, units, rows, n_cu);
+    const int64_t per_wg = has_q4(L) ? kHeadsPerBlock : chunk_rows_per_block(rows, 1);
+    const int64_t units = (int64_t)(batch > 0 ? batch : 1) * L.n_kv_heads * ceil_div(rows, per_wg);
+    const int64_t chunk = decode_split_chunk(L, l_eff, units, std::min(rows, per_wg), n_cu);
     const int64_t n_splits = l_eff > 0 ? ceil_div(l_eff, chunk) : 1;
     if (n_splits > kMaxSplits || chunk > INT_MAX) return KVQ_ERR_UNSUPPORTED;
     out->n_splits = (int32_t)n_splits;
@@ -339,7 +340,10 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
   if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
   if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
   if (batch == 0 || n_tok == 0) return KVQ_OK;
-  if (has_q4(L))
+  if (has_q4(L) && chunk_as_rows(L, n_tok, n_q_heads / L.n_kv_heads))
+    st = launch_chunk_rows_q4(L, k_store, v_store, k_scales, v_scales, q, batch, n_tok, n_q_heads, d_start_pos,
+                              window, sm_scale, *plan, ws, stream);
+  else if (has_q4(L))
     st = launch_chunk_q4(L, k_store, v_store, k_scales, v_scales, q, batch, n_tok, n_q_heads, d_start_pos, window,
                          sm_scale, *plan, ws, stream);
   else if (chunk_as_rows(L, n_tok, n_q_heads / L.n_kv_heads))

@@ -107,6 +107,15 @@ inline int64_t kv_bytes_per_pos(const kvq_layout& L) {
 // when a kv head has more than 16.
 inline int chunk_rows_per_block(int64_t n_tok, int64_t G) { return n_tok * G > kHeadsPerBlock ? 32 : 16; }
 
+// (token, head) rows per kv head up to which a chunk over a 4-bit layout goes
+// through the 4-bit decode partial kernel, in 16-row workgroups (each reading
+// every key). Measured at 128K keys, 8 heads per kv head (kv_chunk_attn
+// alone): 1 / 2 / 4 tokens q4_0 30 / 32 / 46 us against 65 / 63 / 67 us with
+// the 4-bit chunk kernel, k8v4 28 / 29 / 41 us against 54 us; even without
+// any on-chip reuse of the second workgroup's reads two decode-sized passes
+// stay below the chunk kernel's time.
+constexpr int64_t kQ4RowsMax = 32;
+
 // An int8 chunk with at most 32 (token, head) rows per kv head goes through
 // the decode partial kernel (launch_chunk_rows), one workgroup per (sequence,
 // kv head, split) holding all of them: its rows share every key tile, the
@@ -118,6 +127,7 @@ inline int chunk_rows_per_block(int64_t n_tok, int64_t G) { return n_tok * G > k
 // 64 rows (two such workgroups, each reading the keys) the chunk kernel is
 // faster (128K, 8 tokens: 57 against 60 us).
 inline bool chunk_as_rows(const kvq_layout& L, int64_t n_tok, int64_t G) {
+  if (has_q4(L)) return n_tok * G <= kQ4RowsMax;
   return L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8 && n_tok * G <= 2 * kHeadsPerBlock;
 }
 
@@ -166,6 +176,13 @@ int launch_chunk_q4(const kvq_layout& L, const void* k_store, const void* v_stor
 
 int launch_blob(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k_scales, uint16_t* v_scales,
                 int32_t seq, int32_t pos0, int32_t n_pos, void* blob, bool unpack, void* stream);
+
+// Chunk attention through the 4-bit decode partial kernel (q4_0, k8v4): the
+// (token, head) rows of a kv head in blocks of 16, one workgroup per block.
+int launch_chunk_rows_q4(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
+                         const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
+                         const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
+                         void* stream);
 
 // Partials of a layout with a q4 store (q4_decode_supported).
 // k_new / v_new non-null: the fused append of kv_append_decode_splitk.

@@ -102,6 +102,15 @@ CASES = {
     "rows_mha_t17_two_blocks": (wl.Workload("mha17", 1, 4, 4, 128, 128, 128, 1024, 0, 175), [300], 17, 0),
     "rows_gemma_t4_batch2": (wl.WORKLOADS["gemma"].with_(batch=2, max_ctx=1024), [0, 1000], 4, 512),
     "rows_batched_t8_d128": (wl.WORKLOADS["batched"].with_(batch=2, max_ctx=2048), [1500, 17], 8, 0),
+    # the 4-bit layouts with at most 32 rows per kv head: the 4-bit decode
+    # partial kernel in 16-row workgroups (rotated query rows per (token,
+    # head), per-row limits; q4_verify_window above: two workgroups)
+    "rows_q4_t2": (wl.WORKLOADS["long_q4"].with_(max_ctx=8192), [6000], 2, 0),
+    "rows_q4_g16_batch2": (wl.WORKLOADS["long_q4"].with_(batch=2, n_q_heads=32, max_ctx=1024), [0, 600], 1, 0),
+    "rows_q4_t2_window": (wl.WORKLOADS["long_q4"].with_(max_ctx=2048), [1500], 2, 300),
+    "rows_k8v4_t2_window": (wl.WORKLOADS["long_k8v4"].with_(max_ctx=2048), [1500], 2, 300),
+    "rows_k8v4_mha_t16": (wl.WORKLOADS["long_k8v4"].with_(n_q_heads=2, max_ctx=1024), [700], 16, 0),
+    "rows_q4_mha_t17_two_workgroups": (wl.WORKLOADS["long_q4"].with_(n_q_heads=2, max_ctx=1024), [500], 17, 40),
     # just past 32 rows: the chunk kernel
     "chunk_mha_t33": (wl.Workload("mha33", 1, 4, 4, 128, 128, 128, 1024, 0, 176), [300], 33, 7),
     "chunk_gemma_t8_batch2": (wl.WORKLOADS["gemma"].with_(batch=2, max_ctx=1024), [0, 1000], 8, 512),
@@ -153,6 +162,18 @@ def test_rows_path_full_size_verify_window(n_tok):
     got, want, plan = _run(w, [131072 - n_tok], n_tok, 0)
     print(f"[chunk] 128K verify T={n_tok} plan {plan.n_splits} x {plan.chunk}", flush=True)
     _check(got, want, label=f"128K verify window T={n_tok}")
+
+
+@pytest.mark.parametrize("name,n_tok", [("long_q4", 2), ("long_q4", 4), ("long_k8v4", 2)])
+def test_rows_path_q4_full_size_verify_window(name, n_tok):
+    """Verify tokens at the end of the 128K context over the 4-bit layouts (16
+    query / 2 kv heads, head_dim 256; one and two 16-row workgroups per kv
+    head) through the 4-bit decode partial kernel with the planner's split,
+    every output against the oracle."""
+    w = wl.WORKLOADS[name]
+    got, want, plan = _run(w, [131072 - n_tok], n_tok, 0)
+    print(f"[chunk] {name} 128K verify T={n_tok} plan {plan.n_splits} x {plan.chunk}", flush=True)
+    _check(got, want, label=f"{name} 128K verify window T={n_tok}")
 
 
 def test_rows_path_token_past_the_cache_end():
