@@ -502,15 +502,15 @@ def chunk_workload(kvq, kvq_setup, wl, n_cu, name="long"):
             + " + kvq_reduce_kernel"}
 
 
-def verify_windows(kvq, wl, w, lay, caches, L, n_cu, capture, replay_ms, reps, oc=None, sizes=(2, 4, 8)):
+def verify_windows(kvq, wl, w, lay, L, n_cu, time_us, oc=None, sizes=(2, 4, 8)):
     """kv_chunk_attn (partials + combine) of a verify window of T tokens at
-    positions L - T .. L - 1 over the 128K caches of the headline step (all
-    copies, graph-replayed as the steps are; causal inside the window). The
-    keys are read once per 16-row block: T * 8 (token, head) rows per kv head
-    up to 32 go through the decode partial kernel (chunk rows), more through
-    the chunk kernel. The first and last token of each window are checked
-    against the fp64 oracle (its cache oc of positions [0, L), built here if
-    not given)."""
+    positions L - T .. L - 1 over the 128K caches of a decode workload
+    (time_us(fn) runs fn(cache) over all copies, graph-replayed as the steps
+    are, and returns microseconds per call; causal inside the window). Up to
+    32 (token, head) rows per kv head go through the decode partial kernels
+    (chunk rows), more through the chunk kernels. The first and last token of
+    each window are checked against the fp64 oracle (its cache oc of
+    positions [0, L), built here if not given)."""
     import torch
     from oracle import kvq_oracle as orc
     dev = torch.device("cuda:0")
@@ -533,7 +533,7 @@ def verify_windows(kvq, wl, w, lay, caches, L, n_cu, capture, replay_ms, reps, o
             kvq.kv_chunk_attn(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], q, 1, T, w.n_q_heads, sp, 0, sm,
                               plan, ws, ws.numel(), o)
 
-        ms = replay_ms(capture(call), reps)
+        ms = time_us(call) * 1e-3
         got = o.float().cpu().numpy().astype(np.float64)
         toks = [(0, 0), (0, T - 1)]
         want = orc.attend_chunk(qh, oc, np.array([start]), 0, sm, tokens=toks)
@@ -549,7 +549,8 @@ def verify_windows(kvq, wl, w, lay, caches, L, n_cu, capture, replay_ms, reps, o
 def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
     """The decode step over the 4-bit stores at the long-context shape (Strata
     PR 2698, "Not in this PR": q4_0 for K and V, k8v4 for V only, Hadamard-
-    rotated Q4_0 blocks at head_dim 256): kv_append_decode_splitk (the new
+    rotated Q4_0 blocks at head_dim 256), and verify windows of 2 and 4 tokens
+    over the same caches: kv_append_decode_splitk (the new
     token's rotation and quantization fused into the partials) +
     kv_decode_reduce, graph-replayed over COPIES caches of 131072 positions;
     the unfused three-call step beside it. The caches hold the workload's own
@@ -557,6 +558,7 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
     sampled rows' Q4_0 bytes against the oracle's quantizer. The partial kernel
     is also timed alone (its roofline: algorithmic bytes / launch time)."""
     import torch
+    from oracle import kvq_oracle as orc
     dev = torch.device("cuda:0")
     res = {}
     for name in ("long_q4", "long_k8v4"):
@@ -610,7 +612,11 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
         us = graph_us(lambda c: (fused(c), reduce()))
         torch.cuda.synchronize()
         got = out.float().cpu().numpy().astype(np.float64)
-        err = float(np.abs(got[0] - oracle_seq(w, 0, L, wl.queries(w)[0])).max())
+        # the oracle's cache of positions [0, L) (the step's own row included),
+        # for the step and for the verify windows below
+        oc = orc.Cache(1, L, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+        oc.append(wl.kv_rows(w, "k", 0, 0, L)[None], wl.kv_rows(w, "v", 0, 0, L)[None], [0])
+        err = float(np.abs(got[0] - orc.attend(wl.queries(w)[:1], oc, [L], w.window, sm)[0]).max())
         rng = np.random.default_rng(7)
         codes_ok = codes_match(kvq_setup, lay, caches[-1], w, 0,
                                np.unique(np.concatenate([rng.integers(0, L, 64), [L - 1]])))
@@ -618,6 +624,8 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
         part_us = graph_us(partial)
         fpart_us = graph_us(fused)
         kvb = wl.kv_bytes_per_step(w, lens)
+        verify = verify_windows(kvq, wl, w, lay, L, n_cu, graph_us, oc, sizes=(2, 4))
+        del oc
         res[name + "_128k"] = {
             "k_store": w.k_dtype, "v_store": w.v_dtype, "context": L, "cache_copies": COPIES,
             "step": "kv_append_decode_splitk + kv_decode_reduce (rotation and quantize-append fused)",
@@ -630,7 +638,8 @@ def q4_workloads(kvq, kvq_setup, wl, n_cu, steps):
             "partial_traffic": traffic_from_profiles(kernel_source_digest(Q4_SOURCES), plan,
                                                      "partial_q4_long_128k_traffic.json", name),
             "n_splits": plan.n_splits, "chunk": plan.chunk,
-            "max_abs_err": err, "codes_bitexact": codes_ok, "tol": TOL}
+            "max_abs_err": err, "codes_bitexact": codes_ok, "tol": TOL,
+            "verify_windows": verify}
         del caches, c0
         torch.cuda.empty_cache()
     return res
@@ -902,7 +911,7 @@ def main() -> int:
         del ws_c
     log("context sweep: " + ", ".join(f"{d['context']}: {d['us_per_step']} us" for d in sweep))
     log("timing verify windows of 2, 4 and 8 tokens at the end of the 128K context")
-    verify = verify_windows(kvq, wl, w, lay, caches, L, n_cu, capture, replay_ms, reps, oracle_cache)
+    verify = verify_windows(kvq, wl, w, lay, L, n_cu, lambda fn: replay_ms(capture(fn), reps) * 1e3, oracle_cache)
     del oracle_cache
     log("verify windows: " + ", ".join(f"T={d['tokens']}: {d['us']} us" for d in verify))
 
