@@ -4,8 +4,8 @@ k8v4), scale group, kv heads and GQA group size (one or two 16-head blocks),
 batch with ragged lengths (empty contexts included), sliding windows, slot
 width and layout order. Each configuration runs decode (planner plan and a
 forced split count), the fused decode step (its cache bit-identical to
-kv_quant_append's) and, where the stores allow it, chunk attention; outputs
-within 2e-3 of the oracle.
+kv_quant_append's) and, where the stores allow it, chunk attention (planner
+plan and 96-position splits); outputs within 2e-3 of the oracle.
 
 genie-ai-runtime v1.3.0 "split-K decode attention" and "Details" (windows,
 slot width); Strata PR 2698, "What it does" (group-64 scales, k8v32 / k32v8)
@@ -101,19 +101,31 @@ def test_random_configuration(i):
         if cache[name] is not None:
             assert torch.equal(cache[name].view(torch.uint8), fused[name].view(torch.uint8)), name
 
-    # chunk attention (int8 or 4-bit stores): the last n_tok tokens of each context
+    # chunk attention (int8 or 4-bit stores): the last n_tok tokens of each
+    # context, for a chunk of 1-40 tokens and a verify window of at most 32
+    # (token, head) rows per kv head (the decode kernels' chunk rows)
     if (w.k_dtype, w.v_dtype) in (("int8", "int8"), ("q4", "q4"), ("int8", "q4")):
         rng = np.random.default_rng([77, i])
-        n_tok = int(rng.integers(1, 41))
-        starts = np.maximum(lens - n_tok, 0)
-        qc = wl.chunk_queries(w, n_tok)
-        got = kvq.chunk_attn(lay, cache, torch.from_numpy(qc).cuda(),
-                             torch.from_numpy(starts.astype(np.int32)).cuda(), w.window, sm,
-                             max_seq_len=w.max_ctx).cpu().numpy().astype(np.float64)
-        want_c = orc.attend_chunk(qc, oc, starts, w.window, sm)
-        # tokens past a sequence's filled context attend to unfilled (zero) rows
-        # on both sides; compare the tokens inside the context
-        for b in range(w.batch):
-            n_in = int(min(n_tok, lens[b] - starts[b]))
-            if n_in > 0:
-                assert np.abs(got[b, :n_in] - want_c[b, :n_in]).max() <= TOL, b
+        for n_tok in (int(rng.integers(1, 41)), int(rng.integers(1, max(1, 32 // w.gqa) + 1))):
+            starts = np.maximum(lens - n_tok, 0)
+            qc = wl.chunk_queries(w, n_tok)
+            got = kvq.chunk_attn(lay, cache, torch.from_numpy(qc).cuda(),
+                                 torch.from_numpy(starts.astype(np.int32)).cuda(), w.window, sm,
+                                 max_seq_len=w.max_ctx).cpu().numpy().astype(np.float64)
+            want_c = orc.attend_chunk(qc, oc, starts, w.window, sm)
+            # the same chunk with the keys in 96-position splits (the planner's
+            # own choice above): both kernels of kv_chunk_attn cover the keys
+            # whatever the plan
+            ns_c = -(-w.max_ctx // 96)
+            plan_c = kvq.Plan(ns_c, 96, w.batch * n_tok * w.n_q_heads * ns_c * (w.head_dim + 2) * 4)
+            got_f = kvq.chunk_attn(lay, cache, torch.from_numpy(qc).cuda(),
+                                   torch.from_numpy(starts.astype(np.int32)).cuda(), w.window, sm,
+                                   plan=plan_c).cpu().numpy().astype(np.float64)
+            print(f"[fuzz {i}] chunk n_tok={n_tok} rows per kv head {n_tok * w.gqa}", flush=True)
+            # tokens past a sequence's filled context attend to unfilled (zero)
+            # rows on both sides; compare the tokens inside the context
+            for b in range(w.batch):
+                n_in = int(min(n_tok, lens[b] - starts[b]))
+                if n_in > 0:
+                    assert np.abs(got[b, :n_in] - want_c[b, :n_in]).max() <= TOL, (n_tok, b)
+                    assert np.abs(got_f[b, :n_in] - want_c[b, :n_in]).max() <= TOL, (n_tok, b)
