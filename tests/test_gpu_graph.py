@@ -78,3 +78,68 @@ def test_graph_replays_match_eager_steps():
         step()  # the same step eagerly (re-appends the same token: idempotent)
         torch.cuda.synchronize()
         assert torch.equal(got, out), f"graph replay differs from eager step at L={L}"
+
+
+@pytest.mark.parametrize("name,n_tok", [("long", 2), ("long", 4), ("long_q4", 2), ("long_k8v4", 4)])
+def test_graph_verify_window_replays(name, n_tok):
+    """A speculative-decoding verify step -- kv_quant_append of n_tok draft
+    tokens, then kv_chunk_attn over them (through the decode partial kernels:
+    16 or 32 (token, head) rows per kv head) -- captured once and replayed
+    with the window's start advanced in device memory: every replay within
+    2e-3 of the oracle at its position and equal to the same step run eagerly.
+    Strata PR 2698, "What it does" (verify windows over the int8 cache) and
+    "Not in this PR" (the 4-bit layouts); genie-ai-runtime v1.3.0 "Details"
+    (split count fixed at capture, positions from device memory)."""
+    import int8_quantized_kv_quant_amd as kvq
+    import kvq_setup
+
+    w = wl.WORKLOADS[name].with_(max_ctx=4096)
+    S0 = 3000
+    lay, cache = kvq_setup.fill_cache(w, np.array([S0]))
+    sm = 1.0 / math.sqrt(w.head_dim)
+    plan = kvq.kvq_plan_chunk(lay, 1, n_tok, w.n_q_heads, w.max_ctx, 0, kvq_setup.n_cu())
+    ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, n_tok, w.n_q_heads, w.head_dim), dtype=torch.float16, device="cuda")
+    qh = wl.chunk_queries(w, n_tok)
+    q = torch.from_numpy(qh).cuda()
+    sp = torch.tensor([S0], dtype=torch.int32, device="cuda")
+    k_new = torch.empty((1, n_tok, w.n_kv_heads, w.head_dim), dtype=torch.float16, device="cuda")
+    v_new = torch.empty_like(k_new)
+
+    def step():
+        kvq.kv_quant_append(lay, cache["k"], cache["v"], cache["k_scales"], cache["v_scales"], k_new, v_new,
+                            sp, 1, n_tok)
+        kvq.kv_chunk_attn(lay, cache["k"], cache["v"], cache["k_scales"], cache["v_scales"], q, 1, n_tok,
+                          w.n_q_heads, sp, 0, sm, plan, ws, ws.numel(), out)
+
+    def load(S):
+        k_new.copy_(torch.from_numpy(wl.kv_rows(w, "k", 0, S, n_tok))[None])
+        v_new.copy_(torch.from_numpy(wl.kv_rows(w, "v", 0, S, n_tok))[None])
+        sp.fill_(S)
+
+    def oracle(S):
+        oc = orc.Cache(1, w.max_ctx, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+        oc.append(wl.kv_rows(w, "k", 0, 0, S + n_tok)[None], wl.kv_rows(w, "v", 0, 0, S + n_tok)[None], [0])
+        return orc.attend_chunk(qh, oc, np.array([S]), 0, sm)
+
+    load(S0)
+    step()  # warm-up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        S = S0 + n_tok * i
+        load(S)  # eager host->device work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        e = float(np.abs(got.cpu().numpy().astype(np.float64) - oracle(S)).max())
+        print(f"[graph verify] {name} T={n_tok} start {S}: max abs err {e:.3g}", flush=True)
+        assert e <= TOL, f"graph replay at start {S}: max abs err {e:.3g} against the oracle"
+        out.zero_()
+        step()  # the same step eagerly (re-appends the same tokens: idempotent)
+        torch.cuda.synchronize()
+        assert torch.equal(got, out), f"graph replay differs from the eager step at start {S}"
