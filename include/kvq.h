@@ -315,7 +315,9 @@ int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32
  *   out          fp16 [batch][n_tok][n_q_heads][head_dim], contiguous, 16-byte aligned.
  * Store types: int8 K and V, or the 4-bit layouts q4_0 and k8v4 (the query
  * rotated for a q4 K store and the output rotated back, as in
- * kv_decode_attn_splitk); other combinations are refused
+ * kv_decode_attn_splitk); with an fp32 store (k8v32, k32v8, k32v32) only
+ * chunks of at most 16 (token, head) rows per kv head (verify windows);
+ * other combinations and longer chunks over fp32 stores are refused
  * (KVQ_ERR_UNSUPPORTED). Two kernels are enqueued on `stream`: the partials
  * and the combine of kv_decode_reduce. The partials of a chunk with at most
  * 32 (token, head) rows per kv head come from the decode partial kernels,

@@ -182,10 +182,9 @@ template <int D, bool KI8, bool VI8, bool G64, int NW, bool CHUNK = false, int R
 __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   using S = Shape<D, KI8, VI8, G64>;
   constexpr bool kStaged = KI8 && VI8;
-  static_assert(!CHUNK || kStaged, "chunk rows through the int8 kernel only");
   // RB blocks of 16 query rows per workgroup, sharing every key and value
-  // operand (chunk rows only).
-  static_assert(RB == 1 || (CHUNK && RB == 2), "two row blocks for chunk rows only");
+  // operand (chunk rows over int8 K and V only).
+  static_assert(RB == 1 || (CHUNK && kStaged && RB == 2), "two row blocks for int8 chunk rows only");
   // One store int8, the other fp32: the fp32 tile is staged in LDS, the int8
   // operands go straight to registers.
   constexpr bool kMix = KI8 != VI8;
@@ -435,6 +434,21 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     acc[rb].m_ref = -INFINITY;
   }
 
+  // Chunk: keys [rlo, rhi) of the lane's query row c16 of block rb (none for
+  // rows past nh).
+  int rlo[RB], rhi[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    rlo[rb] = 0;
+    rhi[rb] = 0;
+    if constexpr (CHUNK) {
+      const int r = 16 * rb + c16;
+      const int P = s0 + (fr0 + r) / a.G;
+      rhi[rb] = (r < nh && P < a.max_ctx) ? P + 1 : 0;
+      rlo[rb] = a.window > 0 ? max(0, P + 1 - a.window) : 0;
+    }
+  }
+
   if constexpr (kStaged) {
     // Pipeline over this wavefront's tiles p0, p0 + STEP, ... For tile t:
     //   S^T from the K operands already in registers;
@@ -446,20 +460,6 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     // of each half overlap the arithmetic that precedes their use.
     constexpr int NH = kHalfLoads<S>;
     uint8_t* const st = lds_st + wv * STAGE_BYTES;
-    // Chunk: keys [rlo, rhi) of the lane's query row c16 of block rb (none
-    // for rows past nh).
-    int rlo[RB], rhi[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      rlo[rb] = 0;
-      rhi[rb] = 0;
-      if constexpr (CHUNK) {
-        const int r = 16 * rb + c16;
-        const int P = s0 + (fr0 + r) / a.G;
-        rhi[rb] = (r < nh && P < a.max_ctx) ? P + 1 : 0;
-        rlo[rb] = a.window > 0 ? max(0, P + 1 - a.window) : 0;
-      }
-    }
     if (p0 < end) {
       wait_vm<NH>();  // K half of the first tile landed (its V half may still be loading)
       stage_read_k<S>(tk, st, c16, q4);
@@ -518,7 +518,8 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
         f32stage_issue<S, !KI8>(st, frw, pn, end - pn, frow, lane);
       }
       float z[2][4];
-      tile_scores<S>(tk, end - p0, z, qb, corr[0], a.c2, q4);
+      if constexpr (CHUNK) tile_scores<S>(tk, rlo[0] - p0, min(rhi[0], end) - p0, z, qb, corr[0], a.c2, q4);
+      else tile_scores<S>(tk, end - p0, z, qb, corr[0], a.c2, q4);
       const f16x8 pa = tile_softmax<S>(z, acc[0], q4);
       tile_pv<S>(tv, pa, acc[0]);
       if constexpr (KI8) tk = tkn;
@@ -529,7 +530,8 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       load_k_global<S>(tk, krs, ksrs, p0, end, krow, srow, c16, q4);
       load_v_global<S>(tv, vrs, vsrs, p0, end, vrow, srow, c16, q4);
       float z[2][4];
-      tile_scores<S>(tk, end - p0, z, qb, corr[0], a.c2, q4);
+      if constexpr (CHUNK) tile_scores<S>(tk, rlo[0] - p0, min(rhi[0], end) - p0, z, qb, corr[0], a.c2, q4);
+      else tile_scores<S>(tk, end - p0, z, qb, corr[0], a.c2, q4);
       const f16x8 pa = tile_softmax<S>(z, acc[0], q4);
       tile_pv<S>(tv, pa, acc[0]);
     }
@@ -706,17 +708,33 @@ int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
-template <int D, bool G64, int RB>
+template <int D, bool KI8, bool VI8, bool G64, int RB>
 static void launch_rows_t(const PartialArgs& a, dim3 grid, hipStream_t s) {
   constexpr int NW = kPartialWaves;
-  hipLaunchKernelGGL((kvq_partial_kernel<D, true, true, G64, NW, true, RB>), grid, dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((kvq_partial_kernel<D, KI8, VI8, G64, NW, true, RB>), grid, dim3(NW * 64), 0, s, a);
+}
+
+template <int D>
+static void dispatch_rows(const kvq_layout& L, const PartialArgs& a, dim3 grid, hipStream_t s, int rb) {
+  const bool ki8 = L.k_dtype == KVQ_STORE_INT8, vi8 = L.v_dtype == KVQ_STORE_INT8;
+  const bool g64 = L.scale_group == 64 && L.head_dim != 64;  // at D = 64 both granularities coincide
+  if (ki8 && vi8) {
+    if (rb == 2) g64 ? launch_rows_t<D, true, true, true, 2>(a, grid, s) : launch_rows_t<D, true, true, false, 2>(a, grid, s);
+    else g64 ? launch_rows_t<D, true, true, true, 1>(a, grid, s) : launch_rows_t<D, true, true, false, 1>(a, grid, s);
+  } else if (ki8) {
+    g64 ? launch_rows_t<D, true, false, true, 1>(a, grid, s) : launch_rows_t<D, true, false, false, 1>(a, grid, s);
+  } else if (vi8) {
+    g64 ? launch_rows_t<D, false, true, true, 1>(a, grid, s) : launch_rows_t<D, false, true, false, 1>(a, grid, s);
+  } else {
+    launch_rows_t<D, false, false, false, 1>(a, grid, s);
+  }
 }
 
 int launch_chunk_rows(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
                       const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,
                       const int32_t* d_start_pos, int32_t window, float sm_scale, const kvq_plan_t& plan, void* ws,
                       void* stream) {
-  if (L.k_dtype != KVQ_STORE_INT8 || L.v_dtype != KVQ_STORE_INT8) return KVQ_ERR_UNSUPPORTED;
+  if (has_q4(L)) return KVQ_ERR_UNSUPPORTED;
   PartialArgs a{};
   a.k_store = k_store;
   a.v_store = v_store;
@@ -741,7 +759,7 @@ int launch_chunk_rows(const kvq_layout& L, const void* k_store, const void* v_st
   a.n_q = n_q_heads;
   // One or two row blocks of 16 per workgroup (all rows sharing every key and
   // value operand).
-  const int per_wg = chunk_rows_per_block(n_tok, a.G);
+  const int per_wg = chunk_rows_per_block(L, n_tok, a.G);
   const int rb = per_wg / kHeadsPerBlock;
   a.head_blocks = (int32_t)(((int64_t)n_tok * a.G + per_wg - 1) / per_wg);
   a.n_splits = plan.n_splits;
@@ -750,20 +768,10 @@ int launch_chunk_rows(const kvq_layout& L, const void* k_store, const void* v_st
   a.c2 = sm_scale * kLog2e;
   dim3 grid(plan.n_splits, L.n_kv_heads * a.head_blocks, batch);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool g64 = L.scale_group == 64 && L.head_dim != 64;
   switch (L.head_dim) {
-    case 64:
-      if (rb == 2) launch_rows_t<64, false, 2>(a, grid, s);
-      else launch_rows_t<64, false, 1>(a, grid, s);
-      break;
-    case 128:
-      if (rb == 2) g64 ? launch_rows_t<128, true, 2>(a, grid, s) : launch_rows_t<128, false, 2>(a, grid, s);
-      else g64 ? launch_rows_t<128, true, 1>(a, grid, s) : launch_rows_t<128, false, 1>(a, grid, s);
-      break;
-    case 256:
-      if (rb == 2) g64 ? launch_rows_t<256, true, 2>(a, grid, s) : launch_rows_t<256, false, 2>(a, grid, s);
-      else g64 ? launch_rows_t<256, true, 1>(a, grid, s) : launch_rows_t<256, false, 1>(a, grid, s);
-      break;
+    case 64: dispatch_rows<64>(L, a, grid, s, rb); break;
+    case 128: dispatch_rows<128>(L, a, grid, s, rb); break;
+    case 256: dispatch_rows<256>(L, a, grid, s, rb); break;
     default: return KVQ_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;

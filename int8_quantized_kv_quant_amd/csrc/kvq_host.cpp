@@ -282,7 +282,7 @@ int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32
   const int64_t l_eff = window > 0 ? std::min<int64_t>(max_seq_len, (int64_t)window + n_tok) : max_seq_len;
   if (chunk_as_rows(L, n_tok, G)) {  // the decode partial kernel and its split rule
     const int64_t rows = std::max<int64_t>(1, (int64_t)n_tok * G);
-    const int64_t per_wg = has_q4(L) ? kHeadsPerBlock : chunk_rows_per_block(rows, 1);
+    const int64_t per_wg = has_q4(L) ? kHeadsPerBlock : chunk_rows_per_block(L, n_tok, G);
     const int64_t units = (int64_t)(batch > 0 ? batch : 1) * L.n_kv_heads * ceil_div(rows, per_wg);
     const int64_t chunk = decode_split_chunk(L, l_eff, units, std::min(rows, per_wg), n_cu);
     const int64_t n_splits = l_eff > 0 ? ceil_div(l_eff, chunk) : 1;
@@ -316,13 +316,15 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
   int st = check_layout(layout);
   if (st) return st;
   const kvq_layout& L = *layout;
-  // int8 K and V, or the 4-bit layouts of the decode path (q4_0, k8v4)
-  if (!(L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8) && !q4_decode_supported(L))
-    return KVQ_ERR_UNSUPPORTED;
+  // int8 K and V, the 4-bit layouts of the decode path (q4_0, k8v4), or an
+  // fp32 store when the chunk's rows fit the decode kernel's chunk rows
+  if (has_q4(L) && !q4_decode_supported(L)) return KVQ_ERR_UNSUPPORTED;
   if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
   if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
   if ((st = check_heads(L, batch, n_q_heads))) return st;
   if (n_tok < 0) return KVQ_ERR_SHAPE;
+  const bool any_fp32 = L.k_dtype == KVQ_STORE_FP32 || L.v_dtype == KVQ_STORE_FP32;
+  if (any_fp32 && !chunk_as_rows(L, n_tok, n_q_heads / L.n_kv_heads)) return KVQ_ERR_UNSUPPORTED;
   if (!plan) return KVQ_ERR_NULL;
   if (plan->n_splits < 1 || plan->n_splits > kMaxSplits) return KVQ_ERR_SHAPE;
   if (plan->chunk < kTile || plan->chunk % kTile) return KVQ_ERR_SHAPE;

@@ -102,10 +102,14 @@ inline int64_t kv_bytes_per_pos(const kvq_layout& L) {
   return b;
 }
 
-// Query rows per workgroup of the chunk-rows path (launch_chunk_rows): one
-// block of 16 (token, head) rows, or two sharing every key and value operand
-// when a kv head has more than 16.
-inline int chunk_rows_per_block(int64_t n_tok, int64_t G) { return n_tok * G > kHeadsPerBlock ? 32 : 16; }
+// Query rows per workgroup of the chunk-rows path of the int8 / fp32 decode
+// kernel (launch_chunk_rows): one block of 16 (token, head) rows, or, with
+// int8 K and V and more than 16 rows per kv head, two sharing every key and
+// value operand.
+inline int chunk_rows_per_block(const kvq_layout& L, int64_t n_tok, int64_t G) {
+  const bool i8 = L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8;
+  return i8 && n_tok * G > kHeadsPerBlock ? 32 : 16;
+}
 
 // (token, head) rows per kv head up to which a chunk over a 4-bit layout goes
 // through the 4-bit decode partial kernel, in 16-row workgroups (each reading
@@ -116,20 +120,26 @@ inline int chunk_rows_per_block(int64_t n_tok, int64_t G) { return n_tok * G > k
 // stay below the chunk kernel's time.
 constexpr int64_t kQ4RowsMax = 32;
 
-// An int8 chunk with at most 32 (token, head) rows per kv head goes through
-// the decode partial kernel (launch_chunk_rows), one workgroup per (sequence,
-// kv head, split) holding all of them: its rows share every key tile, the
-// waves and splits divide the keys, where the chunk kernel would give a short
-// verify window few workgroups with long key ranges. Measured (kv_chunk_attn
-// alone): 128K keys, 8 heads per kv head, 1 / 2 / 4 tokens 32 / 32 / 42 us
-// against 50 / 50 / 49 us with the chunk kernel; 64 sequences of 32K keys, 4
-// heads per kv head, 1 to 8 tokens 0.75-0.86 ms against 1.40-1.46 ms. With
-// 64 rows (two such workgroups, each reading the keys) the chunk kernel is
-// faster (128K, 8 tokens: 57 against 60 us).
-inline bool chunk_as_rows(const kvq_layout& L, int64_t n_tok, int64_t G) {
-  if (has_q4(L)) return n_tok * G <= kQ4RowsMax;
-  return L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8 && n_tok * G <= 2 * kHeadsPerBlock;
+// A chunk goes through the decode partial kernels ("chunk rows") when a kv
+// head has at most this many (token, head) rows: its rows share every key
+// tile, the waves and splits divide the keys, where the chunk kernels would
+// give a short verify window few workgroups with long key ranges.
+//  - int8 K and V: 32 rows, one workgroup. Measured (kv_chunk_attn alone):
+//    128K keys, 8 heads per kv head, 1 / 2 / 4 tokens 32 / 32 / 42 us against
+//    50 / 50 / 49 us with the chunk kernel; 64 sequences of 32K keys, 4 heads
+//    per kv head, 1 to 8 tokens 0.75-0.86 ms against 1.40-1.46 ms. With 64
+//    rows (two such workgroups, each reading the keys) the chunk kernel is
+//    faster (128K, 8 tokens: 57 against 60 us).
+//  - the 4-bit layouts: kQ4RowsMax.
+//  - an fp32 store (k8v32, k32v8, k32v32): 16 rows, one workgroup; the chunk
+//    kernels take int8 and 4-bit stores only, so longer chunks over these
+//    layouts are refused.
+inline int64_t chunk_rows_max(const kvq_layout& L) {
+  if (has_q4(L)) return kQ4RowsMax;
+  if (L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8) return 2 * kHeadsPerBlock;
+  return kHeadsPerBlock;
 }
+inline bool chunk_as_rows(const kvq_layout& L, int64_t n_tok, int64_t G) { return n_tok * G <= chunk_rows_max(L); }
 
 // Workspace bytes for a plan.
 inline int64_t workspace_bytes(int64_t batch, int64_t n_q, int64_t n_splits, int64_t head_dim) {

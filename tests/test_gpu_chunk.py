@@ -2,7 +2,8 @@
 sequence, causal inside the chunk) on the GPU against the fp64 oracle
 (oracle.attend_chunk): max abs error <= 2e-3 (fp32 accumulation, fp16 output)
 on prompt chunks and verify windows, windows, every GQA grouping and the
-ragged row blocks of a chunk.
+ragged row blocks of a chunk, the chunk kernels and the decode kernels' chunk
+rows (int8, 4-bit and fp32 stores).
 
 Strata PR 2698, "What it does": the prompt chunk and the verify windows read
 the same int8 cache as decode, dequantized on the fly; the 4-bit layouts of
@@ -111,6 +112,14 @@ CASES = {
     "rows_k8v4_t2_window": (wl.WORKLOADS["long_k8v4"].with_(max_ctx=2048), [1500], 2, 300),
     "rows_k8v4_mha_t16": (wl.WORKLOADS["long_k8v4"].with_(n_q_heads=2, max_ctx=1024), [700], 16, 0),
     "rows_q4_mha_t17_two_workgroups": (wl.WORKLOADS["long_q4"].with_(n_q_heads=2, max_ctx=1024), [500], 17, 40),
+    # an fp32 store (k8v32, k32v8, k32v32): verify windows of at most 16 rows
+    # per kv head through the decode partial kernel's mixed and fp32 paths
+    "rows_k8v32_t2": (wl.WORKLOADS["mixed_k8v32"].with_(max_ctx=4096), [3000], 2, 0),
+    "rows_k32v8_t2_window": (wl.WORKLOADS["mixed_k32v8"].with_(max_ctx=4096), [3000], 2, 700),
+    "rows_k32v32_batch2_d128": (wl.Workload("k32v32", 2, 8, 2, 128, 128, 128, 1024, 0, 178,
+                                            k_dtype="fp32", v_dtype="fp32"), [0, 900], 4, 0),
+    "rows_k8v32_mha_t16_d64": (wl.Workload("k8v32m", 1, 2, 2, 64, 64, 64, 1024, 0, 179,
+                                           k_dtype="int8", v_dtype="fp32"), [500], 16, 30),
     # just past 32 rows: the chunk kernel
     "chunk_mha_t33": (wl.Workload("mha33", 1, 4, 4, 128, 128, 128, 1024, 0, 176), [300], 33, 7),
     "chunk_gemma_t8_batch2": (wl.WORKLOADS["gemma"].with_(batch=2, max_ctx=1024), [0, 1000], 8, 512),

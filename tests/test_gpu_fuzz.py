@@ -104,9 +104,15 @@ def test_random_configuration(i):
     # chunk attention (int8 or 4-bit stores): the last n_tok tokens of each
     # context, for a chunk of 1-40 tokens and a verify window of at most 32
     # (token, head) rows per kv head (the decode kernels' chunk rows)
+    # (an fp32 store: the verify window only, of at most 16 rows per kv head)
+    rng = np.random.default_rng([77, i])
+    sizes = []
     if (w.k_dtype, w.v_dtype) in (("int8", "int8"), ("q4", "q4"), ("int8", "q4")):
-        rng = np.random.default_rng([77, i])
-        for n_tok in (int(rng.integers(1, 41)), int(rng.integers(1, max(1, 32 // w.gqa) + 1))):
+        sizes = [int(rng.integers(1, 41)), int(rng.integers(1, max(1, 32 // w.gqa) + 1))]
+    elif w.gqa <= 16:
+        sizes = [int(rng.integers(1, 16 // w.gqa + 1))]
+    if sizes:
+        for n_tok in sizes:
             starts = np.maximum(lens - n_tok, 0)
             qc = wl.chunk_queries(w, n_tok)
             got = kvq.chunk_attn(lay, cache, torch.from_numpy(qc).cuda(),

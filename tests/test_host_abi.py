@@ -218,7 +218,12 @@ def test_fused_append_refuses_what_either_part_refuses():
 @needs_lib
 def test_chunk_attention_refusals():
     lay = _base()
-    assert _chunk(_with(lay, v_dtype=kvq.KVQ_STORE_FP32)) == UNSUP   # int8 K and V only
+    # an fp32 store: verify windows of at most 16 (token, head) rows per kv
+    # head only (the decode kernel's chunk rows; 8 heads per kv head here)
+    assert _chunk(_with(lay, v_dtype=kvq.KVQ_STORE_FP32)) == UNSUP
+    assert _chunk(_with(lay, k_dtype=kvq.KVQ_STORE_FP32), n_tok=3) == UNSUP
+    assert _chunk(_with(lay, v_dtype=kvq.KVQ_STORE_FP32), n_tok=2, batch=0) == 0
+    assert _chunk(_with(lay, k_dtype=kvq.KVQ_STORE_FP32, v_dtype=kvq.KVQ_STORE_FP32), n_tok=1, batch=0) == 0
     assert _chunk(lay, k_scales=None) == NULL_
     assert _chunk(lay, q=None) == NULL_
     assert _chunk(lay, start=None) == NULL_
