@@ -18,8 +18,11 @@
 // covers SLICE dims of one (b, hq) row; lane (column c, split phase p) folds the
 // splits p, p + P, ... of its 4-dim column into a running (max, sum, output)
 // triple, issuing a batch of loads at once; the P phases of a column are P
-// consecutive lanes of one wavefront and combine by a shuffle butterfly (no
-// LDS, no barrier). Narrow slices give small batches many workgroups.
+// consecutive lanes of one wavefront: they take the column's maximum, rescale
+// their own triple to it and add up (sum, output) by butterflies of
+// register-only lane exchanges (DPP moves and permlane swaps: no LDS, no
+// barrier, no exponential per level). Narrow slices give small batches many
+// workgroups.
 #include <math.h>
 
 #include "kvq_device.h"
@@ -53,6 +56,40 @@ __device__ __forceinline__ Triple combine(const Triple& a, const Triple& b) {
   r.o = make_float4(wa * a.o.x + wb * b.o.x, wa * a.o.y + wb * b.o.y, wa * a.o.z + wb * b.o.z,
                     wa * a.o.w + wb * b.o.w);
   return r;
+}
+
+// Maximum and sum over the P consecutive lanes (16, 32 or 64) of a group:
+// every lane of the group gets the result (each level adds the same two
+// operands on both sides of the exchange, so the lanes agree bit for bit).
+template <int P>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (P >= 64) {
+    const float2 t = lane_pair<32>(x);
+    x = fmaxf(t.x, t.y);
+  }
+  if constexpr (P >= 32) {
+    const float2 t = lane_pair<16>(x);
+    x = fmaxf(t.x, t.y);
+  }
+  x = fmaxf(x, lane_xor<8>(x));
+  x = fmaxf(x, lane_xor<4>(x));
+  x = fmaxf(x, lane_xor<2>(x));
+  return fmaxf(x, lane_xor<1>(x));
+}
+template <int P>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (P >= 64) {
+    const float2 t = lane_pair<32>(x);
+    x = t.x + t.y;
+  }
+  if constexpr (P >= 32) {
+    const float2 t = lane_pair<16>(x);
+    x = t.x + t.y;
+  }
+  x = x + lane_xor<8>(x);
+  x = x + lane_xor<4>(x);
+  x = x + lane_xor<2>(x);
+  return x + lane_xor<1>(x);
 }
 
 template <int D, int SLICE>
@@ -107,17 +144,15 @@ __global__ __launch_bounds__(256) void kvq_reduce_kernel(ReduceArgs a) {
     }
   }
 
-  // Butterfly over the P lanes of the column: after log2(P) exchanges every
-  // lane holds the column's total (the same on both sides of each exchange).
-#pragma unroll
-  for (int off = P / 2; off; off >>= 1) {
-    Triple q;
-    q.m = __shfl_xor(run.m, off);
-    q.l = __shfl_xor(run.l, off);
-    q.o = make_float4(__shfl_xor(run.o.x, off), __shfl_xor(run.o.y, off), __shfl_xor(run.o.z, off),
-                      __shfl_xor(run.o.w, off));
-    run = (p & off) ? combine(q, run) : combine(run, q);
-  }
+  // The column's maximum over its P lanes, every lane's triple rescaled to it
+  // (an empty lane, m = -inf, contributes 0), then the sums.
+  const float M = group_max<P>(run.m);
+  const float w = run.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(run.m - M);
+  run.l = group_sum<P>(w * run.l);
+  run.o.x = group_sum<P>(w * run.o.x);
+  run.o.y = group_sum<P>(w * run.o.y);
+  run.o.z = group_sum<P>(w * run.o.z);
+  run.o.w = group_sum<P>(w * run.o.w);
   if (p == 0) {
     const float inv = run.l > 0.0f ? 1.0f / run.l : 0.0f;
     const f16 r0 = (f16)(run.o.x * inv), r1 = (f16)(run.o.y * inv), r2 = (f16)(run.o.z * inv),
