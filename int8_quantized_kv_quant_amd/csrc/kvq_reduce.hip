@@ -44,20 +44,6 @@ struct Triple {
   float4 o;
 };
 
-// (m, l, o) of two disjoint sets of positions -> that of their union.
-__device__ __forceinline__ Triple combine(const Triple& a, const Triple& b) {
-  const float M = fmaxf(a.m, b.m);
-  if (M == -INFINITY) return a;  // both empty
-  const float wa = a.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a.m - M);
-  const float wb = b.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(b.m - M);
-  Triple r;
-  r.m = M;
-  r.l = wa * a.l + wb * b.l;
-  r.o = make_float4(wa * a.o.x + wb * b.o.x, wa * a.o.y + wb * b.o.y, wa * a.o.z + wb * b.o.z,
-                    wa * a.o.w + wb * b.o.w);
-  return r;
-}
-
 // Maximum and sum over the P consecutive lanes (16, 32 or 64) of a group:
 // every lane of the group gets the result (each level adds the same two
 // operands on both sides of the exchange, so the lanes agree bit for bit).
@@ -165,7 +151,7 @@ __global__ __launch_bounds__(256) void kvq_reduce_kernel(ReduceArgs a) {
 
 // Few splits (n_splits <= P, P = 1, 2 or 4): a workgroup covers whole rows,
 // lane (row, 4-dim column, split phase p) loads split p of its column, and the
-// P phases (consecutive lanes) combine by the same butterfly. With one split
+// P phases (consecutive lanes) combine as in kvq_reduce_kernel. With one split
 // this is the normalization out = O / l, one float4 per lane.
 template <int D, int P>
 __global__ __launch_bounds__(256) void kvq_reduce_few_kernel(ReduceArgs a, int64_t rows) {
@@ -186,17 +172,21 @@ __global__ __launch_bounds__(256) void kvq_reduce_few_kernel(ReduceArgs a, int64
       run.o = *reinterpret_cast<const float4*>(a.ws_o + (bh * a.n_splits + p) * D + 4 * c);
     }
   }
+  if constexpr (P > 1) {  // the P phases: max, rescale, sums (as in kvq_reduce_kernel)
+    float M = fmaxf(run.m, lane_xor<1>(run.m));
+    if constexpr (P > 2) M = fmaxf(M, lane_xor<2>(M));
+    const float w = run.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(run.m - M);
+    float r[5] = {w * run.l, w * run.o.x, w * run.o.y, w * run.o.z, w * run.o.w};
 #pragma unroll
-  for (int off = P / 2; off; off >>= 1) {
-    Triple q;
-    q.m = __shfl_xor(run.m, off);
-    q.l = __shfl_xor(run.l, off);
-    q.o = make_float4(__shfl_xor(run.o.x, off), __shfl_xor(run.o.y, off), __shfl_xor(run.o.z, off),
-                      __shfl_xor(run.o.w, off));
-    run = (p & off) ? combine(q, run) : combine(run, q);
+    for (int k = 0; k < 5; ++k) {
+      r[k] = r[k] + lane_xor<1>(r[k]);
+      if constexpr (P > 2) r[k] = r[k] + lane_xor<2>(r[k]);
+    }
+    run.l = r[0];
+    run.o = make_float4(r[1], r[2], r[3], r[4]);
   }
   if (p == 0) {
-    // the value at max m is exp2(0) = 1: out = O / l with O, l taken at the same reference
+    // out = O / l with O and l taken at the same reference
     const float inv = run.l > 0.0f ? 1.0f / run.l : 0.0f;
     const f16 r0 = (f16)(run.o.x * inv), r1 = (f16)(run.o.y * inv), r2 = (f16)(run.o.z * inv),
               r3 = (f16)(run.o.w * inv);
