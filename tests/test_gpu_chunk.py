@@ -233,3 +233,38 @@ def test_full_size_prompt_chunk_sampled(name):
     got, want, plan = _run(w, [start], T, 0, tokens=toks)
     print(f"[chunk] full-size plan {plan.n_splits} x {plan.chunk}", flush=True)
     _check(got, want, tokens=toks, label="full-size")
+
+
+@pytest.mark.parametrize("n_tok", [4, 8])
+def test_rows_path_batched_serving_shape(n_tok):
+    """Verify windows for all 64 sequences of the batched-serving layout (32
+    query / 8 kv heads, head_dim 128, group-64 scales; 16 and 32 (token, head)
+    rows per kv head) at ragged starts, with the planner's split over the whole
+    batch: every token of a sample of sequences (the first, one ending at the
+    cache's end and two others; only these hold the workload's rows, the other
+    caches stay zero) against the oracle."""
+    import int8_quantized_kv_quant_amd as kvq
+    import kvq_setup as ks
+    w = wl.WORKLOADS["batched"].with_(max_ctx=2048)
+    rng = np.random.default_rng(55)
+    starts = rng.integers(0, 2048 - n_tok + 1, w.batch).astype(np.int64)
+    starts[0], starts[1] = 0, 2048 - n_tok
+    sample = [0, 1, 37, 63]
+    ends = starts + n_tok
+    lay, cache = ks.fill_cache(w, ends, seqs=sample)
+    q = wl.chunk_queries(w, n_tok)
+    sm = 1.0 / math.sqrt(w.head_dim)
+    plan = kvq.kvq_plan_chunk(lay, w.batch, n_tok, w.n_q_heads, int(ends.max()), 0, ks.n_cu())
+    got = kvq.chunk_attn(lay, cache, torch.from_numpy(q).cuda(), torch.from_numpy(starts.astype(np.int32)).cuda(),
+                         0, sm, plan=plan)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy().astype(np.float64)
+    print(f"[chunk] batched T={n_tok} plan {plan.n_splits} x {plan.chunk}", flush=True)
+    worst = 0.0
+    for b in sample:
+        oc = orc.Cache(1, w.max_ctx, w.n_kv_heads, w.head_dim, w.scale_group, w.k_dtype, w.v_dtype)
+        oc.append(wl.kv_rows(w, "k", b, 0, int(ends[b]))[None], wl.kv_rows(w, "v", b, 0, int(ends[b]))[None], [0])
+        want = orc.attend_chunk(q[b:b + 1], oc, starts[b:b + 1], 0, sm)
+        worst = max(worst, float(np.abs(got[b] - want[0]).max()))
+    print(f"[chunk] batched T={n_tok} max abs err {worst:.3g}", flush=True)
+    assert worst <= TOL
