@@ -157,11 +157,13 @@ __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a
   f16x8 qv[RB][S::NJ][2];
   float corr[RB][S::NG];
   int vlo[RB], vhi[RB];  // keys [vlo, vhi) of the lane's row in block rb
+  bool has_row[RB];      // the lane's row in block rb is a token of the chunk
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int fr = flat_row(rb);
     const int t = fr / G;
     const bool valid = t < a.T;
+    has_row[rb] = valid;
     const int P = s0 + t;
     vhi[rb] = (valid && P < a.max_ctx) ? P + 1 : 0;
     vlo[rb] = a.window > 0 ? max(0, P + 1 - a.window) : 0;
@@ -196,6 +198,28 @@ __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a
       corr[rb][g] = -kCodeBias * t2;
     }
   }
+
+  // The keys every row of this wavefront keeps, [lo_all_w, hi_all_w)
+  // (wavefront-uniform): a tile inside it needs no mask. Rows past the chunk
+  // are written nowhere and do not count; a token at or past max_ctx (no key
+  // at all) does, so its wavefront always masks.
+  int row_lo = 0, row_hi = 0x7fffffff;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    if (has_row[rb]) {
+      row_lo = max(row_lo, vlo[rb]);
+      row_hi = min(row_hi, vhi[rb]);
+    }
+  row_lo = max(row_lo, lane_xor<8>(row_lo));
+  row_lo = max(row_lo, lane_xor<4>(row_lo));
+  row_lo = max(row_lo, lane_xor<2>(row_lo));
+  row_lo = max(row_lo, lane_xor<1>(row_lo));
+  row_hi = min(row_hi, lane_xor<8>(row_hi));
+  row_hi = min(row_hi, lane_xor<4>(row_hi));
+  row_hi = min(row_hi, lane_xor<2>(row_hi));
+  row_hi = min(row_hi, lane_xor<1>(row_hi));
+  const int lo_all_w = __builtin_amdgcn_readfirstlane(row_lo);  // the 16 rows of lanes 0-15 (q4 lanes repeat them)
+  const int hi_all_w = __builtin_amdgcn_readfirstlane(row_hi);
 
   // ---- key tiles: buffer resources of this (sequence, kv head) slice ----------
   const uint32_t row = (uint32_t)a.s_pos;
@@ -287,10 +311,11 @@ __global__ __launch_bounds__(kChunkWaves * 64) void kvq_chunk_kernel(ChunkArgs a
     KRegs<S> tk;
     stage_read_k<S>(tk, st, c16, q4);
     f16x8 pa[RB];
+    const bool masked = !(p0 >= lo_all_w && p0 + kTile <= min(hi_all_w, end));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float z[2][4];
-      tile_scores_q<S>(tk, max(vlo[rb], p0) - p0, min(vhi[rb], end) - p0, z, qv[rb], corr[rb], a.c2, q4);
+      tile_scores_q<S>(tk, max(vlo[rb], p0) - p0, min(vhi[rb], end) - p0, z, qv[rb], corr[rb], a.c2, q4, masked);
       pa[rb] = row_softmax<D>(z, acc[rb]);
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // the value tile is complete

@@ -87,11 +87,12 @@ __device__ __forceinline__ f16x8 q_get(const uint8_t* __restrict__ qp, int j, in
 // positions x 16 query rows of S^T = K.Q^T; lane (c16, q4) gets positions
 // 16*ct + 4*q4 + i of query row c16. Positions x of the tile with
 // vlo <= x < vhi keep their score, the others get -inf (vlo, vhi may differ
-// per lane: per query row).
+// per lane: per query row). masked = false (wavefront-uniform) skips the
+// mask when every position of the tile is inside every row's range.
 template <class S>
 __device__ __forceinline__ void tile_scores_q(const KRegs<S>& t, int vlo, int vhi, float (&z)[2][4],
                                               const f16x8 (&qv)[S::NJ][2], const float (&corr)[S::NG],
-                                              float c2, int q4) {
+                                              float c2, int q4, bool masked = true) {
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     f32x4 zz = {0.f, 0.f, 0.f, 0.f};
@@ -123,10 +124,15 @@ __device__ __forceinline__ void tile_scores_q(const KRegs<S>& t, int vlo, int vh
       }
       zz = a;
     }
+    if (masked) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int x = 16 * ct + 4 * q4 + i;
-      z[ct][i] = (x >= vlo && x < vhi) ? zz[i] * c2 : -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        const int x = 16 * ct + 4 * q4 + i;
+        z[ct][i] = (x >= vlo && x < vhi) ? zz[i] * c2 : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[ct][i] = zz[i] * c2;
     }
   }
 }
