@@ -247,11 +247,12 @@ __device__ __forceinline__ void read_k_i8(KRegs<Shape<256, true, true, KG64>>& t
 
 // Scores of an int8 K tile (k8v4): as the int8 kernel's, with the bias
 // correction added after each MFMA instead of preloaded into its accumulator
-// (one register per group instead of four).
+// (one register per group instead of four). masked = false (wavefront-
+// uniform): every position of the tile inside [vlo, vhi), no mask.
 template <bool KG64>
 __device__ __forceinline__ void scores_i8(const KRegs<Shape<256, true, true, KG64>>& t, int vlo, int vhi,
                                           float (&z)[2][4], const f16x8 (&qv)[4][2], const float (&corr)[KG64 ? 4 : 1],
-                                          float c2, int q4) {
+                                          float c2, int q4, bool masked = true) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
@@ -276,10 +277,15 @@ __device__ __forceinline__ void scores_i8(const KRegs<Shape<256, true, true, KG6
 #pragma unroll
       for (int i = 0; i < 4; ++i) zz[i] = (a[i] + corr[0]) * scale_of(t.ks[ct][i], 0);
     }
+    if (masked) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int x = 16 * ct + 4 * q4 + i;
-      z[ct][i] = (x >= vlo && x < vhi) ? zz[i] * c2 : -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        const int x = 16 * ct + 4 * q4 + i;
+        z[ct][i] = (x >= vlo && x < vhi) ? zz[i] * c2 : -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[ct][i] = zz[i] * c2;
     }
   }
 }
