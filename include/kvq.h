@@ -139,7 +139,8 @@ typedef struct {
  * context length is covered whatever the planned one. kv_chunk_attn splits
  * the keys of a kv head's query rows the same way (from the lo of its first
  * token to the position of its last) when it runs a chunk of at most 32
- * (token, head) rows per kv head, otherwise contiguously: [lo + s*chunk,
+ * (token, head) rows per kv head (16 with an fp32 store), otherwise
+ * contiguously: [lo + s*chunk,
  * lo + (s+1)*chunk), the last split running to the chunk's end. Either way
  * every key is covered whatever the plan. ws_bytes is the workspace that
  * kv_decode_attn_splitk (or kv_chunk_attn) writes and kv_decode_reduce reads. */
@@ -289,8 +290,9 @@ int kv_decode_attn_static(const kvq_layout* layout,
  * position max_seq_len (the largest start + n_tok). Chunks with many query
  * rows run one split per (sequence, kv head, 64-row block); a few tokens over
  * a long prefix (a verify window) get their keys split so that the grid covers
- * the chip. Chunks with at most 32 (token, head) rows per kv head run
- * through the decode partial kernels and get kvq_plan's split rule.
+ * the chip. Chunks with at most 32 (token, head) rows per kv head (16 with
+ * an fp32 store) run through the decode partial kernels and get kvq_plan's
+ * split rule.
  * ws_bytes = batch * n_tok * n_q_heads * n_splits * (head_dim + 2) * 4.
  * Writes *out; returns KVQ_OK or an error for invalid layout/sizes. */
 int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32_t n_q_heads,
@@ -320,7 +322,8 @@ int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32
  * other combinations and longer chunks over fp32 stores are refused
  * (KVQ_ERR_UNSUPPORTED). Two kernels are enqueued on `stream`: the partials
  * and the combine of kv_decode_reduce. The partials of a chunk with at most
- * 32 (token, head) rows per kv head come from the decode partial kernels,
+ * 32 (token, head) rows per kv head (16 with an fp32 store) come from the
+ * decode partial kernels,
  * whose query rows are then (token, head) pairs with their own causal limits
  * (a verify window reads every key once, or once per 16 rows over a 4-bit
  * layout); larger chunks from the chunk kernels.
