@@ -81,8 +81,8 @@ __global__ __launch_bounds__(256) void kvq_append_kernel(AppendArgs a) {
     return;
   }
 
-  uint16_t scale_bits;
-  const uint32_t packed = quantize4(hb, a.group_lanes, &scale_bits);
+  uint16_t scale_bits;  // a scale group is 16 lanes (64 values) or the whole row
+  const uint32_t packed = a.group_lanes == 16 ? quantize4<16>(hb, &scale_bits) : quantize4<TPR>(hb, &scale_bits);
   *reinterpret_cast<uint32_t*>(static_cast<int8_t*>(S.store) + row_off + 4 * lr) = packed;
   if (lr % a.group_lanes == 0) {
     const int64_t soff = b * a.ss_seq + pos * a.ss_pos + h * a.ss_head + lr / a.group_lanes;
@@ -95,44 +95,8 @@ __global__ __launch_bounds__(256) void kvq_append_kernel(AppendArgs a) {
 // lanes per row (32, 16, 8): one 16-byte load per lane, RW = 64 / LPR rows per
 // wavefront. A workgroup (4 wavefronts) covers 4 RW consecutive tokens of one
 // kv head and one sequence, so the token and head of a row come from the grid
-// (no division per lane).
-
-// Maximum of x over aligned groups of GL lanes (GL = 8, 16, 32 or 64), every
-// lane of a group receiving it: DPP quad permutes (lanes ^ 1, ^ 2), the
-// half-row and row mirrors (lanes 7 - i within 8, 15 - i within 16), then
-// v_permlane16_swap / v_permlane32_swap for lanes ^ 16 and ^ 32.
-template <int GL>
-__device__ __forceinline__ uint32_t group_max(uint32_t x) {
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  if constexpr (GL >= 16) x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));
-  if constexpr (GL >= 32) {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    x = max((uint32_t)r[0], (uint32_t)r[1]);
-  }
-  if constexpr (GL >= 64) {
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    x = max((uint32_t)r[0], (uint32_t)r[1]);
-  }
-  return x;
-}
-
-// Code of x (fp16 value, widened) for the fp16 scale s > 0 with rs = rcp(s)
-// (within 1 ulp): clamp(round-half-even(x / s), -127, 127), exactly as a
-// correctly rounded division followed by rint. For fp16 x and s the exact
-// quotient q is either a half-integer or at least 2^-13 away from every
-// half-integer, while t = x * rs is within 3e-7 |q| (< 6e-5 for |q| <= 190,
-// the largest quotient a subnormal scale allows) of q: so rint(t) is the
-// correctly rounded code except at exact ties, where it may land on the odd
-// neighbour. The residual r = x - c s (exact: c s has at most 19 significant
-// bits and |r| <= 1.5 s) is then +-s/2, and the tie goes to the even code.
-__device__ __forceinline__ int code_of(float x, float s, float rs) {
-  float c = __builtin_rintf(x * rs);
-  const float r = fmaf(-c, s, x);
-  if (fabsf(r) == 0.5f * s && ((int)c & 1)) c += r > 0.0f ? 1.0f : -1.0f;
-  return (int)fminf(fmaxf(c, -127.0f), 127.0f);
-}
+// (no division per lane). The group absmax and the codes: group_max and code_of
+// (kvq_device.h).
 
 struct Append8Args {
   AppendStore st[2];  // [0] = K, [1] = V

@@ -80,7 +80,6 @@ struct PartialArgs {
   // above, which the fused entry point receives writable).
   const uint16_t* k_new;
   const uint16_t* v_new;
-  int32_t group_lanes;  // lanes of one scale group for the quantizer (4 values each)
   const uint16_t* q;
   const int32_t* seq_lens;
   float* ws_o;   // [B][Hq][n_splits][D]
@@ -188,6 +187,10 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   // One store int8, the other fp32: the fp32 tile is staged in LDS, the int8
   // operands go straight to registers.
   constexpr bool kMix = KI8 != VI8;
+  // Lanes of one scale group in the fused append's quantizer (4 values each):
+  // 64 values, or the whole row.
+  constexpr int kQGL = G64 ? 16 : D / 4;
+  static_assert(D % (16 * NW) == 0, "the new position's score: 4-dim steps per lane");
   using FS = F32Stage<S, !KI8>;
   constexpr int STAGE_BYTES = kStaged ? Stage<S>::BYTES : (kMix ? FS::BYTES : 16);
   // One stage per wavefront. After its last tile a wavefront reuses its own
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) float nw_val[2][D];
   __shared__ __attribute__((aligned(16))) uint32_t nw_code[2][D / 4];
   __shared__ uint16_t nw_scale[2][S::NG];
-  __shared__ float nw_z[16];
+  __shared__ float nw_z[NW][16];
 
   const int split = blockIdx.x;
   const int hk = blockIdx.y / a.head_blocks;
@@ -357,13 +360,13 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     float4 val;
     if (i8) {
       uint16_t sb;
-      const uint32_t code = quantize4(hb, a.group_lanes, &sb);  // as kv_quant_append
+      const uint32_t code = quantize4<kQGL>(hb, &sb);  // as kv_quant_append
       const float sc = h_bits_to_f32(sb);
       val = make_float4((float)(int8_t)(code & 0xff) * sc, (float)(int8_t)((code >> 8) & 0xff) * sc,
                         (float)(int8_t)((code >> 16) & 0xff) * sc, (float)(int8_t)(code >> 24) * sc);
       if (lane < D / 4) {
         nw_code[wv][lane] = code;
-        if (lane % a.group_lanes == 0) nw_scale[wv][lane / a.group_lanes] = sb;
+        if (lane % kQGL == 0) nw_scale[wv][lane / kQGL] = sb;
       }
     } else {  // an fp32 store holds the fp16 value widened
       val = make_float4(h_bits_to_f32(hb[0]), h_bits_to_f32(hb[1]), h_bits_to_f32(hb[2]), h_bits_to_f32(hb[3]));
@@ -371,6 +374,28 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     if (lane < D / 4) *reinterpret_cast<float4*>(&nw_val[wv][4 * lane]) = val;
   }
   __syncthreads();  // query rows (and the new rows) in LDS
+  // ---- fused append: the new row into the cache (one head block writes it).
+  // Issued right after the quantization, so that its store latency overlaps
+  // the tiles (no workgroup of this launch reads position L - 1 from the
+  // cache: its owner takes it from LDS, and the other splits' blocks end
+  // before it). The explicit load counts below then over-count by these
+  // stores at most, which only makes a wait stricter.
+  if (own_new && hblk == 0 && wv < 2 && lane < D / 4) {
+    const int64_t r = (int64_t)b * a.s_seq + (int64_t)(L - 1) * a.s_pos + (int64_t)hk * a.s_head;
+    const bool i8 = wv == 0 ? KI8 : VI8;
+    void* store = const_cast<void*>(wv == 0 ? a.k_store : a.v_store);
+    if (i8) {
+      reinterpret_cast<uint32_t*>(static_cast<int8_t*>(store) + r)[lane] = nw_code[wv][lane];
+      if (lane % kQGL == 0) {
+        uint16_t* sc = const_cast<uint16_t*>(wv == 0 ? a.k_scales : a.v_scales);
+        sc[(int64_t)b * a.ss_seq + (int64_t)(L - 1) * a.ss_pos + (int64_t)hk * a.ss_head + lane / kQGL] =
+            nw_scale[wv][lane / kQGL];
+      }
+    } else {
+      reinterpret_cast<float4*>(static_cast<float*>(store) + r)[lane] =
+          *reinterpret_cast<const float4*>(&nw_val[wv][4 * lane]);
+    }
+  }
   // The lane's query row c16 of row block rb: qb + rb * QB.
   const uint8_t* const qb = lds_q + c16 * QOperand<S>::ROW + 32 * q4;
   constexpr int QB = 16 * QOperand<S>::ROW;
@@ -403,27 +428,36 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       corr[rb][g] = KI8 ? -kCodeBias * t : 0.0f;
     }
   }
-  if (own_new && wv == 0) {
-    // Scores of the new position for the 16 heads (rows beyond nh are zero):
-    // lane 4h + r sums a quarter of the dims of head h; lds_q row h holds
-    // q[h][0..D) as consecutive fp16 values.
+  if (own_new) {
+    // Partial scores of the new position for the 16 heads (rows beyond nh are
+    // zero), a 1/NW share of the dims per wavefront: lane 4h + r sums dims
+    // d0 .. d0 + D / (4 NW) of head h; lds_q row h holds q[h][0..D) as
+    // consecutive fp16 values. The merge adds the wavefronts' sums.
+    constexpr int DL = D / (4 * NW);
     const int h = lane >> 2, r = lane & 3;
+    const int d0 = wv * (D / NW) + r * DL;
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(lds_q + h * QOperand<S>::ROW);
     float zs = 0.0f;
-#pragma unroll 4
-    for (int d = r * (D / 4); d < (r + 1) * (D / 4); d += 8) {
-      const f16x8 qv = *reinterpret_cast<const f16x8*>(qrow + d);
-      const float4 k0 = *reinterpret_cast<const float4*>(&nw_val[0][d]);
-      const float4 k1 = *reinterpret_cast<const float4*>(&nw_val[0][d + 4]);
-      zs = fmaf((float)qv[0], k0.x, zs); zs = fmaf((float)qv[1], k0.y, zs);
-      zs = fmaf((float)qv[2], k0.z, zs); zs = fmaf((float)qv[3], k0.w, zs);
-      zs = fmaf((float)qv[4], k1.x, zs); zs = fmaf((float)qv[5], k1.y, zs);
-      zs = fmaf((float)qv[6], k1.z, zs); zs = fmaf((float)qv[7], k1.w, zs);
+#pragma unroll
+    for (int d = d0; d < d0 + DL; d += 4) {
+      const u32x2 qv = *reinterpret_cast<const u32x2*>(qrow + d);
+      const float4 k = *reinterpret_cast<const float4*>(&nw_val[0][d]);
+      zs = fmaf(h_bits_to_f32(qv.x & 0xffffu), k.x, zs);
+      zs = fmaf(h_bits_to_f32(qv.x >> 16), k.y, zs);
+      zs = fmaf(h_bits_to_f32(qv.y & 0xffffu), k.z, zs);
+      zs = fmaf(h_bits_to_f32(qv.y >> 16), k.w, zs);
     }
-    zs += __shfl_xor(zs, 1);
-    zs += __shfl_xor(zs, 2);
-    if (r == 0) nw_z[h] = zs * a.c2;  // read in the epilogue, after its barrier
+    zs += lane_xor<1>(zs);
+    zs += lane_xor<2>(zs);
+    if (r == 0) nw_z[wv][h] = zs;  // read in the merge, after its barrier
   }
+  // The new position's score for head h (log2 units).
+  auto z_new = [&](int h) {
+    float z = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) z += nw_z[k][h];
+    return z * a.c2;
+  };
 
   WaveAcc<S> acc[RB];
 #pragma unroll
@@ -567,7 +601,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     for (int idx = threadIdx.x; idx < nr * (D / 4); idx += NW * 64) {
       const int h = idx / (D / 4);
       const int d = 4 * (idx % (D / 4));
-      const float zn = own_new ? nw_z[h] : -INFINITY;  // the fused new position
+      const float zn = own_new ? z_new(h) : -INFINITY;  // the fused new position
       float M = zn;
 #pragma unroll
       for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
@@ -592,7 +626,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     }
     if (threadIdx.x < nr) {
       const int h = threadIdx.x;
-      const float zn = own_new ? nw_z[h] : -INFINITY;
+      const float zn = own_new ? z_new(h) : -INFINITY;
       float M = zn;
 #pragma unroll
       for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
@@ -612,23 +646,6 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     if (nh > 16) {
       __syncthreads();  // the first block's slots and maxima have been read
       merge(1, nh - 16);
-    }
-  }
-  // ---- fused append: the new row into the cache (one head block writes it) --
-  if (own_new && hblk == 0 && wv < 2 && lane < D / 4) {
-    const int64_t r = (int64_t)b * a.s_seq + (int64_t)(L - 1) * a.s_pos + (int64_t)hk * a.s_head;
-    const bool i8 = wv == 0 ? KI8 : VI8;
-    void* store = const_cast<void*>(wv == 0 ? a.k_store : a.v_store);
-    if (i8) {
-      reinterpret_cast<uint32_t*>(static_cast<int8_t*>(store) + r)[lane] = nw_code[wv][lane];
-      if (lane % a.group_lanes == 0) {
-        uint16_t* sc = const_cast<uint16_t*>(wv == 0 ? a.k_scales : a.v_scales);
-        sc[(int64_t)b * a.ss_seq + (int64_t)(L - 1) * a.ss_pos + (int64_t)hk * a.ss_head + lane / a.group_lanes] =
-            nw_scale[wv][lane / a.group_lanes];
-      }
-    } else {
-      reinterpret_cast<float4*>(static_cast<float*>(store) + r)[lane] =
-          *reinterpret_cast<const float4*>(&nw_val[wv][4 * lane]);
     }
   }
 }
@@ -674,7 +691,6 @@ int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store
   a.v_scales = v_scales;
   a.k_new = k_new;
   a.v_new = v_new;
-  a.group_lanes = L.scale_group == 64 ? 16 : L.head_dim / 4;
   a.q = q;
   a.seq_lens = d_seq_lens;
   const int64_t rows = (int64_t)batch * n_q_heads * plan.n_splits;
@@ -740,7 +756,6 @@ int launch_chunk_rows(const kvq_layout& L, const void* k_store, const void* v_st
   a.v_store = v_store;
   a.k_scales = k_scales;
   a.v_scales = v_scales;
-  a.group_lanes = L.scale_group == 64 ? 16 : L.head_dim / 4;
   a.q = q;
   a.start_pos = d_start_pos;
   a.T = n_tok;

@@ -62,7 +62,6 @@ struct Q4Args {
   // above (the fused entry point receives them writable).
   const uint16_t* k_new;
   const uint16_t* v_new;
-  int32_t group_lanes;  // lanes of one int8 scale group (4 values each), k8v4 keys
   const uint16_t* q;
   const int32_t* seq_lens;
   float* ws_o;   // [B][Hq][n_splits][D]
@@ -157,6 +156,8 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   using T = Q4Stage<KQ4, KG64>;
   using SA = Shape<256, true, true, true>;  // accumulators (16 heads x 256 dims per wavefront)
   using SK = Shape<256, true, true, KG64>;  // int8 keys (k8v4)
+  constexpr int kQGL = KG64 ? 16 : D / 4;   // lanes of one int8 key scale group in the fused quantizer
+  static_assert(D % (32 * NW) == 0, "the new position's score: 8-dim steps per lane");
   constexpr int SLOT_BYTES = 16 * D * 4;    // merge slot: 16 head rows of D floats
   constexpr int PITCH = T::BYTES > SLOT_BYTES ? T::BYTES : SLOT_BYTES;
   constexpr int QROW = QOperand<SA>::ROW;
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   __shared__ __attribute__((aligned(16))) float nw_val[2][D];
   __shared__ __attribute__((aligned(16))) uint32_t nw_code[2][D / 4];
   __shared__ uint16_t nw_scale[2][D / kQ4Block];
-  __shared__ float nw_z[16];
+  __shared__ float nw_z[NW][16];
 
   const int split = blockIdx.x;
   const int hk = blockIdx.y / a.head_blocks;
@@ -305,12 +306,12 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
       if ((lane & 7) == 0) nw_scale[wv][lane >> 3] = sb;
     } else {  // int8 keys (k8v4)
       uint16_t sb;
-      const uint32_t code = quantize4(hb, a.group_lanes, &sb);
+      const uint32_t code = quantize4<kQGL>(hb, &sb);
       const float sc = h_bits_to_f32(sb);
       val = make_float4((float)(int8_t)(code & 0xff) * sc, (float)(int8_t)((code >> 8) & 0xff) * sc,
                         (float)(int8_t)((code >> 16) & 0xff) * sc, (float)(int8_t)(code >> 24) * sc);
       nw_code[wv][lane] = code;
-      if (lane % a.group_lanes == 0) nw_scale[wv][lane / a.group_lanes] = sb;
+      if (lane % kQGL == 0) nw_scale[wv][lane / kQGL] = sb;
     }
     *reinterpret_cast<float4*>(&nw_val[wv][4 * lane]) = val;
   }
@@ -350,31 +351,52 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     }
   }
   __syncthreads();  // every query row in LDS (rotated for a q4 K store), the new rows quantized
+  // ---- fused append: the new row into the cache (one head block writes it),
+  // issued right after the quantization so that its store latency overlaps
+  // the tiles (no workgroup of this launch reads position L - 1 from the
+  // cache; the explicit load counts below then over-count by these stores at
+  // most, which only makes a wait stricter)
+  if (own_new && hblk == 0 && wv < 2) {
+    const int64_t r = (int64_t)b * a.s_seq + (int64_t)(L - 1) * a.s_pos + (int64_t)hk * a.s_head;  // elements
+    const int64_t sr = (int64_t)b * a.ss_seq + (int64_t)(L - 1) * a.ss_pos + (int64_t)hk * a.ss_head;
+    uint16_t* sc = const_cast<uint16_t*>(wv == 0 ? a.k_scales : a.v_scales);
+    if (wv == 1 || KQ4) {  // 128 bytes and 8 scales
+      uint8_t* store = static_cast<uint8_t*>(const_cast<void*>(wv == 0 ? a.k_store : a.v_store));
+      if (lane < D / 8) reinterpret_cast<uint32_t*>(store + r / 2)[lane] = nw_code[wv][lane];
+      if (lane < D / kQ4Block) sc[sr + lane] = nw_scale[wv][lane];
+    } else {
+      int8_t* store = static_cast<int8_t*>(const_cast<void*>(a.k_store));
+      reinterpret_cast<uint32_t*>(store + r)[lane] = nw_code[0][lane];
+      if (lane % kQGL == 0) sc[sr + lane / kQGL] = nw_scale[0][lane / kQGL];
+    }
+  }
   const uint8_t* const qrow = lds_q + c16 * QROW;
-  if (own_new && wv == 0) {
-    // Scores of the new position for the 16 heads (rows beyond nh are zero):
-    // lane 4h + r sums a quarter of the dims of head h.
-    // For q4 keys the query is the rotated row, hi + lo (dims 16..31 of each
-    // block stored divided by 16).
+  if (own_new) {
+    // Partial scores of the new position for the 16 heads (rows beyond nh are
+    // zero), a quarter of the dims per wavefront: lane 4h + r sums dims
+    // 64 wv + 16 r .. + 16 of head h. For q4 keys the query is the rotated row,
+    // hi + lo (dims 16..31 of each block stored divided by 16). The merge adds
+    // the wavefronts' sums.
     const int h = lane >> 2, r = lane & 3;
+    const int d0 = wv * (D / NW) + r * (D / (4 * NW));
     const uint16_t* qr = reinterpret_cast<const uint16_t*>(lds_q + h * QROW);
     const uint16_t* qrl = reinterpret_cast<const uint16_t*>(lds_ql + (KQ4 ? h * QROW : 0));
+    const float f = (KQ4 && (d0 & 31) >= 16) ? 16.0f : 1.0f;  // the lane's 16 dims share a half block
     float zs = 0.0f;
-#pragma unroll 4
-    for (int d = r * (D / 4); d < (r + 1) * (D / 4); d += 8) {
+#pragma unroll
+    for (int d = d0; d < d0 + D / (4 * NW); d += 8) {
       const f16x8 qv = *reinterpret_cast<const f16x8*>(qr + d);
       f16x8 ql = {};
       if constexpr (KQ4) ql = *reinterpret_cast<const f16x8*>(qrl + d);
       const float4 k0 = *reinterpret_cast<const float4*>(&nw_val[0][d]);
       const float4 k1 = *reinterpret_cast<const float4*>(&nw_val[0][d + 4]);
       const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-      const float f = (KQ4 && (d & 31) >= 16) ? 16.0f : 1.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) zs = fmaf(((float)qv[e] + (float)ql[e]) * f, kk[e], zs);
     }
-    zs += __shfl_xor(zs, 1);
-    zs += __shfl_xor(zs, 2);
-    if (r == 0) nw_z[h] = zs * a.c2;  // read in the epilogue, after its barrier
+    zs += lane_xor<1>(zs);
+    zs += lane_xor<2>(zs);
+    if (r == 0) nw_z[wv][h] = zs;  // read in the merge, after its barrier
   }
 
   const float c2s = a.c2 * 16777216.0f;
@@ -509,7 +531,7 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
   __syncthreads();
   for (int h = wv; h < nh; h += NW) {  // uniform per wavefront: the rotation's shuffles see every lane
     const int f = slot_swz(lane);
-    const float zn = own_new ? nw_z[h] : -INFINITY;  // the fused new position
+    const float zn = own_new ? (nw_z[0][h] + nw_z[1][h] + nw_z[2][h] + nw_z[3][h]) * a.c2 : -INFINITY;  // the fused new position
     float M = zn;
 #pragma unroll
     for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
@@ -539,21 +561,6 @@ __global__ __launch_bounds__(256) void kvq_partial_q4_kernel(Q4Args a) {
     reinterpret_cast<float4*>(a.ws_o + rowid(h) * D)[lane] = make_float4(v[0], v[1], v[2], v[3]);
     if (lane == 0) ml[rowid(h)] = make_float2(M, l);
   }
-  // ---- fused append: the new row into the cache (one head block writes it)
-  if (own_new && hblk == 0 && wv < 2) {
-    const int64_t r = (int64_t)b * a.s_seq + (int64_t)(L - 1) * a.s_pos + (int64_t)hk * a.s_head;  // elements
-    const int64_t sr = (int64_t)b * a.ss_seq + (int64_t)(L - 1) * a.ss_pos + (int64_t)hk * a.ss_head;
-    uint16_t* sc = const_cast<uint16_t*>(wv == 0 ? a.k_scales : a.v_scales);
-    if (wv == 1 || KQ4) {  // 128 bytes and 8 scales
-      uint8_t* store = static_cast<uint8_t*>(const_cast<void*>(wv == 0 ? a.k_store : a.v_store));
-      if (lane < D / 8) reinterpret_cast<uint32_t*>(store + r / 2)[lane] = nw_code[wv][lane];
-      if (lane < D / kQ4Block) sc[sr + lane] = nw_scale[wv][lane];
-    } else {
-      int8_t* store = static_cast<int8_t*>(const_cast<void*>(a.k_store));
-      reinterpret_cast<uint32_t*>(store + r)[lane] = nw_code[0][lane];
-      if (lane % a.group_lanes == 0) sc[sr + lane / a.group_lanes] = nw_scale[0][lane / a.group_lanes];
-    }
-  }
 }
 
 int launch_partial_q4(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
@@ -568,7 +575,6 @@ int launch_partial_q4(const kvq_layout& L, const void* k_store, const void* v_st
   a.v_scales = v_scales;
   a.k_new = k_new;
   a.v_new = v_new;
-  a.group_lanes = L.scale_group == 64 ? 16 : L.head_dim / 4;
   a.q = q;
   a.seq_lens = d_seq_lens;
   const int64_t rows = (int64_t)batch * n_q_heads * plan.n_splits;
@@ -610,7 +616,6 @@ int launch_chunk_rows_q4(const kvq_layout& L, const void* k_store, const void* v
   a.v_store = v_store;
   a.k_scales = k_scales;
   a.v_scales = v_scales;
-  a.group_lanes = L.scale_group == 64 ? 16 : L.head_dim / 4;
   a.q = q;
   a.start_pos = d_start_pos;
   a.T = n_tok;

@@ -135,34 +135,70 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Quantizer of one group of values spread over `group_lanes` consecutive lanes
-// (a power of two, groups aligned to it), 4 fp16 values (bit patterns hb) per
-// lane. Strata PR 2698, "What it does": the FP16 scale of a group is its absmax
-// / 127; each value becomes the int8 code of x / scale.
+// Maximum of x over aligned groups of GL consecutive lanes (GL = 8, 16, 32 or
+// 64), every lane of a group receiving it: DPP quad permutes (lanes ^ 1, ^ 2),
+// the half-row and row mirrors (lanes 7 - i within 8, 15 - i within 16), then
+// v_permlane16_swap / v_permlane32_swap for lanes ^ 16 and ^ 32.
+template <int GL>
+__device__ __forceinline__ uint32_t group_max(uint32_t x) {
+  static_assert(GL == 8 || GL == 16 || GL == 32 || GL == 64, "scale group lanes");
+  x = max(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = max(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = max(x, dpp_u32<0x141>(x));  // row_half_mirror
+  if constexpr (GL >= 16) x = max(x, dpp_u32<0x140>(x));  // row_mirror
+  if constexpr (GL >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max((uint32_t)r[0], (uint32_t)r[1]);
+  }
+  if constexpr (GL >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    x = max((uint32_t)r[0], (uint32_t)r[1]);
+  }
+  return x;
+}
+
+// Code of x (fp16 value, widened) for the fp16 scale s > 0 with rs = rcp(s)
+// (within 1 ulp): clamp(round-half-even(x / s), -127, 127), exactly as a
+// correctly rounded division followed by rint. For fp16 x and s the exact
+// quotient q is either a half-integer or at least 2^-13 away from every
+// half-integer, while t = x * rs is within 3e-7 |q| (< 6e-5 for |q| <= 190,
+// the largest quotient a subnormal scale allows) of q: so rint(t) is the
+// correctly rounded code except at exact ties, where it may land on the odd
+// neighbour. The residual r = x - c s (exact: c s has at most 19 significant
+// bits and |r| <= 1.5 s) is then +-s/2, and the tie goes to the even code.
+__device__ __forceinline__ int code_of(float x, float s, float rs) {
+  float c = __builtin_rintf(x * rs);
+  const float r = fmaf(-c, s, x);
+  if (fabsf(r) == 0.5f * s && ((int)c & 1)) c += r > 0.0f ? 1.0f : -1.0f;
+  return (int)fminf(fmaxf(c, -127.0f), 127.0f);
+}
+
+// Quantizer of one group of values spread over GL consecutive lanes (groups
+// aligned to GL), 4 fp16 values (bit patterns hb) per lane. Strata PR 2698,
+// "What it does": the FP16 scale of a group is its absmax / 127; each value
+// becomes the int8 code of x / scale.
 //   absmax: exact, on the fp16 bit patterns (for finite values the ordering
 //           of |x| is the integer ordering of the bits with the sign cleared);
 //   scale = fp16_rne(absmax / 127.0f), the division correctly rounded in fp32;
-//   code  = clamp(rint(x / scale), -127, 127), a correctly rounded fp32
-//           division (x and scale are fp16, so the quotient rounds to the same
-//           integer as the exact one, ties to even); 0 where scale == 0.
-// Returns the 4 codes packed little-endian; *scale_bits gets the fp16 scale.
-__device__ __forceinline__ uint32_t quantize4(const uint32_t (&hb)[4], int group_lanes, uint16_t* scale_bits) {
+//   code  = clamp(rint(x / scale), -127, 127) as a correctly rounded fp32
+//           division would give it (x and scale are fp16, so that quotient
+//           rounds to the same integer as the exact one, ties to even),
+//           computed by code_of; 0 where scale == 0.
+// Every lane of a group must be active. Returns the 4 codes packed
+// little-endian; *scale_bits gets the fp16 scale.
+template <int GL>
+__device__ __forceinline__ uint32_t quantize4(const uint32_t (&hb)[4], uint16_t* scale_bits) {
   uint32_t amax = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) amax = max(amax, hb[e] & 0x7fffu);
-  for (int o = 1; o < group_lanes; o <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o));
-  const float absmax = h_bits_to_f32(amax);
-  const f16 scale_h = (f16)(absmax / 127.0f);  // fp32 IEEE division, then fp16 RNE
-  const float scale = (float)scale_h;
+  amax = group_max<GL>(amax);
+  const f16 scale_h = (f16)(h_bits_to_f32(amax) / 127.0f);  // fp32 IEEE division, then fp16 RNE
+  const float s = (float)scale_h;
+  const float rs = __builtin_amdgcn_rcpf(s);
   uint32_t packed = 0;
+  if (s > 0.0f) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float c = 0.0f;
-    if (scale > 0.0f) {
-      c = __builtin_rintf(h_bits_to_f32(hb[e]) / scale);
-      c = fminf(fmaxf(c, -127.0f), 127.0f);
-    }
-    packed |= ((uint32_t)(int32_t)c & 0xffu) << (8 * e);
+    for (int e = 0; e < 4; ++e) packed |= ((uint32_t)code_of(h_bits_to_f32(hb[e]), s, rs) & 0xffu) << (8 * e);
   }
   *scale_bits = __builtin_bit_cast(uint16_t, scale_h);
   return packed;
