@@ -3,8 +3,8 @@
 Usage: python -m int8_quantized_kv_quant_amd.build_lib [--verbose]
 
 Every HIP source is compiled for gfx950 only. Flags that matter for results:
-  -fhip-fp32-correctly-rounded-divide-sqrt  the quantizer's divisions must be
-      IEEE correctly rounded (a reciprocal-multiply breaks exact .5 ties);
+  -fhip-fp32-correctly-rounded-divide-sqrt  the scale divisions (absmax / 127,
+      the Q4_0 reciprocal 1 / d) must be IEEE correctly rounded;
   -Xclang -target-feature -Xclang -packed-fp32-ops  no packed fp32 VALU ops;
   -mllvm -amdgpu-mfma-vgpr-form  MFMA accumulators in VGPRs: the decode kernels
       scale MFMA results with VALU ops, and AGPR-resident accumulators cost a
