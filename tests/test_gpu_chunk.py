@@ -87,6 +87,8 @@ CASES = {
     "q4_batch_g16": (wl.WORKLOADS["long_q4"].with_(batch=2, n_q_heads=32, max_ctx=1024), [100, 600], 33, 0),
     "k8v4_window_smaller_than_chunk": (wl.WORKLOADS["long_k8v4"].with_(max_ctx=2048), [1000], 100, 64),
     "k8v4_mha_g1": (wl.WORKLOADS["long_k8v4"].with_(n_q_heads=2, max_ctx=1024), [300], 70, 0),
+    # k8v4 with one int8 key scale per row (scale group = head_dim)
+    "k8v4_row_scales_prompt": (wl.WORKLOADS["long_k8v4"].with_(scale_group=256, max_ctx=2048), [1000], 70, 0),
     # int8 chunks with at most 32 (token, head) rows per kv head run through
     # the decode partial kernel (one or two 16-row blocks per workgroup,
     # per-row causal limits): 16, 12 and 32 rows, a second block of one row,
@@ -110,6 +112,7 @@ CASES = {
     "rows_q4_g16_batch2": (wl.WORKLOADS["long_q4"].with_(batch=2, n_q_heads=32, max_ctx=1024), [0, 600], 1, 0),
     "rows_q4_t2_window": (wl.WORKLOADS["long_q4"].with_(max_ctx=2048), [1500], 2, 300),
     "rows_k8v4_t2_window": (wl.WORKLOADS["long_k8v4"].with_(max_ctx=2048), [1500], 2, 300),
+    "rows_k8v4_row_scales_t2": (wl.WORKLOADS["long_k8v4"].with_(scale_group=256, max_ctx=2048), [1500], 2, 0),
     "rows_k8v4_mha_t16": (wl.WORKLOADS["long_k8v4"].with_(n_q_heads=2, max_ctx=1024), [700], 16, 0),
     "rows_q4_mha_t17_two_workgroups": (wl.WORKLOADS["long_q4"].with_(n_q_heads=2, max_ctx=1024), [500], 17, 40),
     # an fp32 store (k8v32, k32v8, k32v32): verify windows of at most 16 rows

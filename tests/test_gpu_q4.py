@@ -29,6 +29,14 @@ def _setup():
     return kvq_setup
 
 
+def _workload(name):
+    """The 4-bit layouts by name; "long_k8v4_rowscale" is long_k8v4 with one int8
+    key scale per row (scale group = head_dim) instead of one per 64 values."""
+    if name == "long_k8v4_rowscale":
+        return wl.WORKLOADS["long_k8v4"].with_(scale_group=256)
+    return wl.WORKLOADS[name]
+
+
 def _want_q4(rows):
     """Oracle packed bytes and scale bits of fp16 rows [n][256]."""
     codes, scales = orc.quantize_q4_0(orc.rotate_f32(rows))
@@ -53,13 +61,13 @@ def _check(lay, cache, w, b, positions, k_rows, v_rows):
                 np.testing.assert_array_equal(gs.view(np.uint16), want_s.view(np.uint16))
 
 
-@pytest.mark.parametrize("name", ["long_q4", "long_k8v4"])
+@pytest.mark.parametrize("name", ["long_q4", "long_k8v4", "long_k8v4_rowscale"])
 @pytest.mark.parametrize("order", ["pos", "head"])
 def test_q4_append_bit_exact(name, order):
     """3000 positions of the long-context rows (K with outlier channels),
     appended in ragged blocks, every position compared."""
     ks = _setup()
-    w = wl.WORKLOADS[name].with_(max_ctx=4096)
+    w = _workload(name).with_(max_ctx=4096)
     L = 3000
     print(f"[q4 append] {name} {order} L={L}", flush=True)
     lay = ks.layout_for(w, order)
@@ -174,13 +182,13 @@ def _run(w, lay, cache, q, lens, window, plan=None):
     return out.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("name", ["long_q4", "long_k8v4"])
+@pytest.mark.parametrize("name", ["long_q4", "long_k8v4", "long_k8v4_rowscale"])
 @pytest.mark.parametrize("order", ["pos", "head"])
 def test_q4_decode_ragged_lengths_and_split_sweep(name, order):
     """Lengths 0, 1, 33, 517, 1100 in one batch (tiles, a ragged tail, an
     empty context); every split size gives the oracle's result."""
     import int8_quantized_kv_quant_amd as kvq
-    w = wl.WORKLOADS[name].with_(batch=5, max_ctx=1100)
+    w = _workload(name).with_(batch=5, max_ctx=1100)
     lens = np.array([0, 1, 33, 517, 1100], dtype=np.int32)
     print(f"[q4 decode] {name} {order} lens {lens.tolist()}", flush=True)
     lay, cache = _setup().fill_cache(w, lens, order=order)
@@ -279,12 +287,12 @@ def _fused_pair(w, lens, plan=None):
     return out_a.cpu().numpy().astype(np.float64), out_b.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("name", ["long_q4", "long_k8v4"])
+@pytest.mark.parametrize("name", ["long_q4", "long_k8v4", "long_k8v4_rowscale"])
 @pytest.mark.parametrize("window", [0, 700])
 def test_q4_fused_step_equals_append_then_decode(name, window):
     """The fused step leaves the cache bit-identical to kv_quant_append's and
     gives the oracle's output, on a batch of 3 with ragged contexts."""
-    w = wl.WORKLOADS[name].with_(batch=3, max_ctx=5000, window=window)
+    w = _workload(name).with_(batch=3, max_ctx=5000, window=window)
     lens = np.array([5000, 2, 1337], dtype=np.int64)
     print(f"[q4 fused] {name} window {window}", flush=True)
     out_a, out_b = _fused_pair(w, lens)
