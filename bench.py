@@ -5,7 +5,7 @@ A step is the whole hot path for one new token of one sequence:
   kvq_plan (host)  ->  kv_append_decode_splitk (the token's K/V quantized and
   written into the cache, fused with the split-K partials)  ->  kv_decode_reduce
 on the long-context workload: batch 1, 16 query / 2 kv heads, head_dim 256,
-int8 codes with one fp16 scale per 64 values, context 131072 (K with 1 % outlier
+int8 codes under an fp16 scale per 64-value group, context 131072 (K with 1 % outlier
 channels x20). Inputs are seeded synthetic data (workloads.py), resident in HBM
 before timing.
 

@@ -38,8 +38,8 @@
  *   [G121] genie-ai-runtime releases, v1.2.1 "Bugs fixed": head_dim 256 stored
  *          in a 512-wide cache slot; strides must come from the slot width.
  *   [S2698] Strata pull request 2698 (int8 K/V cache), "What it does": int8
- *          codes with one FP16 scale per 64 values equal to the group absmax /
- *          127; head_dim must be a multiple of 64 or the host refuses; k8v32 and
+ *          codes, each 64-value group sharing an FP16 scale (its absmax /
+ *          127); head_dim must be a multiple of 64 or the host refuses; k8v32 and
  *          k32v8 quantize one store only; the fp32 store is plain attention.
  *          "Not in this PR": 4-bit stores (q4_0 for K and V, k8v4 for V only)
  *          use a Hadamard rotation over head_dim 256 with Q4_0 blocks; K is

@@ -20,8 +20,8 @@ written to be checked by eye against the pages:
   is split into blocks that each form an online-softmax partial, and a reduce
   combines them; results equal the single-pass kernel. "Details": sliding
   window mask, Gemma slot width (v1.2.1 "Bugs fixed").
-* Strata pull request 2698, "What it does": int8 codes with one FP16 scale per
-  64 values, the scale being the group absmax / 127; k8v32 / k32v8 quantize
+* Strata pull request 2698, "What it does": int8 codes, each 64-value group
+  sharing an FP16 scale equal to its absmax / 127; k8v32 / k32v8 quantize
   one store only; the fp32 store is plain attention.
 * Strata pull request 2698, "Not in this PR": the 4-bit stores (q4_0 for both,
   k8v4 for V only) use a Hadamard rotation over head_dim 256 with Q4_0
@@ -64,8 +64,8 @@ def scale_from_absmax(absmax) -> np.ndarray:
     """FP16 scale of a group from its absolute maximum: the fp16 value nearest
     to absmax / 127 (ties to even).
 
-    Strata pull request 2698, "What it does": one FP16 scale per 64 values,
-    equal to the group absmax / 127. The float64 quotient is rounded once to
+    Strata pull request 2698, "What it does": a 64-value group shares one FP16
+    scale, its absmax / 127. The float64 quotient is rounded once to
     float16 by numpy (round-to-nearest-even)."""
     a = np.asarray(absmax, dtype=np.float64)
     return (a / SCALE_DIVISOR).astype(np.float16)
