@@ -31,6 +31,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -52,11 +53,21 @@ def log(msg: str) -> None:
 Q4_SOURCES = ("kvq_decode_q4.hip", "kvq_q4_tile.h", "kvq_q4.h", "kvq_tile.h", "kvq_device.h")
 
 
+def _code_only(text: str) -> str:
+    """C++/HIP source with its comments removed and whitespace runs collapsed:
+    what the compiler sees, so that a comment edit does not count as a kernel
+    change (none of these sources has a comment marker inside a string)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest(files=("kvq_decode.hip", "kvq_tile.h", "kvq_device.h")) -> str:
+    """Digest of the code (comments excluded) of the sources a kernel is built from."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "int8_quantized_kv_quant_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "int8_quantized_kv_quant_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

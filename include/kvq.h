@@ -39,8 +39,8 @@
  *          in a 512-wide cache slot; strides must come from the slot width.
  *   [S2698] Strata pull request 2698 (int8 K/V cache), "What it does": int8
  *          codes, each 64-value group sharing an FP16 scale (its absmax /
- *          127); head_dim must be a multiple of 64 or the host refuses; k8v32 and
- *          k32v8 quantize one store only; the fp32 store is plain attention.
+ *          127); the host refuses a head_dim not divisible by 64; k8v32 and
+ *          k32v8 leave one store unquantized, attended as fp32.
  *          "Not in this PR": 4-bit stores (q4_0 for K and V, k8v4 for V only)
  *          use a Hadamard rotation over head_dim 256 with Q4_0 blocks; K is
  *          rotated after RoPE together with the queries, V is rotated and the
@@ -338,8 +338,8 @@ int kv_chunk_attn(const kvq_layout* layout, const void* k_store, const void* v_s
 
 /* Cache blob: positions [pos0, pos0 + n_pos) of one sequence as one
  * contiguous payload that carries, for every int8 store, the fp16 scales next
- * to the codes ([G11 "--int8-kv triage": a saved cache must persist the scales
- * region too], [G12 "Path F (#45) interop guard": int8 bytes saved without
+ * to the codes ([G11 "--int8-kv triage": saving a cache means saving its scale
+ * region as well], [G12 "Path F (#45) interop guard": int8 bytes saved without
  * their per-head scales read back as garbage]).
  * Payload (device memory): K values, V values, then the K scales and the V
  * scales of int8 and q4 stores; each region positions-major ([position]

@@ -2,7 +2,7 @@
 //
 // genie-ai-runtime v0.1.0-alpha.12, "Path I series" #64: per-head conversion
 // with scale capture (one scale per position and kv head). Strata PR 2698,
-// "What it does": one FP16 scale per 64 values equal to the group absmax / 127;
+// "What it does": each 64-value group shares an FP16 scale, its absmax / 127;
 // k8v32 / k32v8 quantize only one of the stores.
 //
 // Work mapping: each lane owns 4 consecutive elements of a row, so a row of

@@ -3,8 +3,8 @@
 // every int8 or q4 store -- and its placement back into a cache of the same
 // store types, scale group, head count and head_dim (any strides).
 //
-// genie-ai-runtime release v0.1.0-alpha.11, "--int8-kv triage": a saved cache
-// must persist the scales region too; release v0.1.0-alpha.12, "Path F (#45)
+// genie-ai-runtime release v0.1.0-alpha.11, "--int8-kv triage": saving a cache
+// means saving its scale region as well; release v0.1.0-alpha.12, "Path F (#45)
 // interop guard": int8 bytes saved without their per-head scales read back as
 // garbage. The payload therefore always carries the scales next to the codes,
 // and the host refuses to place a blob whose layout facts differ.

@@ -5,7 +5,7 @@
 // a head is split over blocks that each form an online-softmax partial, later
 // combined by a reduce kernel. v0.1.0-alpha.12 "Path I series" #65: each key and
 // value is dequantized as code * scale of its (position, kv head). Strata
-// PR 2698 "What it does": one FP16 scale per 64 values; k8v32 / k32v8.
+// PR 2698 "What it does": an FP16 scale for each 64-value group; k8v32 / k32v8.
 //
 // Mapping. One workgroup = (sequence b, kv head, block of up to 16 query heads
 // sharing it, split s). Split s owns the 128-position blocks s, s + S,

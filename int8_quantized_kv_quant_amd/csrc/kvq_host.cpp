@@ -14,8 +14,8 @@ static bool aligned(const void* p, uint64_t a) { return (reinterpret_cast<uintpt
 int check_layout(const kvq_layout* L) {
   if (!L) return KVQ_ERR_NULL;
   if (L->n_kv_heads < 1 || L->head_dim < 1 || L->max_ctx < 1) return KVQ_ERR_SHAPE;
-  // Strata PR 2698 "What it does": head_dim must be a multiple of 64 or the
-  // host refuses; the library also bounds it to the instantiated tile shapes.
+  // Strata PR 2698 "What it does": the host refuses a head_dim not divisible by
+  // 64; the library also bounds it to the instantiated tile shapes.
   if (L->head_dim % 64 != 0) return KVQ_ERR_UNSUPPORTED;
   if (L->head_dim != 64 && L->head_dim != 128 && L->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
   if (L->slot_dim < L->head_dim) return KVQ_ERR_SHAPE;  // genie v1.2.1: slot >= head_dim

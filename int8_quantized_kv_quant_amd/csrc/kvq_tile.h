@@ -6,7 +6,7 @@
 //
 // genie-ai-runtime release v0.1.0-alpha.12, "Path I series" #65: keys and
 // values are dequantized as code * scale of their (position, kv head); Strata
-// PR 2698, "What it does": one FP16 scale per 64 values.
+// PR 2698, "What it does": an FP16 scale for each 64-value group.
 #pragma once
 
 #include <math.h>

@@ -21,8 +21,8 @@ written to be checked by eye against the pages:
   combines them; results equal the single-pass kernel. "Details": sliding
   window mask, Gemma slot width (v1.2.1 "Bugs fixed").
 * Strata pull request 2698, "What it does": int8 codes, each 64-value group
-  sharing an FP16 scale equal to its absmax / 127; k8v32 / k32v8 quantize
-  one store only; the fp32 store is plain attention.
+  sharing an FP16 scale equal to its absmax / 127; in k8v32 / k32v8 only
+  one of the two stores is quantized, and the fp32 one enters attention as is.
 * Strata pull request 2698, "Not in this PR": the 4-bit stores (q4_0 for both,
   k8v4 for V only) use a Hadamard rotation over head_dim 256 with Q4_0
   blocks; K is rotated together with the queries, V is rotated and the output
@@ -85,7 +85,7 @@ def quantize_rows(x, group: int):
     x = np.asarray(x, dtype=np.float16)
     d = x.shape[-1]
     if d % group:
-        raise ValueError("head_dim must be a multiple of the scale group")
+        raise ValueError("the scale group must divide head_dim")
     xg = x.astype(np.float64).reshape(x.shape[:-1] + (d // group, group))
     a = np.abs(xg).max(axis=-1)
     s16 = scale_from_absmax(a)
@@ -240,8 +240,8 @@ class Cache:
         land at positions start_pos[b] .. start_pos[b] + n_tok - 1.
 
         int8 stores get codes + scales from quantize_rows; fp32 stores get the
-        fp16 values widened exactly (Strata PR 2698: k8v32 / k32v8 quantize
-        one store only)."""
+        fp16 values widened exactly (Strata PR 2698: k8v32 / k32v8 leave one
+        of the two stores unquantized)."""
         n_tok = k_new.shape[1]
         for s, new in (("k", k_new), ("v", v_new)):
             new = np.asarray(new, dtype=np.float16)
@@ -395,9 +395,10 @@ def split_partials(q, K, V, sm_scale: float, bounds):
 
 
 def combine_partials(m, l, O) -> np.ndarray:
-    """Reduce of the split partials (genie releases v1.3.0: a reduce kernel
-    combines them per head): M = max_s m_s, w_s = exp(m_s - M),
-    out = sum_s w_s O_s / sum_s w_s l_s. Empty splits weigh 0; all-empty -> 0."""
+    """Reduce of the split partials (genie releases v1.3.0, "split-K decode
+    attention": the per-split partials of each head merged in a second pass):
+    M = max_s m_s, w_s = exp(m_s - M), out = sum_s w_s O_s / sum_s w_s l_s.
+    Empty splits weigh 0; all-empty -> 0."""
     M = m.max(axis=0)
     out = np.zeros(O.shape[1:])
     ok = np.isfinite(M)
