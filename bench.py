@@ -273,10 +273,13 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
     dev = torch.device("cuda:0")
     res = {}
 
-    def timed(w, lens, lay, caches, k_new, v_new, parity=None):
+    def timed(w, lens, lay, caches, k_new, v_new, parity=None, one_call=False):
         """Graph-replayed decode steps over the cache copies; parity(out, q)
         -> dict of checks on the output of the last step (every copy holds the
-        same rows, so every step's output is the same)."""
+        same rows, so every step's output is the same). one_call: the step is
+        one kv_decode_attn call (one kernel launch for plans of at most 8
+        splits over int8 stores), else kv_append_decode_splitk +
+        kv_decode_reduce."""
         B = w.batch
         qd = torch.from_numpy(wl.queries(w)).to(dev)
         ld = torch.from_numpy(lens.astype(np.int32)).to(dev)
@@ -284,8 +287,13 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
         plan = kvq.kvq_plan(lay, B, w.n_q_heads, w.max_ctx, w.window, n_cu)
         ws = torch.zeros(plan.ws_bytes, dtype=torch.uint8, device=dev)
         out = torch.empty((B, w.n_q_heads, w.head_dim), dtype=torch.float16, device=dev)
+        arrive = torch.zeros(kvq.arrive_count(lay, B, w.n_q_heads), dtype=torch.int32, device=dev)
 
         def step(c):
+            if one_call:
+                kvq.kv_decode_attn(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], k_new, v_new, qd, B,
+                                   w.n_q_heads, ld, w.window, sm, plan, ws, ws.numel(), arrive, out)
+                return
             kvq.kv_append_decode_splitk(lay, c["k"], c["v"], c["k_scales"], c["v_scales"], k_new, v_new, qd, B,
                                         w.n_q_heads, ld, w.window, sm, plan, ws, ws.numel())
             kvq.kv_decode_reduce(lay, ws, ws.numel(), ld, B, w.n_q_heads, w.window, plan, out)
@@ -316,6 +324,9 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
         res = {"us_per_step": round(us, 2), "kv_bytes_per_step": int(kvb), "GB_s": round(kvb / us / 1e3, 1),
                "pct_hbm_peak": round(100 * kvb / us / 1e3 / HBM_PEAK_GBS, 2), "n_splits": plan.n_splits,
                "chunk": plan.chunk, "steps": reps * per_graph, "steps_per_graph": per_graph}
+        if one_call:
+            res["launches"] = kvq.kvq_decode_launches(lay, B, w.n_q_heads, plan)
+            res["arrive_left_zero"] = int(torch.count_nonzero(arrive)) == 0
         if parity is not None:
             res.update(parity(out.float().cpu().numpy().astype(np.float64), wl.queries(w)))
         return res
@@ -339,9 +350,14 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
         caches = [c0] + [{k: (None if t is None else t.clone()) for k, t in c0.items()} for _ in range(COPIES - 1)]
         k_new = torch.from_numpy(wl.kv_rows(w, "k", 0, L - 1, 1)).to(dev)
         v_new = torch.from_numpy(wl.kv_rows(w, "v", 0, L - 1, 1)).to(dev)
+        two = timed(w, lens, lay, caches, k_new, v_new)
         res[key] = {"context": L, "window": w.window, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                     "head_dim": w.head_dim, "cache_copies": COPIES,
-                    **timed(w, lens, lay, caches, k_new, v_new, single_parity(w, L, lay, caches[-1]))}
+                    "step": "kv_decode_attn (append, partials, combine: one launch for units of <= 1024 "
+                            "head x dim values, else partials + reduce)",
+                    **timed(w, lens, lay, caches, k_new, v_new, single_parity(w, L, lay, caches[-1]), one_call=True),
+                    "two_call_us_per_step": two["us_per_step"],
+                    "two_call_step": "kv_append_decode_splitk + kv_decode_reduce"}
         del caches, c0
 
     res["prefill_chunk"] = chunk_workload(kvq, kvq_setup, wl, n_cu)

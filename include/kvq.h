@@ -10,6 +10,8 @@
  *   kv_append_decode_splitk  the decode step's one-token quantize-append fused
  *                          into kv_decode_attn_splitk
  *   kv_decode_reduce       combine the split partials into the fp16 output
+ *   kv_decode_attn         append + partials + combine in one call (one launch
+ *                          for small int8 plans)
  *   kv_decode_attn_static  partials + combine in one call, with the partials
  *                          in the library's static device scratch (no
  *                          workspace, no allocation)
@@ -260,6 +262,48 @@ int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,
                      const int32_t* d_seq_lens, int32_t batch, int32_t n_q_heads,
                      int32_t window, const kvq_plan_t* plan, uint16_t* out,
                      void* stream);
+
+/* kv_decode_attn -- a whole decode step in one call: the new token's
+ * quantize-append (when k_new, v_new are given), the split-K partials and
+ * their combine into the fp16 output. [G130 "split-K decode attention" and
+ * "Details"], [G12 #64, #65], [S2698 "What it does"].
+ * The output is what kv_append_decode_splitk (k_new and v_new non-null) or
+ * kv_decode_attn_splitk (both null), followed by kv_decode_reduce, computes
+ * with the same plan, up to the order of the fp32 sums of the combine; the
+ * cache rows appended are bit-identical to theirs.
+ * Plans of at most 8 splits over int8 K and V stores whose units (sequence,
+ * kv head, block of up to 16 query heads) hold at most 1024 (query head x
+ * dim) values -- e.g. 4 heads x 256 dims, 16 x 64 -- run as ONE kernel
+ * launch: every workgroup writes its partial through to memory and counts its
+ * arrival in d_arrive, and the last workgroup of each unit combines that
+ * unit's splits and writes its rows of out (the genie reduce's arithmetic,
+ * inside the partial kernel; no workgroup waits for another). Other plans and
+ * stores run the partial kernel and the reduce, two launches (measured faster
+ * there); kvq_decode_launches tells which.
+ *   d_arrive  device uint32 [batch * n_kv_heads * ceil((n_q_heads / n_kv_heads)
+ *             / 16)], 4-byte aligned: zero before the first call that uses it;
+ *             every call leaves it zero. Calls that share it (or ws) must not
+ *             overlap on the device.
+ *   out       fp16 [batch][n_q_heads][head_dim], contiguous, 16-byte aligned.
+ *   other arguments as for kv_append_decode_splitk; k_new and v_new are both
+ *   null or both non-null (KVQ_ERR_NULL otherwise).
+ * Errors as kv_append_decode_splitk / kv_decode_attn_splitk; nothing is
+ * enqueued when a check fails. */
+int kv_decode_attn(const kvq_layout* layout, void* k_store, void* v_store,
+                   uint16_t* k_scales, uint16_t* v_scales,
+                   const uint16_t* k_new, const uint16_t* v_new,
+                   const uint16_t* q, int32_t batch, int32_t n_q_heads,
+                   const int32_t* d_seq_lens, int32_t window, float sm_scale,
+                   const kvq_plan_t* plan, void* ws, int64_t ws_bytes,
+                   uint32_t* d_arrive, uint16_t* out, void* stream);
+
+/* kvq_decode_launches -- host only, no device call. The number of kernel
+ * launches kv_decode_attn makes for these arguments: 1 (the one-launch step),
+ * 2 (partials, then the reduce) or 0 (batch 0). Writes *launches; returns
+ * KVQ_OK or the error kv_decode_attn would return for the layout, heads and
+ * plan. */
+int kvq_decode_launches(const kvq_layout* layout, int32_t batch, int32_t n_q_heads,
+                        const kvq_plan_t* plan, int32_t* launches);
 
 /* kv_decode_attn_static -- for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid

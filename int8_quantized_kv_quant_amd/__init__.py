@@ -20,7 +20,7 @@ __all__ = [
     "lib_path", "load", "kvq_version", "kvq_status_string", "kvq_plan", "kv_quant_append",
     "kv_decode_attn_splitk", "kv_append_decode_splitk", "kv_decode_reduce", "kvq_plan_chunk",
     "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack", "kv_cache_unpack", "kvq_stream_read", "BlobHeader",
-    "kv_decode_attn_static", "STATIC_SCRATCH_BYTES",
+    "kv_decode_attn_static", "STATIC_SCRATCH_BYTES", "kv_decode_attn", "arrive_count", "kvq_decode_launches",
     "make_layout",
     "alloc_cache", "decode", "chunk_attn",
     "EXPORTED_SYMBOLS",
@@ -35,7 +35,7 @@ Q4_BLOCK = 32  # values per Q4_0 block (one fp16 scale each)
 EXPORTED_SYMBOLS = ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
                     "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack",
                     "kv_cache_unpack", "kvq_stream_read", "kvq_status_string", "kvq_version",
-                    "kv_decode_attn_static")
+                    "kv_decode_attn_static", "kv_decode_attn", "kvq_decode_launches")
 
 # Bytes of the library's static device scratch (KVQ_STATIC_SCRATCH_BYTES).
 STATIC_SCRATCH_BYTES = 16 << 20
@@ -133,6 +133,9 @@ def load():
                                             i64, vp]
     lib.kv_decode_reduce.argtypes = [LP, vp, i64, vp, i32, i32, i32, PP, vp, vp]
     lib.kv_decode_attn_static.argtypes = [LP, vp, vp, vp, vp, vp, i32, i32, vp, i32, f32, PP, vp, vp]
+    lib.kv_decode_attn.argtypes = [LP, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, f32, PP, vp, i64, vp, vp,
+                                   vp]
+    lib.kvq_decode_launches.argtypes = [LP, i32, i32, PP, ctypes.POINTER(i32)]
     lib.kvq_plan_chunk.argtypes = [LP, i32, i32, i32, i32, i32, i32, PP]
     HP = ctypes.POINTER(BlobHeader)
     lib.kvq_blob_size.argtypes = [LP, i32, ctypes.POINTER(i64)]
@@ -145,7 +148,8 @@ def load():
     lib.kvq_version.argtypes = []
     for fn in ("kvq_plan", "kv_quant_append", "kv_decode_attn_splitk", "kv_append_decode_splitk",
                "kv_decode_reduce", "kvq_plan_chunk", "kv_chunk_attn", "kvq_blob_size", "kv_cache_pack",
-               "kv_cache_unpack", "kvq_stream_read", "kvq_version", "kv_decode_attn_static"):
+               "kv_cache_unpack", "kvq_stream_read", "kvq_version", "kv_decode_attn_static", "kv_decode_attn",
+               "kvq_decode_launches"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -222,6 +226,32 @@ def kv_decode_reduce(layout: Layout, ws, ws_bytes: int, seq_lens, batch: int, n_
     _check("kv_decode_reduce", load().kv_decode_reduce(
         ctypes.byref(layout.c()), _ptr(ws), ws_bytes, _ptr(seq_lens), batch, n_q_heads, window,
         ctypes.byref(plan.c()), _ptr(out), _stream(stream)))
+
+
+def kv_decode_attn(layout: Layout, k_store, v_store, k_scales, v_scales, k_new, v_new, q, batch: int,
+                   n_q_heads: int, seq_lens, window: int, sm_scale: float, plan: Plan, ws, ws_bytes: int,
+                   arrive, out, stream=None) -> None:
+    """Append (k_new, v_new non-None) + partials + combine into out in one call;
+    arrive: zeroed int32/uint32 device counters, one per (sequence, kv head,
+    16-head block), left zero by every call."""
+    _check("kv_decode_attn", load().kv_decode_attn(
+        ctypes.byref(layout.c()), _ptr(k_store), _ptr(v_store), _ptr(k_scales), _ptr(v_scales), _ptr(k_new),
+        _ptr(v_new), _ptr(q), batch, n_q_heads, _ptr(seq_lens), window, sm_scale, ctypes.byref(plan.c()), _ptr(ws),
+        ws_bytes, _ptr(arrive), _ptr(out), _stream(stream)))
+
+
+def kvq_decode_launches(layout: Layout, batch: int, n_q_heads: int, plan: Plan) -> int:
+    """Kernel launches kv_decode_attn makes for these arguments (1, 2, or 0)."""
+    n = ctypes.c_int32(-1)
+    _check("kvq_decode_launches", load().kvq_decode_launches(ctypes.byref(layout.c()), batch, n_q_heads,
+                                                             ctypes.byref(plan.c()), ctypes.byref(n)))
+    return n.value
+
+
+def arrive_count(layout: Layout, batch: int, n_q_heads: int) -> int:
+    """Number of kv_decode_attn arrival counters: batch * n_kv_heads * ceil(G / 16)."""
+    g = n_q_heads // layout.n_kv_heads
+    return max(1, batch * layout.n_kv_heads * ((g + 15) // 16))
 
 
 def kv_decode_attn_static(layout: Layout, k_store, v_store, k_scales, v_scales, q, batch: int, n_q_heads: int,
@@ -332,12 +362,14 @@ def alloc_cache(layout: Layout, batch: int, device="cuda", fill=0):
 
 def decode(layout: Layout, cache: dict, q, seq_lens, window: int, sm_scale: float | None = None,
            plan: Plan | None = None, ws=None, out=None, n_cu: int | None = None, stream=None,
-           new_kv=None):
+           new_kv=None, arrive=None):
     """One decode step: kv_decode_attn_splitk then kv_decode_reduce on the
     current stream; with new_kv = (k_new, v_new) (fp16 [batch][n_kv][head_dim] on
     the device) the token's quantize-append is fused in (kv_append_decode_splitk,
-    appending at position seq_lens[b] - 1). q: fp16 [batch][n_q][head_dim] on the
-    device; seq_lens: int32 [batch] on the device. Returns the fp16 output."""
+    appending at position seq_lens[b] - 1). With arrive (zeroed int32 device
+    counters, arrive_count of them) the step is one kv_decode_attn call instead.
+    q: fp16 [batch][n_q][head_dim] on the device; seq_lens: int32 [batch] on the
+    device. Returns the fp16 output."""
     import torch
     batch, n_q, d = q.shape
     if sm_scale is None:
@@ -350,6 +382,11 @@ def decode(layout: Layout, cache: dict, q, seq_lens, window: int, sm_scale: floa
         ws = torch.empty(max(plan.ws_bytes, 16), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((batch, n_q, d), dtype=torch.float16, device=q.device)
+    if arrive is not None:
+        k_new, v_new = new_kv if new_kv is not None else (None, None)
+        kv_decode_attn(layout, cache["k"], cache["v"], cache["k_scales"], cache["v_scales"], k_new, v_new, q,
+                       batch, n_q, seq_lens, window, sm_scale, plan, ws, ws.numel(), arrive, out, stream)
+        return out
     if new_kv is None:
         kv_decode_attn_splitk(layout, cache["k"], cache["v"], cache["k_scales"], cache["v_scales"], q,
                               batch, n_q, seq_lens, window, sm_scale, plan, ws, ws.numel(), stream)

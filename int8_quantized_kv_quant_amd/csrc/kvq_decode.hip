@@ -96,7 +96,32 @@ struct PartialArgs {
   // q is fp16 [B][T][n_q][D], and the partial rows are (b, t, hq).
   const int32_t* start_pos;
   int32_t T;
+  // One-launch step (the ONE instances): the fp16 output [B][n_q][D], one
+  // arrival counter per (sequence, kv head, head block), and the byte size of
+  // the partial region (ws_o then ws_ml) for its write-through accesses.
+  uint16_t* out;
+  uint32_t* arrive;
+  uint32_t ws_bytes;
 };
+
+// Cache policy of the one-launch step's partial stores and loads: device scope
+// (sc1), i.e. stores written through the XCD's L2 to memory and loads that miss
+// in it. A workgroup on one XCD can then read what a workgroup on another XCD
+// wrote once that write has completed, without the write-back and
+// invalidation of whole L2 caches that a release/acquire fence pair costs.
+constexpr int kWriteThrough = 16;
+__device__ __forceinline__ void st128_wt(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, kWriteThrough);
+}
+__device__ __forceinline__ void st64_wt(__amdgpu_buffer_rsrc_t r, uint32_t off, float2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)off, 0, kWriteThrough);
+}
+__device__ __forceinline__ float4 ld128_wt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kWriteThrough));
+}
+__device__ __forceinline__ float2 ld64_wt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kWriteThrough));
+}
 
 // ---- operand loads straight from HBM into registers (any store dtype) ----------
 // K operands (codes or fp32 rows, and an int8 store's scale rows) of the tile
@@ -177,10 +202,12 @@ __device__ __forceinline__ void wait_vm0_visible() { __builtin_amdgcn_s_waitcnt(
 __device__ __forceinline__ int merge_swz(int f) { return f ^ ((f >> 4) & 3); }
 
 // ---- kernel ----------------------------------------------------------------------
-template <int D, bool KI8, bool VI8, bool G64, int NW, bool CHUNK = false, int RB = 1>
+template <int D, bool KI8, bool VI8, bool G64, int NW, bool CHUNK = false, int RB = 1, bool ONE = false>
 __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   using S = Shape<D, KI8, VI8, G64>;
   constexpr bool kStaged = KI8 && VI8;
+  // ONE: the one-launch decode step (kv_decode_attn) over int8 K and V.
+  static_assert(!ONE || (kStaged && !CHUNK && RB == 1), "one-launch step: int8 decode only");
   // RB blocks of 16 query rows per workgroup, sharing every key and value
   // operand (chunk rows over int8 K and V only).
   static_assert(RB == 1 || (CHUNK && kStaged && RB == 2), "two row blocks for int8 chunk rows only");
@@ -212,6 +239,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t nw_code[2][D / 4];
   __shared__ uint16_t nw_scale[2][S::NG];
   __shared__ float nw_z[NW][16];
+  __shared__ int sm_last;  // ONE: this workgroup arrived last in its unit
 
   const int split = blockIdx.x;
   const int hk = blockIdx.y / a.head_blocks;
@@ -249,6 +277,97 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
     L = L_in < 0 ? 0 : (L_in > a.max_ctx ? a.max_ctx : L_in);
     lo = a.window > 0 ? max(0, L - a.window) : 0;
   }
+  // Partial stores. ONE: written through to memory (the last workgroup of the
+  // unit, possibly on another XCD, reads them below); else ordinary stores
+  // that the reduce kernel reads after this launch.
+  const auto wsr = make_rsrc(a.ws_o, ONE ? a.ws_bytes : 0u);
+  const uint32_t ml_base = (uint32_t)((a.ws_ml - a.ws_o) * 4);
+  auto put_o = [&](int64_t row, int d, float4 v) {
+    if constexpr (ONE) st128_wt(wsr, (uint32_t)((row * D + d) * 4), v);
+    else reinterpret_cast<float4*>(a.ws_o + row * D)[d / 4] = v;
+  };
+  auto put_ml = [&](int64_t row, float2 v) {
+    if constexpr (ONE) st64_wt(wsr, ml_base + (uint32_t)(row * 8), v);
+    else ml[row] = v;
+  };
+  // ONE: after the workgroup's partial stores. Arrival is counted per unit
+  // (sequence, kv head, head block) with a device-scope atomic once every lane's
+  // write-through stores have completed; the workgroup that brings the count
+  // to n_splits resets it to zero for the next call and combines the unit's
+  // splits -- as the reduce kernel does: M = max m_s, out = sum 2^(m_s - M) O_s /
+  // sum 2^(m_s - M) l_s, fp16 (RNE) -- from loads that miss every cache.
+  // No workgroup waits for another, so the launch always drains.
+  auto arrive_and_combine = [&]() {
+    if constexpr (ONE) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint32_t* cnt = a.arrive + ((int64_t)b * a.n_kv + hk) * a.head_blocks + hblk;
+        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old + 1u == (uint32_t)a.n_splits;
+        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_last = last ? 1 : 0;
+      }
+      __syncthreads();
+      if (!sm_last) return;
+      // Every lane takes up to kPairs (head, 4-dim) columns per round and
+      // issues all their loads before using any (one memory round trip per
+      // round; a unit of up to 8 heads at D = 256 is one round).
+      constexpr int kPairs = 2;
+      constexpr int K = kOneLaunchMaxSplits;
+      for (int base = threadIdx.x; base < nh * (D / 4); base += kPairs * NW * 64) {
+        float2 mls[kPairs][K];
+        float4 os[kPairs][K];
+#pragma unroll
+        for (int u = 0; u < kPairs; ++u) {
+          const int idx = base + u * NW * 64;
+          const int h = idx / (D / 4);
+          const int d = 4 * (idx % (D / 4));
+          const int64_t hrow = ((int64_t)b * a.n_q + hq0 + h) * a.n_splits;  // split 0 of head h
+#pragma unroll
+          for (int s = 0; s < K; ++s) {
+            // an empty split's O row is unwritten: loaded, but never used
+            mls[u][s] = make_float2(-INFINITY, 0.0f);
+            os[u][s] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (idx < nh * (D / 4) && s < a.n_splits) {
+              mls[u][s] = ld64_wt(wsr, ml_base + (uint32_t)((hrow + s) * 8));
+              os[u][s] = ld128_wt(wsr, (uint32_t)(((hrow + s) * D + d) * 4));
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kPairs; ++u) {
+          const int idx = base + u * NW * 64;
+          if (idx >= nh * (D / 4)) continue;
+          const int h = idx / (D / 4);
+          const int d = 4 * (idx % (D / 4));
+          float M = -INFINITY;
+#pragma unroll
+          for (int s = 0; s < K; ++s) M = fmaxf(M, mls[u][s].x);
+          float l = 0.0f;
+          float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int s = 0; s < K; ++s) {
+            if (mls[u][s].x != -INFINITY) {
+              const float w = __builtin_amdgcn_exp2f(mls[u][s].x - M);
+              l = fmaf(w, mls[u][s].y, l);
+              o.x = fmaf(w, os[u][s].x, o.x);
+              o.y = fmaf(w, os[u][s].y, o.y);
+              o.z = fmaf(w, os[u][s].z, o.z);
+              o.w = fmaf(w, os[u][s].w, o.w);
+            }
+          }
+          const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+          const f16 r0 = (f16)(o.x * inv), r1 = (f16)(o.y * inv), r2 = (f16)(o.z * inv), r3 = (f16)(o.w * inv);
+          const u32x2 pk = {
+              (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16),
+              (uint32_t)__builtin_bit_cast(uint16_t, r2) | ((uint32_t)__builtin_bit_cast(uint16_t, r3) << 16)};
+          *reinterpret_cast<u32x2*>(a.out + ((int64_t)b * a.n_q + hq0 + h) * D + d) = pk;
+        }
+      }
+    }
+  };
+
   // Split s takes the blocks s, s + S, s + 2 S, ... of BLK positions of
   // [lo, L) (block-cyclic), S = min(n_splits, ceil((L - lo) / chunk)): as many
   // splits as contiguous ranges of `chunk` positions would use, each reading
@@ -257,7 +376,8 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   const int n_used = (int)min((int64_t)a.n_splits, ((int64_t)L - lo + a.chunk - 1) / a.chunk);
   const int64_t start64 = (int64_t)lo + (int64_t)split * BLK;
   if (split >= n_used || start64 >= L) {  // empty split: recorded as (m, l) = (-inf, 0), O not written
-    if ((int)threadIdx.x < nh) ml[rowid(threadIdx.x)] = make_float2(-INFINITY, 0.0f);
+    if ((int)threadIdx.x < nh) put_ml(rowid(threadIdx.x), make_float2(-INFINITY, 0.0f));
+    arrive_and_combine();
     return;
   }
   const int start = (int)start64;
@@ -622,7 +742,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
         v.z = fmaf(wk, u.z, v.z);
         v.w = fmaf(wk, u.w, v.w);
       }
-      reinterpret_cast<float4*>(a.ws_o + rowid(16 * rb + h) * D)[d / 4] = v;
+      put_o(rowid(16 * rb + h), d, v);
     }
     if (threadIdx.x < nr) {
       const int h = threadIdx.x;
@@ -636,11 +756,12 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
         const float mk = sm_m[k][h];
         if (mk != -INFINITY) l += sm_l[k][h] * __builtin_amdgcn_exp2f(mk - M);
       }
-      ml[rowid(16 * rb + h)] = make_float2(M, l);
+      put_ml(rowid(16 * rb + h), make_float2(M, l));
     }
   };
   if constexpr (RB == 1) {
     merge(0, nh);
+    arrive_and_combine();
   } else {
     merge(0, min(16, nh));
     if (nh > 16) {
@@ -657,6 +778,12 @@ static void launch_partial_t(const PartialArgs& a, dim3 grid, hipStream_t s) {
   // first tiles in flight) and end (merge, partial stores) overlap another's
   // streaming, which measured faster than one 8-wavefront workgroup per unit.
   constexpr int NW = kPartialWaves;
+  if constexpr (KI8 && VI8) {
+    if (a.out) {  // the one-launch step of kv_decode_attn
+      hipLaunchKernelGGL((kvq_partial_kernel<D, KI8, VI8, G64, NW, false, 1, true>), grid, dim3(NW * 64), 0, s, a);
+      return;
+    }
+  }
   hipLaunchKernelGGL((kvq_partial_kernel<D, KI8, VI8, G64, NW>), grid, dim3(NW * 64), 0, s, a);
 }
 
@@ -683,8 +810,13 @@ int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store
                    const uint16_t* k_scales, const uint16_t* v_scales, const uint16_t* k_new,
                    const uint16_t* v_new, const uint16_t* q, int32_t batch, int32_t n_q_heads,
                    const int32_t* d_seq_lens, int32_t window, float sm_scale, const kvq_plan_t& plan,
-                   void* ws, void* stream) {
+                   void* ws, void* stream, uint16_t* out, uint32_t* arrive) {
+  if ((out != nullptr) != (arrive != nullptr)) return KVQ_ERR_NULL;
+  if (out && !one_launch_ok(L, batch, n_q_heads, plan)) return KVQ_ERR_UNSUPPORTED;
   PartialArgs a{};
+  a.out = out;
+  a.arrive = arrive;
+  if (out) a.ws_bytes = (uint32_t)workspace_bytes(batch, n_q_heads, plan.n_splits, L.head_dim);
   a.k_store = k_store;
   a.v_store = v_store;
   a.k_scales = k_scales;

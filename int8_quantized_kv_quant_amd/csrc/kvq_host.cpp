@@ -269,6 +269,55 @@ int kv_append_decode_splitk(const kvq_layout* layout, void* k_store, void* v_sto
                         d_seq_lens, window, sm_scale, *plan, ws, stream);
 }
 
+int kvq_decode_launches(const kvq_layout* layout, int32_t batch, int32_t n_q_heads, const kvq_plan_t* plan,
+                        int32_t* launches) {
+  int st = check_layout(layout);
+  if (st) return st;
+  const kvq_layout& L = *layout;
+  if ((st = check_heads(L, batch, n_q_heads))) return st;
+  if ((st = check_plan(L, batch, n_q_heads, plan))) return st;
+  if (!launches) return KVQ_ERR_NULL;
+  *launches = batch == 0 ? 0 : (!has_q4(L) && one_launch_ok(L, batch, n_q_heads, *plan) ? 1 : 2);
+  return KVQ_OK;
+}
+
+int kv_decode_attn(const kvq_layout* layout, void* k_store, void* v_store, uint16_t* k_scales, uint16_t* v_scales,
+                   const uint16_t* k_new, const uint16_t* v_new, const uint16_t* q, int32_t batch,
+                   int32_t n_q_heads, const int32_t* d_seq_lens, int32_t window, float sm_scale,
+                   const kvq_plan_t* plan, void* ws, int64_t ws_bytes, uint32_t* d_arrive, uint16_t* out,
+                   void* stream) {
+  int st = check_layout(layout);
+  if (st) return st;
+  const kvq_layout& L = *layout;
+  if ((st = check_store_ptrs(L, L.k_dtype, k_store, k_scales))) return st;
+  if ((st = check_store_ptrs(L, L.v_dtype, v_store, v_scales))) return st;
+  if ((st = check_heads(L, batch, n_q_heads))) return st;
+  if ((st = check_plan(L, batch, n_q_heads, plan))) return st;
+  if ((k_new == nullptr) != (v_new == nullptr)) return KVQ_ERR_NULL;
+  if (!q || !d_seq_lens || !out || !d_arrive) return KVQ_ERR_NULL;
+  if ((k_new && (!aligned(k_new, 16) || !aligned(v_new, 16))) || !aligned(q, 16) || !aligned(d_seq_lens, 4) ||
+      !aligned(out, 16) || !aligned(d_arrive, 4))
+    return KVQ_ERR_ALIGN;
+  if (window < 0) return KVQ_ERR_SHAPE;
+  if (!(sm_scale == sm_scale) || sm_scale > 3.0e38f || sm_scale < -3.0e38f) return KVQ_ERR_SHAPE;
+  if (!ws) return KVQ_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
+  if (ws_bytes < plan->ws_bytes) return KVQ_ERR_WORKSPACE;
+  if (has_q4(L) && !q4_decode_supported(L)) return KVQ_ERR_UNSUPPORTED;
+  if (batch == 0) return KVQ_OK;
+  if (!has_q4(L) && one_launch_ok(L, batch, n_q_heads, *plan))
+    return launch_partial(L, k_store, v_store, k_scales, v_scales, k_new, v_new, q, batch, n_q_heads, d_seq_lens,
+                          window, sm_scale, *plan, ws, stream, out, d_arrive);
+  if (has_q4(L))
+    st = launch_partial_q4(L, k_store, v_store, k_scales, v_scales, k_new, v_new, q, batch, n_q_heads, d_seq_lens,
+                           window, sm_scale, *plan, ws, stream);
+  else
+    st = launch_partial(L, k_store, v_store, k_scales, v_scales, k_new, v_new, q, batch, n_q_heads, d_seq_lens,
+                        window, sm_scale, *plan, ws, stream);
+  if (st) return st;
+  return launch_reduce(L, ws, batch, n_q_heads, *plan, out, stream);
+}
+
 int kvq_plan_chunk(const kvq_layout* layout, int32_t batch, int32_t n_tok, int32_t n_q_heads,
                    int32_t max_seq_len, int32_t window, int32_t n_cu, kvq_plan_t* out) {
   int st = check_layout(layout);

@@ -14,6 +14,9 @@ constexpr int kHeadsPerBlock = 16;   // query heads one wave carries (MFMA M/N =
 constexpr int kPartialWaves = 4;     // wavefronts per partial-kernel workgroup
 constexpr int kMinSplitChunk = kPartialWaves * kTile;  // planner: one tile per wavefront at least
 constexpr int kChunkWaves = 4;       // wavefronts per chunk-attention workgroup
+// kv_decode_attn: plans of at most this many splits over int8 K and V run as
+// one launch (the last workgroup of a unit combines its splits in registers).
+constexpr int kOneLaunchMaxSplits = 8;
 
 // A layout with a 4-bit store.
 inline bool has_q4(const kvq_layout& L) { return L.k_dtype == KVQ_STORE_Q4 || L.v_dtype == KVQ_STORE_Q4; }
@@ -159,11 +162,28 @@ int launch_append(const kvq_layout& L, void* k_store, void* v_store, uint16_t* k
                   const int32_t* d_start_pos, int32_t batch, int32_t n_tok, void* stream);
 
 // k_new / v_new non-null: the fused append of kv_append_decode_splitk.
+// out and arrive non-null: the one-launch step of kv_decode_attn (int8 K and V
+// stores, one_launch_ok): the last workgroup of each unit writes the output.
 int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store,
                    const uint16_t* k_scales, const uint16_t* v_scales, const uint16_t* k_new,
                    const uint16_t* v_new, const uint16_t* q, int32_t batch, int32_t n_q_heads,
                    const int32_t* d_seq_lens, int32_t window, float sm_scale, const kvq_plan_t& plan,
-                   void* ws, void* stream);
+                   void* ws, void* stream, uint16_t* out = nullptr, uint32_t* arrive = nullptr);
+
+// Whether kv_decode_attn runs the plan as one launch: int8 K and V stores, at
+// most kOneLaunchMaxSplits splits, units of at most kOneLaunchMaxRowValues
+// (query head x dim) values, and a partial region that one buffer resource
+// covers. (Measured against the two launches: one launch is 0.2-0.7 us faster
+// per step with 4 KB of fp32 partial per split and unit -- 4 heads x 256 dims,
+// 16 x 64, 4 x 128 -- and 0.3-0.7 us slower with 8 KB, 8 heads x 256 dims.)
+constexpr int kOneLaunchMaxRowValues = 1024;
+inline bool one_launch_ok(const kvq_layout& L, int64_t batch, int64_t n_q_heads, const kvq_plan_t& plan) {
+  const int64_t G = n_q_heads / L.n_kv_heads;
+  const int64_t rows = G < kHeadsPerBlock ? G : kHeadsPerBlock;
+  return L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8 && plan.n_splits <= kOneLaunchMaxSplits &&
+         rows * L.head_dim <= kOneLaunchMaxRowValues &&
+         workspace_bytes(batch, n_q_heads, plan.n_splits, L.head_dim) <= 0x7fffffff;
+}
 
 int launch_chunk(const kvq_layout& L, const void* k_store, const void* v_store, const uint16_t* k_scales,
                  const uint16_t* v_scales, const uint16_t* q, int32_t batch, int32_t n_tok, int32_t n_q_heads,

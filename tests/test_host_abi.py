@@ -136,6 +136,18 @@ def _fused(lay, plan=None, **kw):
         args["sm"], ctypes.byref(plan.c()), args["ws"], args["ws_bytes"], None)
 
 
+def _one(lay, plan=None, **kw):
+    plan = plan or kvq.Plan(4, 256, 1 * 16 * 4 * 258 * 4)
+    args = dict(k_store=FAKE, v_store=FAKE, k_scales=FAKE, v_scales=FAKE, k_new=FAKE, v_new=FAKE, q=FAKE,
+                batch=1, n_q=16, seq_lens=FAKE, window=0, sm=0.0625, ws=FAKE, ws_bytes=plan.ws_bytes, arrive=FAKE,
+                out=FAKE)
+    args.update(kw)
+    return kvq.load().kv_decode_attn(
+        ctypes.byref(lay.c()), args["k_store"], args["v_store"], args["k_scales"], args["v_scales"],
+        args["k_new"], args["v_new"], args["q"], args["batch"], args["n_q"], args["seq_lens"], args["window"],
+        args["sm"], ctypes.byref(plan.c()), args["ws"], args["ws_bytes"], args["arrive"], args["out"], None)
+
+
 def _chunk(lay, plan=None, **kw):
     plan = plan or kvq.Plan(2, 256, 1 * 8 * 16 * 2 * 258 * 4)
     args = dict(k_store=FAKE, v_store=FAKE, k_scales=FAKE, v_scales=FAKE, q=FAKE, batch=1, n_tok=8, n_q=16,
@@ -213,6 +225,60 @@ def test_fused_append_refuses_what_either_part_refuses():
     assert _fused(lay, window=-1) == SHAPE
     assert _fused(lay, ws=None) == WS
     assert _fused(lay, batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
+
+
+@needs_lib
+def test_one_call_step_refusals():
+    """kv_decode_attn refuses what the partial or the reduce would, plus a
+    missing output or arrival array and a half-given new token."""
+    lay = _base()
+    assert _one(lay, out=None) == NULL_
+    assert _one(lay, arrive=None) == NULL_
+    assert _one(lay, k_new=None) == NULL_
+    assert _one(lay, v_new=None) == NULL_
+    assert _one(lay, q=None) == NULL_
+    assert _one(lay, out=FAKE + 8) == ALIGN
+    assert _one(lay, arrive=FAKE + 2) == ALIGN
+    assert _one(lay, k_new=FAKE + 2) == ALIGN
+    assert _one(lay, n_q=15) == SHAPE
+    assert _one(lay, window=-1) == SHAPE
+    assert _one(lay, sm=float("nan")) == SHAPE
+    assert _one(lay, ws=None) == WS
+    assert _one(lay, ws_bytes=16) == WS
+    assert _one(lay, plan=kvq.Plan(0, 256, 0)) == SHAPE
+    assert _one(lay, batch=0, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
+    assert _one(lay, batch=0, k_new=None, v_new=None, plan=kvq.Plan(4, 256, 0), ws_bytes=0) == 0
+
+
+@needs_lib
+def test_decode_launches():
+    """kv_decode_attn: one launch for small int8 units and plans, two otherwise."""
+    def n(w, plan=None, batch=None):
+        lay = _layout(w)
+        plan = plan or kvq.kvq_plan(lay, w.batch, w.n_q_heads, w.max_ctx, w.window, 256)
+        return kvq.kvq_decode_launches(lay, w.batch if batch is None else batch, w.n_q_heads, plan)
+    assert n(wl.WORKLOADS["tiny"]) == 1                               # 4 heads x 64 dims, 2 splits
+    assert n(wl.WORKLOADS["gemma"].with_(n_q_heads=4)) == 1           # 4 x 256
+    assert n(wl.WORKLOADS["gemma"]) == 2                              # 8 x 256: measured faster as two
+    assert n(wl.WORKLOADS["long"]) == 2                               # 128 splits
+    assert n(wl.WORKLOADS["mixed_k8v32"].with_(max_ctx=512)) == 2     # fp32 store
+    assert n(wl.WORKLOADS["long_q4"].with_(max_ctx=512)) == 2         # 4-bit stores
+    t = wl.WORKLOADS["tiny"]
+    assert n(t, kvq.Plan(8, 32, 1 * 8 * 8 * 66 * 4)) == 1
+    assert n(t, kvq.Plan(9, 32, 1 * 8 * 9 * 66 * 4)) == 2
+    assert n(t, batch=0) == 0
+    lay = _layout(t)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_decode_launches(lay, 1, 7, kvq.Plan(2, 128, 1 << 20))    # heads not a multiple of kv heads
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_decode_launches(lay, 1, 8, kvq.Plan(2, 128, 16))         # plan workspace too small
+
+
+def test_arrive_count():
+    lay = kvq.make_layout(2, 128, 1024, 3)
+    assert kvq.arrive_count(lay, 3, 8) == 3 * 2 * 1
+    assert kvq.arrive_count(lay, 3, 40) == 3 * 2 * 2   # 20 query heads per kv head: two blocks of 16
+    assert kvq.arrive_count(lay, 0, 8) == 1
 
 
 @needs_lib
