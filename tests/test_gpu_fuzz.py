@@ -4,7 +4,8 @@ k8v4), scale group, kv heads and GQA group size (one or two 16-head blocks),
 batch with ragged lengths (empty contexts included), sliding windows, slot
 width and layout order. Each configuration runs decode (planner plan and a
 forced split count), the fused decode step (its cache bit-identical to
-kv_quant_append's) and, where the stores allow it, chunk attention (planner
+kv_quant_append's), the same step through kv_decode_attn (both plans) and,
+where the stores allow it, chunk attention (planner
 plan and 96-position splits); outputs within 2e-3 of the oracle.
 
 genie-ai-runtime v1.3.0 "split-K decode attention" and "Details" (windows,
@@ -100,6 +101,21 @@ def test_random_configuration(i):
     for name in ("k", "v", "k_scales", "v_scales"):
         if cache[name] is not None:
             assert torch.equal(cache[name].view(torch.uint8), fused[name].view(torch.uint8)), name
+
+    # the same step through kv_decode_attn (one launch where its rule allows,
+    # else partials + reduce), under the planner's plan and the forced one;
+    # the arrival counters are left at zero
+    arrive = torch.zeros(kvq.arrive_count(lay, w.batch, w.n_q_heads), dtype=torch.int32, device="cuda")
+    for pl in (None, plan):
+        one = {k: (None if t is None else t.clone()) for k, t in cache.items()}
+        got = kvq.decode(lay, one, qd, ld, w.window, sm, plan=pl, n_cu=ks.n_cu(), new_kv=(k_new, v_new),
+                         arrive=arrive)
+        torch.cuda.synchronize()
+        assert np.abs(got.cpu().numpy().astype(np.float64) - want).max() <= TOL
+        assert int(torch.count_nonzero(arrive)) == 0
+        for name in ("k", "v", "k_scales", "v_scales"):
+            if cache[name] is not None:
+                assert torch.equal(cache[name].view(torch.uint8), one[name].view(torch.uint8)), name
 
     # chunk attention (int8 or 4-bit stores): the last n_tok tokens of each
     # context, for a chunk of 1-40 tokens and a verify window of at most 32
