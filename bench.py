@@ -353,8 +353,8 @@ def secondary_workloads(kvq, kvq_setup, wl, n_cu, steps):
         two = timed(w, lens, lay, caches, k_new, v_new)
         res[key] = {"context": L, "window": w.window, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                     "head_dim": w.head_dim, "cache_copies": COPIES,
-                    "step": "kv_decode_attn (append, partials, combine: one launch for units of <= 1024 "
-                            "head x dim values, else partials + reduce)",
+                    "step": "kv_decode_attn (append, partials and the combine in one launch: plans of <= 8 "
+                            "splits over int8 stores, query heads in units of <= 512 / head_dim)",
                     **timed(w, lens, lay, caches, k_new, v_new, single_parity(w, L, lay, caches[-1]), one_call=True),
                     "two_call_us_per_step": two["us_per_step"],
                     "two_call_step": "kv_append_decode_splitk + kv_decode_reduce"}

@@ -271,19 +271,17 @@ int kv_decode_reduce(const kvq_layout* layout, const void* ws, int64_t ws_bytes,
  * kv_decode_attn_splitk (both null), followed by kv_decode_reduce, computes
  * with the same plan, up to the order of the fp32 sums of the combine; the
  * cache rows appended are bit-identical to theirs.
- * Plans of at most 8 splits over int8 K and V stores whose units (sequence,
- * kv head, block of up to 16 query heads) hold at most 1024 (query head x
- * dim) values -- e.g. 4 heads x 256 dims, 16 x 64 -- run as ONE kernel
- * launch: every workgroup writes its partial through to memory and counts its
- * arrival in d_arrive, and the last workgroup of each unit combines that
- * unit's splits and writes its rows of out (the genie reduce's arithmetic,
- * inside the partial kernel; no workgroup waits for another). Other plans and
- * stores run the partial kernel and the reduce, two launches (measured faster
- * there); kvq_decode_launches tells which.
- *   d_arrive  device uint32 [batch * n_kv_heads * ceil((n_q_heads / n_kv_heads)
- *             / 16)], 4-byte aligned: zero before the first call that uses it;
- *             every call leaves it zero. Calls that share it (or ws) must not
- *             overlap on the device.
+ * Plans of at most 8 splits over int8 K and V stores run as ONE kernel
+ * launch: the query heads of a kv head are taken in units of at most
+ * 512 / head_dim of them (16 at most), every workgroup writes its unit's
+ * partial through to memory and counts its arrival in d_arrive, and the last
+ * workgroup of each unit combines that unit's splits and writes its rows of
+ * out (the genie reduce's arithmetic, inside the partial kernel; no
+ * workgroup waits for another). Other plans and stores run the partial
+ * kernel and the reduce, two launches; kvq_decode_launches tells which.
+ *   d_arrive  device uint32 [batch * n_q_heads], 4-byte aligned: zero before
+ *             the first call that uses it; every call leaves it zero. Calls
+ *             that share it (or ws) must not overlap on the device.
  *   out       fp16 [batch][n_q_heads][head_dim], contiguous, 16-byte aligned.
  *   other arguments as for kv_append_decode_splitk; k_new and v_new are both
  *   null or both non-null (KVQ_ERR_NULL otherwise).

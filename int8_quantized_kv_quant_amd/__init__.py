@@ -232,8 +232,8 @@ def kv_decode_attn(layout: Layout, k_store, v_store, k_scales, v_scales, k_new, 
                    n_q_heads: int, seq_lens, window: int, sm_scale: float, plan: Plan, ws, ws_bytes: int,
                    arrive, out, stream=None) -> None:
     """Append (k_new, v_new non-None) + partials + combine into out in one call;
-    arrive: zeroed int32/uint32 device counters, one per (sequence, kv head,
-    16-head block), left zero by every call."""
+    arrive: zeroed int32/uint32 device counters (arrive_count of them), left
+    zero by every call."""
     _check("kv_decode_attn", load().kv_decode_attn(
         ctypes.byref(layout.c()), _ptr(k_store), _ptr(v_store), _ptr(k_scales), _ptr(v_scales), _ptr(k_new),
         _ptr(v_new), _ptr(q), batch, n_q_heads, _ptr(seq_lens), window, sm_scale, ctypes.byref(plan.c()), _ptr(ws),
@@ -249,9 +249,8 @@ def kvq_decode_launches(layout: Layout, batch: int, n_q_heads: int, plan: Plan) 
 
 
 def arrive_count(layout: Layout, batch: int, n_q_heads: int) -> int:
-    """Number of kv_decode_attn arrival counters: batch * n_kv_heads * ceil(G / 16)."""
-    g = n_q_heads // layout.n_kv_heads
-    return max(1, batch * layout.n_kv_heads * ((g + 15) // 16))
+    """Number of kv_decode_attn arrival counters: batch * n_q_heads."""
+    return max(1, batch * n_q_heads)
 
 
 def kv_decode_attn_static(layout: Layout, k_store, v_store, k_scales, v_scales, q, batch: int, n_q_heads: int,

@@ -102,6 +102,7 @@ struct PartialArgs {
   uint16_t* out;
   uint32_t* arrive;
   uint32_t ws_bytes;
+  int32_t rows_per_block;  // query heads per head block (<= 16)
 };
 
 // Cache policy of the one-launch step's partial stores and loads: device scope
@@ -250,8 +251,11 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
   // Decode: heads hblk * 16 .. of kv head hk, at context seq_lens[b]. Chunk:
   // flat rows fr0 + r = t * G + h of kv head hk; token t sits at s0 + t and
   // attends [max(0, s0 + t + 1 - window) (window > 0), s0 + t + 1).
-  const int fr0 = hblk * 16 * RB;
-  const int nh = CHUNK ? min(16 * RB, a.T * a.G - fr0) : min(16, a.G - fr0);
+  // Query rows per head block: 16, or fewer in the one-launch step
+  // (a.rows_per_block), so that a unit's partial stays small.
+  const int RPB = ONE ? a.rows_per_block : 16;
+  const int fr0 = hblk * RPB * RB;
+  const int nh = CHUNK ? min(16 * RB, a.T * a.G - fr0) : min(RPB, a.G - fr0);
   const int hq0 = hk * a.G + fr0;
   const int64_t row0 = ((int64_t)b * a.n_q + hq0) * a.n_splits + split;
   float2* const ml = reinterpret_cast<float2*>(a.ws_ml);
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(NW * 64) void kvq_partial_kernel(PartialArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (threadIdx.x == 0) {
-        uint32_t* cnt = a.arrive + ((int64_t)b * a.n_kv + hk) * a.head_blocks + hblk;
+        uint32_t* cnt = a.arrive + ((int64_t)b * a.n_kv + hk) * a.head_blocks + hblk;  // < batch * n_q
         const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = old + 1u == (uint32_t)a.n_splits;
         if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -816,7 +820,11 @@ int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store
   PartialArgs a{};
   a.out = out;
   a.arrive = arrive;
-  if (out) a.ws_bytes = (uint32_t)workspace_bytes(batch, n_q_heads, plan.n_splits, L.head_dim);
+  a.rows_per_block = kHeadsPerBlock;
+  if (out) {
+    a.ws_bytes = (uint32_t)workspace_bytes(batch, n_q_heads, plan.n_splits, L.head_dim);
+    a.rows_per_block = one_launch_rows(L.head_dim, n_q_heads / L.n_kv_heads);
+  }
   a.k_store = k_store;
   a.v_store = v_store;
   a.k_scales = k_scales;
@@ -838,7 +846,7 @@ int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store
   a.n_kv = L.n_kv_heads;
   a.G = n_q_heads / L.n_kv_heads;
   a.n_q = n_q_heads;
-  a.head_blocks = (a.G + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  a.head_blocks = (a.G + a.rows_per_block - 1) / a.rows_per_block;
   a.n_splits = plan.n_splits;
   a.chunk = plan.chunk;
   a.window = window;

@@ -170,18 +170,26 @@ int launch_partial(const kvq_layout& L, const void* k_store, const void* v_store
                    const int32_t* d_seq_lens, int32_t window, float sm_scale, const kvq_plan_t& plan,
                    void* ws, void* stream, uint16_t* out = nullptr, uint32_t* arrive = nullptr);
 
+// The one-launch step of kv_decode_attn: query heads per unit (sequence, kv
+// head, head block), at most kOneLaunchMaxRowValues (query head x dim) values
+// per unit: min(G, 16, 512 / head_dim) -- 2 heads at head_dim 256, 4 at 128,
+// 8 at 64. Every workgroup writes its unit's partial through to memory, and
+// measured against the partials + reduce that hand-off pays when the partial
+// is small: with 8 heads x 256 dims per unit (8 KB per split) one launch was
+// 0.3-0.7 us slower per step, with 4 x 256 0.2-0.7 us faster and with
+// 2 x 256 faster again (Gemma 4K 9.8 -> 8.9 us); 1 x 256 ties with 2 x 256.
+constexpr int kOneLaunchMaxRowValues = 512;
+inline int one_launch_rows(int64_t head_dim, int64_t G) {
+  int64_t r = G < kHeadsPerBlock ? G : kHeadsPerBlock;
+  if (r * head_dim > kOneLaunchMaxRowValues) r = kOneLaunchMaxRowValues / head_dim;
+  return (int)(r > 0 ? r : 1);
+}
+
 // Whether kv_decode_attn runs the plan as one launch: int8 K and V stores, at
-// most kOneLaunchMaxSplits splits, units of at most kOneLaunchMaxRowValues
-// (query head x dim) values, and a partial region that one buffer resource
-// covers. (Measured against the two launches: one launch is 0.2-0.7 us faster
-// per step with 4 KB of fp32 partial per split and unit -- 4 heads x 256 dims,
-// 16 x 64, 4 x 128 -- and 0.3-0.7 us slower with 8 KB, 8 heads x 256 dims.)
-constexpr int kOneLaunchMaxRowValues = 1024;
+// most kOneLaunchMaxSplits splits, and a partial region that one buffer
+// resource covers.
 inline bool one_launch_ok(const kvq_layout& L, int64_t batch, int64_t n_q_heads, const kvq_plan_t& plan) {
-  const int64_t G = n_q_heads / L.n_kv_heads;
-  const int64_t rows = G < kHeadsPerBlock ? G : kHeadsPerBlock;
   return L.k_dtype == KVQ_STORE_INT8 && L.v_dtype == KVQ_STORE_INT8 && plan.n_splits <= kOneLaunchMaxSplits &&
-         rows * L.head_dim <= kOneLaunchMaxRowValues &&
          workspace_bytes(batch, n_q_heads, plan.n_splits, L.head_dim) <= 0x7fffffff;
 }
 

@@ -92,21 +92,23 @@ def _check(w, lens, out_a, out_b):
             assert not out_a[b].any()
 
 
-GEMMA_G4 = wl.WORKLOADS["gemma"].with_(n_q_heads=4)   # 4 heads x 256 dims per unit: one launch
+GEMMA = wl.WORKLOADS["gemma"]   # 8 query heads of head_dim 256 per kv head: four 2-head units
 
 # name: (workload, contexts, launches of kv_decode_attn under the planner's plan)
 CASES = {
-    "tiny": (wl.WORKLOADS["tiny"], [256], 1),
-    "gemma_g4_512": (GEMMA_G4.with_(max_ctx=512), [512], 1),
-    "gemma_g4_1024": (GEMMA_G4.with_(max_ctx=1024), [1024], 1),
-    "gemma_g4_4096": (GEMMA_G4, [4096], 1),
-    "gemma_g4_ragged": (GEMMA_G4.with_(batch=3, max_ctx=2048), [1, 700, 2048], 1),
-    # 20 query heads per kv head at head_dim 64: two head blocks (16 + 4 rows),
-    # each its own unit with its own counter
+    "tiny": (wl.WORKLOADS["tiny"], [256], 1),                     # one 4-head unit per kv head
+    "gemma_512": (GEMMA.with_(max_ctx=512), [512], 1),
+    "gemma_1024": (GEMMA.with_(max_ctx=1024), [1024], 1),
+    "gemma_4096": (GEMMA, [4096], 1),
+    "gemma_ragged": (GEMMA.with_(batch=3, max_ctx=2048), [1, 700, 2048], 1),
+    # 5 query heads per kv head at head_dim 256: units of 2, 2 and 1 heads
+    "gqa5_d256": (wl.Workload("gqa5", 2, 10, 2, 256, 256, 64, 1024, 0, 173, contexts=(1024,)), [1000, 77], 1),
+    # 20 query heads per kv head at head_dim 64: units of 8, 8 and 4 heads
     "gqa20": (wl.Workload("gqa20", 2, 40, 2, 64, 64, 64, 1024, 0, 171, contexts=(1024,)), [1000, 333], 1),
+    # 16 heads per kv head at head_dim 128: four 4-head units
+    "gqa16_d128": (wl.Workload("gqa16", 1, 16, 1, 128, 128, 64, 1024, 0, 174, contexts=(1024,)), [1024], 1),
     "ragged_empty": (wl.WORKLOADS["batched"].with_(batch=4, max_ctx=512), [512, 0, 1, 300], 1),
-    # two launches through the same call: 8 heads x 256 dims per unit, an fp32 store
-    "gemma_4096": (wl.WORKLOADS["gemma"], [4096], 2),
+    # two launches through the same call: an fp32 store
     "k8v32": (wl.WORKLOADS["mixed_k8v32"].with_(max_ctx=2048), [1500], 2),
 }
 
@@ -134,7 +136,7 @@ def test_forced_split_counts(n_splits, chunk):
     for the shorter sequences), two launches beyond; every one against the
     oracle."""
     import int8_quantized_kv_quant_amd as kvq
-    w = wl.Workload("forced", 3, 8, 2, 256, 256, 64, 1024, 0, 172, contexts=(1024,))
+    w = wl.Workload("forced", 3, 16, 2, 256, 256, 64, 1024, 0, 172, contexts=(1024,))
     lens = np.array([1024, 200, 641], dtype=np.int64)
     plan = kvq.Plan(n_splits, chunk, w.batch * w.n_q_heads * n_splits * (w.head_dim + 2) * 4)
     assert _launches(w, plan) == (1 if n_splits <= 8 else 2)
@@ -162,7 +164,7 @@ def test_one_launch_step_in_a_graph():
     runs it), the counters back at zero after every replay."""
     import int8_quantized_kv_quant_amd as kvq
     import kvq_setup as ks
-    w = GEMMA_G4
+    w = GEMMA
     L0 = 3000
     lay, cache = ks.fill_cache(w, np.array([L0 + 8]), upto=np.array([L0 - 1]))
     plan = kvq.kvq_plan(lay, 1, w.n_q_heads, w.max_ctx, w.window, ks.n_cu())

@@ -257,9 +257,8 @@ def test_decode_launches():
         lay = _layout(w)
         plan = plan or kvq.kvq_plan(lay, w.batch, w.n_q_heads, w.max_ctx, w.window, 256)
         return kvq.kvq_decode_launches(lay, w.batch if batch is None else batch, w.n_q_heads, plan)
-    assert n(wl.WORKLOADS["tiny"]) == 1                               # 4 heads x 64 dims, 2 splits
-    assert n(wl.WORKLOADS["gemma"].with_(n_q_heads=4)) == 1           # 4 x 256
-    assert n(wl.WORKLOADS["gemma"]) == 2                              # 8 x 256: measured faster as two
+    assert n(wl.WORKLOADS["tiny"]) == 1                               # 2 splits
+    assert n(wl.WORKLOADS["gemma"]) == 1                              # 4 splits (four 2-head units)
     assert n(wl.WORKLOADS["long"]) == 2                               # 128 splits
     assert n(wl.WORKLOADS["mixed_k8v32"].with_(max_ctx=512)) == 2     # fp32 store
     assert n(wl.WORKLOADS["long_q4"].with_(max_ctx=512)) == 2         # 4-bit stores
@@ -276,8 +275,8 @@ def test_decode_launches():
 
 def test_arrive_count():
     lay = kvq.make_layout(2, 128, 1024, 3)
-    assert kvq.arrive_count(lay, 3, 8) == 3 * 2 * 1
-    assert kvq.arrive_count(lay, 3, 40) == 3 * 2 * 2   # 20 query heads per kv head: two blocks of 16
+    assert kvq.arrive_count(lay, 3, 8) == 3 * 8
+    assert kvq.arrive_count(lay, 3, 40) == 3 * 40
     assert kvq.arrive_count(lay, 0, 8) == 1
 
 
